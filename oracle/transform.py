@@ -1,0 +1,82 @@
+"""Basis of the transform coder (oracle, float64).
+
+Pages: KV-COBRA project page, "How KV-COBRA Works": calibration takes a
+per-head SVD of prefill keys; at inference each key is rotated and truncated
+with H V^T; the "Hadamard rotation" paragraph folds a Walsh-Hadamard transform
+with a fixed random sign flip into the projection; the "Attention-KL
+reordering" paragraph weights direction i by sigma^2_Q,i * sigma^2_K,i (KL) or
+by the eigenvalue lambda_i (MSE) and sorts the basis by that weight.  SPECTRA
+abstract: rotate the cache into a coordinate system computed from its own
+statistics.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """Walsh-Hadamard matrix of order n (a power of two) in Sylvester's natural order.
+
+    H_1 = [1],  H_2m = [[H_m, H_m], [H_m, -H_m]]  (entries +-1, H H^T = n I).
+    """
+    if n < 1 or n & (n - 1):
+        raise ValueError("Hadamard order must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def eigenbasis(cov: np.ndarray):
+    """Eigenvalues (descending) and eigenvectors (columns) of a symmetric covariance.
+
+    The right singular vectors of a centred sample matrix are the eigenvectors
+    of its covariance, so this is the per-head SVD basis of the calibration
+    paragraph computed from the covariance.
+    """
+    w, v = np.linalg.eigh(np.asarray(cov, np.float64))
+    order = np.argsort(w)[::-1]
+    return w[order], v[:, order]
+
+
+def direction_weights(lam: np.ndarray, vecs: np.ndarray, query_cov=None) -> np.ndarray:
+    """Per-direction weight: lambda_i (MSE) or sigma^2_Q,i * lambda_i (attention KL).
+
+    sigma^2_Q,i is the query variance along key eigenvector e_i, e_i^T Sigma_Q e_i.
+    """
+    if query_cov is None:
+        return np.asarray(lam, np.float64).copy()
+    sq = np.einsum("ij,ik,kj->j", vecs, np.asarray(query_cov, np.float64), vecs)
+    return sq * lam
+
+
+def ordered_basis(cov: np.ndarray, query_cov=None):
+    """Eigenvectors of ``cov`` sorted by decreasing direction weight, with the weights.
+
+    Returns (weights, vectors) -- vectors are columns; stable sort keeps the
+    eigenvalue order among equal weights.
+    """
+    lam, vecs = eigenbasis(cov)
+    w = direction_weights(lam, vecs, query_cov)
+    order = np.argsort(-w, kind="stable")
+    return w[order], vecs[:, order]
+
+
+def folded_basis(vecs: np.ndarray, r: int, signs: np.ndarray) -> np.ndarray:
+    """P = E_r D_s H_r / sqrt(r): d x r basis with the random-sign Hadamard folded in.
+
+    The code coordinates of a vector x are c = P^T x = (H_r / sqrt(r)) D_s E_r^T x:
+    project onto the top-r directions, flip signs, then apply the normalised
+    Hadamard.  P has orthonormal columns.
+    """
+    e = np.asarray(vecs, np.float64)[:, :r]
+    s = np.asarray(signs, np.float64)
+    if s.shape != (r,) or not np.all(np.abs(s) == 1.0):
+        raise ValueError("signs must be r values in {-1, +1}")
+    return (e * s[None, :]) @ sylvester_hadamard(r) / np.sqrt(r)
+
+
+def basis_for_head(cov, r, signs, query_cov=None) -> np.ndarray:
+    """Full calibration of one head for a given rank: ordered eigenbasis, then the fold."""
+    _, vecs = ordered_basis(cov, query_cov)
+    return folded_basis(vecs, r, signs)

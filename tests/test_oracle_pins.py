@@ -1,0 +1,346 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics (no GPU).
+
+Each test fixes one part of the oracle against something other than its own
+code: closed forms, hand-worked examples (tests/golden), brute force on tiny
+inputs, or a textbook special case.
+"""
+import itertools
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import workloads as W
+from conftest import read_golden
+from oracle import allocation, attention, codec, packing, quantizer, transform
+
+
+# ---------------------------------------------------------------- Hadamard
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64, 128])
+def test_hadamard_orthogonality_exact(n):
+    h = transform.sylvester_hadamard(n)
+    assert np.array_equal(h @ h.T, n * np.eye(n))
+
+
+@pytest.mark.parametrize("n", [2, 8, 64, 128])
+def test_hadamard_closed_form(n):
+    # Sylvester's natural order: H[i, j] = (-1)^popcount(i & j)
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i & j)
+    assert np.array_equal(transform.sylvester_hadamard(n), (-1.0) ** pc)
+
+
+@pytest.mark.parametrize("r", [16, 32, 64, 128])
+def test_signed_normalized_hadamard_is_orthogonal(r):
+    s = W.random_basis_signs(r, r)
+    m = (s[:, None] * transform.sylvester_hadamard(r)) / np.sqrt(r)
+    assert np.abs(m @ m.T - np.eye(r)).max() < 1e-15
+
+
+# ---------------------------------------------------------------- basis
+@pytest.mark.parametrize("r", [16, 32, 64, 128])
+def test_folded_basis_orthonormal_and_spans_top_eigenvectors(r):
+    cov = W.random_covariance(7, 128)
+    lam, vecs = transform.eigenbasis(cov)
+    p = transform.basis_for_head(cov, r, W.random_basis_signs(3, r))
+    assert np.abs(p.T @ p - np.eye(r)).max() < 1e-13
+    er = vecs[:, :r]
+    assert np.abs(p @ p.T - er @ er.T).max() < 1e-12
+    # eigen-decomposition really diagonalises the covariance, descending
+    assert np.all(np.diff(lam) <= 1e-15)
+    assert np.abs(cov @ vecs - vecs * lam[None, :]).max() < 1e-12
+
+
+@pytest.mark.parametrize("r", [16, 64])
+def test_truncation_error_matches_tail_eigenvalues(r):
+    wl = W.TINY
+    cov = W.covariance(wl, "K", 0)
+    lam, _ = transform.eigenbasis(cov)
+    p = transform.basis_for_head(cov, r, W.hadamard_signs(wl, "K", 0, r))
+    x = W.tokens(wl, "K", 0, 0, 0, 100_000, dtype="f64")
+    resid = x - (x @ p) @ p.T
+    emp = (resid ** 2).sum(axis=1).mean()
+    assert emp == pytest.approx(lam[r:].sum(), rel=0.02)
+
+
+def test_generated_covariance_matches_samples():
+    for wl in (W.TINY, W.QWEN_T128K):
+        cov = W.covariance(wl, "V", 1 % wl.n_kv_heads)
+        x = W.tokens(wl, "V", 0, 1 % wl.n_kv_heads, 0, 60_000, dtype="f64")
+        emp = x.T @ x / len(x)
+        scale = np.sqrt(np.outer(np.diag(cov), np.diag(cov)))
+        assert np.abs(emp - cov).max() / scale.max() < 0.05
+
+
+def test_kl_weights_use_query_variance_along_key_directions():
+    cov = W.random_covariance(11, 16)
+    qcov = W.random_covariance(12, 16, alpha=0.7)
+    lam, vecs = transform.eigenbasis(cov)
+    w = transform.direction_weights(lam, vecs, qcov)
+    # sigma^2_Q,i is the variance of e_i . q, checked by sampling q ~ N(0, Sigma_Q)
+    rng = np.random.default_rng(0)
+    q = rng.multivariate_normal(np.zeros(16), qcov, size=200_000)
+    sq = ((q @ vecs) ** 2).mean(axis=0)
+    assert np.allclose(w, sq * lam, rtol=0.03)
+    ws, vs = transform.ordered_basis(cov, qcov)
+    assert np.all(np.diff(ws) <= 0)
+    assert np.allclose(transform.direction_weights(lam, vecs), lam)
+
+
+# ---------------------------------------------------------------- fp16 rounding
+def test_fp16_round_is_single_rounding_ties_to_even():
+    one = 1.0
+    ulp = 2.0 ** -10
+    mid = one + ulp / 2  # midpoint between 1 and 1 + 2^-10
+    assert quantizer.fp16_round(mid) == 1.0                     # tie -> even (1.0)
+    assert quantizer.fp16_round(mid + 2.0 ** -40) == 1.0 + ulp  # above midpoint by less than a float32 ulp
+    assert quantizer.fp16_round(mid - 2.0 ** -40) == 1.0
+    mid2 = one + 1.5 * ulp                                       # tie between odd and even -> even (1 + 2 ulp)
+    assert quantizer.fp16_round(mid2) == 1.0 + 2 * ulp
+    # subnormals: spacing 2^-24
+    assert quantizer.fp16_round(2.5 * 2.0 ** -24) == 2 * 2.0 ** -24
+    assert quantizer.fp16_round(2.5 * 2.0 ** -24 + 2.0 ** -60) == 3 * 2.0 ** -24
+    # bit patterns
+    assert int(quantizer.fp16_bits(1.0)) == 0x3C00
+    assert int(quantizer.fp16_bits(-2.0)) == 0xC000
+    assert int(quantizer.fp16_bits(2.0 ** -24)) == 0x0001
+
+
+# ---------------------------------------------------------------- quantizer
+def test_quantizer_golden_examples():
+    rows = read_golden("quantizer_examples.txt")
+    assert len(rows) >= 9
+    for b, coords, mu, sigma, codes in rows:
+        c = np.array([float(v) for v in coords.split()])
+        m, s, k = quantizer.quantize(c, int(b))
+        assert m == float(mu), (coords, m)
+        assert s == float(sigma), (coords, s)
+        assert k.tolist() == [int(v) for v in codes.split()], (coords, k)
+
+
+def test_q_of_b_matches_textbook_uniform_quantizer():
+    # textbook b-bit quantizer on U[0,1): 2^b cells of width 2^-b, reconstruction at cell midpoints
+    x = W.uniform_coords(1, 400_000, 1)[:, 0]
+    for b in (2, 4, 8):
+        cells = np.floor(x * 2 ** b)
+        xhat = (cells + 0.5) / 2 ** b
+        mse = ((x - xhat) ** 2).mean()
+        assert mse / quantizer.q_noise(b) == pytest.approx(1.0, abs=0.01)
+
+
+@pytest.mark.parametrize("b", [2, 4, 8])
+def test_deployed_quantizer_noise_closed_form(b):
+    r = 32
+    n = 100_000
+    x = W.uniform_coords(2, n, r)
+    mu, sigma, codes = quantizer.quantize(x, b)
+    xhat = quantizer.dequantize(mu, sigma, codes)
+    mse = ((x - xhat) ** 2).mean()
+    L = 2 ** b
+    # interior points uniform on [min, max] (error uniform over one step), the two
+    # extremes reproduced; range of r uniforms ~ Beta(r-1, 2): E[R^2] = (r-1) r / ((r+1)(r+2))
+    expect = quantizer.q_noise(b) * (L / (L - 1)) ** 2 * ((r - 2) / r) * ((r - 1) * r / ((r + 1) * (r + 2)))
+    assert mse / expect == pytest.approx(1.0, abs=0.02)
+
+
+def test_quantizer_error_bound_and_range():
+    x = W.random_coords(5, 3000, 64).astype(np.float64)
+    for b in range(2, 9):
+        mu, sigma, codes = quantizer.quantize(x, b)
+        xhat = quantizer.dequantize(mu, sigma, codes)
+        assert codes.min() >= 0 and codes.max() <= 2 ** b - 1
+        # every coordinate inside [mu, mu + (2^b-1) sigma] is within half a step
+        top = mu + (2 ** b - 1) * sigma
+        inside = (x >= mu[:, None]) & (x <= top[:, None])
+        err = np.abs(x - xhat)
+        half = np.broadcast_to(sigma[:, None] / 2 * (1 + 1e-12), err.shape)
+        assert np.all(err[inside] <= half[inside])
+        # only the extremes can fall outside (fp16 rounding of min and step); they stay close
+        assert inside.mean() > 0.95
+        slack = np.broadcast_to((sigma + 2.0 ** -10 * (np.abs(mu) + (2 ** b - 1) * sigma))[:, None], err.shape)
+        assert np.all(err[~inside] <= slack[~inside])
+        # the fp16 header is exactly what is stored
+        assert np.array_equal(quantizer.fp16_round(mu), mu)
+        assert np.array_equal(quantizer.fp16_round(sigma), sigma)
+
+
+# ---------------------------------------------------------------- packing
+def test_pack_golden_examples():
+    for r, b, mu, sigma, codes, words in read_golden("pack_examples.txt"):
+        r, b = int(r), int(b)
+        c = np.array([int(v) for v in codes.split()])
+        assert len(c) == r
+        rec = packing.pack(np.array(float(mu)), np.array(float(sigma)), c, b)
+        want = [int(w, 16) for w in words.split()]
+        assert len(want) == packing.record_words(r, b)
+        assert [int(v) for v in rec] == want
+
+
+def _bigint_pack(codes, b, w):
+    """Independent packer: the code stream as one Python integer, cut into 32-bit words."""
+    acc = 0
+    for j, c in enumerate(codes):
+        acc |= int(c) << (j * b)
+    return [(acc >> (32 * i)) & 0xFFFFFFFF for i in range(w - 1)]
+
+
+@pytest.mark.parametrize("r,b", list(itertools.product([16, 32, 64, 128], range(2, 9))))
+def test_pack_matches_bigint_and_round_trips(r, b):
+    codes = W.random_codes(r * 10 + b, 40, r, b)
+    x = W.random_coords(b, 40, r).astype(np.float64)
+    mu, sigma, _ = quantizer.quantize(x, b)
+    rec = packing.pack(mu, sigma, codes, b)
+    w = packing.record_words(r, b)
+    assert rec.shape == (40, w)
+    for t in range(40):
+        assert rec[t, 1:].tolist() == _bigint_pack(codes[t], b, w)
+    m2, s2, c2 = packing.unpack(rec, r, b)
+    assert np.array_equal(m2, mu) and np.array_equal(s2, sigma) and np.array_equal(c2, codes)
+    assert packing.padding_is_zero(rec, r, b)
+
+
+def test_record_words():
+    assert packing.record_words(16, 4) == 3
+    assert packing.record_words(32, 4) == 5
+    assert packing.record_words(128, 2) == 9
+    assert packing.record_words(16, 6) == 4
+    assert packing.record_words(128, 8) == 33
+
+
+# ---------------------------------------------------------------- attention
+def _textbook(q, k, v, scale):
+    # softmax(q . k_t * scale) weighted sum of v_t, written out from the definition
+    logits = np.array([scale * sum(qi * ki for qi, ki in zip(q, kt)) for kt in k])
+    w = np.exp(logits - logits.max())
+    w = w / w.sum()
+    return (w[:, None] * v).sum(axis=0)
+
+
+def test_full_rank_unquantized_reproduces_exact_attention():
+    d, T = 128, 300
+    wl = W.TINY
+    cov = W.covariance(wl, "K", 0)
+    pk = transform.basis_for_head(cov, d, W.hadamard_signs(wl, "K", 0, d))
+    pv = transform.basis_for_head(W.covariance(wl, "V", 0), d, W.hadamard_signs(wl, "V", 0, d))
+    k = W.tokens(wl, "K", 0, 0, 0, T, dtype="f64")
+    v = W.tokens(wl, "V", 0, 0, 0, T, dtype="f64")
+    q = W.random_vectors(1, (d,))
+    scale = 1 / np.sqrt(d)
+    o = attention.attend_coords(q, pk, codec.project(k, pk), pv, codec.project(v, pv), scale)
+    ref = _textbook(q, k, v, scale)
+    assert np.abs(o - ref).max() / np.abs(ref).max() < 1e-12
+    # scores themselves: (P^T q).(P^T k) = q.k
+    s1 = codec.project(k, pk) @ (pk.T @ q)
+    assert np.abs(s1 - k @ q).max() / np.abs(k @ q).max() < 1e-12
+
+
+def test_attention_invariants():
+    rng = np.random.default_rng(3)
+    d, T, r = 128, 257, 32
+    pk = transform.folded_basis(transform.eigenbasis(W.random_covariance(1, d))[1], r, W.random_basis_signs(1, r))
+    pv = transform.folded_basis(transform.eigenbasis(W.random_covariance(2, d))[1], r, W.random_basis_signs(2, r))
+    ck = rng.normal(size=(T, r))
+    cv = rng.normal(size=(T, r))
+    q = rng.normal(size=d)
+    o = attention.attend_coords(q, pk, ck, pv, cv, 0.1)
+    perm = rng.permutation(T)
+    assert np.allclose(attention.attend_coords(q, pk, ck[perm], pv, cv[perm], 0.1), o, rtol=1e-13, atol=1e-15)
+    # a single token returns its own value
+    assert np.allclose(attention.attend_coords(q, pk, ck[:1], pv, cv[:1], 0.1), pv @ cv[0])
+    # adding a constant to every score leaves the output unchanged (shift q along a direction
+    # orthogonal to nothing is hard; instead duplicate every token: weights unchanged)
+    o2 = attention.attend_coords(q, pk, np.vstack([ck, ck]), pv, np.vstack([cv, cv]), 0.1)
+    assert np.allclose(o2, o, rtol=1e-12)
+
+
+def test_gqa_head_equals_single_head_on_its_kv_head():
+    wl = W.TINY
+    d, T = 128, 64
+    alloc = [(16, 4, 32, 4), (32, 8, 16, 2)]
+    B, cap = 2, 64
+    g = 3
+    bases_k, bases_v, caches_k, caches_v = [], [], [], []
+    rk, bk, rv, bv = zip(*alloc)
+    ck_flat = np.zeros(codec.region_offsets(rk, bk, B, cap)[-1], np.uint32)
+    cv_flat = np.zeros(codec.region_offsets(rv, bv, B, cap)[-1], np.uint32)
+    for h, (a, b1, c, b2) in enumerate(alloc):
+        pk = transform.basis_for_head(W.random_covariance(10 + h, d), a, W.random_basis_signs(h, a)).astype(np.float32)
+        pv = transform.basis_for_head(W.random_covariance(20 + h, d), c, W.random_basis_signs(h + 5, c)).astype(np.float32)
+        bases_k.append(pk)
+        bases_v.append(pv)
+        for b in range(B):
+            k = W.tokens(wl, "K", b, 0, 0, T, dtype="f64") + h
+            v = W.tokens(wl, "V", b, 0, 0, T, dtype="f64") - h
+            s0, s1, _ = codec.record_slice(rk, bk, B, cap, h, b, 0, T)
+            ck_flat[s0:s1] = codec.encode_tokens(k, pk, b1).reshape(-1)
+            s0, s1, _ = codec.record_slice(rv, bv, B, cap, h, b, 0, T)
+            cv_flat[s0:s1] = codec.encode_tokens(v, pv, b2).reshape(-1)
+    q = W.random_vectors(4, (B, 2 * g, d))
+    out = attention.attend_cache(q, bases_k, bases_v, ck_flat, cv_flat, alloc, B, cap, T, 0.088)
+    for b in range(B):
+        for hq in range(2 * g):
+            h = hq // g
+            s0, s1, wk = codec.record_slice(rk, bk, B, cap, h, b, 0, T)
+            t0, t1, wv = codec.record_slice(rv, bv, B, cap, h, b, 0, T)
+            kh = codec.decode_records(ck_flat[s0:s1].reshape(T, wk), rk[h], bk[h]) @ bases_k[h].astype(np.float64).T
+            vh = codec.decode_records(cv_flat[t0:t1].reshape(T, wv), rv[h], bv[h]) @ bases_v[h].astype(np.float64).T
+            ref = _textbook(q[b, hq], kh, vh, 0.088)
+            assert np.abs(out[b, hq] - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+# ---------------------------------------------------------------- allocation
+def test_distortion_golden():
+    for w, r, b, frac in read_golden("distortion_examples.txt"):
+        wv = [float(v) for v in w.split()]
+        num, den = frac.split("/")
+        assert allocation.distortion(wv, int(r), int(b)) == pytest.approx(float(Fraction(int(num), int(den))), rel=1e-15)
+
+
+def _brute_force(w, budget, ranks):
+    d = len(w)
+    best = None
+    for r in ranks:
+        for b in range(2, 9):
+            if r * b > budget:
+                continue
+            tail = sum(w[r:])
+            head = sum(w[:r])
+            dist = tail + head / (12 * 4 ** b)
+            key = (dist, r * b, r)
+            if best is None or key < best[0]:
+                best = (key, r, b)
+    return best
+
+
+@pytest.mark.parametrize("d", [8, 16])
+def test_c1_equals_brute_force(d):
+    for seed in range(12):
+        w = W.random_weights(seed * 31 + d, d)
+        for ranks in (None, [r for r in (2, 4, 8, 16) if r <= d]):
+            rr = list(range(2, d + 1, 2)) if ranks is None else ranks
+            for budget in range(0, 8 * d + 1):
+                bf = _brute_force(list(w), budget, rr)
+                if bf is None:
+                    with pytest.raises(ValueError):
+                        allocation.c1(w, budget, ranks)
+                    continue
+                r, b, dist = allocation.c1(w, budget, ranks)
+                assert (r, b) == (bf[1], bf[2]), (seed, budget)
+                assert dist == pytest.approx(bf[0][0], rel=1e-12)
+
+
+def test_c1_on_generated_heads_uses_the_budget():
+    wl = W.LLAMA_T32K
+    for h in range(wl.n_kv_heads):
+        lam, _ = transform.eigenbasis(W.covariance(wl, "K", h))
+        r, b, _ = allocation.c1(lam, 256, W.C1_RANKS)
+        assert r * b <= 256 and (r, b) in {(16, 8), (32, 8), (64, 4), (128, 2)}
+
+
+# ---------------------------------------------------------------- layout
+def test_region_offsets_and_record_slices():
+    rk, bk = [16, 128, 16], [4, 2, 6]
+    off = codec.region_offsets(rk, bk, 2, 8)
+    assert off.tolist() == [0, 2 * 8 * 3, 2 * 8 * 3 + 2 * 8 * 9, 2 * 8 * 3 + 2 * 8 * 9 + 2 * 8 * 4]
+    s0, s1, w = codec.record_slice(rk, bk, 2, 8, 1, 1, 2, 5)
+    assert w == 9 and s0 == 48 + (1 * 8 + 2) * 9 and s1 == s0 + 3 * 9
