@@ -1,0 +1,255 @@
+"""Decode-attention throughput over the transform-coded KV cache on one MI355X.
+
+One step = one decode step of one layer at 128K context: kv_append of the new
+token's key and value (encode: project -> quantize -> pack) followed by
+kv_attend_decode over the T+1 compressed records of every (sequence, KV head)
+(query projection, split-K attention over packed codes, log-sum-exp combine
+and value back-projection).  Inputs are resident in HBM before timing starts;
+steps rotate over several layer caches (>= 1 GB in total) so that no step is
+served from the 256 MB Infinity Cache.
+
+Prints one JSON line (metric, value, roofline, cpu_baseline, ...); details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn compressed-KV GB/s (% of HBM peak) + context tokens/s @128K"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pick_workload(name: str) -> W.Workload:
+    table = {
+        "tiny": W.TINY,
+        "llama-32k": W.LLAMA_T32K,
+        "qwen-128k": W.QWEN_T128K,
+        "llama-prefill-r32b8": W.llama_prefill(32, 8),
+        "llama-prefill-r64b4": W.llama_prefill(64, 4),
+    }
+    for bpd in W.ALL_BUDGETS:
+        table[f"llama-128k-{bpd:g}bpd"] = W.llama_t128k(bpd)
+    if name not in table:
+        raise SystemExit(f"unknown workload {name}; choose from {sorted(table)}")
+    return table[name]
+
+
+def calibrate(wl: W.Workload):
+    from decode_attention_04_amd import calib
+
+    alloc, bk, bv = [], [], []
+    for h in range(wl.n_kv_heads):
+        fixed = wl.allocation[1][h] if wl.allocation[0] == "fixed" else None
+        a, pk, pv = calib.calibrate_head(
+            W.covariance(wl, "K", h), W.covariance(wl, "V", h),
+            lambda r, h=h: W.hadamard_signs(wl, "K", h, r), lambda r, h=h: W.hadamard_signs(wl, "V", h, r),
+            wl.allocation, W.query_covariance(wl, h), fixed=fixed, head_dim=wl.head_dim)
+        alloc.append(a)
+        bk.append(pk)
+        bv.append(pv)
+    return alloc, bk, bv
+
+
+def step_bytes(wl, alloc, T):
+    """Algorithmic HBM bytes of one decode step: attention part and append part."""
+    from decode_attention_04_amd import kv_record_words
+
+    B, hq, d = wl.batch, wl.n_q_heads, wl.head_dim
+    esz = 4 if wl.dtype == "f32" else 2
+    rec = sum(4 * (kv_record_words(a[0], a[1]) + kv_record_words(a[2], a[3])) for a in alloc)
+    basis = sum(4 * d * (a[0] + a[2]) for a in alloc)
+    attend = B * T * rec + B * hq * d * esz + basis + B * hq * d * 4
+    append = B * wl.n_kv_heads * 2 * d * esz + B * rec + basis
+    return attend, append
+
+
+def cpu_baseline(wl, alloc, bk, bv, T, budget_s=12.0):
+    """The oracle (float64 numpy, one BLAS thread) on whole (sequence, KV head) units of the same workload."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention, codec
+
+    q = W.query_array(wl, 0).astype(np.float64)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    done, secs, nbytes = 0, 0.0, 0
+    units = [(b, h) for b in range(wl.batch) for h in range(wl.n_kv_heads)]
+    with threadpool_limits(limits=1):
+        for b, h in units:
+            rk, b_k, rv, b_v = alloc[h]
+            xk = W.tokens(wl, "K", b, h, 0, T)
+            xv = W.tokens(wl, "V", b, h, 0, T)
+            rec_k = np.concatenate([codec.encode_tokens(xk[i:i + 16384], bk[h], b_k) for i in range(0, T, 16384)])
+            rec_v = np.concatenate([codec.encode_tokens(xv[i:i + 16384], bv[h], b_v) for i in range(0, T, 16384)])
+            g = wl.group
+            t0 = time.perf_counter()
+            attention.attend_head_records(q[b, h * g:(h + 1) * g], bk[h], rec_k, rk, b_k, bv[h], rec_v, rv, b_v, scale)
+            secs += time.perf_counter() - t0
+            nbytes += (rec_k.nbytes + rec_v.nbytes)
+            done += 1
+            if secs >= budget_s:
+                break
+    return {
+        "value": round(nbytes / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {len(units)} (sequence, KV head) units, attention of its {wl.group} query heads "
+                  f"over {T} records each ({nbytes / 1e6:.1f} MB of records, {secs:.2f} s); oracle encode not timed",
+        "seconds": round(secs, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama-128k-2bpd")
+    ap.add_argument("--replica-bytes", type=float, default=1.2e9, help="total bytes of rotated layer caches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        raise SystemExit(2)
+
+    import torch
+
+    import decode_attention_04_amd as K
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = pick_workload(args.workload)
+    T = wl.context
+    B, hkv, hq, d = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim
+    t_setup = time.time()
+    alloc, bk, bv = calibrate(wl)
+    log(f"workload {wl.name}: allocation (rk, bk, rv, bv) per KV head {alloc}")
+    lay = K.Layout(hkv, hq, B, T + 1, alloc)
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if wl.dtype == "f32" else torch.float16
+    pk = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bk])).to(dev)
+    pv = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bv])).to(dev)
+
+    # prefill: keys/values of the context, encoded on the GPU
+    ck0 = torch.zeros(K.kv_cache_bytes(lay, 0) // 4, dtype=torch.int32, device=dev)
+    cv0 = torch.zeros(K.kv_cache_bytes(lay, 1) // 4, dtype=torch.int32, device=dev)
+    chunk = max(1, (1 << 15))
+    enc_ms = 0.0
+    for t0 in range(0, T, chunk):
+        n = min(chunk, T - t0)
+        kx = torch.from_numpy(W.kv_array(wl, "K", t0, n)).to(dev)
+        vx = torch.from_numpy(W.kv_array(wl, "V", t0, n)).to(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        K.kv_encode(lay, kx, vx, n, t0, pk, pv, ck0, cv0)
+        e1.record()
+        torch.cuda.synchronize()
+        enc_ms += e0.elapsed_time(e1)
+        del kx, vx
+    enc_in_bytes = 2 * B * hkv * T * d * (4 if wl.dtype == "f32" else 2)
+    cache_bytes = (ck0.numel() + cv0.numel()) * 4
+    n_rep = max(2, int(math.ceil(args.replica_bytes / cache_bytes)))
+    caches = [(ck0, cv0)] + [(ck0.clone(), cv0.clone()) for _ in range(n_rep - 1)]
+    k_new = torch.from_numpy(W.kv_array(wl, "K", T, 1)[:, :, 0]).to(dev)
+    v_new = torch.from_numpy(W.kv_array(wl, "V", T, 1)[:, :, 0]).to(dev)
+    q = torch.from_numpy(W.query_array(wl, 0)).to(dev)
+    out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(K.kv_workspace_bytes(lay, T + 1) // 4, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f} s; {n_rep} layer caches of {cache_bytes / 1e6:.1f} MB; "
+        f"GPU encode of the {T}-token prefill: {enc_ms:.3f} ms ({enc_in_bytes / enc_ms / 1e6:.1f} GB/s of fp input)")
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        ck, cv = caches[i % n_rep]
+        K.kv_append(lay, k_new, v_new, T, pk, pv, ck, cv)
+        if ev is not None:
+            ev[0].record(stream)
+        K.kv_attend_decode(lay, q, T + 1, pk, pv, ck, cv, scale, out, ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    att_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = total_ms / args.steps
+    att_avg = float(np.mean(att_ms))
+    attend_bytes, append_bytes = step_bytes(wl, alloc, T + 1)
+    gbs = (attend_bytes + append_bytes) / (ms_step * 1e-3) / 1e9
+    att_gbs = attend_bytes / (att_avg * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us (attend {att_avg * 1e3:.1f} us, p10 {np.percentile(att_ms, 10) * 1e3:.1f} "
+        f"p90 {np.percentile(att_ms, 90) * 1e3:.1f}); {gbs:.1f} GB/s step, {att_gbs:.1f} GB/s attend "
+        f"({100 * att_gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, alloc, bk, bv, T + 1, args.cpu_seconds)
+        log(f"cpu baseline (oracle): {cpu}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "batch": B, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d, "context_tokens": T + 1,
+            "allocation": [list(a) for a in alloc],
+            "step": "kv_append (1 token) + kv_attend_decode",
+            "layer_caches_rotated": n_rep,
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "context_tokens_per_s": round(B * (T + 1) / (ms_step * 1e-3), 1),
+            "bytes_per_step": attend_bytes + append_bytes,
+            "encode_prefill_ms": round(enc_ms, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kv_attend_decode",
+            "achieved": round(att_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(att_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

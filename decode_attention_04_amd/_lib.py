@@ -1,0 +1,187 @@
+"""ctypes binding of libkvtc.so: argument marshalling only.
+
+Every computation of the encode and decode path runs in the HIP kernels of
+the library; this module converts tensors to device pointers, passes the
+caller's current HIP stream and turns non-zero status codes into exceptions.
+Importing it fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvtc.so")
+
+KV_OK, KV_ERR_INVALID, KV_ERR_UNSUPPORTED, KV_ERR_CAPACITY, KV_ERR_DEVICE = range(5)
+KV_F32, KV_F16 = 0, 1
+
+EXPORTED = (
+    "kv_record_words", "kv_cache_bytes", "kv_workspace_bytes", "kv_workspace_bytes_split",
+    "kv_encode", "kv_append", "kv_attend_decode", "kv_attend_decode_split",
+    "kv_quantize_pack", "kv_unpack", "kv_last_error",
+)
+
+
+class KvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"kvtc status {status}: {message}")
+        self.status = status
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [
+        ("head_dim", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("capacity", ctypes.c_int64),
+        ("rank_k", ctypes.POINTER(ctypes.c_int32)),
+        ("bits_k", ctypes.POINTER(ctypes.c_int32)),
+        ("rank_v", ctypes.POINTER(ctypes.c_int32)),
+        ("bits_v", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m decode_attention_04_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L = ctypes.POINTER(_Layout)
+    sig = {
+        "kv_record_words": (i32, [i32, i32]),
+        "kv_cache_bytes": (i32, [L, i32, ctypes.POINTER(sz)]),
+        "kv_workspace_bytes": (i32, [L, i64, ctypes.POINTER(sz)]),
+        "kv_workspace_bytes_split": (i32, [L, i64, i64, ctypes.POINTER(sz)]),
+        "kv_encode": (i32, [L, P, P, i32, i64, i64, P, P, P, P, P]),
+        "kv_append": (i32, [L, P, P, i32, i64, P, P, P, P, P]),
+        "kv_attend_decode": (i32, [L, P, i32, i64, P, P, P, P, f32, P, P, sz, P]),
+        "kv_attend_decode_split": (i32, [L, P, i32, i64, i64, P, P, P, P, f32, P, P, sz, P]),
+        "kv_quantize_pack": (i32, [P, i64, i32, i32, P, P]),
+        "kv_unpack": (i32, [P, i64, i32, i32, P, P, P]),
+        "kv_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int):
+    if status != KV_OK:
+        raise KvError(status, _lib.kv_last_error().decode())
+
+
+class Layout:
+    """Shape and per-head (rank, bits) allocation of one layer's compressed cache.
+
+    ``alloc`` lists (rank_k, bits_k, rank_v, bits_v) per KV head.
+    """
+
+    def __init__(self, n_kv_heads: int, n_q_heads: int, batch: int, capacity: int,
+                 alloc: Sequence[Tuple[int, int, int, int]], head_dim: int = 128):
+        if len(alloc) != n_kv_heads:
+            raise ValueError("alloc needs one (rank_k, bits_k, rank_v, bits_v) per KV head")
+        self.head_dim, self.n_kv_heads, self.n_q_heads = head_dim, n_kv_heads, n_q_heads
+        self.batch, self.capacity = batch, capacity
+        self.alloc = [tuple(int(x) for x in a) for a in alloc]
+        arr = ctypes.c_int32 * n_kv_heads
+        self._rk = arr(*[a[0] for a in self.alloc])
+        self._bk = arr(*[a[1] for a in self.alloc])
+        self._rv = arr(*[a[2] for a in self.alloc])
+        self._bv = arr(*[a[3] for a in self.alloc])
+        self._c = _Layout(head_dim, n_kv_heads, n_q_heads, batch, capacity,
+                          self._rk, self._bk, self._rv, self._bv)
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    def ref(self):
+        return ctypes.byref(self._c)
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if hasattr(t, "is_cuda") and not t.is_cuda:
+        raise ValueError("tensor must live in device memory")
+    if hasattr(t, "is_contiguous") and not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return KV_F32
+    if t.dtype == torch.float16:
+        return KV_F16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def kv_record_words(rank: int, bits: int) -> int:
+    return int(_lib.kv_record_words(rank, bits))
+
+
+def kv_cache_bytes(layout: Layout, which: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.kv_cache_bytes(layout.ref(), which, ctypes.byref(out)))
+    return out.value
+
+
+def kv_workspace_bytes(layout: Layout, n_tokens: int, split_tokens: int = 0) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.kv_workspace_bytes_split(layout.ref(), n_tokens, split_tokens, ctypes.byref(out)))
+    return out.value
+
+
+def kv_encode(layout, k, v, n_tokens, pos0, basis_k, basis_v, cache_k, cache_v, stream=None):
+    """Prefill encode of k, v [batch, n_kv_heads, n_tokens, head_dim] (float32 or float16)."""
+    _check(_lib.kv_encode(layout.ref(), _ptr(k), _ptr(v), _dtype_code(k), n_tokens, pos0,
+                          _ptr(basis_k), _ptr(basis_v), _ptr(cache_k), _ptr(cache_v), _stream(stream)))
+
+
+def kv_append(layout, k1, v1, pos, basis_k, basis_v, cache_k, cache_v, stream=None):
+    """Append one token per (sequence, head): k1, v1 [batch, n_kv_heads, head_dim]."""
+    _check(_lib.kv_append(layout.ref(), _ptr(k1), _ptr(v1), _dtype_code(k1), pos,
+                          _ptr(basis_k), _ptr(basis_v), _ptr(cache_k), _ptr(cache_v), _stream(stream)))
+
+
+def kv_attend_decode(layout, q, n_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale, out,
+                     workspace, split_tokens: int = 0, stream=None):
+    """Decode attention: q [batch, n_q_heads, head_dim] -> out (float32, same shape)."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.kv_attend_decode_split(layout.ref(), _ptr(q), _dtype_code(q), n_tokens, split_tokens,
+                                       _ptr(basis_k), _ptr(basis_v), _ptr(cache_k), _ptr(cache_v),
+                                       float(softmax_scale), _ptr(out), _ptr(workspace), nbytes,
+                                       _stream(stream)))
+
+
+def kv_quantize_pack(coords, rank, bits, records, stream=None):
+    """coords float32 [n, rank] -> records uint32/int32 [n, W]."""
+    n = coords.shape[0] if coords.dim() > 1 else 0
+    _check(_lib.kv_quantize_pack(_ptr(coords), n, rank, bits, _ptr(records), _stream(stream)))
+
+
+def kv_unpack(records, n, rank, bits, min_step, codes, stream=None):
+    """records [n, W] -> min_step int16/uint16 [n, 2] (fp16 bits) and codes uint8 [n, rank]."""
+    _check(_lib.kv_unpack(_ptr(records), n, rank, bits, _ptr(min_step), _ptr(codes), _stream(stream)))
+
+
+def raw():
+    """The underlying ctypes library handle (for ABI tests)."""
+    return _lib

@@ -1,0 +1,138 @@
+"""The C-ABI library loads, exports every declared symbol, and validates on the host (no GPU).
+
+Every call here fails validation (or is a pure size query) before anything is
+launched, so it runs without a device.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+from oracle import codec
+
+lib_mod = pytest.importorskip("decode_attention_04_amd._lib")
+L = lib_mod.raw()
+HEADER = os.path.join(ROOT, "include", "kvtc.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(lib_mod.EXPORTED)
+
+
+def test_record_words():
+    for r in (16, 32, 64, 128):
+        for b in range(2, 9):
+            assert lib_mod.kv_record_words(r, b) == 1 + (r * b + 31) // 32
+    for r, b in ((8, 4), (48, 4), (16, 1), (16, 9), (256, 2)):
+        assert lib_mod.kv_record_words(r, b) == 0
+
+
+def _layout(**kw):
+    args = dict(n_kv_heads=3, n_q_heads=12, batch=2, capacity=1000,
+                alloc=[(16, 4, 32, 4), (128, 2, 64, 4), (32, 8, 16, 6)])
+    args.update(kw)
+    return lib_mod.Layout(**args)
+
+
+def test_cache_bytes_match_the_oracle_layout():
+    lay = _layout()
+    rk, bk, rv, bv = zip(*lay.alloc)
+    assert lib_mod.kv_cache_bytes(lay, 0) == 4 * codec.region_offsets(rk, bk, 2, 1000)[-1]
+    assert lib_mod.kv_cache_bytes(lay, 1) == 4 * codec.region_offsets(rv, bv, 2, 1000)[-1]
+
+
+def test_workspace_grows_with_context_and_split_count():
+    lay = _layout()
+    w0 = lib_mod.kv_workspace_bytes(lay, 0)
+    w1 = lib_mod.kv_workspace_bytes(lay, 1000)
+    assert 0 < w0 <= w1
+    assert lib_mod.kv_workspace_bytes(lay, 1000, 256) >= lib_mod.kv_workspace_bytes(lay, 1000, 512)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), lib_mod.KV_ERR_UNSUPPORTED),
+    (dict(n_q_heads=13), lib_mod.KV_ERR_INVALID),
+    (dict(n_q_heads=3 * 17), lib_mod.KV_ERR_UNSUPPORTED),
+    (dict(alloc=[(16, 4, 32, 4), (48, 2, 64, 4), (32, 8, 16, 6)]), lib_mod.KV_ERR_UNSUPPORTED),
+    (dict(alloc=[(16, 4, 32, 9), (128, 2, 64, 4), (32, 8, 16, 6)]), lib_mod.KV_ERR_UNSUPPORTED),
+    (dict(alloc=[(16, 1, 32, 4), (128, 2, 64, 4), (32, 8, 16, 6)]), lib_mod.KV_ERR_UNSUPPORTED),
+    (dict(batch=0), lib_mod.KV_ERR_INVALID),
+    (dict(capacity=0), lib_mod.KV_ERR_INVALID),
+])
+def test_invalid_layouts_are_rejected(kw, status):
+    lay = _layout(**kw)
+    with pytest.raises(lib_mod.KvError) as e:
+        lib_mod.kv_cache_bytes(lay, 0)
+    assert e.value.status == status
+    assert L.kv_last_error().decode()
+
+
+def test_too_many_kv_heads():
+    lay = lib_mod.Layout(65, 65, 1, 16, [(16, 4, 16, 4)] * 65)
+    with pytest.raises(lib_mod.KvError) as e:
+        lib_mod.kv_workspace_bytes(lay, 16)
+    assert e.value.status == lib_mod.KV_ERR_UNSUPPORTED
+
+
+def test_null_layout_and_bad_which():
+    out = ctypes.c_size_t()
+    assert L.kv_cache_bytes(None, 0, ctypes.byref(out)) == lib_mod.KV_ERR_INVALID
+    assert L.kv_cache_bytes(_layout().ref(), 2, ctypes.byref(out)) == lib_mod.KV_ERR_INVALID
+    assert L.kv_cache_bytes(_layout().ref(), 1, ctypes.byref(out)) == lib_mod.KV_OK
+    assert L.kv_last_error().decode() == ""
+
+
+def test_encode_validation_happens_before_launch():
+    lay = _layout()
+    ref = lay.ref()
+    # positions past the capacity
+    assert L.kv_encode(ref, 16, 16, 1, 10, 995, 16, 16, 16, 16, None) == lib_mod.KV_ERR_CAPACITY
+    assert L.kv_encode(ref, 16, 16, 1, 1, -1, 16, 16, 16, 16, None) == lib_mod.KV_ERR_CAPACITY
+    assert L.kv_append(ref, 16, 16, 1, 1000, 16, 16, 16, 16, None) == lib_mod.KV_ERR_CAPACITY
+    # NULL pointers
+    assert L.kv_encode(ref, 0, 16, 1, 10, 0, 16, 16, 16, 16, None) == lib_mod.KV_ERR_INVALID
+    assert L.kv_encode(ref, 16, 16, 1, 10, 0, 16, 16, 0, 16, None) == lib_mod.KV_ERR_INVALID
+    # misaligned cache
+    assert L.kv_encode(ref, 16, 16, 1, 10, 0, 16, 16, 18, 16, None) == lib_mod.KV_ERR_INVALID
+    # unknown dtype
+    assert L.kv_encode(ref, 16, 16, 7, 10, 0, 16, 16, 16, 16, None) == lib_mod.KV_ERR_INVALID
+    # zero tokens: nothing to do, no launch
+    assert L.kv_encode(ref, 0, 0, 1, 0, 0, 0, 0, 0, 0, None) == lib_mod.KV_OK
+
+
+def test_attend_validation_happens_before_launch():
+    lay = _layout()
+    ref = lay.ref()
+    need = lib_mod.kv_workspace_bytes(lay, 500)
+    args = lambda T, ws_bytes, split=0, out=16, ws=16: (ref, 16, 1, T, split, 16, 16, 16, 16, 0.1, out, ws,
+                                                          ws_bytes, None)
+    assert L.kv_attend_decode_split(*args(1001, need)) == lib_mod.KV_ERR_CAPACITY
+    assert L.kv_attend_decode_split(*args(500, need - 4)) == lib_mod.KV_ERR_INVALID
+    assert "workspace" in L.kv_last_error().decode()
+    assert L.kv_attend_decode_split(*args(500, need, split=100)) == lib_mod.KV_ERR_INVALID
+    assert L.kv_attend_decode_split(*args(500, need, out=0)) == lib_mod.KV_ERR_INVALID
+    assert L.kv_attend_decode_split(*args(500, need, ws=8)) == lib_mod.KV_ERR_INVALID
+    assert L.kv_attend_decode_split(*args(-1, need)) == lib_mod.KV_ERR_INVALID
+
+
+def test_pack_validation():
+    assert L.kv_quantize_pack(16, 10, 48, 4, 16, None) == lib_mod.KV_ERR_UNSUPPORTED
+    assert L.kv_quantize_pack(16, 10, 16, 9, 16, None) == lib_mod.KV_ERR_UNSUPPORTED
+    assert L.kv_quantize_pack(0, 10, 16, 4, 16, None) == lib_mod.KV_ERR_INVALID
+    assert L.kv_quantize_pack(16, -1, 16, 4, 16, None) == lib_mod.KV_ERR_INVALID
+    assert L.kv_quantize_pack(0, 0, 16, 4, 0, None) == lib_mod.KV_OK
+    assert L.kv_unpack(16, 10, 16, 4, 0, 16, None) == lib_mod.KV_ERR_INVALID
+    assert L.kv_unpack(16, 10, 20, 4, 16, 16, None) == lib_mod.KV_ERR_UNSUPPORTED

@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+* quantize/pack and unpack: bit-exact for every (rank, bits) and the edge cases;
+* encode / append: headers exact, codes equal except at rounding ties (<= 1e-5
+  of codes, each off by one), records outside the written range untouched;
+* attention over an identical (oracle-built) cache: max over (sequence, query
+  head) of ||o_gpu - o_ref||_inf / ||o_ref||_inf <= 2e-3, for several split sizes;
+* end-to-end (GPU encode -> GPU attend vs oracle encode -> oracle attend).
+"""
+import numpy as np
+import pytest
+
+import harness as H
+import workloads as W
+from oracle import attention, codec, packing, quantizer, transform
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+REL_TOL = 2e-3        # attention output, max relative error per (sequence, query head)
+TIE_FRACTION = 1e-5   # codes allowed to differ (by one) at rounding ties
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_attention_04_amd as K
+    K.kv_record_words(16, 2)  # loads the library (fails loudly if it is missing)
+    return K
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ quantize / pack / unpack
+def _edge_rows(r, b):
+    L = 2 ** b - 1
+    rows = []
+    rows.append(np.full(r, 0.3))                                   # all equal: step 0
+    tie = np.zeros(r)
+    tie[1] = L
+    tie[2:] = (np.arange(r - 2) % L) + 0.5                          # exact half-way values
+    rows.append(tie)
+    rows.append(-np.abs(np.linspace(0.0, 5.0, r)))                 # negative values
+    mid = 1.0 + 2.0 ** -11                                         # min exactly between two fp16 values
+    rows.append(np.linspace(mid, mid + 3.0, r))
+    rows.append(np.linspace(1e-6, 3e-6, r))                        # subnormal fp16 step
+    rows.append(np.linspace(-3e4, 3e4, r))                         # large range
+    big = np.zeros(r)
+    big[0] = 1.0
+    rows.append(big)                                               # one non-zero coordinate
+    return np.array(rows, np.float32)
+
+
+@pytest.mark.parametrize("r", [16, 32, 64, 128])
+@pytest.mark.parametrize("b", list(range(2, 9)))
+def test_quantize_pack_bit_exact(K, r, b):
+    say(f"quantize_pack r={r} b={b}")
+    x = np.concatenate([W.random_coords(r * 16 + b, 1037, r), _edge_rows(r, b)])
+    n, w = len(x), packing.record_words(r, b)
+    rec = torch.empty((n, w), dtype=torch.int32, device="cuda")
+    K.kv_quantize_pack(H.dev(x), r, b, rec)
+    got = H.u32_host(rec)
+    mu, sg, codes = quantizer.quantize(x.astype(np.float64), b)
+    ref = packing.pack(mu, sg, codes, b)
+    bad = np.nonzero((got != ref).any(axis=1))[0]
+    assert len(bad) == 0, f"{len(bad)} records differ, first token {bad[:5]}"
+
+
+@pytest.mark.parametrize("r,b", [(16, 2), (16, 3), (32, 5), (64, 6), (128, 7), (128, 8), (64, 4)])
+def test_unpack_bit_exact(K, r, b):
+    say(f"unpack r={r} b={b}")
+    n = 777
+    codes = W.random_codes(5 + r + b, n, r, b)
+    x = W.random_coords(77, n, r).astype(np.float64)
+    mu, sg, _ = quantizer.quantize(x, b)
+    rec = packing.pack(mu, sg, codes, b)
+    ms = torch.empty((n, 2), dtype=torch.int16, device="cuda")
+    cg = torch.empty((n, r), dtype=torch.uint8, device="cuda")
+    K.kv_unpack(H.u32_dev(rec), n, r, b, ms, cg)
+    torch.cuda.synchronize()
+    ms_h = ms.cpu().numpy().view(np.uint16)
+    assert np.array_equal(ms_h[:, 0], quantizer.fp16_bits(mu).astype(np.uint16))
+    assert np.array_equal(ms_h[:, 1], quantizer.fp16_bits(sg).astype(np.uint16))
+    assert np.array_equal(cg.cpu().numpy().astype(np.int64), codes)
+
+
+# ------------------------------------------------------------------ layouts used below
+MIXED_ALLOC = [(16, 2, 128, 8), (32, 3, 64, 5), (64, 6, 32, 7), (128, 4, 16, 8)]
+
+
+def _mixed_bases(alloc, seed=0):
+    bk, bv = [], []
+    for h, (rk, _, rv, _) in enumerate(alloc):
+        ck = W.random_covariance(seed + 10 + h, 128)
+        cv = W.random_covariance(seed + 40 + h, 128)
+        bk.append(transform.basis_for_head(ck, rk, W.random_basis_signs(seed + h, rk)).astype(np.float32))
+        bv.append(transform.basis_for_head(cv, rv, W.random_basis_signs(seed + 50 + h, rv)).astype(np.float32))
+    return bk, bv
+
+
+def _compare_records(got, ref, r, b, what):
+    """Headers exact; codes equal except at rounding ties (<= TIE_FRACTION, off by one)."""
+    g_mu, g_sg, g_c = packing.unpack(got, r, b)
+    r_mu, r_sg, r_c = packing.unpack(ref, r, b)
+    hdr_bad = int(((g_mu != r_mu) | (g_sg != r_sg)).sum())
+    diff = np.abs(g_c - r_c)
+    assert hdr_bad == 0, f"{what}: {hdr_bad} headers differ"
+    assert diff.max(initial=0) <= 1, f"{what}: code off by {diff.max()}"
+    frac = (diff > 0).mean() if diff.size else 0.0
+    assert frac <= TIE_FRACTION, f"{what}: {frac:.2e} of codes differ"
+    return frac
+
+
+def _encode_case(K, wl_tokens, alloc, bases_k, bases_v, batch, cap, pos0, n, dtype):
+    hkv = len(alloc)
+    lay = K.Layout(hkv, hkv, batch, cap, alloc)
+    sentinel = np.uint32(0xA5A5A5A5)
+    nk = K.kv_cache_bytes(lay, 0) // 4
+    nv = K.kv_cache_bytes(lay, 1) // 4
+    ck = H.u32_dev(np.full(nk, sentinel, np.uint32))
+    cv = H.u32_dev(np.full(nv, sentinel, np.uint32))
+    kx = np.stack([np.stack([wl_tokens("K", b, h, n) for h in range(hkv)]) for b in range(batch)])
+    vx = np.stack([np.stack([wl_tokens("V", b, h, n) for h in range(hkv)]) for b in range(batch)])
+    tdt = torch.float32 if dtype == "f32" else torch.float16
+    K.kv_encode(lay, H.dev(kx, tdt), H.dev(vx, tdt), n, pos0, H.dev(codec.concat_bases(bases_k)),
+                H.dev(codec.concat_bases(bases_v)), ck, cv)
+    gk, gv = H.u32_host(ck), H.u32_host(cv)
+    rk, bk, rv, bv = zip(*alloc)
+    for tensor, got_all, ranks, bits, bases, x in (("K", gk, rk, bk, bases_k, kx), ("V", gv, rv, bv, bases_v, vx)):
+        for h in range(hkv):
+            for b in range(batch):
+                s0, s1, w = codec.record_slice(ranks, bits, batch, cap, h, b, pos0, pos0 + n)
+                ref = codec.encode_tokens(x[b, h].astype(np.float64), bases[h], bits[h])
+                _compare_records(got_all[s0:s1].reshape(n, w), ref, ranks[h], bits[h], f"{tensor} h{h} b{b}")
+                a0, _, _ = codec.record_slice(ranks, bits, batch, cap, h, b, 0, 0)
+                a1, _, _ = codec.record_slice(ranks, bits, batch, cap, h, b, cap, cap)
+                outside = np.concatenate([got_all[a0:s0], got_all[s1:a1]])
+                assert np.all(outside == sentinel), f"{tensor} h{h} b{b}: write outside the range"
+    return lay
+
+
+def test_encode_tiny_fp32_matches_oracle(K):
+    say("encode tiny-1head-T4096 fp32")
+    wl = W.TINY
+    alloc, bk, bv = H.oracle_calibrate(wl)
+    _encode_case(K, lambda t, b, h, n: W.tokens(wl, t, b, h, 0, n), alloc, bk, bv, 1, 4096, 0, 4096, "f32")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_encode_mixed_allocation_matches_oracle(K, dtype):
+    say(f"encode mixed allocation {dtype}")
+    wl = W.LLAMA_T32K
+    bk, bv = _mixed_bases(MIXED_ALLOC)
+    _encode_case(K, lambda t, b, h, n: W.tokens(wl, t, b, h, 0, n, dtype), MIXED_ALLOC, bk, bv,
+                 2, 1100, 37, 1001, dtype)
+
+
+def test_append_matches_oracle(K):
+    say("append mixed allocation")
+    wl = W.QWEN_T128K
+    alloc = [(128, 2, 128, 2), (16, 6, 16, 6)]
+    bk, bv = _mixed_bases(alloc, seed=3)
+    lay = _encode_case(K, lambda t, b, h, n: W.tokens(wl, t, b, h, 50, n), alloc, bk, bv, 3, 64, 63, 1, "f16")
+    assert lay.capacity == 64
+
+
+# ------------------------------------------------------------------ attention on an identical cache
+def _attend(K, lay, q, T, bases_k, bases_v, ck, cv, split=0, qdtype=torch.float16):
+    B, hq = lay.batch, lay.n_q_heads
+    out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(K.kv_workspace_bytes(lay, T, split) // 4, dtype=torch.float32, device="cuda")
+    K.kv_attend_decode(lay, H.dev(q, qdtype), T, H.dev(codec.concat_bases(bases_k)),
+                       H.dev(codec.concat_bases(bases_v)), ck, cv, H.SCALE, out, ws, split_tokens=split)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _attention_case(K, alloc, bases_k, bases_v, batch, g, cap, T, splits, qdtype="f16", seed=0, wl=W.LLAMA_T32K):
+    hkv = len(alloc)
+    ck_h, cv_h = H.oracle_cache(wl, alloc, bases_k, bases_v, batch, cap, T,
+                                kv={(t, b, h): W.tokens(wl, t, b, h % wl.n_kv_heads, 0, T)
+                                    for t in "KV" for b in range(batch) for h in range(hkv)})
+    q = W.random_vectors(seed, (batch, hkv * g, 128)).astype(np.float32 if qdtype == "f32" else np.float16)
+    ref = attention.attend_cache(q.astype(np.float64), bases_k, bases_v, ck_h, cv_h, alloc, batch, cap, T, H.SCALE)
+    lay = K.Layout(hkv, hkv * g, batch, cap, alloc)
+    ck, cv = H.u32_dev(ck_h), H.u32_dev(cv_h)
+    errs = {}
+    for split in splits:
+        got = _attend(K, lay, q, T, bases_k, bases_v, ck, cv, split,
+                      torch.float32 if qdtype == "f32" else torch.float16)
+        assert np.isfinite(got).all()
+        errs[split] = H.rel_err_per_head(got, ref)
+        say(f"  split={split} max rel err {errs[split]:.3e}")
+        assert errs[split] <= REL_TOL
+    return errs
+
+
+def test_attention_tiny_fp32(K):
+    say("attention tiny-1head-T4096 fp32")
+    wl = W.TINY
+    alloc, bk, bv = H.oracle_calibrate(wl)
+    _attention_case(K, alloc, bk, bv, 1, 1, 4096, 4096, [0, 256, 1024], qdtype="f32", wl=wl)
+
+
+def test_attention_mixed_allocations_gqa4(K):
+    say("attention mixed allocation g=4")
+    bk, bv = _mixed_bases(MIXED_ALLOC, seed=5)
+    _attention_case(K, MIXED_ALLOC, bk, bv, 2, 4, 3100, 3000, [0, 256, 768])
+
+
+def test_attention_gqa7_qwen_allocation(K):
+    say("attention g=7 (128,2)+(16,6)")
+    alloc = [(128, 2, 128, 2), (16, 6, 16, 6)]
+    bk, bv = _mixed_bases(alloc, seed=9)
+    _attention_case(K, alloc, bk, bv, 2, 7, 2000, 1999, [0, 512], wl=W.QWEN_T128K)
+
+
+def test_attention_every_bit_width(K):
+    say("attention all bit widths")
+    alloc = [(32, b, 64, 10 - b) for b in range(2, 9)]
+    bk, bv = _mixed_bases(alloc, seed=13)
+    _attention_case(K, alloc, bk, bv, 1, 2, 700, 700, [0, 256])
+
+
+@pytest.mark.parametrize("T", [1, 2, 255, 256, 257])
+def test_attention_short_and_ragged_contexts(K, T):
+    say(f"attention T={T}")
+    alloc = [(64, 4, 32, 8), (16, 8, 128, 2)]
+    bk, bv = _mixed_bases(alloc, seed=17)
+    _attention_case(K, alloc, bk, bv, 2, 3, T, T, [0])
+
+
+def test_attention_empty_context_is_zero(K):
+    say("attention T=0")
+    alloc = [(64, 4, 32, 8)]
+    bk, bv = _mixed_bases(alloc, seed=19)
+    lay = K.Layout(1, 2, 1, 16, alloc)
+    ck = H.u32_dev(np.zeros(K.kv_cache_bytes(lay, 0) // 4, np.uint32))
+    cv = H.u32_dev(np.zeros(K.kv_cache_bytes(lay, 1) // 4, np.uint32))
+    got = _attend(K, lay, W.random_vectors(1, (1, 2, 128)).astype(np.float16), 0, bk, bv, ck, cv)
+    assert np.array_equal(got, np.zeros_like(got))
+
+
+# ------------------------------------------------------------------ end to end
+def test_end_to_end_encode_append_attend(K):
+    say("end to end: encode + append + attend")
+    wl = W.LLAMA_T32K
+    alloc, bk, bv = H.oracle_calibrate(wl)
+    B, T = 1, 2000
+    lay = K.Layout(wl.n_kv_heads, wl.n_q_heads, B, T + 1, alloc)
+    ck = torch.zeros(K.kv_cache_bytes(lay, 0) // 4, dtype=torch.int32, device="cuda")
+    cv = torch.zeros(K.kv_cache_bytes(lay, 1) // 4, dtype=torch.int32, device="cuda")
+    kx = np.stack([np.stack([W.tokens(wl, "K", b, h, 0, T + 1) for h in range(wl.n_kv_heads)]) for b in range(B)])
+    vx = np.stack([np.stack([W.tokens(wl, "V", b, h, 0, T + 1) for h in range(wl.n_kv_heads)]) for b in range(B)])
+    pk, pv = H.dev(codec.concat_bases(bk)), H.dev(codec.concat_bases(bv))
+    K.kv_encode(lay, H.dev(kx[:, :, :T]), H.dev(vx[:, :, :T]), T, 0, pk, pv, ck, cv)
+    K.kv_append(lay, H.dev(kx[:, :, T]), H.dev(vx[:, :, T]), T, pk, pv, ck, cv)
+    q = W.query_array(wl, 0)
+    got = _attend(K, lay, q, T + 1, bk, bv, ck, cv)
+    ck_h, cv_h = H.oracle_cache(wl, alloc, bk, bv, B, T + 1, T + 1,
+                                kv={(t, b, h): (kx if t == "K" else vx)[b, h]
+                                    for t in "KV" for b in range(B) for h in range(wl.n_kv_heads)})
+    gk, gv = H.u32_host(ck), H.u32_host(cv)
+    rk, bits_k, rv, bits_v = zip(*alloc)
+    for h in range(wl.n_kv_heads):
+        s0, s1, w = codec.record_slice(rk, bits_k, B, T + 1, h, 0, 0, T + 1)
+        _compare_records(gk[s0:s1].reshape(-1, w), ck_h[s0:s1].reshape(-1, w), rk[h], bits_k[h], f"K h{h}")
+        s0, s1, w = codec.record_slice(rv, bits_v, B, T + 1, h, 0, 0, T + 1)
+        _compare_records(gv[s0:s1].reshape(-1, w), cv_h[s0:s1].reshape(-1, w), rv[h], bits_v[h], f"V h{h}")
+    ref = attention.attend_cache(q.astype(np.float64), bk, bv, ck_h, cv_h, alloc, B, T + 1, T + 1, H.SCALE)
+    err = H.rel_err_per_head(got, ref)
+    say(f"  end-to-end max rel err {err:.3e}")
+    assert err <= REL_TOL

@@ -287,3 +287,26 @@ def random_weights(seed: int, d: int) -> np.ndarray:
 
 def random_vectors(seed: int, shape: Sequence[int], dtype=np.float64) -> np.ndarray:
     return _rng(1006, seed, *shape).standard_normal(tuple(shape)).astype(dtype)
+
+
+def kv_array(wl: Workload, tensor: str, t0: int, n: int, dtype: Optional[str] = None,
+             threads: int = 8) -> np.ndarray:
+    """Keys or values of every (sequence, KV head) for tokens [t0, t0+n): array [B, Hkv, n, d]."""
+    import concurrent.futures as cf
+
+    dt = {"f64": np.float64, "f32": np.float32, "f16": np.float16}[dtype or wl.dtype]
+    out = np.empty((wl.batch, wl.n_kv_heads, n, wl.head_dim), dt)
+    units = [(b, h) for b in range(wl.batch) for h in range(wl.n_kv_heads)]
+
+    def fill(u):
+        b, h = u
+        out[b, h] = tokens(wl, tensor, b, h, t0, n, dtype)
+
+    with cf.ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, units))
+    return out
+
+
+def query_array(wl: Workload, step: int = 0, dtype: Optional[str] = None) -> np.ndarray:
+    """Queries of every sequence at decode step ``step``: array [B, Hq, d]."""
+    return np.stack([queries(wl, b, step, dtype) for b in range(wl.batch)])
