@@ -47,6 +47,13 @@ class _Layout(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m decode_attention_04_amd.build`")
+    # PyTorch ships its own HIP runtime under the same soname.  Loading it first makes
+    # the library bind to that runtime, so that both see the same devices, streams and
+    # allocations (two HIP runtimes in one process do not share device state).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     L = ctypes.POINTER(_Layout)
