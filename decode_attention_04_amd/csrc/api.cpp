@@ -88,6 +88,14 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
     bk_total += (int64_t)kHeadDim * rk;
     bv_total += (int64_t)kHeadDim * rv;
   }
+  // kernels address one (sequence, head) region with 32-bit byte offsets
+  for (int h = 0; h < L->n_kv_heads; ++h) {
+    const int64_t region = L->capacity * 4 * (int64_t)(out.table.h[h].wk > out.table.h[h].wv ? out.table.h[h].wk
+                                                                                            : out.table.h[h].wv);
+    if (region >= ((int64_t)1 << 31))
+      return fail(KV_ERR_UNSUPPORTED, "capacity %lld too large: one sequence's records of a head must stay below 2 GiB",
+                  (long long)L->capacity);
+  }
   out.words_k = wk_total;
   out.words_v = wv_total;
   out.basis_k_floats = bk_total;
@@ -95,11 +103,11 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
   return KV_OK;
 }
 
-// Default split-K size: enough workgroups to fill 256 CUs several times over,
-// each split a multiple of the 256-token tile.
+// Default split-K size: about two resident workgroups (8 waves) per CU on the
+// 256 CUs, each split a multiple of 256 tokens (64 per wave).
 int64_t default_split_tokens(const Layout& L, int64_t T) {
   const int64_t units = (int64_t)L.batch * L.n_kv;
-  const int64_t target = 2048;
+  const int64_t target = 512;
   int64_t ns = (target + units - 1) / units;
   if (ns < 1) ns = 1;
   int64_t st = (T + ns - 1) / ns;
