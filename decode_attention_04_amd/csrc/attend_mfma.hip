@@ -58,42 +58,53 @@ __device__ inline float uniform(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
-// ----------------------------------------------------------------- buffer loads
+// ----------------------------------------------------------------- record tiles in LDS
 // One buffer resource per (sequence, KV head) cache region: 32-bit byte offsets,
-// loads past the region return zero.
+// loads past the region return zero.  Tiles of 64 consecutive records are copied
+// HBM -> LDS with buffer_load_dwordx4 ... lds (16 bytes per lane, lane-contiguous
+// in LDS), so the copy of the next tile is in flight while the current one is
+// unpacked, and every unpacking access is an LDS read.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ inline uint32_t ld16(rsrc_t r, uint32_t off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+
+// Copy `nbytes` starting at byte `src` of the region to LDS `dst` (whole 16-byte
+// chunks: up to 1023 bytes past the end are copied too and never read).
+__device__ inline void tile_copy(rsrc_t r, uint32_t src, uint32_t nbytes, uint32_t* dst) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t n16 = (nbytes + 15u) >> 4;
+  for (uint32_t c = 0; c < n16; c += 64) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 4 * c), 16, (int)(src + 16u * (c + lane)), 0, 0, 0);
+  }
 }
-__device__ inline uint32_t ld32(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0); }
-__device__ inline u32x2 ld64(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0); }
-__device__ inline u32x4 ld128(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0); }
+
+__device__ inline void wait_tiles() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int N>
-__device__ inline void load_words(rsrc_t r, uint32_t off, uint32_t (&w)[N]) {
+__device__ inline void lds_words(const uint32_t* p, uint32_t (&w)[N]) {
   if constexpr (N == 1) {
-    w[0] = ld32(r, off);
+    w[0] = p[0];
   } else if constexpr (N == 2) {
-    const u32x2 a = ld64(r, off);
+    const u32x2a a = *(const u32x2a*)p;
     w[0] = a[0]; w[1] = a[1];
   } else {
 #pragma unroll
     for (int k = 0; k < N; k += 4) {
-      const u32x4 a = ld128(r, off + 4 * k);
+      const u32x4a a = *(const u32x4a*)(p + k);
       w[k] = a[0]; w[k + 1] = a[1]; w[k + 2] = a[2]; w[k + 3] = a[3];
     }
   }
 }
 
-// Adjacent codes at stream bit `bit` (general widths): low code in bits 0..B-1.
-__device__ inline uint32_t window(rsrc_t r, uint32_t rec_off, int bit) {
-  const u32x2 a = ld64(r, rec_off + 4u * (1 + (bit >> 5)));
-  return __builtin_amdgcn_alignbit(a[1], a[0], bit & 31);
+// B adjacent-code bits starting at stream bit `bit` of a record in LDS (low code in bits 0..).
+__device__ inline uint32_t lds_window(const uint32_t* rec, int bit) {
+  const uint32_t* p = rec + 1 + (bit >> 5);
+  return __builtin_amdgcn_alignbit(p[1], p[0], bit & 31);
 }
 
 // ----------------------------------------------------------------- code fields
@@ -135,26 +146,28 @@ __device__ inline void k_slot(int G, int nks, int ks, int p, int rk, bool& valid
   }
 }
 
-// ----------------------------------------------------------------- per-tile phases
+// ----------------------------------------------------------------- per-tile phases (records in LDS)
 // Scores of one 64-token tile: four 16-token sub-tiles, C[head][token] on the
 // matrix cores, written to S[token][GM] (log2 units before min/step are applied).
+// kt: the tile's records (wk words each); tokens past `nlast` read record nlast.
 template <int B, int NKS, int GM>
-__device__ __attribute__((always_inline)) inline void k_phase(rsrc_t rk_, uint32_t wkb, int t0, int tlast,
+__device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt, int wk, int nlast,
                                                               const u32x4 (&aq_hi)[4], const u32x4 (&aq_lo)[4],
                                                               float* S) {
   const int lane = threadIdx.x & 63, n = lane & 15, G = lane >> 4;
-  if constexpr (pow2_bits(B)) {
-    constexpr int PPW = Pow2<B>::kPerHalf;
-    constexpr int NWL = (NKS * 4 * B + 15) / 16;
-    const int base = G * NKS * 4;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      int tok = t0 + tt * 16 + n;
-      tok = tok < tlast ? tok : tlast;
+  for (int tt = 0; tt < 4; ++tt) {
+    int tok = tt * 16 + n;
+    tok = tok < nlast ? tok : nlast;
+    const uint32_t* rec = kt + tok * wk;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (pow2_bits(B)) {
+      constexpr int PPW = Pow2<B>::kPerHalf;
+      constexpr int NWL = (NKS * 4 * B + 15) / 16;
+      const int base = G * NKS * 4;
       uint32_t w[NWL];
-      load_words<NWL>(rk_, (uint32_t)tok * wkb + 4u * (1 + base / PPW), w);
+      lds_words<NWL>(rec + 1 + base / PPW, w);
       if constexpr (NKS * 4 < PPW) w[0] >>= (base % PPW) * B;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         u32x4 bop;
@@ -166,40 +179,31 @@ __device__ __attribute__((always_inline)) inline void k_phase(rsrc_t rk_, uint32
         acc = mfma(aq_hi[ks], bop, acc);
         acc = mfma(aq_lo[ks], bop, acc);
       }
-      if (4 * G < GM) *(f32x4*)(S + (tt * 16 + n) * GM + 4 * G) = acc;
-    }
-  } else {
-    // general widths: one window load per pair, one sub-tile in flight
-    constexpr uint32_t M = (1u << B) - 1u;
-#pragma unroll 1
-    for (int tt = 0; tt < 4; ++tt) {
-      int tok = t0 + tt * 16 + n;
-      tok = tok < tlast ? tok : tlast;
-      const uint32_t rec = (uint32_t)tok * wkb;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    } else {
+      constexpr uint32_t M = (1u << B) - 1u;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         u32x4 bop;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int pi = G * NKS * 4 + ks * 4 + p;
-          const uint32_t f = window(rk_, rec, 2 * pi * B);
+          const uint32_t f = lds_window(rec, 2 * pi * B);
           bop[p] = (f & M) | (((f >> B) & M) << 16);
         }
         acc = mfma(aq_hi[ks], bop, acc);
         acc = mfma(aq_lo[ks], bop, acc);
       }
-      if (4 * G < GM) *(f32x4*)(S + (tt * 16 + n) * GM + 4 * G) = acc;
     }
+    if (4 * G < GM) *(f32x4*)(S + (tt * 16 + n) * GM + 4 * G) = acc;
   }
 }
 
-// One 32-token value step (tokens t0 .. t0+31): for each N-tile of 16 codes the
-// B operand (lane n owns codes [n*NT, (n+1)*NT) of the 8 tokens of its lane
-// group, one aligned field of NT*B bits for power-of-two widths) and its two
+// One 32-token value step (tile tokens 32*kk .. 32*kk+31): for each N-tile of 16
+// codes the B operand (lane n owns codes [n*NT, (n+1)*NT) of the 8 tokens of its
+// lane group, one aligned field of NT*B bits for power-of-two widths) and its two
 // MFMAs with A = p*step_V (hi, lo).
 template <int B, int NT>
-__device__ __attribute__((always_inline)) inline void v_phase(rsrc_t rv_, uint32_t wvb, int t0, int tlast,
+__device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt, int wv, int kk, int nlast,
                                                               u32x4 ahi, u32x4 alo, f32x4 (&acc2)[8]) {
   const int lane = threadIdx.x & 63, n = lane & 15, G = lane >> 4;
   if constexpr (pow2_bits(B)) {
@@ -208,18 +212,18 @@ __device__ __attribute__((always_inline)) inline void v_phase(rsrc_t rv_, uint32
     uint32_t f0[8], f1[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      int tok = t0 + 8 * G + e;
-      tok = tok < tlast ? tok : tlast;
-      const uint32_t rec = (uint32_t)tok * wvb + 4u;
+      int tok = 32 * kk + 8 * G + e;
+      tok = tok < nlast ? tok : nlast;
+      const uint32_t* rec = vt + tok * wv + 1;
       f1[e] = 0u;
       if constexpr (FS <= 16) {
         const int bit = n * FS;
-        const uint32_t x = ld16(rv_, rec + 2u * (bit >> 4)) >> (bit & 15);
+        const uint32_t x = (uint32_t)((const uint16_t*)rec)[bit >> 4] >> (bit & 15);
         f0[e] = FS == 16 ? x : (x & ((1u << FS) - 1u));
       } else if constexpr (FS == 32) {
-        f0[e] = ld32(rv_, rec + 4u * n);
+        f0[e] = rec[n];
       } else {
-        const u32x2 a = ld64(rv_, rec + 8u * n);
+        const u32x2a a = *(const u32x2a*)(rec + 2 * n);
         f0[e] = a[0];
         f1[e] = a[1];
       }
@@ -240,29 +244,17 @@ __device__ __attribute__((always_inline)) inline void v_phase(rsrc_t rv_, uint32
     }
   } else {
     constexpr uint32_t M = (1u << B) - 1u;
-    const int fbit = n * NT * B;  // first bit of the lane's NT codes
-    uint32_t w0[8], w1[8], w2[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      int tok = t0 + 8 * G + e;
-      tok = tok < tlast ? tok : tlast;
-      const uint32_t off = (uint32_t)tok * wvb + 4u * (1 + (fbit >> 5));
-      const u32x2 a = ld64(rv_, off);
-      w0[e] = a[0];
-      w1[e] = a[1];
-      w2[e] = ld32(rv_, off + 8u);
-    }
-    const int o0 = fbit & 31;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int o = o0 + nt * B;  // < 32 + 56
+      const int bit = (n * NT + nt) * B;
       u32x4 bop;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const uint32_t ca = (o < 32 ? __builtin_amdgcn_alignbit(w1[2 * p], w0[2 * p], o)
-                                    : __builtin_amdgcn_alignbit(w2[2 * p], w1[2 * p], o - 32)) & M;
-        const uint32_t cb = (o < 32 ? __builtin_amdgcn_alignbit(w1[2 * p + 1], w0[2 * p + 1], o)
-                                    : __builtin_amdgcn_alignbit(w2[2 * p + 1], w1[2 * p + 1], o - 32)) & M;
+        int ta = 32 * kk + 8 * G + 2 * p, tb = ta + 1;
+        ta = ta < nlast ? ta : nlast;
+        tb = tb < nlast ? tb : nlast;
+        const uint32_t ca = lds_window(vt + ta * wv, bit) & M;
+        const uint32_t cb = lds_window(vt + tb * wv, bit) & M;
         bop[p] = ca | (cb << 16);
       }
       acc2[nt] = mfma(ahi, bop, acc2[nt]);
@@ -311,27 +303,35 @@ __device__ inline int v_shift(int B, int nt) {
 
 #define KVTC_K_CASE(B)                                                              \
   case B:                                                                           \
-    if (nks == 1) k_phase<B, 1, GM>(rk_, wkb, t0, tlast, aq_hi, aq_lo, S);          \
-    else if (nks == 2) k_phase<B, 2, GM>(rk_, wkb, t0, tlast, aq_hi, aq_lo, S);     \
-    else k_phase<B, 4, GM>(rk_, wkb, t0, tlast, aq_hi, aq_lo, S);                   \
+    if (nks == 1) k_phase<B, 1, GM>(kt, wk, nlast, aq_hi, aq_lo, S);                 \
+    else if (nks == 2) k_phase<B, 2, GM>(kt, wk, nlast, aq_hi, aq_lo, S);            \
+    else k_phase<B, 4, GM>(kt, wk, nlast, aq_hi, aq_lo, S);                          \
     break;
 #define KVTC_V_CASE(B)                                                              \
   case B:                                                                           \
-    if (NT == 1) v_phase<B, 1>(rv_, wvb, t0 + 32 * kk, tlast, ahi, alo, acc2);       \
-    else if (NT == 2) v_phase<B, 2>(rv_, wvb, t0 + 32 * kk, tlast, ahi, alo, acc2);  \
-    else if (NT == 4) v_phase<B, 4>(rv_, wvb, t0 + 32 * kk, tlast, ahi, alo, acc2);  \
-    else v_phase<B, 8>(rv_, wvb, t0 + 32 * kk, tlast, ahi, alo, acc2);               \
+    if (NT == 1) v_phase<B, 1>(vt, wv, kk, nlast, ahi, alo, acc2);                   \
+    else if (NT == 2) v_phase<B, 2>(vt, wv, kk, nlast, ahi, alo, acc2);              \
+    else if (NT == 4) v_phase<B, 4>(vt, wv, kk, nlast, ahi, alo, acc2);              \
+    else v_phase<B, 8>(vt, wv, kk, nlast, ahi, alo, acc2);                           \
     break;
 
+// Words of LDS per wave: tile buffers for K and V (a.nbuf each) and the score /
+// probability area (128 * GM words).
+__host__ __device__ inline int wave_lds_words(int kbuf_words, int vbuf_words, int nbuf, int gm) {
+  return nbuf * (kbuf_words + vbuf_words) + 128 * gm;
+}
+
 // ----------------------------------------------------------------- kernel
-// Grid (n_wg, n_kv_heads, batch), 256 threads; GM bounds the GQA group (g <= GM).
-// Workgroup x covers tokens [x*split_tokens, (x+1)*split_tokens), a quarter per
-// wave; each wave runs its own online softmax and the four states are merged in
-// LDS into one partial (m, l, o~[r_V]) per query head and split.
+// Grid (n_wg, n_kv_heads, batch), 256 threads; GM bounds the GQA group (g <= GM);
+// GEN adds the general-width (3, 5, 6, 7 bits) unpacking paths.  Workgroup x
+// covers tokens [x*split_tokens, (x+1)*split_tokens), a quarter per wave; each
+// wave streams its records through LDS in 64-token tiles and runs its own online
+// softmax; the four wave states are merged in LDS into one partial (m, l, o~[r_V])
+// per query head and split.
 template <int GM, bool GEN>
 __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
   extern __shared__ float lds[];
-  constexpr int WA = 128 * GM;  // words per wave area
+  const int WA = wave_lds_words(a.kbuf_words, a.vbuf_words, a.nbuf, GM);
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the token loop scalar
@@ -349,12 +349,33 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
   float* areas = lds + 64 + kWaves * 48;  // per wave: WA words
   float* wl = areas + wave * WA;
 
-  // ---- prologue: q~ = scale * log2(e) * P_K^T q of the g heads (raw q and q~ over the wave areas)
-  float* q_raw = areas;
-  float* qt = areas + GM * kHeadDim;
+  // ---- this wave's token range and cache regions; start streaming the first tile
+  const int wq = (int)(a.split_tokens / kWaves);
+  const int t_begin = (int)blockIdx.x * (int)a.split_tokens + wave * wq;
+  int t_end = t_begin + wq;
+  if (t_end > (int)a.n_tokens) t_end = (int)a.n_tokens;
+  const int wk = hd.wk, wv = hd.wv;
+  const uint32_t* kreg = a.cache_k + hd.base_k + (int64_t)b * a.capacity * wk;
+  const uint32_t* vreg = a.cache_v + hd.base_v + (int64_t)b * a.capacity * wv;
+  const rsrc_t rk_ = make_rsrc(kreg, (uint32_t)a.capacity * 4u * wk);
+  const rsrc_t rv_ = make_rsrc(vreg, (uint32_t)a.capacity * 4u * wv);
+  uint32_t* ktile = (uint32_t*)wl;                          // [nbuf][kbuf_words]
+  uint32_t* vtile = ktile + a.nbuf * a.kbuf_words;          // [nbuf][vbuf_words]
+  float* S = (float*)(vtile + a.nbuf * a.vbuf_words);       // [64][GM] fp32
+  _Float16* P = (_Float16*)(S + 64 * GM);                   // [2][GM][64] fp16, rows >= g stay zero
+
+  // ---- prologue: q~ = scale * log2(e) * P_K^T q of the g heads (raw q and q~ in the
+  // score areas of waves 0..3, which are not in use yet)
+  float* q_raw = (float*)((uint32_t*)areas + (WA - 128 * GM));     // wave 0's score area
+  float* qt = (float*)((uint32_t*)areas + WA + (WA - 128 * GM));   // wave 1's score area
   for (int i = tid; i < g * kHeadDim; i += 256) {
     const int64_t off = (bq0 + i / kHeadDim) * kHeadDim + (i % kHeadDim);
     q_raw[i] = a.dtype == 0 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
+  }
+  if (t_begin < t_end) {
+    const int n0 = (t_end - t_begin) < kTileT ? (t_end - t_begin) : kTileT;
+    tile_copy(rk_, (uint32_t)t_begin * 4u * wk, (uint32_t)n0 * 4u * wk, ktile);
+    tile_copy(rv_, (uint32_t)t_begin * 4u * wv, (uint32_t)n0 * 4u * wv, vtile);
   }
   __syncthreads();
   {
@@ -402,21 +423,8 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
     sq[hh] = uniform(sc[hh]);
     kf[hh] = uniform(sc[kMaxGroup + hh]);
   }
-  __syncthreads();  // q~ in the wave areas is no longer needed
-  float* S = wl;                               // [64][GM] fp32
-  _Float16* P = (_Float16*)(wl + 64 * GM);     // [2][GM][64] fp16, rows >= g stay zero
+  __syncthreads();  // the prologue's q and q~ are consumed
   for (int i = lane; i < GM * 64; i += 64) ((uint32_t*)P)[i] = 0u;
-
-  // ---- this wave's token range and cache regions
-  const int wq = (int)(a.split_tokens / kWaves);
-  const int t_begin = (int)blockIdx.x * (int)a.split_tokens + wave * wq;
-  int t_end = t_begin + wq;
-  if (t_end > (int)a.n_tokens) t_end = (int)a.n_tokens;
-  const uint32_t wkb = 4u * hd.wk, wvb = 4u * hd.wv;
-  const uint32_t* kreg = a.cache_k + hd.base_k + (int64_t)b * a.capacity * hd.wk;
-  const uint32_t* vreg = a.cache_v + hd.base_v + (int64_t)b * a.capacity * hd.wv;
-  const rsrc_t rk_ = make_rsrc(kreg, (uint32_t)a.capacity * wkb);
-  const rsrc_t rv_ = make_rsrc(vreg, (uint32_t)a.capacity * wvb);
 
   float m_run[GM], l_run[GM], c_run[GM];
 #pragma unroll
@@ -430,8 +438,19 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
   for (int nt = 0; nt < 8; ++nt) acc2[nt] = {0.f, 0.f, 0.f, 0.f};
   lds_fence();
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kTileT) {
-    const int tlast = t_end - 1;
+  int it = 0;
+  for (int t0 = t_begin; t0 < t_end; t0 += kTileT, ++it) {
+    const int nlast = (t_end - t0 < kTileT ? t_end - t0 : kTileT) - 1;
+    const int buf = a.nbuf == 2 ? (it & 1) : 0;
+    const uint32_t* kt = ktile + buf * a.kbuf_words;
+    const uint32_t* vt = vtile + buf * a.vbuf_words;
+    wait_tiles();  // this tile is in LDS
+    const int t1 = t0 + kTileT;
+    if (a.nbuf == 2 && t1 < t_end) {  // next tile streams in while this one is processed
+      const int n1 = (t_end - t1) < kTileT ? (t_end - t1) : kTileT;
+      tile_copy(rk_, (uint32_t)t1 * 4u * wk, (uint32_t)n1 * 4u * wk, ktile + (buf ^ 1) * a.kbuf_words);
+      tile_copy(rv_, (uint32_t)t1 * 4u * wv, (uint32_t)n1 * 4u * wv, vtile + (buf ^ 1) * a.vbuf_words);
+    }
     if constexpr (GEN) {
       switch (bk) {
         KVTC_K_CASE(2) KVTC_K_CASE(3) KVTC_K_CASE(4) KVTC_K_CASE(5) KVTC_K_CASE(6) KVTC_K_CASE(7) KVTC_K_CASE(8)
@@ -440,11 +459,10 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
       switch (bk) { KVTC_K_CASE(2) KVTC_K_CASE(4) KVTC_K_CASE(8) }
     }
     // ---- online softmax, one token per lane
-    const int tok = t0 + lane;
-    const bool valid = tok < t_end;
-    const uint32_t tokc = (uint32_t)(valid ? tok : tlast);
-    const uint32_t kh = ld32(rk_, tokc * wkb);
-    const uint32_t vh = ld32(rv_, tokc * wvb);
+    const bool valid = lane <= nlast;
+    const int tokc = valid ? lane : nlast;
+    const uint32_t kh = kt[tokc * wk];
+    const uint32_t vh = vt[tokc * wv];
     const float muk = f16_bits_to_f32(kh & 0xFFFFu), sgk = f16_bits_to_f32(kh >> 16);
     const float muv = f16_bits_to_f32(vh & 0xFFFFu), sgv = f16_bits_to_f32(vh >> 16);
     lds_fence();
@@ -522,7 +540,13 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
       }
     }
     lds_fence();
+    if (a.nbuf == 1 && t1 < t_end) {  // single buffer: refill after the tile is consumed
+      const int n1 = (t_end - t1) < kTileT ? (t_end - t1) : kTileT;
+      tile_copy(rk_, (uint32_t)t1 * 4u * wk, (uint32_t)n1 * 4u * wk, ktile);
+      tile_copy(rv_, (uint32_t)t1 * 4u * wv, (uint32_t)n1 * 4u * wv, vtile);
+    }
   }
+  wait_tiles();
 
   // ---- wave partial: m, l, sum of p*min (per head), o~[head][j] in natural code order
   float* mlw = ml + wave * 48;
@@ -584,70 +608,75 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
 }
 
 // ----------------------------------------------------------------- combine + back-projection
-// Grid batch * n_q_heads, 256 threads.  Log-sum-exp merge of the split partials,
-// then o = P_V o~ / l (d x r_V back-projection of the value sum).
+// Grid (n_kv_heads, batch), 256 threads: the g query heads of one KV head.  Each
+// wave merges the split partials of its heads with a running log-sum-exp (one
+// pass, loads independent across splits); then o = P_V o~ / l with P_V read once
+// for all g heads (thread pair per output row, half the codes each).
 __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
-  __shared__ float wgt[1024];
-  __shared__ float ot[4][kMaxRank];
-  __shared__ float red[8];
-  const int bq = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float ot[kMaxGroup][kMaxRank];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = a.group;
+  const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
   if (a.n_tokens <= 0) {  // attention over no tokens is defined as zero output
-    if (tid < kHeadDim) a.out[(int64_t)bq * kHeadDim + tid] = 0.0f;
+    for (int i = tid; i < g * kHeadDim; i += 256) a.out[bq0 * kHeadDim + i] = 0.0f;
     return;
   }
-  const int hq = bq % a.n_q_heads;
-  const HeadDesc& hd = a.heads.h[hq / a.group];
+  const HeadDesc& hd = a.heads.h[h];
   const int rv = hd.rv, ns = a.n_splits;
-  const float* part = a.part + (int64_t)bq * ns * kPartStride;
-  float M = -__builtin_inff();
-  for (int s = tid; s < ns; s += 256) M = fmaxf(M, part[(int64_t)s * kPartStride]);
-  M = wave_max(M);
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float mu = M == -__builtin_inff() ? 0.0f : M;
-  float L = 0.0f;
-  for (int s = tid; s < ns; s += 256) {
-    const float* ps = part + (int64_t)s * kPartStride;
-    const float w = exp2f(ps[0] - mu);
-    if (s < 1024) wgt[s] = w;
-    L = fmaf(w, ps[1], L);
-  }
-  L = wave_sum(L);
-  if (lane == 0) red[4 + wave] = L;
-  __syncthreads();
-  L = red[4] + red[5] + red[6] + red[7];
-  // o~: wave w sums splits w, w+4, ...; lanes cover the code indices
-  for (int j = lane; j < rv; j += 64) {
-    float acc0 = 0.0f, acc1 = 0.0f;
-    int s = wave;
-    for (; s + 4 < ns; s += 8) {
-      const float w0 = s < 1024 ? wgt[s] : exp2f(part[(int64_t)s * kPartStride] - mu);
-      const float w1 = s + 4 < 1024 ? wgt[s + 4] : exp2f(part[(int64_t)(s + 4) * kPartStride] - mu);
-      acc0 = fmaf(w0, part[(int64_t)s * kPartStride + 2 + j], acc0);
-      acc1 = fmaf(w1, part[(int64_t)(s + 4) * kPartStride + 2 + j], acc1);
+  for (int hh = wave; hh < g; hh += kWaves) {
+    const float* part = a.part + (bq0 + hh) * ns * (int64_t)kPartStride;
+    float M = -__builtin_inff(), L = 0.0f, a0 = 0.0f, a1 = 0.0f;
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+      const float* ps = part + (int64_t)s * kPartStride;
+      const float m = ps[0], l = ps[1];
+      const float o0 = lane < rv ? ps[2 + lane] : 0.0f;
+      const float o1 = lane + 64 < rv ? ps[2 + 64 + lane] : 0.0f;
+      const float mn = fmaxf(M, m);
+      const float mu = mn == -__builtin_inff() ? 0.0f : mn;
+      const float sc = exp2f(M - mu), w = exp2f(m - mu);
+      L = fmaf(L, sc, w * l);
+      a0 = fmaf(a0, sc, w * o0);
+      a1 = fmaf(a1, sc, w * o1);
+      M = mn;
     }
-    for (; s < ns; s += 4) {
-      const float w0 = s < 1024 ? wgt[s] : exp2f(part[(int64_t)s * kPartStride] - mu);
-      acc0 = fmaf(w0, part[(int64_t)s * kPartStride + 2 + j], acc0);
-    }
-    ot[wave][j] = acc0 + acc1;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    if (lane < rv) ot[hh][lane] = a0 * inv;
+    if (lane + 64 < rv) ot[hh][lane + 64] = a1 * inv;
   }
   __syncthreads();
-  if (tid < rv) ot[0][tid] = ot[0][tid] + ot[1][tid] + ot[2][tid] + ot[3][tid];
-  __syncthreads();
-  // back-projection: wave w covers rows i = 32w .. 32w+31, two lanes per row
   const float* PV = a.basis_v + hd.boff_v;
-  const int i = wave * 32 + (lane >> 1), half = lane & 1;
-  float acc = 0.0f;
-  for (int j = half; j < rv; j += 2) acc = fmaf(PV[(int64_t)i * rv + j], ot[0][j], acc);
-  acc += __shfl_xor(acc, 1);
-  if (half == 0) a.out[(int64_t)bq * kHeadDim + i] = L > 0.0f ? acc / L : 0.0f;
+  const int i = tid >> 1, half = tid & 1;
+  const int jh = rv / 2;
+  float acc[kMaxGroup];
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh) acc[hh] = 0.0f;
+  const float* row = PV + (int64_t)i * rv + half * jh;
+  for (int j = 0; j < jh; j += 4) {
+    const float4 pv = *(const float4*)(row + j);
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) {
+      if (hh < g) {
+        const float* o = &ot[hh][half * jh + j];
+        acc[hh] = fmaf(pv.x, o[0], fmaf(pv.y, o[1], fmaf(pv.z, o[2], fmaf(pv.w, o[3], acc[hh]))));
+      }
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh) {
+    if (hh < g) {
+      const float v = acc[hh] + __shfl_xor(acc[hh], 1);
+      if (half == 0) a.out[(bq0 + hh) * kHeadDim + i] = v;
+    }
+  }
 }
 
 template <int GM, bool GEN>
 static hipError_t launch_gm(const AttendArgs& a, hipStream_t s) {
-  const size_t lds = (64 + kWaves * 48 + kWaves * 128 * GM) * sizeof(float);
+  const size_t lds = (64 + kWaves * 48 + kWaves * (size_t)wave_lds_words(a.kbuf_words, a.vbuf_words, a.nbuf, GM)) *
+                     sizeof(float);
   const dim3 grid((unsigned)a.n_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch);
   hipLaunchKernelGGL((attend_mfma_kernel<GM, GEN>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
@@ -658,18 +687,31 @@ static hipError_t launch_widths(const AttendArgs& a, hipStream_t s) {
   return a.group <= 4 ? launch_gm<4, GEN>(a, s) : a.group <= 8 ? launch_gm<8, GEN>(a, s) : launch_gm<16, GEN>(a, s);
 }
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
+size_t attend_lds_bytes(int kbuf_words, int vbuf_words, int nbuf, int group) {
+  const int gm = group <= 4 ? 4 : group <= 8 ? 8 : 16;
+  return (64 + kWaves * 48 + kWaves * (size_t)wave_lds_words(kbuf_words, vbuf_words, nbuf, gm)) * sizeof(float);
+}
+
+hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
+  AttendArgs a = a_in;
   if (a.n_tokens > 0) {
-    // layouts whose widths are all powers of two use the instance without the general-width paths
+    // tile buffers: 64 records (+ one word read past the last) in whole 1 KB DMA rows
+    int wkm = 0, wvm = 0;
     bool gen = false;
     for (int h = 0; h < a.n_kv_heads; ++h) {
       const HeadDesc& d = a.heads.h[h];
+      wkm = d.wk > wkm ? d.wk : wkm;
+      wvm = d.wv > wvm ? d.wv : wvm;
       gen |= !(pow2_bits(d.bk) && pow2_bits(d.bv));
     }
+    a.kbuf_words = 256 * ((wkm + 1 + 3) / 4);
+    a.vbuf_words = 256 * ((wvm + 1 + 3) / 4);
+    a.nbuf = attend_lds_bytes(a.kbuf_words, a.vbuf_words, 2, a.group) <= 160 * 1024 ? 2 : 1;
+    // layouts whose widths are all powers of two use the instance without the general-width paths
     const hipError_t e = gen ? launch_widths<true>(a, s) : launch_widths<false>(a, s);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.batch * a.n_q_heads)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)a.n_kv_heads, (unsigned)a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -44,7 +44,10 @@ struct AttendArgs {
   int32_t group;
   int32_t batch;
   int32_t dtype;
-  float scale_log2;  // softmax_scale * log2(e)
+  float scale_log2;   // softmax_scale * log2(e)
+  int32_t kbuf_words;  // LDS words per K / V record-tile buffer (set by launch_attend)
+  int32_t vbuf_words;
+  int32_t nbuf;        // tile buffers per wave: 2 (next tile streams in) or 1
 };
 
 hipError_t launch_quantize_pack(const float* coords, int64_t n, int r, int b, uint32_t* records,
