@@ -48,6 +48,26 @@ __device__ inline float wave_max(float x) {
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;
 }
+
+// Wave-uniform maximum with DPP row operations (pairs, quads, half rows, rows),
+// then the four row results through scalar reads.
+template <int CTRL>
+__device__ inline float dpp_max(float x) {
+  const int y = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false);
+  return fmaxf(x, __builtin_bit_cast(float, y));
+}
+__device__ inline float wave_max_uniform(float x) {
+  x = dpp_max<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_max<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_max<0x141>(x);  // row_half_mirror
+  x = dpp_max<0x140>(x);  // row_mirror
+  const int xi = __builtin_bit_cast(int, x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
 __device__ inline float wave_sum(float x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
   return x;
@@ -73,14 +93,16 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Copy `nbytes` starting at byte `src` of the region to LDS `dst` (whole 16-byte
-// chunks: up to 1023 bytes past the end are copied too and never read).
+// Copy `nbytes` starting at byte `src` of the region to LDS `dst` in 16-byte
+// chunks (up to 12 bytes past the end are copied too).
 __device__ inline void tile_copy(rsrc_t r, uint32_t src, uint32_t nbytes, uint32_t* dst) {
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t n16 = (nbytes + 15u) >> 4;
-  for (uint32_t c = 0; c < n16; c += 64) {
+  uint32_t c = 0;
+  for (; c + 64 <= n16; c += 64)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 4 * c), 16, (int)(src + 16u * (c + lane)), 0, 0, 0);
-  }
+  if (c + lane < n16)  // tail: only the lanes whose 16 bytes belong to the tile
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 4 * c), 16, (int)(src + 16u * (c + lane)), 0, 0, 0);
 }
 
 __device__ inline void wait_tiles() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -151,15 +173,16 @@ __device__ inline void k_slot(int G, int nks, int ks, int p, int rk, bool& valid
 // matrix cores, written to S[token][GM] (log2 units before min/step are applied).
 // kt: the tile's records (wk words each); tokens past `nlast` read record nlast.
 template <int B, int NKS, int GM>
-__device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt, int wk, int nlast,
+__device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt, int wk,
                                                               const u32x4 (&aq_hi)[4], const u32x4 (&aq_lo)[4],
                                                               float* S) {
+  // tokens past the tile's last record read stale LDS: their codes are finite and
+  // their scores are replaced by -inf before the softmax
   const int lane = threadIdx.x & 63, n = lane & 15, G = lane >> 4;
+  const uint32_t* rec0 = kt + n * wk;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    int tok = tt * 16 + n;
-    tok = tok < nlast ? tok : nlast;
-    const uint32_t* rec = kt + tok * wk;
+    const uint32_t* rec = rec0 + tt * 16 * wk;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (pow2_bits(B)) {
       constexpr int PPW = Pow2<B>::kPerHalf;
@@ -194,7 +217,8 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
         acc = mfma(aq_lo[ks], bop, acc);
       }
     }
-    if (4 * G < GM) *(f32x4*)(S + (tt * 16 + n) * GM + 4 * G) = acc;
+    // S[token][GM]; lanes holding head rows >= GM (all zero) store into the dump slot
+    *(f32x4*)(S + (4 * G < GM ? (tt * 16 + n) * GM + 4 * G : 64 * GM)) = acc;
   }
 }
 
@@ -203,27 +227,27 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
 // lane group, one aligned field of NT*B bits for power-of-two widths) and its two
 // MFMAs with A = p*step_V (hi, lo).
 template <int B, int NT>
-__device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt, int wv, int kk, int nlast,
+__device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt, int wv, int kk,
                                                               u32x4 ahi, u32x4 alo, f32x4 (&acc2)[8]) {
+  // tokens past the tile's last record carry p = 0 in A, so their (finite) codes add nothing
   const int lane = threadIdx.x & 63, n = lane & 15, G = lane >> 4;
+  const uint32_t* rec0 = vt + (32 * kk + 8 * G) * wv + 1;
   if constexpr (pow2_bits(B)) {
     constexpr int PPW = Pow2<B>::kPerHalf;
     constexpr int FS = NT * B;
     uint32_t f0[8], f1[8];
+    const int bit = n * FS;
+    const uint16_t* h0 = (const uint16_t*)rec0 + (bit >> 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      int tok = 32 * kk + 8 * G + e;
-      tok = tok < nlast ? tok : nlast;
-      const uint32_t* rec = vt + tok * wv + 1;
       f1[e] = 0u;
       if constexpr (FS <= 16) {
-        const int bit = n * FS;
-        const uint32_t x = (uint32_t)((const uint16_t*)rec)[bit >> 4] >> (bit & 15);
+        const uint32_t x = (uint32_t)h0[2 * e * wv] >> (bit & 15);
         f0[e] = FS == 16 ? x : (x & ((1u << FS) - 1u));
       } else if constexpr (FS == 32) {
-        f0[e] = rec[n];
+        f0[e] = rec0[e * wv + n];
       } else {
-        const u32x2a a = *(const u32x2a*)(rec + 2 * n);
+        const u32x2a a = *(const u32x2a*)(rec0 + e * wv + 2 * n);
         f0[e] = a[0];
         f1[e] = a[1];
       }
@@ -250,11 +274,8 @@ __device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt
       u32x4 bop;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        int ta = 32 * kk + 8 * G + 2 * p, tb = ta + 1;
-        ta = ta < nlast ? ta : nlast;
-        tb = tb < nlast ? tb : nlast;
-        const uint32_t ca = lds_window(vt + ta * wv, bit) & M;
-        const uint32_t cb = lds_window(vt + tb * wv, bit) & M;
+        const uint32_t ca = lds_window(rec0 - 1 + (2 * p) * wv, bit) & M;
+        const uint32_t cb = lds_window(rec0 - 1 + (2 * p + 1) * wv, bit) & M;
         bop[p] = ca | (cb << 16);
       }
       acc2[nt] = mfma(ahi, bop, acc2[nt]);
@@ -303,22 +324,24 @@ __device__ inline int v_shift(int B, int nt) {
 
 #define KVTC_K_CASE(B)                                                              \
   case B:                                                                           \
-    if (nks == 1) k_phase<B, 1, GM>(kt, wk, nlast, aq_hi, aq_lo, S);                 \
-    else if (nks == 2) k_phase<B, 2, GM>(kt, wk, nlast, aq_hi, aq_lo, S);            \
-    else k_phase<B, 4, GM>(kt, wk, nlast, aq_hi, aq_lo, S);                          \
+    if (nks == 1) k_phase<B, 1, GM>(kt, wk, aq_hi, aq_lo, S);                            \
+    else if (nks == 2) k_phase<B, 2, GM>(kt, wk, aq_hi, aq_lo, S);                       \
+    else k_phase<B, 4, GM>(kt, wk, aq_hi, aq_lo, S);                                     \
     break;
 #define KVTC_V_CASE(B)                                                              \
   case B:                                                                           \
-    if (NT == 1) v_phase<B, 1>(vt, wv, kk, nlast, ahi, alo, acc2);                   \
-    else if (NT == 2) v_phase<B, 2>(vt, wv, kk, nlast, ahi, alo, acc2);              \
-    else if (NT == 4) v_phase<B, 4>(vt, wv, kk, nlast, ahi, alo, acc2);              \
-    else v_phase<B, 8>(vt, wv, kk, nlast, ahi, alo, acc2);                           \
+    if (NT == 1) v_phase<B, 1>(vt, wv, kk, ahi, alo, acc2);                          \
+    else if (NT == 2) v_phase<B, 2>(vt, wv, kk, ahi, alo, acc2);                     \
+    else if (NT == 4) v_phase<B, 4>(vt, wv, kk, ahi, alo, acc2);                     \
+    else v_phase<B, 8>(vt, wv, kk, ahi, alo, acc2);                                  \
     break;
 
-// Words of LDS per wave: tile buffers for K and V (a.nbuf each) and the score /
-// probability area (128 * GM words).
+// Words of LDS per wave: tile buffers for K and V (nbuf each), the scores
+// S[64][GM] plus a 4-word dump slot for the score rows >= GM, and the
+// probabilities P[2][GM][64] (fp16) plus a 4-word zero slot read as rows >= GM.
+__host__ __device__ constexpr int score_words(int gm) { return 64 * gm + 4 + gm * 64 + 4; }
 __host__ __device__ inline int wave_lds_words(int kbuf_words, int vbuf_words, int nbuf, int gm) {
-  return nbuf * (kbuf_words + vbuf_words) + 128 * gm;
+  return nbuf * (kbuf_words + vbuf_words) + score_words(gm);
 }
 
 // ----------------------------------------------------------------- kernel
@@ -361,19 +384,21 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
   const rsrc_t rv_ = make_rsrc(vreg, (uint32_t)a.capacity * 4u * wv);
   uint32_t* ktile = (uint32_t*)wl;                          // [nbuf][kbuf_words]
   uint32_t* vtile = ktile + a.nbuf * a.kbuf_words;          // [nbuf][vbuf_words]
-  float* S = (float*)(vtile + a.nbuf * a.vbuf_words);       // [64][GM] fp32
-  _Float16* P = (_Float16*)(S + 64 * GM);                   // [2][GM][64] fp16, rows >= g stay zero
+  float* S = (float*)(vtile + a.nbuf * a.vbuf_words);       // [64][GM] fp32, then a dump slot
+  _Float16* P = (_Float16*)(S + 64 * GM + 4);               // [2][GM][64] fp16 (rows >= g stay zero), zero slot
 
   // ---- prologue: q~ = scale * log2(e) * P_K^T q of the g heads (raw q and q~ in the
   // score areas of waves 0..3, which are not in use yet)
-  float* q_raw = (float*)((uint32_t*)areas + (WA - 128 * GM));     // wave 0's score area
-  float* qt = (float*)((uint32_t*)areas + WA + (WA - 128 * GM));   // wave 1's score area
+  // q (g x 128) and q~ (g x 128) over the tile buffers of waves 2 and 3, which start
+  // streaming only after the prologue
+  float* q_raw = areas + 2 * WA;
+  float* qt = areas + 3 * WA;
   for (int i = tid; i < g * kHeadDim; i += 256) {
     const int64_t off = (bq0 + i / kHeadDim) * kHeadDim + (i % kHeadDim);
     q_raw[i] = a.dtype == 0 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
   }
-  if (t_begin < t_end) {
-    const int n0 = (t_end - t_begin) < kTileT ? (t_end - t_begin) : kTileT;
+  const int n0 = (t_end - t_begin) < kTileT ? (t_end - t_begin) : kTileT;
+  if (wave < 2 && t_begin < t_end) {  // waves 2 and 3 lend their buffers to the prologue
     tile_copy(rk_, (uint32_t)t_begin * 4u * wk, (uint32_t)n0 * 4u * wk, ktile);
     tile_copy(rv_, (uint32_t)t_begin * 4u * wv, (uint32_t)n0 * 4u * wv, vtile);
   }
@@ -424,32 +449,40 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
     kf[hh] = uniform(sc[kMaxGroup + hh]);
   }
   __syncthreads();  // the prologue's q and q~ are consumed
-  for (int i = lane; i < GM * 64; i += 64) ((uint32_t*)P)[i] = 0u;
+  if (wave >= 2 && t_begin < t_end) {
+    tile_copy(rk_, (uint32_t)t_begin * 4u * wk, (uint32_t)n0 * 4u * wk, ktile);
+    tile_copy(rv_, (uint32_t)t_begin * 4u * wv, (uint32_t)n0 * 4u * wv, vtile);
+  }
+  for (int i = lane; i < GM * 64 + 4; i += 64) ((uint32_t*)P)[i] = 0u;
 
+  // running state: reference maximum (finite start, so heads >= g never form -inf - -inf),
+  // per-lane partial sums of p and p * min_V, value accumulators of 8 N-tiles
   float m_run[GM], l_run[GM], c_run[GM];
 #pragma unroll
   for (int hh = 0; hh < GM; ++hh) {
-    m_run[hh] = -__builtin_inff();
+    m_run[hh] = -1e30f;
     l_run[hh] = 0.0f;
     c_run[hh] = 0.0f;
   }
   f32x4 acc2[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) acc2[nt] = {0.f, 0.f, 0.f, 0.f};
+  const int n = lane & 15, G = lane >> 4;
+  const int hoff_k = lane * wk, hoff_v = lane * wv;  // this lane's token header in a tile
+  const uint32_t* kt = ktile;
+  const uint32_t* vt = vtile;
+  uint32_t* kt_next = ktile + (a.nbuf == 2 ? a.kbuf_words : 0);
+  uint32_t* vt_next = vtile + (a.nbuf == 2 ? a.vbuf_words : 0);
   lds_fence();
 
-  int it = 0;
-  for (int t0 = t_begin; t0 < t_end; t0 += kTileT, ++it) {
-    const int nlast = (t_end - t0 < kTileT ? t_end - t0 : kTileT) - 1;
-    const int buf = a.nbuf == 2 ? (it & 1) : 0;
-    const uint32_t* kt = ktile + buf * a.kbuf_words;
-    const uint32_t* vt = vtile + buf * a.vbuf_words;
+  for (int t0 = t_begin; t0 < t_end; t0 += kTileT) {
+    const int nvalid = t_end - t0 < kTileT ? t_end - t0 : kTileT;
     wait_tiles();  // this tile is in LDS
     const int t1 = t0 + kTileT;
     if (a.nbuf == 2 && t1 < t_end) {  // next tile streams in while this one is processed
       const int n1 = (t_end - t1) < kTileT ? (t_end - t1) : kTileT;
-      tile_copy(rk_, (uint32_t)t1 * 4u * wk, (uint32_t)n1 * 4u * wk, ktile + (buf ^ 1) * a.kbuf_words);
-      tile_copy(rv_, (uint32_t)t1 * 4u * wv, (uint32_t)n1 * 4u * wv, vtile + (buf ^ 1) * a.vbuf_words);
+      tile_copy(rk_, (uint32_t)t1 * 4u * wk, (uint32_t)n1 * 4u * wk, kt_next);
+      tile_copy(rv_, (uint32_t)t1 * 4u * wv, (uint32_t)n1 * 4u * wv, vt_next);
     }
     if constexpr (GEN) {
       switch (bk) {
@@ -458,13 +491,13 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
     } else {
       switch (bk) { KVTC_K_CASE(2) KVTC_K_CASE(4) KVTC_K_CASE(8) }
     }
-    // ---- online softmax, one token per lane
-    const bool valid = lane <= nlast;
-    const int tokc = valid ? lane : nlast;
-    const uint32_t kh = kt[tokc * wk];
-    const uint32_t vh = vt[tokc * wv];
+    // ---- online softmax, one token per lane (branch-free over heads)
+    const bool valid = lane < nvalid;
+    const uint32_t kh = kt[hoff_k];
+    const uint32_t vh = vt[hoff_v];
     const float muk = f16_bits_to_f32(kh & 0xFFFFu), sgk = f16_bits_to_f32(kh >> 16);
-    const float muv = f16_bits_to_f32(vh & 0xFFFFu), sgv = f16_bits_to_f32(vh >> 16);
+    const float muv = valid ? f16_bits_to_f32(vh & 0xFFFFu) : 0.0f;
+    const float sgv = valid ? f16_bits_to_f32(vh >> 16) : 0.0f;
     lds_fence();
     float s[GM];
 #pragma unroll
@@ -473,7 +506,8 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int hh = 4 * q4 + e;
-        s[hh] = (valid && hh < g) ? fmaf(sgk * kf[hh], d[e], muk * sq[hh]) : -__builtin_inff();
+        const float x = fmaf(sgk * kf[hh], d[e], muk * sq[hh]);
+        s[hh] = (valid && hh < g) ? x : -__builtin_inff();
       }
     }
     // lazy maximum: the reference only moves when a score exceeds it, so p <= 1
@@ -484,16 +518,11 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
       float alpha[GM];
 #pragma unroll
       for (int hh = 0; hh < GM; ++hh) {
-        alpha[hh] = 1.0f;
-        if (hh < g) {
-          const float mn = uniform(fmaxf(m_run[hh], wave_max(s[hh])));
-          if (mn > m_run[hh]) {
-            alpha[hh] = exp2f(m_run[hh] - mn);  // 0 while the old reference is -inf
-            m_run[hh] = mn;
-          }
-          l_run[hh] *= alpha[hh];
-          c_run[hh] *= alpha[hh];
-        }
+        const float mn = fmaxf(m_run[hh], wave_max_uniform(s[hh]));
+        alpha[hh] = exp2f(m_run[hh] - mn);  // 1 if unchanged, 0 on the first tile
+        m_run[hh] = mn;
+        l_run[hh] *= alpha[hh];
+        c_run[hh] *= alpha[hh];
       }
       // value accumulators: lane (n, G) holds heads 4G..4G+3
       lds_fence();
@@ -502,35 +531,27 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
         for (int hh = 0; hh < GM; ++hh) S[hh] = alpha[hh];
       }
       lds_fence();
-      const int G = lane >> 4;
-      if (4 * G < GM) {
-        const f32x4 f = *(const f32x4*)(S + 4 * G);
+      const f32x4 f = 4 * G < GM ? *(const f32x4*)(S + 4 * G) : f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc2[nt] *= f;
-      }
+      for (int nt = 0; nt < 8; ++nt) acc2[nt] *= f;
     }
 #pragma unroll
     for (int hh = 0; hh < GM; ++hh) {
-      if (hh < g) {
-        const float p = exp2f(s[hh] - m_run[hh]);
-        l_run[hh] += p;
-        c_run[hh] = fmaf(p, muv, c_run[hh]);
-        const float x = p * sgv;
-        const _Float16 hi = (_Float16)x;
-        const _Float16 lo = (_Float16)(x - (float)hi);
-        P[hh * 64 + lane] = hi;
-        P[GM * 64 + hh * 64 + lane] = lo;
-      }
+      const float p = exp2f(s[hh] - m_run[hh]);
+      l_run[hh] += p;
+      c_run[hh] = fmaf(p, muv, c_run[hh]);
+      const float x = p * sgv;
+      const _Float16 hi = (_Float16)x;
+      const _Float16 lo = (_Float16)(x - (float)hi);
+      P[hh * 64 + lane] = hi;
+      P[GM * 64 + hh * 64 + lane] = lo;
     }
     lds_fence();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int n = lane & 15, G = lane >> 4;
-      u32x4 ahi = {0u, 0u, 0u, 0u}, alo = {0u, 0u, 0u, 0u};
-      if (n < GM) {
-        ahi = *(const u32x4*)(P + n * 64 + 32 * kk + 8 * G);
-        alo = *(const u32x4*)(P + GM * 64 + n * 64 + 32 * kk + 8 * G);
-      }
+      // A rows >= GM read the zero slot
+      const u32x4 ahi = *(const u32x4*)(P + (n < GM ? n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
+      const u32x4 alo = *(const u32x4*)(P + (n < GM ? GM * 64 + n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
       if constexpr (GEN) {
         switch (bv) {
           KVTC_V_CASE(2) KVTC_V_CASE(3) KVTC_V_CASE(4) KVTC_V_CASE(5) KVTC_V_CASE(6) KVTC_V_CASE(7) KVTC_V_CASE(8)
@@ -540,10 +561,19 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
       }
     }
     lds_fence();
-    if (a.nbuf == 1 && t1 < t_end) {  // single buffer: refill after the tile is consumed
-      const int n1 = (t_end - t1) < kTileT ? (t_end - t1) : kTileT;
-      tile_copy(rk_, (uint32_t)t1 * 4u * wk, (uint32_t)n1 * 4u * wk, ktile);
-      tile_copy(rv_, (uint32_t)t1 * 4u * wv, (uint32_t)n1 * 4u * wv, vtile);
+    if (a.nbuf == 1) {
+      if (t1 < t_end) {  // single buffer: refill after the tile is consumed
+        const int n1 = (t_end - t1) < kTileT ? (t_end - t1) : kTileT;
+        tile_copy(rk_, (uint32_t)t1 * 4u * wk, (uint32_t)n1 * 4u * wk, ktile);
+        tile_copy(rv_, (uint32_t)t1 * 4u * wv, (uint32_t)n1 * 4u * wv, vtile);
+      }
+    } else {
+      const uint32_t* tk = kt;
+      kt = kt_next;
+      kt_next = (uint32_t*)tk;
+      const uint32_t* tv = vt;
+      vt = vt_next;
+      vt_next = (uint32_t*)tv;
     }
   }
   wait_tiles();
@@ -562,7 +592,6 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
   }
   lds_fence();
   {
-    const int n = lane & 15, G = lane >> 4;
     if (4 * G < GM) {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
@@ -695,7 +724,7 @@ size_t attend_lds_bytes(int kbuf_words, int vbuf_words, int nbuf, int group) {
 hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
   AttendArgs a = a_in;
   if (a.n_tokens > 0) {
-    // tile buffers: 64 records (+ one word read past the last) in whole 1 KB DMA rows
+    // tile buffers: 64 records plus the 16-byte copy granule and one word read past the last record
     int wkm = 0, wvm = 0;
     bool gen = false;
     for (int h = 0; h < a.n_kv_heads; ++h) {
@@ -704,8 +733,8 @@ hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
       wvm = d.wv > wvm ? d.wv : wvm;
       gen |= !(pow2_bits(d.bk) && pow2_bits(d.bv));
     }
-    a.kbuf_words = 256 * ((wkm + 1 + 3) / 4);
-    a.vbuf_words = 256 * ((wvm + 1 + 3) / 4);
+    a.kbuf_words = ((64 * wkm + 4 + 3) / 4) * 4;
+    a.vbuf_words = ((64 * wvm + 4 + 3) / 4) * 4;
     a.nbuf = attend_lds_bytes(a.kbuf_words, a.vbuf_words, 2, a.group) <= 160 * 1024 ? 2 : 1;
     // layouts whose widths are all powers of two use the instance without the general-width paths
     const hipError_t e = gen ? launch_widths<true>(a, s) : launch_widths<false>(a, s);
