@@ -117,7 +117,7 @@ int64_t default_split_tokens(const Layout& L, int64_t T) {
 }
 
 struct Workspace {
-  int64_t qt = 0, sq = 0, part = 0, floats = 0;
+  int64_t aq = 0, hs = 0, cnt = 0, part = 0, floats = 0;  // offsets in 4-byte words
   int32_t n_splits = 1;
   int64_t split_tokens = 0;
 };
@@ -133,11 +133,13 @@ kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Works
   int64_t ns = T > 0 ? (T + split_tokens - 1) / split_tokens : 1;
   if (ns > 65535) return fail(KV_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)ns);
   const int64_t nbq = (int64_t)L.batch * L.n_q;
+  const int64_t units = (int64_t)L.batch * L.n_kv;
   w.split_tokens = split_tokens;
   w.n_splits = (int32_t)ns;
-  w.qt = 0;
-  w.sq = nbq * kQtStride;
-  w.part = w.sq + ((nbq + 3) / 4) * 4;
+  w.aq = 0;
+  w.hs = units * kAqWords;
+  w.cnt = w.hs + units * kHsFloats;
+  w.part = w.cnt + ((units + 3) / 4) * 4;
   w.floats = w.part + nbq * ns * kPartStride;
   return KV_OK;
 }
@@ -252,8 +254,9 @@ kv_status kv_attend_decode_split(const kv_layout* layout, const void* q, kv_dtyp
   a.cache_v = cache_v;
   a.out = out;
   float* ws = (float*)workspace;
-  a.qt = ws + w.qt;
-  a.sq = ws + w.sq;
+  a.aq = (uint32_t*)(ws + w.aq);
+  a.hs = ws + w.hs;
+  a.cnt = (uint32_t*)(ws + w.cnt);
   a.part = ws + w.part;
   a.n_tokens = n_tokens;
   a.capacity = L.capacity;

@@ -1,0 +1,704 @@
+// Device building blocks of the split-K decode attention kernels (gfx950):
+// record-tile streaming HBM -> LDS, the per-tile score / softmax / value phases
+// on the matrix cores, and the workgroup and split merges.  Included by the
+// generic kernel and by the kernels specialised per record format.
+#pragma once
+
+#include "kvtc_common.h"
+#include "kvtc_launch.h"
+
+namespace kvtc {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));  // records are 4-byte aligned
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+
+constexpr int kWaves = 4;       // waves per workgroup
+constexpr int kTileT = 64;      // tokens per wave iteration
+
+__device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+__device__ inline uint32_t h2u(_Float16 x) { return (uint32_t)__builtin_bit_cast(uint16_t, x); }
+
+__device__ inline void lds_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
+
+__device__ inline float wave_max(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Wave-uniform maximum with DPP row operations (pairs, quads, half rows, rows),
+// then the four row results through scalar reads.
+template <int CTRL>
+__device__ inline float dpp_max(float x) {
+  const int y = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false);
+  return fmaxf(x, __builtin_bit_cast(float, y));
+}
+__device__ inline float wave_max_uniform(float x) {
+  x = dpp_max<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_max<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_max<0x141>(x);  // row_half_mirror
+  x = dpp_max<0x140>(x);  // row_mirror
+  const int xi = __builtin_bit_cast(int, x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ inline float wave_sum(float x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+
+__device__ inline float uniform(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+// ----------------------------------------------------------------- record tiles in LDS
+// One buffer resource per (sequence, KV head) cache region: 32-bit byte offsets,
+// loads past the region return zero.  Tiles of 64 consecutive records are copied
+// HBM -> LDS with buffer_load_dwordx4 ... lds (16 bytes per lane, lane-contiguous
+// in LDS), so the copy of the next tile is in flight while the current one is
+// unpacked, and every unpacking access is an LDS read.
+// Buffer resource of a cache region as four SGPRs: base, stride 0, byte size
+// (out-of-range offsets read zero), raw 32-bit dword format.
+typedef u32x4 rsrc_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  rsrc_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xFFFFu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// One 16-byte-per-lane buffer load straight into LDS: lane l's bytes land at
+// lds + 16*l.  Written as asm so that the compiler does not treat it as an LDS
+// store and wait for it before every later LDS read: the tile loop orders these
+// copies with explicit vmcnt waits instead.  M0 carries the LDS base; one wait
+// state separates its write from the load that reads it.
+__device__ inline void dma16(rsrc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)p);
+}
+
+// Copy `nbytes` starting at byte `src` of the region to LDS `dst` in 16-byte
+// chunks (up to 12 bytes past the end are copied too); issues copy_insts(nbytes)
+// vector-memory instructions.
+__device__ inline void tile_copy(rsrc_t r, uint32_t src, uint32_t nbytes, uint32_t* dst) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t n16 = (nbytes + 15u) >> 4;
+  const uint32_t base = lds_addr(dst);
+  uint32_t c = 0;
+  for (; c + 64 <= n16; c += 64) dma16(r, base + 16u * c, src + 16u * (c + lane));
+  if (c + lane < n16)  // tail: only the lanes whose 16 bytes belong to the tile
+    dma16(r, base + 16u * c, src + 16u * (c + lane));
+}
+
+// tile_copy of a compile-time size: the 64-lane chunks unrolled, then the tail.
+template <uint32_t NBYTES>
+__device__ inline void tile_copy_n(rsrc_t r, uint32_t src, uint32_t* dst) {
+  constexpr uint32_t n16 = (NBYTES + 15u) >> 4;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t base = lds_addr(dst);
+#pragma unroll
+  for (uint32_t c = 0; c + 64 <= n16; c += 64) dma16(r, base + 16u * c, src + 16u * (c + lane));
+  if constexpr (n16 % 64 != 0) {
+    constexpr uint32_t c = n16 / 64 * 64;
+    if (c + lane < n16) dma16(r, base + 16u * c, src + 16u * (c + lane));
+  }
+}
+
+__device__ inline void wait_tiles() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most N vector-memory instructions of this wave are outstanding.
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Vector-memory instructions tile_copy issues for `nbytes`.
+__device__ inline int copy_insts(uint32_t nbytes) { return (int)((((nbytes + 15u) >> 4) + 63u) >> 6); }
+
+template <int N>
+__device__ inline void lds_words(const uint32_t* p, uint32_t (&w)[N]) {
+  if constexpr (N == 1) {
+    w[0] = p[0];
+  } else if constexpr (N == 2) {
+    const u32x2a a = *(const u32x2a*)p;
+    w[0] = a[0]; w[1] = a[1];
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; k += 4) {
+      const u32x4a a = *(const u32x4a*)(p + k);
+      w[k] = a[0]; w[k + 1] = a[1]; w[k + 2] = a[2]; w[k + 3] = a[3];
+    }
+  }
+}
+
+// B adjacent-code bits starting at stream bit `bit` of a record in LDS (low code in bits 0..).
+__device__ inline uint32_t lds_window(const uint32_t* rec, int bit) {
+  const uint32_t* p = rec + 1 + (bit >> 5);
+  return __builtin_amdgcn_alignbit(p[1], p[0], bit & 31);
+}
+
+// ----------------------------------------------------------------- code fields
+// Power-of-two widths (2, 4, 8): a pair operand holds the codes at the same
+// offset of the two 16-bit halves of a word; offsets whose field would reach the
+// fp16 exponent bits (10..14) are taken after a pre-shift of kShift bits.
+template <int B> struct Pow2 {
+  static constexpr int kPerHalf = 16 / B;
+  static constexpr int kShift = (B == 2) ? 10 : 8;
+  static constexpr uint32_t kMask = (1u << B) - 1u;
+  __device__ static constexpr int pre(int o) { return (o + B <= 10) ? 0 : kShift; }
+  __device__ static constexpr int at(int o) { return o - pre(o); }
+  __device__ static inline uint32_t pair(uint32_t y, int o) {
+    return (y >> pre(o)) & ((kMask << at(o)) | (kMask << (16 + at(o))));
+  }
+};
+
+__host__ __device__ constexpr bool pow2_bits(int b) { return b == 2 || b == 4 || b == 8; }
+
+// Key pair slots.  Lane group G of a 16-token sub-tile owns pair slots
+// [G*nks*4, (G+1)*nks*4) of its token (nks = max(1, r_K/32) K-steps of 32 codes).
+// Power-of-two widths: pair pi = the codes at half-offset (pi % (16/B))*B of code
+// word pi / (16/B); general widths: codes 2*pi and 2*pi + 1.  Returns the code
+// indices of the low / high fp16 element and the operand's 2^s code scale.
+template <int B>
+__device__ inline void k_slot(int G, int nks, int ks, int p, int rk, bool& valid, int& j_lo, int& j_hi, int& s) {
+  const int pi = G * nks * 4 + ks * 4 + p;
+  valid = pi < rk / 2;
+  if constexpr (pow2_bits(B)) {
+    constexpr int PPW = Pow2<B>::kPerHalf;
+    const int w = pi / PPW, u = pi % PPW;
+    j_lo = w * (32 / B) + u;
+    j_hi = j_lo + PPW;
+    s = Pow2<B>::at(((ks * 4 + p) % PPW) * B);  // after the per-lane pre-shift of k_phase
+  } else {
+    j_lo = 2 * pi;
+    j_hi = 2 * pi + 1;
+    s = 0;
+  }
+}
+
+// ----------------------------------------------------------------- per-tile phases (records in LDS)
+// Scores of one 64-token tile: four 16-token sub-tiles, C[head][token] on the
+// matrix cores, written to S[token][GM] (log2 units before min/step are applied).
+// kt: the tile's records (wk words each); tokens past `nlast` read record nlast.
+template <int B, int NKS, int GM>
+__device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt, int wk,
+                                                              const u32x4 (&aq_hi)[4], const u32x4 (&aq_lo)[4],
+                                                              float* S) {
+  // tokens past the tile's last record read stale LDS: their codes are finite and
+  // their scores are replaced by -inf before the softmax.  The four 16-token
+  // sub-tiles are interleaved so that consecutive MFMAs never depend on each other.
+  const int lane = threadIdx.x & 63, n = lane & 15, G = lane >> 4;
+  const uint32_t* rec0 = kt + n * wk;
+  f32x4 acc[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) acc[tt] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (pow2_bits(B)) {
+    constexpr int PPW = Pow2<B>::kPerHalf;
+    constexpr int NWL = (NKS * 4 * B + 15) / 16;
+    const int base = G * NKS * 4;
+    uint32_t w[4][NWL];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      lds_words<NWL>(rec0 + tt * 16 * wk + 1 + base / PPW, w[tt]);
+      if constexpr (NKS * 4 < PPW) w[tt][0] >>= (base % PPW) * B;
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 bop[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int pl = ks * 4 + p;
+          bop[tt][p] = Pow2<B>::pair(w[tt][pl / PPW], (pl % PPW) * B);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_hi[ks], bop[tt], acc[tt]);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_lo[ks], bop[tt], acc[tt]);
+    }
+  } else {
+    constexpr uint32_t M = (1u << B) - 1u;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 bop[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int pi = G * NKS * 4 + ks * 4 + p;
+          const uint32_t f = lds_window(rec0 + tt * 16 * wk, 2 * pi * B);
+          bop[tt][p] = (f & M) | (((f >> B) & M) << 16);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_hi[ks], bop[tt], acc[tt]);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_lo[ks], bop[tt], acc[tt]);
+    }
+  }
+  // S[token][GM]: the lanes of head rows >= GM (all zero) store nothing
+  if (4 * G < GM) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) *(f32x4*)(S + (tt * 16 + n) * GM + 4 * G) = acc[tt];
+  }
+}
+
+// One 32-token value step (tile tokens 32*kk .. 32*kk+31): for each N-tile of 16
+// codes the B operand (lane n owns codes [n*NT, (n+1)*NT) of the 8 tokens of its
+// lane group, one aligned field of NT*B bits for power-of-two widths) and its two
+// MFMAs with A = p*step_V (hi, lo).
+template <int B, int NT>
+__device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt, int wv, int kk,
+                                                              u32x4 ahi, u32x4 alo, f32x4 (&acc2)[8]) {
+  // tokens past the tile's last record carry p = 0 in A, so their (finite) codes add nothing
+  const int lane = threadIdx.x & 63, n = lane & 15, G = lane >> 4;
+  const uint32_t* rec0 = vt + (32 * kk + 8 * G) * wv + 1;
+  if constexpr (pow2_bits(B)) {
+    constexpr int PPW = Pow2<B>::kPerHalf;
+    constexpr int FS = NT * B;
+    uint32_t f0[8], f1[8];
+    const int bit = n * FS;
+    const uint16_t* h0 = (const uint16_t*)rec0 + (bit >> 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f1[e] = 0u;
+      if constexpr (FS <= 16) {
+        const uint32_t x = (uint32_t)h0[2 * e * wv] >> (bit & 15);
+        f0[e] = FS == 16 ? x : (x & ((1u << FS) - 1u));
+      } else if constexpr (FS == 32) {
+        f0[e] = rec0[e * wv + n];
+      } else {
+        const u32x2a a = *(const u32x2a*)(rec0 + e * wv + 2 * n);
+        f0[e] = a[0];
+        f1[e] = a[1];
+      }
+    }
+    // N-tiles in pairs: both hi MFMAs, then both lo MFMAs (no back-to-back dependency)
+#pragma unroll
+    for (int n2 = 0; n2 < NT; n2 += 2) {
+      u32x4 bop[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int nt = n2 + u < NT ? n2 + u : NT - 1;
+        const int k = nt / PPW;  // 16-bit slice of the field
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t fa = k < 2 ? f0[2 * p] : f1[2 * p];
+          const uint32_t fb = k < 2 ? f0[2 * p + 1] : f1[2 * p + 1];
+          const uint32_t y = (k & 1) ? ((fa >> 16) | (fb & 0xFFFF0000u)) : ((fa & 0xFFFFu) | (fb << 16));
+          bop[u][p] = Pow2<B>::pair(y, (nt % PPW) * B);
+        }
+      }
+      acc2[n2] = mfma(ahi, bop[0], acc2[n2]);
+      if (n2 + 1 < NT) acc2[n2 + 1] = mfma(ahi, bop[1], acc2[n2 + 1]);
+      acc2[n2] = mfma(alo, bop[0], acc2[n2]);
+      if (n2 + 1 < NT) acc2[n2 + 1] = mfma(alo, bop[1], acc2[n2 + 1]);
+    }
+  } else {
+    constexpr uint32_t M = (1u << B) - 1u;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int bit = (n * NT + nt) * B;
+      u32x4 bop;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t ca = lds_window(rec0 - 1 + (2 * p) * wv, bit) & M;
+        const uint32_t cb = lds_window(rec0 - 1 + (2 * p + 1) * wv, bit) & M;
+        bop[p] = ca | (cb << 16);
+      }
+      acc2[nt] = mfma(ahi, bop, acc2[nt]);
+      acc2[nt] = mfma(alo, bop, acc2[nt]);
+    }
+  }
+}
+
+// 2^s code scale of value N-tile nt (power-of-two widths; general widths use s = 0).
+__device__ inline int v_shift(int B, int nt) {
+  switch (B) {
+    case 2: return Pow2<2>::at((nt % Pow2<2>::kPerHalf) * 2);
+    case 4: return Pow2<4>::at((nt % Pow2<4>::kPerHalf) * 4);
+    case 8: return Pow2<8>::at((nt % Pow2<8>::kPerHalf) * 8);
+    default: return 0;
+  }
+}
+
+// Words of LDS per wave: tile buffers for K and V (nbuf each), then the scores
+// S[64][GM] (fp32), overwritten by the probabilities P[2][GM][64] (fp16, hi then
+// lo) once read, and a 4-word zero slot read as the A rows >= GM.
+__host__ __device__ constexpr int score_words(int gm) { return 64 * gm + 4; }
+// The area also holds the wave's value partial o~[g][r_V] at the end.
+__host__ __device__ inline int wave_lds_words(int kbuf_words, int vbuf_words, int nbuf, int gm) {
+  const int w = nbuf * (kbuf_words + vbuf_words) + score_words(gm);
+  return w > gm * kMaxRank ? w : gm * kMaxRank;
+}
+// Workgroup-common LDS words: per wave m[16] l[16] c[16], then a flag word (padded).
+constexpr int kCommonWords = kWaves * 48 + 4;
+
+// Dynamic LDS bytes of an attend workgroup.
+__host__ __device__ inline size_t attend_lds_bytes(int kbuf_words, int vbuf_words, int nbuf, int group) {
+  const int gm = group <= 4 ? 4 : group <= 8 ? 8 : 16;
+  return (kCommonWords + kWaves * (size_t)wave_lds_words(kbuf_words, vbuf_words, nbuf, gm)) * sizeof(float);
+}
+
+// ----------------------------------------------------------------- split merge + back-projection
+// Split partials cross workgroups (and XCDs, whose L2 caches are not coherent with
+// each other): they are written and read as relaxed device-scope atomics, which
+// bypass the non-coherent cache level, and ordered by the arrival counter after
+// each writer has waited for its stores to complete.  This avoids the whole-cache
+// write-back and invalidate of device-scope fences.
+__device__ inline void part_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float part_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Run by the last workgroup of a (sequence, KV head) to finish its split partials:
+// per query head a log-sum-exp merge over the splits, o~ / l, then o = P_V o~ with
+// P_V read once for all g heads (thread pair per output row, half the codes each).
+// `w` is LDS scratch of at least 2 * 16 + 16 * 128 floats.
+__device__ inline void merge_splits(const AttendArgs& a, int h, int b, float* w) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const HeadDesc& hd = a.heads.h[h];
+  const int g = a.group, rv = hd.rv, ns = a.n_splits;
+  const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
+  float* Mh = w;                  // [16] merged maximum (0 when no split has tokens)
+  float* Ih = w + kMaxGroup;      // [16] 1 / merged sum (0 when empty)
+  float* ot = w + 2 * kMaxGroup;  // [16][128] normalised o~
+  for (int hh = wave; hh < g; hh += kWaves) {
+    const float* part = a.part + (bq0 + hh) * ns * (int64_t)kPartStride;
+    float m = -__builtin_inff();
+    for (int s = lane; s < ns; s += 64) m = fmaxf(m, part_load(part + (int64_t)s * kPartStride));
+    m = wave_max(m);
+    const float mu = m == -__builtin_inff() ? 0.0f : m;
+    float l = 0.0f;
+    for (int s = lane; s < ns; s += 64) {
+      const float* ps = part + (int64_t)s * kPartStride;
+      l = fmaf(exp2f(part_load(ps) - mu), part_load(ps + 1), l);
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      Mh[hh] = mu;
+      Ih[hh] = l > 0.0f ? 1.0f / l : 0.0f;
+    }
+  }
+  __syncthreads();
+  for (int o = tid; o < g * rv; o += 256) {
+    const int hh = o / rv, j = o % rv;
+    const float* part = a.part + (bq0 + hh) * ns * (int64_t)kPartStride;
+    const float mu = Mh[hh];
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+      const float* ps = part + (int64_t)s * kPartStride;
+      acc = fmaf(exp2f(part_load(ps) - mu), part_load(ps + 2 + j), acc);  // empty splits: m = -inf, weight 0
+    }
+    ot[hh * kMaxRank + j] = acc * Ih[hh];
+  }
+  __syncthreads();
+  const float* PV = a.basis_v + hd.boff_v;
+  const int i = tid >> 1, half = tid & 1;
+  const int jh = rv / 2;
+  float acc[kMaxGroup];
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh) acc[hh] = 0.0f;
+  const float* row = PV + (int64_t)i * rv + half * jh;
+  for (int j = 0; j < jh; j += 4) {
+    const float4 pv = *(const float4*)(row + j);
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) {
+      if (hh < g) {
+        const float* o = &ot[hh * kMaxRank + half * jh + j];
+        acc[hh] = fmaf(pv.x, o[0], fmaf(pv.y, o[1], fmaf(pv.z, o[2], fmaf(pv.w, o[3], acc[hh]))));
+      }
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh) {
+    if (hh < g) {
+      const float v = acc[hh] + __shfl_xor(acc[hh], 1);
+      if (half == 0) a.out[(bq0 + hh) * kHeadDim + i] = v;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- wave state and context
+// Running state of one wave: reference maximum, per-lane partial sums of p and
+// p * min_V per head, and the value accumulators of up to 8 N-tiles (lane (n, G)
+// holds heads 4G..4G+3 of codes n*NT + nt).
+template <int GM>
+struct WaveState {
+  float m[GM], l[GM], c[GM];
+  f32x4 acc2[8];
+};
+
+// What a wave's tile loop needs of the kernel prologue.
+struct WaveCtx {
+  rsrc_t rk_, rv_;          // cache regions of this (sequence, KV head)
+  uint32_t* ktile;          // [nbuf][kbuf] K record tiles
+  uint32_t* vtile;          // [nbuf][vbuf] V record tiles
+  float* S;                 // scores, then probabilities, then the zero slot
+  int kbuf, vbuf, nbuf;
+  int t_begin, t_end;       // this wave's tokens
+  int g;
+  int64_t unit;             // sequence * n_kv_heads + KV head
+};
+
+// Query operands and per-head constants written by the prep kernel.
+template <int GM>
+__device__ __attribute__((always_inline)) inline void load_query(const AttendArgs& a, int64_t unit, int nks,
+                                                                 u32x4 (&aq_hi)[4], u32x4 (&aq_lo)[4],
+                                                                 float (&sq)[GM], float (&kf)[GM]) {
+  const int lane = threadIdx.x & 63;
+  const u32x4* aq = (const u32x4*)(a.aq + unit * kAqWords);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks < nks) {
+      aq_hi[ks] = aq[ks * 64 + lane];
+      aq_lo[ks] = aq[256 + ks * 64 + lane];
+    } else {
+      aq_hi[ks] = u32x4{0u, 0u, 0u, 0u};
+      aq_lo[ks] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  const float* hs = a.hs + unit * kHsFloats;
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh) {
+    sq[hh] = uniform(hs[hh]);
+    kf[hh] = uniform(hs[kMaxGroup + hh]);
+  }
+}
+
+template <int GM>
+__device__ __attribute__((always_inline)) inline void init_state(WaveState<GM>& st) {
+  // finite start, so heads >= g never form -inf - -inf
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh) {
+    st.m[hh] = -1e30f;
+    st.l[hh] = 0.0f;
+    st.c[hh] = 0.0f;
+  }
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) st.acc2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Online softmax of one tile, one token per lane (branch-free over heads), after
+// the score phase has left S[token][GM]: s = min_K * sum(q~) + step_K 2^(24-E) S
+// (log2 units), a lazy maximum (the reference only moves when a score exceeds it,
+// so p <= 1), then P = p * step_V as fp16 hi + lo rows for the value MFMAs.
+template <int GM>
+__device__ __attribute__((always_inline)) inline void softmax_tile(const uint32_t* kt, const uint32_t* vt, int wk,
+                                                                   int wv, int nvalid, int g, float* S,
+                                                                   const float (&sq)[GM], const float (&kf)[GM],
+                                                                   WaveState<GM>& st) {
+  const int lane = threadIdx.x & 63, G = lane >> 4;
+  _Float16* P = (_Float16*)S;
+  const bool valid = lane < nvalid;
+  const uint32_t kh = kt[lane * wk];
+  const uint32_t vh = vt[lane * wv];
+  const float muk = f16_bits_to_f32(kh & 0xFFFFu), sgk = f16_bits_to_f32(kh >> 16);
+  const float muv = valid ? f16_bits_to_f32(vh & 0xFFFFu) : 0.0f;
+  const float sgv = valid ? f16_bits_to_f32(vh >> 16) : 0.0f;
+  lds_fence();
+  float s[GM];
+#pragma unroll
+  for (int q4 = 0; q4 < GM / 4; ++q4) {
+    const f32x4 d = *(const f32x4*)(S + lane * GM + 4 * q4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int hh = 4 * q4 + e;
+      const float x = fmaf(sgk * kf[hh], d[e], muk * sq[hh]);
+      s[hh] = (valid && hh < g) ? x : -__builtin_inff();
+    }
+  }
+  bool up = false;
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh) up |= s[hh] > st.m[hh];
+  if (__any(up)) {
+    float alpha[GM];
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh) {
+      const float mn = fmaxf(st.m[hh], wave_max_uniform(s[hh]));
+      alpha[hh] = exp2f(st.m[hh] - mn);  // 1 if unchanged, 0 on the first tile
+      st.m[hh] = mn;
+      st.l[hh] *= alpha[hh];
+      st.c[hh] *= alpha[hh];
+    }
+    // value accumulators: lane (n, G) holds heads 4G..4G+3; alpha through LDS
+    lds_fence();
+    if (lane == 0) {
+#pragma unroll
+      for (int hh = 0; hh < GM; ++hh) S[hh] = alpha[hh];
+    }
+    lds_fence();
+    const f32x4 f = 4 * G < GM ? *(const f32x4*)(S + 4 * G) : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) st.acc2[nt] *= f;
+    lds_fence();
+  }
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh) {
+    const float p = __builtin_amdgcn_exp2f(s[hh] - st.m[hh]);  // s <= m: p in [0, 1]
+    st.l[hh] += p;
+    st.c[hh] = fmaf(p, muv, st.c[hh]);
+    const float x = p * sgv;
+    const _Float16 hi = (_Float16)x;
+    const _Float16 lo = (_Float16)(x - (float)hi);
+    P[hh * 64 + lane] = hi;
+    P[GM * 64 + hh * 64 + lane] = lo;
+  }
+  lds_fence();
+}
+
+// A operands of value step kk: P rows (hi, lo) for tokens 32kk + 8G .. +7; rows >= GM
+// read the zero slot.
+template <int GM>
+__device__ __attribute__((always_inline)) inline void p_operands(const float* S, int kk, u32x4& ahi, u32x4& alo) {
+  const int lane = threadIdx.x & 63, n = lane & 15, G = lane >> 4;
+  const _Float16* P = (const _Float16*)S;
+  ahi = *(const u32x4*)(P + (n < GM ? n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
+  alo = *(const u32x4*)(P + (n < GM ? GM * 64 + n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
+}
+
+// ----------------------------------------------------------------- kernel body
+// Grid (n_splits, n_kv_heads, batch), 256 threads; GM bounds the GQA group (g <= GM).
+// Workgroup x covers tokens [x*split_tokens, (x+1)*split_tokens), a quarter per
+// wave; `run(ctx, state)` streams the wave's records and runs its online softmax.
+// The four wave states are merged in LDS into one partial (m, l, o~[r_V]) per
+// query head and split, and the last workgroup of the (sequence, KV head) to
+// finish merges the splits and writes the output.
+template <int GM, class Run>
+__device__ __attribute__((always_inline)) inline void attend_body(const AttendArgs& a, Run&& run) {
+  extern __shared__ float lds[];
+  const int WA = wave_lds_words(a.kbuf_words, a.vbuf_words, a.nbuf, GM);
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the token loop scalar
+  const HeadDesc& hd = a.heads.h[h];
+  const int g = __builtin_amdgcn_readfirstlane(a.group);
+  const int rv = __builtin_amdgcn_readfirstlane(hd.rv);
+  const int bv = __builtin_amdgcn_readfirstlane(hd.bv);
+  const int NT = rv / 16;
+  const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
+
+  float* ml = lds;                    // per wave: m[16] l[16] c[16]; then the flag word
+  float* areas = lds + kCommonWords;  // per wave: WA words
+  float* wl = areas + wave * WA;
+
+  WaveCtx c;
+  const int wq = (int)(a.split_tokens / kWaves);
+  c.t_begin = (int)blockIdx.x * (int)a.split_tokens + wave * wq;
+  c.t_end = c.t_begin + wq;
+  if (c.t_end > (int)a.n_tokens) c.t_end = (int)a.n_tokens;
+  const int wk = hd.wk, wv = hd.wv;
+  const uint32_t* kreg = a.cache_k + hd.base_k + (int64_t)b * a.capacity * wk;
+  const uint32_t* vreg = a.cache_v + hd.base_v + (int64_t)b * a.capacity * wv;
+  c.rk_ = make_rsrc(kreg, (uint32_t)a.capacity * 4u * wk);
+  c.rv_ = make_rsrc(vreg, (uint32_t)a.capacity * 4u * wv);
+  c.kbuf = a.kbuf_words;
+  c.vbuf = a.vbuf_words;
+  c.nbuf = a.nbuf;
+  c.ktile = (uint32_t*)wl;
+  c.vtile = c.ktile + c.nbuf * c.kbuf;
+  c.S = (float*)(c.vtile + c.nbuf * c.vbuf);
+  c.g = g;
+  c.unit = (int64_t)b * a.n_kv_heads + h;
+
+  WaveState<GM> st;
+  run(c, st);
+  wait_tiles();
+
+  // ---- wave partial: m, l, sum of p*min (per head), o~[head][j] in natural code order
+  const int n = lane & 15, G = lane >> 4;
+  float* mlw = ml + wave * 48;
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh) {
+    const float ls = wave_sum(st.l[hh]);
+    const float cs = wave_sum(st.c[hh]);
+    if (lane == 0 && hh < g) {
+      mlw[hh] = st.m[hh];
+      mlw[16 + hh] = ls;
+      mlw[32 + hh] = cs;
+    }
+  }
+  lds_fence();
+  if (4 * G < GM) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      if (nt < NT) {
+        const float f = ldexpf(1.0f, 24 - v_shift(bv, nt));
+        const int j = n * NT + nt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int hh = 4 * G + e;
+          if (hh < g) wl[hh * rv + j] = fmaf(st.acc2[nt][e], f, mlw[32 + hh]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the four wave partials, one partial per query head
+  float* part0 = a.part + (bq0 * a.n_splits + blockIdx.x) * (int64_t)kPartStride;
+  for (int o = tid; o < g * rv; o += 256) {
+    const int hh = o / rv, j = o % rv;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if ((int)blockIdx.x * (int)a.split_tokens + w * wq < (int)a.n_tokens) M = fmaxf(M, ml[w * 48 + hh]);
+    const float mu = M == -__builtin_inff() ? 0.0f : M;
+    float acc = 0.0f, lacc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if ((int)blockIdx.x * (int)a.split_tokens + w * wq < (int)a.n_tokens) {
+        const float wgt = exp2f(ml[w * 48 + hh] - mu);
+        acc = fmaf(wgt, areas[w * WA + hh * rv + j], acc);
+        lacc = fmaf(wgt, ml[w * 48 + 16 + hh], lacc);
+      }
+    }
+    float* ph = part0 + (int64_t)hh * a.n_splits * kPartStride;
+    part_store(ph + 2 + j, acc);
+    if (j == 0) {
+      part_store(ph, M);
+      part_store(ph + 1, lacc);
+    }
+  }
+
+  // ---- arrival: the last workgroup of this (sequence, KV head) merges all splits
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores have completed
+  __syncthreads();
+  uint32_t* flag = (uint32_t*)(ml + kWaves * 48);
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(a.cnt + c.unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = prev + 1u == (uint32_t)a.n_splits ? 1u : 0u;
+  }
+  __syncthreads();
+  if (*flag == 0u) return;
+  merge_splits(a, h, b, areas);
+}
+
+}  // namespace kvtc

@@ -32,8 +32,9 @@ struct AttendArgs {
   const uint32_t* cache_k;
   const uint32_t* cache_v;
   float* out;
-  float* qt;     // [batch][n_q_heads][kQtStride] projected, pre-scaled queries
-  float* sq;     // [batch][n_q_heads] sum of the projected query
+  uint32_t* aq;  // [batch][n_kv_heads][kAqWords] query MFMA operands (written by the prep kernel)
+  float* hs;     // [batch][n_kv_heads][kHsFloats] per-head constants of the projected queries
+  uint32_t* cnt; // [batch][n_kv_heads] split arrival counters (zeroed by the prep kernel)
   float* part;   // [batch][n_q_heads][n_splits][kPartStride]
   int64_t n_tokens;
   int64_t capacity;
@@ -50,11 +51,20 @@ struct AttendArgs {
   int32_t nbuf;        // tile buffers per wave: 2 (next tile streams in) or 1
 };
 
+// Kernel arguments travel in the kernarg segment, at most 4 KB.
+static_assert(sizeof(AttendArgs) <= 4096, "AttendArgs exceeds the kernel argument limit");
+static_assert(sizeof(EncodeArgs) <= 4096, "EncodeArgs exceeds the kernel argument limit");
+
 hipError_t launch_quantize_pack(const float* coords, int64_t n, int r, int b, uint32_t* records,
                                 hipStream_t s);
 hipError_t launch_unpack(const uint32_t* records, int64_t n, int r, int b, uint16_t* min_step,
                          uint8_t* codes, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+// Decode attention specialised for the record formats of one budget class (group <= 8).
+hipError_t launch_attend_spec0(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_spec1(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_spec2(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_spec3(const AttendArgs& a, hipStream_t s);
 
 }  // namespace kvtc
