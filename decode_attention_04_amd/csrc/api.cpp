@@ -103,11 +103,12 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
   return KV_OK;
 }
 
-// Default split-K size: about two resident workgroups (8 waves) per CU on the
-// 256 CUs, each split a multiple of 256 tokens (64 per wave).
+// Default split-K size: one workgroup for every resident slot of the 256 CUs
+// (as many per CU as the layout's kernel and LDS use allow), each split a
+// multiple of 256 tokens (64 per wave).
 int64_t default_split_tokens(const Layout& L, int64_t T) {
   const int64_t units = (int64_t)L.batch * L.n_kv;
-  const int64_t target = 512;
+  const int64_t target = 256 * (int64_t)plan_attend(L.table, L.n_kv, L.group).wg_per_cu;
   int64_t ns = (target + units - 1) / units;
   if (ns < 1) ns = 1;
   int64_t st = (T + ns - 1) / ns;

@@ -508,8 +508,16 @@ __device__ __attribute__((always_inline)) inline void init_state(WaveState<GM>& 
 
 // Online softmax of one tile, one token per lane (branch-free over heads), after
 // the score phase has left S[token][GM]: s = min_K * sum(q~) + step_K 2^(24-E) S
-// (log2 units), a lazy maximum (the reference only moves when a score exceeds it,
-// so p <= 1), then P = p * step_V as fp16 hi + lo rows for the value MFMAs.
+// (log2 units).  Each head keeps a reference M that bounds the log2 value weight
+// u = s + log2(step_V) of every token seen (step_V clamped to >= 2^-24), so that
+// x = 2^kPScale * 2^(s - M) * step_V <= 2^kPScale: the value operand P = x (fp16
+// hi + lo) neither overflows nor, for tokens within 2^-28 of the heaviest one,
+// leaves the normal fp16 range.  M moves lazily: only when a token exceeds it, and
+// then to the tile's maximum plus kLazyMargin, so that later tiles rarely move it.
+// p = 2^(s - M) <= 2^24 feeds the fp32 sums l and c.
+constexpr int kPScale = 14;
+constexpr float kLazyMargin = 8.0f;
+
 template <int GM>
 __device__ __attribute__((always_inline)) inline void softmax_tile(const uint32_t* kt, const uint32_t* vt, int wk,
                                                                    int wv, int nvalid, int g, float* S,
@@ -523,8 +531,10 @@ __device__ __attribute__((always_inline)) inline void softmax_tile(const uint32_
   const float muk = f16_bits_to_f32(kh & 0xFFFFu), sgk = f16_bits_to_f32(kh >> 16);
   const float muv = valid ? f16_bits_to_f32(vh & 0xFFFFu) : 0.0f;
   const float sgv = valid ? f16_bits_to_f32(vh >> 16) : 0.0f;
+  const float lsg = __builtin_amdgcn_logf(fmaxf(sgv, 0x1p-24f));  // log2 of the clamped step
+  const float sgx = sgv * (float)(1 << kPScale);
   lds_fence();
-  float s[GM];
+  float s[GM], u[GM];
 #pragma unroll
   for (int q4 = 0; q4 < GM / 4; ++q4) {
     const f32x4 d = *(const f32x4*)(S + lane * GM + 4 * q4);
@@ -533,16 +543,18 @@ __device__ __attribute__((always_inline)) inline void softmax_tile(const uint32_
       const int hh = 4 * q4 + e;
       const float x = fmaf(sgk * kf[hh], d[e], muk * sq[hh]);
       s[hh] = (valid && hh < g) ? x : -__builtin_inff();
+      u[hh] = s[hh] + lsg;
     }
   }
   bool up = false;
 #pragma unroll
-  for (int hh = 0; hh < GM; ++hh) up |= s[hh] > st.m[hh];
+  for (int hh = 0; hh < GM; ++hh) up |= u[hh] > st.m[hh];
   if (__any(up)) {
     float alpha[GM];
 #pragma unroll
     for (int hh = 0; hh < GM; ++hh) {
-      const float mn = fmaxf(st.m[hh], wave_max_uniform(s[hh]));
+      const float mx = wave_max_uniform(u[hh]);
+      const float mn = mx > st.m[hh] ? mx + kLazyMargin : st.m[hh];
       alpha[hh] = exp2f(st.m[hh] - mn);  // 1 if unchanged, 0 on the first tile
       st.m[hh] = mn;
       st.l[hh] *= alpha[hh];
@@ -562,10 +574,10 @@ __device__ __attribute__((always_inline)) inline void softmax_tile(const uint32_
   }
 #pragma unroll
   for (int hh = 0; hh < GM; ++hh) {
-    const float p = __builtin_amdgcn_exp2f(s[hh] - st.m[hh]);  // s <= m: p in [0, 1]
+    const float p = __builtin_amdgcn_exp2f(s[hh] - st.m[hh]);
     st.l[hh] += p;
     st.c[hh] = fmaf(p, muv, st.c[hh]);
-    const float x = p * sgv;
+    const float x = p * sgx;
     const _Float16 hi = (_Float16)x;
     const _Float16 lo = (_Float16)(x - (float)hi);
     P[hh * 64 + lane] = hi;
@@ -650,7 +662,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       if (nt < NT) {
-        const float f = ldexpf(1.0f, 24 - v_shift(bv, nt));
+        const float f = ldexpf(1.0f, 24 - kPScale - v_shift(bv, nt));
         const int j = n * NT + nt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

@@ -74,14 +74,40 @@ __global__ __launch_bounds__(256) void prep_kernel(AttendArgs a) {
   float* Eh = qt + g * kMaxRank;       // [16]
   const float* PK = a.basis_k + hd.boff_k;
   const int npk = kHeadDim * rk;
-  if ((((uintptr_t)PK) & 15) == 0) {  // all loads of the basis in flight at once
-    for (int i = tid; i < npk / 4; i += 256) ((float4*)pk)[i] = ((const float4*)PK)[i];
-  } else {
-    for (int i = tid; i < npk; i += 256) pk[i] = PK[i];
-  }
-  for (int i = tid; i < g * kHeadDim; i += 256) {
-    const int64_t off = bq0 * kHeadDim + i;
-    qr[i] = a.dtype == 0 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
+  // every load of the basis and the queries is issued before the first LDS store
+  {
+    constexpr int kPk4 = kHeadDim * kMaxRank / 4 / 256;  // float4 per thread at r_K = 128
+    constexpr int kQ = kMaxGroup * kHeadDim / 256;        // query values per thread at g = 16
+    float4 r[kPk4];
+    float qv[kQ];
+    const bool vec = (((uintptr_t)PK) & 15) == 0;
+#pragma unroll
+    for (int k = 0; k < kPk4; ++k) {
+      const int i = tid + 256 * k;
+      if (vec && i < npk / 4) r[k] = ((const float4*)PK)[i];
+    }
+#pragma unroll
+    for (int k = 0; k < kQ; ++k) {
+      const int i = tid + 256 * k;
+      if (i < g * kHeadDim) {
+        const int64_t off = bq0 * kHeadDim + i;
+        qv[k] = a.dtype == 0 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
+      }
+    }
+    if (vec) {
+#pragma unroll
+      for (int k = 0; k < kPk4; ++k) {
+        const int i = tid + 256 * k;
+        if (i < npk / 4) ((float4*)pk)[i] = r[k];
+      }
+    } else {
+      for (int i = tid; i < npk; i += 256) pk[i] = PK[i];
+    }
+#pragma unroll
+    for (int k = 0; k < kQ; ++k) {
+      const int i = tid + 256 * k;
+      if (i < g * kHeadDim) qr[i] = qv[k];
+    }
   }
   __syncthreads();
   for (int o = tid; o < g * rk; o += 256) {
@@ -246,52 +272,77 @@ static hipError_t launch_widths(const AttendArgs& a, hipStream_t s) {
   return a.group <= 4 ? launch_gm<4, GEN>(a, s) : a.group <= 8 ? launch_gm<8, GEN>(a, s) : launch_gm<16, GEN>(a, s);
 }
 
-hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
-  AttendArgs a = a_in;
-  int rkm = 16, wkm = 1, wvm = 1;
-  bool gen = false;
-  for (int h = 0; h < a.n_kv_heads; ++h) {
-    const HeadDesc& d = a.heads.h[h];
-    rkm = d.rk > rkm ? d.rk : rkm;
+// Kernel, tile buffers and resident workgroups per CU for a layout.  The
+// specialised kernels fit three waves per SIMD (at most 168 VGPRs), the generic
+// ones two; resident workgroups count for more than a third tile buffer (more
+// waves hide the LDS and matrix-core latencies of the tile loop).
+AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group) {
+  AttendPlan p;
+  int wkm = 1, wvm = 1;
+  for (int h = 0; h < n_kv_heads; ++h) {
+    const HeadDesc& d = heads.h[h];
     wkm = d.wk > wkm ? d.wk : wkm;
     wvm = d.wv > wvm ? d.wv : wvm;
-    gen |= !(pow2_bits(d.bk) && pow2_bits(d.bv));
+    p.gen |= !(pow2_bits(d.bk) && pow2_bits(d.bv));
   }
+  p.spec_class = -1;
+  if (group <= 8) {
+    for (int cls = 0; cls < kSpecClasses && p.spec_class < 0; ++cls) {
+      bool all = true;
+      for (int h = 0; h < n_kv_heads && all; ++h) {
+        const HeadDesc& d = heads.h[h];
+        all = spec_index(cls, d.rk, d.bk, d.rv, d.bv) >= 0;
+      }
+      if (all) p.spec_class = cls;
+    }
+  }
+  // tile buffers: 64 records plus the 16-byte copy granule and one word read past the last record
+  p.kbuf_words = ((64 * wkm + 4 + 3) / 4) * 4;
+  p.vbuf_words = ((64 * wvm + 4 + 3) / 4) * 4;
+  const size_t kLds = 160 * 1024;
+  const int max_wpc = p.spec_class >= 0 ? 3 : 2;
+  p.nbuf = 0;
+  for (int wpc = max_wpc; wpc >= 1 && p.nbuf == 0; --wpc) {
+    for (int nb = 3; nb >= (wpc == 1 ? 1 : 2) && p.nbuf == 0; --nb) {
+      if ((size_t)wpc * attend_lds_bytes(p.kbuf_words, p.vbuf_words, nb, group) <= kLds) {
+        p.nbuf = nb;
+        p.wg_per_cu = wpc;
+      }
+    }
+  }
+  if (p.nbuf == 0) {  // larger than one CU's LDS at one buffer: not reachable for supported formats
+    p.nbuf = 1;
+    p.wg_per_cu = 1;
+  }
+  return p;
+}
+
+hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
+  AttendArgs a = a_in;
+  const AttendPlan p = plan_attend(a.heads, a.n_kv_heads, a.group);
+  int rkm = 16;
+  for (int h = 0; h < a.n_kv_heads; ++h) rkm = a.heads.h[h].rk > rkm ? a.heads.h[h].rk : rkm;
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)a.n_kv_heads, (unsigned)a.batch), dim3(256),
                      prep_lds_bytes(rkm, a.group), s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // tile buffers: 64 records plus the 16-byte copy granule and one word read past the last record
-  a.kbuf_words = ((64 * wkm + 4 + 3) / 4) * 4;
-  a.vbuf_words = ((64 * wvm + 4 + 3) / 4) * 4;
-  // as many tile buffers as keep two workgroups per CU (else one) within 160 KB of LDS
-  const size_t kLds = 160 * 1024;
-  a.nbuf = 1;
-  for (int nb = 3; nb >= 1 && a.nbuf == 1; --nb)
-    if (2 * attend_lds_bytes(a.kbuf_words, a.vbuf_words, nb, a.group) <= kLds) a.nbuf = nb;
-  if (a.nbuf == 1)
-    for (int nb = 3; nb >= 2 && a.nbuf == 1; --nb)
-      if (attend_lds_bytes(a.kbuf_words, a.vbuf_words, nb, a.group) <= kLds) a.nbuf = nb;
-  // a layout whose every head has a format of one budget class runs the specialised kernel
-  if (a.group <= 8) {
-    for (int cls = 0; cls < kSpecClasses; ++cls) {
-      bool all = true;
-      for (int h = 0; h < a.n_kv_heads && all; ++h) {
-        HeadDesc& d = a.heads.h[h];
-        d.spec = spec_index(cls, d.rk, d.bk, d.rv, d.bv);
-        all = d.spec >= 0;
-      }
-      if (!all) continue;
-      switch (cls) {
-        case 0: return launch_attend_spec0(a, s);
-        case 1: return launch_attend_spec1(a, s);
-        case 2: return launch_attend_spec2(a, s);
-        default: return launch_attend_spec3(a, s);
-      }
+  a.kbuf_words = p.kbuf_words;
+  a.vbuf_words = p.vbuf_words;
+  a.nbuf = p.nbuf;
+  if (p.spec_class >= 0) {
+    for (int h = 0; h < a.n_kv_heads; ++h) {
+      HeadDesc& d = a.heads.h[h];
+      d.spec = spec_index(p.spec_class, d.rk, d.bk, d.rv, d.bv);
+    }
+    switch (p.spec_class) {
+      case 0: return launch_attend_spec0(a, s);
+      case 1: return launch_attend_spec1(a, s);
+      case 2: return launch_attend_spec2(a, s);
+      default: return launch_attend_spec3(a, s);
     }
   }
-  // otherwise the generic kernel; all power-of-two widths skip the general-width paths
-  return gen ? launch_widths<true>(a, s) : launch_widths<false>(a, s);
+  // the generic kernel; all power-of-two widths skip the general-width paths
+  return p.gen ? launch_widths<true>(a, s) : launch_widths<false>(a, s);
 }
 
 }  // namespace kvtc

@@ -117,7 +117,7 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
 
 #define KVTC_DEFINE_SPEC_CLASS(CLS)                                                                  \
   template <int GM>                                                                                  \
-  __global__ __launch_bounds__(256, 2) void attend_spec##CLS##_kernel(AttendArgs a) {               \
+  __global__ __launch_bounds__(256, 3) void attend_spec##CLS##_kernel(AttendArgs a) {               \
     attend_body<GM>(a, [&](const WaveCtx& c, WaveState<GM>& st) {                                    \
       switch (__builtin_amdgcn_readfirstlane(a.heads.h[blockIdx.y].spec)) {                          \
         KVTC_SPEC_CLASS##CLS(KVTC_SPEC_CASE) default : break;                                        \

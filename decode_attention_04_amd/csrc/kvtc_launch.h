@@ -60,6 +60,14 @@ hipError_t launch_quantize_pack(const float* coords, int64_t n, int r, int b, ui
 hipError_t launch_unpack(const uint32_t* records, int64_t n, int r, int b, uint16_t* min_step,
                          uint8_t* codes, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
+// How a layout's decode attention runs: the specialised kernel class (-1: the
+// generic kernel), LDS tile buffers per wave and resident workgroups per CU.
+struct AttendPlan {
+  int spec_class = -1;
+  bool gen = false;
+  int kbuf_words = 0, vbuf_words = 0, nbuf = 1, wg_per_cu = 1;
+};
+AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 // Decode attention specialised for the record formats of one budget class (group <= 8).
 hipError_t launch_attend_spec0(const AttendArgs& a, hipStream_t s);
