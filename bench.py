@@ -169,7 +169,7 @@ def main():
     v_new = torch.from_numpy(W.kv_array(wl, "V", T, 1)[:, :, 0]).to(dev)
     q = torch.from_numpy(W.query_array(wl, 0)).to(dev)
     out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
-    ws = torch.empty(K.kv_workspace_bytes(lay, T + 1) // 4, dtype=torch.float32, device=dev)
+    ws = torch.zeros(K.kv_workspace_bytes(lay, T + 1) // 4, dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(d)
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f} s; {n_rep} layer caches of {cache_bytes / 1e6:.1f} MB; "

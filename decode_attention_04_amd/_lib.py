@@ -170,7 +170,11 @@ def kv_append(layout, k1, v1, pos, basis_k, basis_v, cache_k, cache_v, stream=No
 
 def kv_attend_decode(layout, q, n_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale, out,
                      workspace, split_tokens: int = 0, stream=None):
-    """Decode attention: q [batch, n_q_heads, head_dim] -> out (float32, same shape)."""
+    """Decode attention: q [batch, n_q_heads, head_dim] -> out (float32, same shape).
+
+    ``workspace`` holds at least kv_workspace_bytes(layout, n_tokens, split_tokens)
+    bytes and starts zero-filled (torch.zeros); calls leave its counter words zero.
+    """
     nbytes = workspace.numel() * workspace.element_size()
     _check(_lib.kv_attend_decode_split(layout.ref(), _ptr(q), _dtype_code(q), n_tokens, split_tokens,
                                        _ptr(basis_k), _ptr(basis_v), _ptr(cache_k), _ptr(cache_v),

@@ -118,7 +118,7 @@ int64_t default_split_tokens(const Layout& L, int64_t T) {
 }
 
 struct Workspace {
-  int64_t aq = 0, hs = 0, cnt = 0, part = 0, floats = 0;  // offsets in 4-byte words
+  int64_t cnt = 0, part = 0, floats = 0;  // offsets in 4-byte words
   int32_t n_splits = 1;
   int64_t split_tokens = 0;
 };
@@ -137,10 +137,8 @@ kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Works
   const int64_t units = (int64_t)L.batch * L.n_kv;
   w.split_tokens = split_tokens;
   w.n_splits = (int32_t)ns;
-  w.aq = 0;
-  w.hs = units * kAqWords;
-  w.cnt = w.hs + units * kHsFloats;
-  w.part = w.cnt + ((units + 3) / 4) * 4;
+  w.cnt = 0;
+  w.part = ((units + 3) / 4) * 4;
   w.floats = w.part + nbq * ns * kPartStride;
   return KV_OK;
 }
@@ -255,8 +253,6 @@ kv_status kv_attend_decode_split(const kv_layout* layout, const void* q, kv_dtyp
   a.cache_v = cache_v;
   a.out = out;
   float* ws = (float*)workspace;
-  a.aq = (uint32_t*)(ws + w.aq);
-  a.hs = ws + w.hs;
   a.cnt = (uint32_t*)(ws + w.cnt);
   a.part = ws + w.part;
   a.n_tokens = n_tokens;

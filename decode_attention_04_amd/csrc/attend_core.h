@@ -197,6 +197,25 @@ __device__ inline void k_slot(int G, int nks, int ks, int p, int rk, bool& valid
   }
 }
 
+// k_slot with the width known only at run time (generic kernel).
+__device__ inline void k_slot_rt(int B, int G, int nks, int ks, int p, int rk, bool& valid, int& j_lo, int& j_hi,
+                                 int& s) {
+  const int pi = G * nks * 4 + ks * 4 + p;
+  valid = pi < rk / 2;
+  if (pow2_bits(B)) {
+    const int ppw = 16 / B;
+    const int w = pi / ppw, u = pi % ppw;
+    j_lo = w * (32 / B) + u;
+    j_hi = j_lo + ppw;
+    const int o = ((ks * 4 + p) % ppw) * B;
+    s = o + B <= 10 ? o : o - (B == 2 ? 10 : 8);
+  } else {
+    j_lo = 2 * pi;
+    j_hi = 2 * pi + 1;
+    s = 0;
+  }
+}
+
 // ----------------------------------------------------------------- per-tile phases (records in LDS)
 // Scores of one 64-token tile: four 16-token sub-tiles, C[head][token] on the
 // matrix cores, written to S[token][GM] (log2 units before min/step are applied).
@@ -345,22 +364,27 @@ __device__ inline int v_shift(int B, int nt) {
   }
 }
 
-// Words of LDS per wave: tile buffers for K and V (nbuf each), then the scores
-// S[64][GM] (fp32), overwritten by the probabilities P[2][GM][64] (fp16, hi then
-// lo) once read, and a 4-word zero slot read as the A rows >= GM.
+// LDS of an attend workgroup, in 32-bit words:
+//   common: per wave m[16] l[16] c[16]; a flag word (padded); per head E, sum(q~), 2^(24-E)
+//   scores: per wave S[64][GM] (fp32), overwritten by the probabilities
+//           P[2][GM][64] (fp16, hi then lo) once read, and a 4-word zero slot read
+//           as the A rows >= GM; before the tile loop the whole region holds the
+//           query staging of the projection (q[g][128], q~[g][128])
+//   tiles:  per wave nbuf K and nbuf V record tiles; at the end the wave's value
+//           partial o~[g][r_V], then the split merge's o~[g][128]
 __host__ __device__ constexpr int score_words(int gm) { return 64 * gm + 4; }
-// The area also holds the wave's value partial o~[g][r_V] at the end.
-__host__ __device__ inline int wave_lds_words(int kbuf_words, int vbuf_words, int nbuf, int gm) {
-  const int w = nbuf * (kbuf_words + vbuf_words) + score_words(gm);
+__host__ __device__ inline int tile_lds_words(int kbuf_words, int vbuf_words, int nbuf, int gm) {
+  const int w = nbuf * (kbuf_words + vbuf_words);
   return w > gm * kMaxRank ? w : gm * kMaxRank;
 }
-// Workgroup-common LDS words: per wave m[16] l[16] c[16], then a flag word (padded).
-constexpr int kCommonWords = kWaves * 48 + 4;
+constexpr int kHeadStats = 3 * kMaxGroup;
+constexpr int kCommonWords = kWaves * 48 + 4 + kHeadStats;
 
 // Dynamic LDS bytes of an attend workgroup.
 __host__ __device__ inline size_t attend_lds_bytes(int kbuf_words, int vbuf_words, int nbuf, int group) {
   const int gm = group <= 4 ? 4 : group <= 8 ? 8 : 16;
-  return (kCommonWords + kWaves * (size_t)wave_lds_words(kbuf_words, vbuf_words, nbuf, gm)) * sizeof(float);
+  return (kCommonWords + kWaves * (size_t)(score_words(gm) + tile_lds_words(kbuf_words, vbuf_words, nbuf, gm))) *
+         sizeof(float);
 }
 
 // ----------------------------------------------------------------- split merge + back-projection
@@ -377,63 +401,71 @@ __device__ inline float part_load(const float* p) {
 }
 
 // Run by the last workgroup of a (sequence, KV head) to finish its split partials:
-// per query head a log-sum-exp merge over the splits, o~ / l, then o = P_V o~ with
-// P_V read once for all g heads (thread pair per output row, half the codes each).
-// `w` is LDS scratch of at least 2 * 16 + 16 * 128 floats.
+// each thread merges the splits of its (head, code) pairs with a running
+// log-sum-exp (the loads of 16 splits in flight at once), o~ / l goes to LDS, then
+// o = P_V o~ with each thread's half row of P_V loaded before the merge (thread
+// pair per output row, half the codes each).  `w` is LDS scratch of 16 * 128
+// floats.  The arrival counter is left at zero for the next call.
 __device__ inline void merge_splits(const AttendArgs& a, int h, int b, float* w) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = threadIdx.x;
   const HeadDesc& hd = a.heads.h[h];
   const int g = a.group, rv = hd.rv, ns = a.n_splits;
   const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
-  float* Mh = w;                  // [16] merged maximum (0 when no split has tokens)
-  float* Ih = w + kMaxGroup;      // [16] 1 / merged sum (0 when empty)
-  float* ot = w + 2 * kMaxGroup;  // [16][128] normalised o~
-  for (int hh = wave; hh < g; hh += kWaves) {
-    const float* part = a.part + (bq0 + hh) * ns * (int64_t)kPartStride;
-    float m = -__builtin_inff();
-    for (int s = lane; s < ns; s += 64) m = fmaxf(m, part_load(part + (int64_t)s * kPartStride));
-    m = wave_max(m);
-    const float mu = m == -__builtin_inff() ? 0.0f : m;
-    float l = 0.0f;
-    for (int s = lane; s < ns; s += 64) {
-      const float* ps = part + (int64_t)s * kPartStride;
-      l = fmaf(exp2f(part_load(ps) - mu), part_load(ps + 1), l);
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-      Mh[hh] = mu;
-      Ih[hh] = l > 0.0f ? 1.0f / l : 0.0f;
-    }
-  }
-  __syncthreads();
+  const int i = tid >> 1, half = tid & 1, jh = rv / 2;
+  const float* row = a.basis_v + hd.boff_v + (int64_t)i * rv + half * jh;
+  float4 pv[kMaxRank / 8];
+#pragma unroll
+  for (int k = 0; k < kMaxRank / 8; ++k)
+    if (4 * k < jh) pv[k] = *(const float4*)(row + 4 * k);
+  float* ot = w;  // [16][128] normalised o~
   for (int o = tid; o < g * rv; o += 256) {
     const int hh = o / rv, j = o % rv;
     const float* part = a.part + (bq0 + hh) * ns * (int64_t)kPartStride;
-    const float mu = Mh[hh];
-    float acc = 0.0f;
-#pragma unroll 4
-    for (int s = 0; s < ns; ++s) {
-      const float* ps = part + (int64_t)s * kPartStride;
-      acc = fmaf(exp2f(part_load(ps) - mu), part_load(ps + 2 + j), acc);  // empty splits: m = -inf, weight 0
+    float M = -__builtin_inff(), L = 0.0f, A = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += 16) {
+      float mv[16], lv[16], ov[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        mv[k] = -__builtin_inff();
+        lv[k] = 0.0f;
+        ov[k] = 0.0f;
+        if (s0 + k < ns) {
+          const float* ps = part + (int64_t)(s0 + k) * kPartStride;
+          mv[k] = part_load(ps);
+          lv[k] = part_load(ps + 1);
+          ov[k] = part_load(ps + 2 + j);
+        }
+      }
+      float mc = M;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) mc = fmaxf(mc, mv[k]);
+      const float mu = mc == -__builtin_inff() ? 0.0f : mc;  // empty splits carry m = -inf, weight 0
+      const float sc = exp2f(M - mu);
+      L *= sc;
+      A *= sc;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float wgt = exp2f(mv[k] - mu);
+        L = fmaf(wgt, lv[k], L);
+        A = fmaf(wgt, ov[k], A);
+      }
+      M = mc;
     }
-    ot[hh * kMaxRank + j] = acc * Ih[hh];
+    ot[hh * kMaxRank + j] = L > 0.0f ? A / L : 0.0f;
   }
   __syncthreads();
-  const float* PV = a.basis_v + hd.boff_v;
-  const int i = tid >> 1, half = tid & 1;
-  const int jh = rv / 2;
   float acc[kMaxGroup];
 #pragma unroll
   for (int hh = 0; hh < kMaxGroup; ++hh) acc[hh] = 0.0f;
-  const float* row = PV + (int64_t)i * rv + half * jh;
-  for (int j = 0; j < jh; j += 4) {
-    const float4 pv = *(const float4*)(row + j);
 #pragma unroll
-    for (int hh = 0; hh < kMaxGroup; ++hh) {
-      if (hh < g) {
-        const float* o = &ot[hh * kMaxRank + half * jh + j];
-        acc[hh] = fmaf(pv.x, o[0], fmaf(pv.y, o[1], fmaf(pv.z, o[2], fmaf(pv.w, o[3], acc[hh]))));
+  for (int k = 0; k < kMaxRank / 8; ++k) {
+    if (4 * k < jh) {
+#pragma unroll
+      for (int hh = 0; hh < kMaxGroup; ++hh) {
+        if (hh < g) {
+          const float* o = &ot[hh * kMaxRank + half * jh + 4 * k];
+          acc[hh] = fmaf(pv[k].x, o[0], fmaf(pv[k].y, o[1], fmaf(pv[k].z, o[2], fmaf(pv[k].w, o[3], acc[hh]))));
+        }
       }
     }
   }
@@ -444,6 +476,8 @@ __device__ inline void merge_splits(const AttendArgs& a, int h, int b, float* w)
       if (half == 0) a.out[(bq0 + hh) * kHeadDim + i] = v;
     }
   }
+  if (tid == 0)
+    __hip_atomic_store(a.cnt + (int64_t)b * a.n_kv_heads + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------- wave state and context
@@ -462,35 +496,145 @@ struct WaveCtx {
   uint32_t* ktile;          // [nbuf][kbuf] K record tiles
   uint32_t* vtile;          // [nbuf][vbuf] V record tiles
   float* S;                 // scores, then probabilities, then the zero slot
+  float* stage;             // the workgroup's score region: query staging before the tile loop
+  float* stats;             // per head E, sum(q~), 2^(24-E)
   int kbuf, vbuf, nbuf;
   int t_begin, t_end;       // this wave's tokens
   int g;
   int64_t unit;             // sequence * n_kv_heads + KV head
 };
 
-// Query operands and per-head constants written by the prep kernel.
-template <int GM>
-__device__ __attribute__((always_inline)) inline void load_query(const AttendArgs& a, int64_t unit, int nks,
-                                                                 u32x4 (&aq_hi)[4], u32x4 (&aq_lo)[4],
-                                                                 float (&sq)[GM], float (&kf)[GM]) {
-  const int lane = threadIdx.x & 63;
-  const u32x4* aq = (const u32x4*)(a.aq + unit * kAqWords);
+// Key operand (A of the score MFMA) for one (K-step, lane): row = head (lane % 16),
+// element of pair slot = q~_j * 2^(E_head - s), split into fp16 hi + lo.
+// B = 0: the width bk is known only at run time.
+template <int B>
+__device__ inline void aq_slot(const float* qt, const float* E_h, int g, int rk, int bk, int ks, int lane,
+                               u32x4& hi, u32x4& lo) {
+  const int i = lane & 15, G = lane >> 4;
+  const int nks = rk >= 32 ? rk / 32 : 1;
+  const int E = i < g ? (int)E_h[i] : 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    bool valid;
+    int jl, jh, sh;
+    if constexpr (B == 0) k_slot_rt(bk, G, nks, ks, p, rk, valid, jl, jh, sh);
+    else k_slot<B>(G, nks, ks, p, rk, valid, jl, jh, sh);
+    float xl = 0.0f, xh = 0.0f;
+    if (valid && i < g && ks < nks) {
+      xl = ldexpf(qt[i * kMaxRank + jl], E - sh);
+      xh = ldexpf(qt[i * kMaxRank + jh], E - sh);
+    }
+    const _Float16 hl = (_Float16)xl, hh = (_Float16)xh;
+    const _Float16 ll = (_Float16)(xl - (float)hl), lh = (_Float16)(xh - (float)hh);
+    hi[p] = h2u(hl) | (h2u(hh) << 16);
+    lo[p] = h2u(ll) | (h2u(lh) << 16);
+  }
+}
+
+// The g query heads of this KV head projected into its key basis by the whole
+// workgroup, q~ = scale * log2(e) * P_K^T q (the inverse key transform folded into
+// the query), while the first record tiles stream in.  Wave w owns columns
+// [w r_K / 4, (w+1) r_K / 4) of P_K; its lanes split the 128 rows into groups
+// (each lane loads its column segment once and serves all g heads), and the row
+// groups are summed across lanes.  Then per head the exponent E (max |q~| 2^E <
+// 2^14), sum(q~) and 2^(24-E), and each wave's MFMA A operands of q~ (B: the key
+// code width as unpacked by the score phase, 0 to read it from the head at run time).
+template <int GM, int B>
+__device__ __attribute__((always_inline)) inline void project_query(const AttendArgs& a, const WaveCtx& c, int rk,
+                                                                    u32x4 (&aq_hi)[4], u32x4 (&aq_lo)[4],
+                                                                    float (&sq)[GM], float (&kf)[GM]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.y, b = blockIdx.z, g = c.g;
+  const HeadDesc& hd = a.heads.h[h];
+  const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
+  float* qs = c.stage;                    // [128][GM] raw queries, row-major over the head dimension
+  float* qt = c.stage + GM * kHeadDim;    // [g][kMaxRank] projected
+  const int cw = rk / 4;                  // columns per wave
+  const int rg = 64 / cw;                 // row groups per column
+  const int rpg = kHeadDim / rg;          // rows per group (r_K / 2)
+  const int jj = lane % cw, rgi = lane / cw;
+  const int j = wave * cw + jj;
+  const float* col = a.basis_k + hd.boff_k + (int64_t)(rgi * rpg) * rk + j;
+  // every load in flight before the first use: the column segment, then the queries
+  float pk[kMaxRank / 2];
+#pragma unroll
+  for (int k = 0; k < kMaxRank / 2; ++k)
+    if (k < rpg) pk[k] = col[(int64_t)k * rk];
+  constexpr int kQ = GM * kHeadDim / 256;
+  float qv[kQ];
+#pragma unroll
+  for (int k = 0; k < kQ; ++k) {
+    const int idx = tid + 256 * k;
+    qv[k] = 0.0f;
+    if (idx < g * kHeadDim) {
+      const int64_t off = bq0 * kHeadDim + idx;
+      qv[k] = a.dtype == 0 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kQ; ++k) {
+    const int idx = tid + 256 * k;  // head idx / 128, dimension idx % 128
+    qs[(idx % kHeadDim) * GM + idx / kHeadDim] = qv[k];
+  }
+  __syncthreads();
+  for (int h4 = 0; h4 < g; h4 += 4) {  // four heads at a time; the column segment stays in registers
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kMaxRank / 2; ++k) {
+      if (k < rpg) {
+        const f32x4 qq = *(const f32x4*)(qs + (rgi * rpg + k) * GM + h4);
+        acc[0] = fmaf(pk[k], qq[0], acc[0]);
+        acc[1] = fmaf(pk[k], qq[1], acc[1]);
+        acc[2] = fmaf(pk[k], qq[2], acc[2]);
+        acc[3] = fmaf(pk[k], qq[3], acc[3]);
+      }
+    }
+    for (int off = cw; off < 64; off <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off);
+    }
+    if (rgi == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (h4 + e < g) qt[(h4 + e) * kMaxRank + j] = acc[e] * a.scale_log2;
+    }
+  }
+  __syncthreads();
+  float* Eh = c.stats;
+  for (int hh = wave; hh < g; hh += kWaves) {  // one wave per head: sum and max |q~| over the rank
+    const float v0 = lane < rk ? qt[hh * kMaxRank + lane] : 0.0f;
+    const float v1 = lane + 64 < rk ? qt[hh * kMaxRank + lane + 64] : 0.0f;
+    const float sum = wave_sum(v0 + v1);
+    const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    int e = 0;
+    if (mx > 0.0f) {
+      frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
+      e = 14 - e;      // max |q~| * 2^E < 2^14
+    }
+    if (lane == 0) {
+      Eh[hh] = (float)e;
+      Eh[kMaxGroup + hh] = sum;
+      Eh[2 * kMaxGroup + hh] = ldexpf(1.0f, 24 - e);
+    }
+  }
+  __syncthreads();
+  const int nks = rk >= 32 ? rk / 32 : 1;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (ks < nks) {
-      aq_hi[ks] = aq[ks * 64 + lane];
-      aq_lo[ks] = aq[256 + ks * 64 + lane];
+      aq_slot<B>(qt, Eh, g, rk, hd.bk, ks, lane, aq_hi[ks], aq_lo[ks]);
     } else {
       aq_hi[ks] = u32x4{0u, 0u, 0u, 0u};
       aq_lo[ks] = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  const float* hs = a.hs + unit * kHsFloats;
 #pragma unroll
   for (int hh = 0; hh < GM; ++hh) {
-    sq[hh] = uniform(hs[hh]);
-    kf[hh] = uniform(hs[kMaxGroup + hh]);
+    sq[hh] = hh < g ? uniform(Eh[kMaxGroup + hh]) : 0.0f;
+    kf[hh] = hh < g ? uniform(Eh[2 * kMaxGroup + hh]) : 0.0f;
   }
+  __syncthreads();  // the staging region becomes the waves' score areas
 }
 
 template <int GM>
@@ -606,7 +750,7 @@ __device__ __attribute__((always_inline)) inline void p_operands(const float* S,
 template <int GM, class Run>
 __device__ __attribute__((always_inline)) inline void attend_body(const AttendArgs& a, Run&& run) {
   extern __shared__ float lds[];
-  const int WA = wave_lds_words(a.kbuf_words, a.vbuf_words, a.nbuf, GM);
+  const int WA = tile_lds_words(a.kbuf_words, a.vbuf_words, a.nbuf, GM);
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the token loop scalar
@@ -617,8 +761,9 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   const int NT = rv / 16;
   const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
 
-  float* ml = lds;                    // per wave: m[16] l[16] c[16]; then the flag word
-  float* areas = lds + kCommonWords;  // per wave: WA words
+  float* ml = lds;                                    // per wave: m[16] l[16] c[16]; then the flag word
+  float* scores = lds + kCommonWords;                 // per wave: score_words(GM)
+  float* areas = scores + kWaves * score_words(GM);   // per wave: WA words of record tiles
   float* wl = areas + wave * WA;
 
   WaveCtx c;
@@ -636,7 +781,9 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   c.nbuf = a.nbuf;
   c.ktile = (uint32_t*)wl;
   c.vtile = c.ktile + c.nbuf * c.kbuf;
-  c.S = (float*)(c.vtile + c.nbuf * c.vbuf);
+  c.S = scores + wave * score_words(GM);
+  c.stage = scores;
+  c.stats = ml + kWaves * 48 + 4;
   c.g = g;
   c.unit = (int64_t)b * a.n_kv_heads + h;
 

@@ -25,143 +25,6 @@
 
 namespace kvtc {
 
-// ----------------------------------------------------------------- query operands
-// Key operand (A of the score MFMA) for one (K-step, lane): row = head (lane % 16),
-// element of pair slot = q~_j * 2^(E_head - s), split into fp16 hi + lo.
-template <int B>
-__device__ inline void aq_slot(const float* qt, const float* E_h, int g, int rk, int ks, int lane, u32x4& hi,
-                               u32x4& lo) {
-  const int i = lane & 15, G = lane >> 4;
-  const int nks = rk >= 32 ? rk / 32 : 1;
-  const int E = i < g ? (int)E_h[i] : 0;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    bool valid;
-    int jl, jh, sh;
-    k_slot<B>(G, nks, ks, p, rk, valid, jl, jh, sh);
-    float xl = 0.0f, xh = 0.0f;
-    if (valid && i < g && ks < nks) {
-      xl = ldexpf(qt[i * kMaxRank + jl], E - sh);
-      xh = ldexpf(qt[i * kMaxRank + jh], E - sh);
-    }
-    const _Float16 hl = (_Float16)xl, hh = (_Float16)xh;
-    const _Float16 ll = (_Float16)(xl - (float)hl), lh = (_Float16)(xh - (float)hh);
-    hi[p] = h2u(hl) | (h2u(hh) << 16);
-    lo[p] = h2u(ll) | (h2u(lh) << 16);
-  }
-}
-
-// Dynamic LDS of prep_kernel: P_K [128][r_K], q [g][128], q~ [g][128], E [16].
-__host__ __device__ inline size_t prep_lds_bytes(int rk, int g) {
-  return ((size_t)kHeadDim * rk + 2 * (size_t)g * kHeadDim + 16) * sizeof(float);
-}
-
-// Grid (n_kv_heads, batch), 256 threads: projects the g query heads of one KV head
-// into its key basis once per call, q~ = scale * log2(e) * P_K^T q (the inverse key
-// transform folded into the query), and stores the MFMA A operands of q~ with a
-// per-head exponent E (max |q~| 2^E < 2^14), sum(q~), 2^(24-E), and a zero arrival
-// counter for the split merge.
-__global__ __launch_bounds__(256) void prep_kernel(AttendArgs a) {
-  extern __shared__ float lds[];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const HeadDesc& hd = a.heads.h[h];
-  const int g = a.group, rk = hd.rk, bk = hd.bk;
-  const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
-  const int64_t unit = (int64_t)b * a.n_kv_heads + h;
-  float* pk = lds;                     // [128][rk]
-  float* qr = pk + kHeadDim * rk;      // [g][128]
-  float* qt = qr + g * kHeadDim;       // [g][kMaxRank]
-  float* Eh = qt + g * kMaxRank;       // [16]
-  const float* PK = a.basis_k + hd.boff_k;
-  const int npk = kHeadDim * rk;
-  // every load of the basis and the queries is issued before the first LDS store
-  {
-    constexpr int kPk4 = kHeadDim * kMaxRank / 4 / 256;  // float4 per thread at r_K = 128
-    constexpr int kQ = kMaxGroup * kHeadDim / 256;        // query values per thread at g = 16
-    float4 r[kPk4];
-    float qv[kQ];
-    const bool vec = (((uintptr_t)PK) & 15) == 0;
-#pragma unroll
-    for (int k = 0; k < kPk4; ++k) {
-      const int i = tid + 256 * k;
-      if (vec && i < npk / 4) r[k] = ((const float4*)PK)[i];
-    }
-#pragma unroll
-    for (int k = 0; k < kQ; ++k) {
-      const int i = tid + 256 * k;
-      if (i < g * kHeadDim) {
-        const int64_t off = bq0 * kHeadDim + i;
-        qv[k] = a.dtype == 0 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
-      }
-    }
-    if (vec) {
-#pragma unroll
-      for (int k = 0; k < kPk4; ++k) {
-        const int i = tid + 256 * k;
-        if (i < npk / 4) ((float4*)pk)[i] = r[k];
-      }
-    } else {
-      for (int i = tid; i < npk; i += 256) pk[i] = PK[i];
-    }
-#pragma unroll
-    for (int k = 0; k < kQ; ++k) {
-      const int i = tid + 256 * k;
-      if (i < g * kHeadDim) qr[i] = qv[k];
-    }
-  }
-  __syncthreads();
-  for (int o = tid; o < g * rk; o += 256) {
-    const int hh = o / rk, j = o % rk;
-    const float* qh = qr + hh * kHeadDim;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int i = 0; i < kHeadDim; ++i) acc = fmaf(pk[i * rk + j], qh[i], acc);
-    qt[hh * kMaxRank + j] = acc * a.scale_log2;
-  }
-  __syncthreads();
-  float* hs = a.hs + unit * kHsFloats;
-  {
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    for (int hh = wave; hh < kMaxGroup; hh += 4) {  // one wave per head: sum and max |q~| over the rank
-      float sum = 0.0f, mx = 0.0f;
-      if (hh < g) {
-        for (int j = lane; j < rk; j += 64) {
-          const float v = qt[hh * kMaxRank + j];
-          sum += v;
-          mx = fmaxf(mx, fabsf(v));
-        }
-      }
-      sum = wave_sum(sum);
-      mx = wave_max(mx);
-      int e = 0;
-      if (mx > 0.0f) {
-        frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
-        e = 14 - e;      // max |q~| * 2^E < 2^14
-      }
-      if (lane == 0) {
-        Eh[hh] = (float)e;
-        hs[hh] = sum;                                           // 0 for heads >= g
-        hs[kMaxGroup + hh] = hh < g ? ldexpf(1.0f, 24 - e) : 0.0f;
-      }
-    }
-  }
-  if (tid == 0) __hip_atomic_store(a.cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  {
-    const int ks = tid >> 6, lane = tid & 63;
-    u32x4 hi, lo;
-    switch (pow2_bits(bk) ? bk : 3) {  // general widths share the adjacent-pair slot map
-      case 2: aq_slot<2>(qt, Eh, g, rk, ks, lane, hi, lo); break;
-      case 4: aq_slot<4>(qt, Eh, g, rk, ks, lane, hi, lo); break;
-      case 8: aq_slot<8>(qt, Eh, g, rk, ks, lane, hi, lo); break;
-      default: aq_slot<3>(qt, Eh, g, rk, ks, lane, hi, lo); break;
-    }
-    u32x4* aq = (u32x4*)(a.aq + unit * kAqWords);
-    aq[ks * 64 + lane] = hi;
-    aq[256 + ks * 64 + lane] = lo;
-  }
-}
-
 #define KVTC_K_CASE(B)                                                              \
   case B:                                                                           \
     if (nks == 1) k_phase<B, 1, GM>(kt, wk, aq_hi, aq_lo, S);                       \
@@ -200,7 +63,7 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
   }
   u32x4 aq_hi[4], aq_lo[4];
   float sq[GM], kf[GM];
-  load_query<GM>(a, c.unit, nks, aq_hi, aq_lo, sq, kf);
+  project_query<GM, 0>(a, c, rk, aq_hi, aq_lo, sq, kf);
   init_state(st);
   float* S = c.S;
   f32x4 (&acc2)[8] = st.acc2;
@@ -320,12 +183,6 @@ AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group) {
 hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
   AttendArgs a = a_in;
   const AttendPlan p = plan_attend(a.heads, a.n_kv_heads, a.group);
-  int rkm = 16;
-  for (int h = 0; h < a.n_kv_heads; ++h) rkm = a.heads.h[h].rk > rkm ? a.heads.h[h].rk : rkm;
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)a.n_kv_heads, (unsigned)a.batch), dim3(256),
-                     prep_lds_bytes(rkm, a.group), s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   a.kbuf_words = p.kbuf_words;
   a.vbuf_words = p.vbuf_words;
   a.nbuf = p.nbuf;

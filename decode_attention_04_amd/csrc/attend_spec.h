@@ -76,7 +76,7 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
     if (t_begin + t * kTileT < t_end) issue_tile<WK, WV>(c, t_begin + t * kTileT, t_end, t);
   u32x4 aq_hi[4], aq_lo[4];
   float sq[GM], kf[GM];
-  load_query<GM>(a, c.unit, NKS, aq_hi, aq_lo, sq, kf);
+  project_query<GM, BK>(a, c, RK, aq_hi, aq_lo, sq, kf);
   init_state(st);
   if (lane < 4) ((uint32_t*)c.S)[GM * 64 + lane] = 0u;  // zero slot
   int slot = 0;

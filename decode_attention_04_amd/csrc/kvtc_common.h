@@ -19,8 +19,6 @@ constexpr int kMaxBits = 8;
 constexpr int kMaxWords = 1 + (kMaxRank * kMaxBits + 31) / 32;  // 33
 constexpr int kSplitQuantum = 256;  // split-K sizes are multiples of this
 constexpr int kPartStride = 132;    // floats per split partial: m, l, o~[128], pad
-constexpr int kAqWords = 2 * 4 * 64 * 4;  // query MFMA operands per (sequence, KV head): hi/lo x 4 K-steps x 64 lanes
-constexpr int kHsFloats = 32;             // per (sequence, KV head): sum(q~)[16], 2^(24-E)[16]
 
 __host__ __device__ inline int record_words(int r, int b) { return 1 + (r * b + 31) / 32; }
 

@@ -32,9 +32,7 @@ struct AttendArgs {
   const uint32_t* cache_k;
   const uint32_t* cache_v;
   float* out;
-  uint32_t* aq;  // [batch][n_kv_heads][kAqWords] query MFMA operands (written by the prep kernel)
-  float* hs;     // [batch][n_kv_heads][kHsFloats] per-head constants of the projected queries
-  uint32_t* cnt; // [batch][n_kv_heads] split arrival counters (zeroed by the prep kernel)
+  uint32_t* cnt; // [batch][n_kv_heads] split arrival counters: zero on entry, left zero
   float* part;   // [batch][n_q_heads][n_splits][kPartStride]
   int64_t n_tokens;
   int64_t capacity;

@@ -121,7 +121,12 @@ kv_status kv_append(const kv_layout *layout, const void *k1, const void *v1, kv_
  *   out: [batch][n_q_heads][head_dim] float32, fully overwritten
  *   softmax_scale: multiplies q . k (1/sqrt(head_dim) for standard attention)
  *   workspace: at least kv_workspace_bytes(layout, n_tokens) bytes, 16-byte
- *              aligned; its contents on entry are ignored.
+ *              aligned, caller-owned.  Its first 4 * batch * n_kv_heads bytes
+ *              are split arrival counters: they must be zero before the first
+ *              call (zero-fill a new workspace, and again after using it for
+ *              anything else) and every completed call leaves them zero; the
+ *              rest is scratch whose contents on entry are ignored.  Calls that
+ *              share a workspace must not overlap in time.
  * n_tokens == 0 writes zeros to `out`.  Errors: KV_ERR_CAPACITY if
  * n_tokens > capacity; KV_ERR_INVALID if the workspace is too small.
  * [KV-COBRA project page, "Efficiency"; pith.science NOVA-KV verdict,

@@ -171,7 +171,7 @@ def test_append_matches_oracle(K):
 def _attend(K, lay, q, T, bases_k, bases_v, ck, cv, split=0, qdtype=torch.float16):
     B, hq = lay.batch, lay.n_q_heads
     out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(K.kv_workspace_bytes(lay, T, split) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(K.kv_workspace_bytes(lay, T, split) // 4, dtype=torch.float32, device="cuda")
     K.kv_attend_decode(lay, H.dev(q, qdtype), T, H.dev(codec.concat_bases(bases_k)),
                        H.dev(codec.concat_bases(bases_v)), ck, cv, H.SCALE, out, ws, split_tokens=split)
     torch.cuda.synchronize()
@@ -231,6 +231,52 @@ def test_attention_short_and_ragged_contexts(K, T):
     alloc = [(64, 4, 32, 8), (16, 8, 128, 2)]
     bk, bv = _mixed_bases(alloc, seed=17)
     _attention_case(K, alloc, bk, bv, 2, 3, T, T, [0])
+
+
+def _budget_formats(budget_bits):
+    """(rank, bits) the per-head search can pick under one budget of bits per vector:
+    b = min(8, floor(budget / r)) for every rank with b >= 2."""
+    return [(r, min(8, budget_bits // r)) for r in (16, 32, 64, 128) if min(8, budget_bits // r) >= 2]
+
+
+@pytest.mark.parametrize("budget", [64, 128, 256, 512])
+@pytest.mark.parametrize("g", [4, 7])
+def test_attention_every_format_pair_of_a_budget(K, budget, g):
+    """All (K, V) format pairs of one budget in one layout (the specialised kernels)."""
+    fm = _budget_formats(budget)
+    alloc = [(rk, bk, rv, bv) for (rk, bk) in fm for (rv, bv) in fm]
+    say(f"attention budget {budget} bits, g={g}, {len(alloc)} heads")
+    bk, bv = _mixed_bases(alloc, seed=31 + budget + g)
+    _attention_case(K, alloc, bk, bv, 1, g, 800, 777, [0, 256])
+
+
+def test_attention_workspace_reuse_across_calls(K):
+    """One zero-filled workspace serves consecutive calls with different split counts:
+    every call leaves its split arrival counters at zero for the next."""
+    say("attention: one workspace, several calls")
+    wl = W.LLAMA_T32K
+    alloc = [(64, 4, 64, 4), (128, 2, 32, 8)]
+    bk, bv = _mixed_bases(alloc, seed=23)
+    B, g, T = 2, 4, 1500
+    ck_h, cv_h = H.oracle_cache(wl, alloc, bk, bv, B, T, T,
+                                kv={(t, b, h): W.tokens(wl, t, b, h, 0, T) for t in "KV" for b in range(B) for h in range(2)})
+    q = W.random_vectors(29, (B, 2 * g, 128)).astype(np.float16)
+    ref = attention.attend_cache(q.astype(np.float64), bk, bv, ck_h, cv_h, alloc, B, T, T, H.SCALE)
+    lay = K.Layout(2, 2 * g, B, T, alloc)
+    ck, cv = H.u32_dev(ck_h), H.u32_dev(cv_h)
+    splits = [256, 0, 512, 256, 1536]
+    ws = torch.zeros(max(K.kv_workspace_bytes(lay, T, s) for s in splits) // 4, dtype=torch.float32, device="cuda")
+    pk, pv = H.dev(codec.concat_bases(bk)), H.dev(codec.concat_bases(bv))
+    qd = H.dev(q, torch.float16)
+    for split in splits:
+        out = torch.empty((B, 2 * g, 128), dtype=torch.float32, device="cuda")
+        K.kv_attend_decode(lay, qd, T, pk, pv, ck, cv, H.SCALE, out, ws, split_tokens=split)
+        torch.cuda.synchronize()
+        err = H.rel_err_per_head(out.cpu().numpy(), ref)
+        say(f"  split={split} max rel err {err:.3e}")
+        assert err <= REL_TOL
+    cnt = ws[: 2 * B].view(torch.int32).cpu().numpy()
+    assert (cnt == 0).all()
 
 
 def test_attention_empty_context_is_zero(K):
