@@ -51,6 +51,24 @@ __device__ inline float wave_max_uniform(float x) {
   const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
+template <int CTRL>
+__device__ inline float dpp_add(float x) {
+  const int y = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false);
+  return x + __builtin_bit_cast(float, y);
+}
+// Wave-uniform sum: DPP within rows of 16 lanes, then the four row results.
+__device__ inline float wave_sum_uniform(float x) {
+  x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_add<0x141>(x);  // row_half_mirror
+  x = dpp_add<0x140>(x);  // row_mirror
+  const int xi = __builtin_bit_cast(int, x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+  return (r0 + r1) + (r2 + r3);
+}
 __device__ inline float wave_sum(float x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
   return x;
@@ -399,59 +417,102 @@ __device__ inline void part_store(float* p, float v) {
 __device__ inline float part_load(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Two adjacent partial floats (8-byte aligned) in one coherent load.
+__device__ inline void part_load2(const float* p, float& x, float& y) {
+  const uint64_t v = __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  x = __builtin_bit_cast(float, (uint32_t)v);
+  y = __builtin_bit_cast(float, (uint32_t)(v >> 32));
+}
+// Offsets in a split partial: o~[0, r_V), then m and l.
+constexpr int kPartM = kMaxRank, kPartL = kMaxRank + 1;
 
-// Run by the last workgroup of a (sequence, KV head) to finish its split partials:
-// each thread merges the splits of its (head, code) pairs with a running
-// log-sum-exp (the loads of 16 splits in flight at once), o~ / l goes to LDS, then
-// o = P_V o~ with each thread's half row of P_V loaded before the merge (thread
-// pair per output row, half the codes each).  `w` is LDS scratch of 16 * 128
-// floats.  The arrival counter is left at zero for the next call.
+constexpr int kMergeChunk = 8;  // splits whose loads one merging thread has in flight
+
+// Run by the last workgroup of a (sequence, KV head) to finish its split partials.
+// Work item = (head, 4 consecutive codes); with at most 128 items two threads share
+// one, each taking every other kMergeChunk splits.  A thread issues the coherent
+// loads of kMergeChunk splits (o~ quad, m and l) at once and folds them into a
+// running log-sum-exp, with its half row of P_V already loading;
+// the two halves combine through a lane exchange, o~ / l goes to LDS, then
+// o = P_V o~ (thread pair per output row, half the codes each).  `w` is LDS scratch
+// of 16 * 128 floats.  The arrival counter is left at zero for the next call.
 __device__ inline void merge_splits(const AttendArgs& a, int h, int b, float* w) {
   const int tid = threadIdx.x;
   const HeadDesc& hd = a.heads.h[h];
   const int g = a.group, rv = hd.rv, ns = a.n_splits;
   const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
+  float* ot = w;  // [16][128] normalised o~
+  // this thread's half row of P_V for the back-projection, in flight during the merge
   const int i = tid >> 1, half = tid & 1, jh = rv / 2;
   const float* row = a.basis_v + hd.boff_v + (int64_t)i * rv + half * jh;
   float4 pv[kMaxRank / 8];
 #pragma unroll
   for (int k = 0; k < kMaxRank / 8; ++k)
     if (4 * k < jh) pv[k] = *(const float4*)(row + 4 * k);
-  float* ot = w;  // [16][128] normalised o~
-  for (int o = tid; o < g * rv; o += 256) {
-    const int hh = o / rv, j = o % rv;
-    const float* part = a.part + (bq0 + hh) * ns * (int64_t)kPartStride;
-    float M = -__builtin_inff(), L = 0.0f, A = 0.0f;
-    for (int s0 = 0; s0 < ns; s0 += 16) {
-      float mv[16], lv[16], ov[16];
+  const int nq = rv / 4, items = g * nq;
+  const int tpi = items <= 128 ? 2 : 1;
+  for (int t0 = 0; t0 < items * tpi; t0 += 256) {
+    const int t = t0 + tid;
+    const int item = t / tpi, sp = t % tpi;  // sp: which splits of the item this thread takes
+    const int hh = item / nq, jq = item % nq;
+    const bool act = item < items;
+    const float* part = a.part + (bq0 + (act ? hh : 0)) * ns * (int64_t)kPartStride + 4 * jq;
+    float M = -__builtin_inff(), L = 0.0f, A0 = 0.0f, A1 = 0.0f, A2 = 0.0f, A3 = 0.0f;
+    for (int s0 = kMergeChunk * sp; s0 < ns; s0 += kMergeChunk * tpi) {
+      float o[kMergeChunk][4], mv[kMergeChunk], lv[kMergeChunk];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < kMergeChunk; ++k) {
         mv[k] = -__builtin_inff();
         lv[k] = 0.0f;
-        ov[k] = 0.0f;
-        if (s0 + k < ns) {
+        o[k][0] = o[k][1] = o[k][2] = o[k][3] = 0.0f;
+        if (act && s0 + k < ns) {
           const float* ps = part + (int64_t)(s0 + k) * kPartStride;
-          mv[k] = part_load(ps);
-          lv[k] = part_load(ps + 1);
-          ov[k] = part_load(ps + 2 + j);
+          part_load2(ps, o[k][0], o[k][1]);
+          part_load2(ps + 2, o[k][2], o[k][3]);
+          part_load2(ps - 4 * jq + kPartM, mv[k], lv[k]);
         }
       }
       float mc = M;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) mc = fmaxf(mc, mv[k]);
+      for (int k = 0; k < kMergeChunk; ++k) mc = fmaxf(mc, mv[k]);
       const float mu = mc == -__builtin_inff() ? 0.0f : mc;  // empty splits carry m = -inf, weight 0
       const float sc = exp2f(M - mu);
       L *= sc;
-      A *= sc;
+      A0 *= sc;
+      A1 *= sc;
+      A2 *= sc;
+      A3 *= sc;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < kMergeChunk; ++k) {
         const float wgt = exp2f(mv[k] - mu);
         L = fmaf(wgt, lv[k], L);
-        A = fmaf(wgt, ov[k], A);
+        A0 = fmaf(wgt, o[k][0], A0);
+        A1 = fmaf(wgt, o[k][1], A1);
+        A2 = fmaf(wgt, o[k][2], A2);
+        A3 = fmaf(wgt, o[k][3], A3);
       }
       M = mc;
     }
-    ot[hh * kMaxRank + j] = L > 0.0f ? A / L : 0.0f;
+    if (tpi == 2) {  // the two halves of an item sit in adjacent lanes
+      const float Mo = __shfl_xor(M, 1);
+      const float Mx = fmaxf(M, Mo);
+      const float mu = Mx == -__builtin_inff() ? 0.0f : Mx;
+      const float sc = exp2f(M - mu);
+      L *= sc;
+      A0 *= sc;
+      A1 *= sc;
+      A2 *= sc;
+      A3 *= sc;
+      L += __shfl_xor(L, 1);
+      A0 += __shfl_xor(A0, 1);
+      A1 += __shfl_xor(A1, 1);
+      A2 += __shfl_xor(A2, 1);
+      A3 += __shfl_xor(A3, 1);
+    }
+    if (act && sp == 0) {
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      *(f32x4*)(ot + hh * kMaxRank + 4 * jq) = f32x4{A0 * inv, A1 * inv, A2 * inv, A3 * inv};
+    }
   }
   __syncthreads();
   float acc[kMaxGroup];
@@ -796,8 +857,8 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   float* mlw = ml + wave * 48;
 #pragma unroll
   for (int hh = 0; hh < GM; ++hh) {
-    const float ls = wave_sum(st.l[hh]);
-    const float cs = wave_sum(st.c[hh]);
+    const float ls = wave_sum_uniform(st.l[hh]);
+    const float cs = wave_sum_uniform(st.c[hh]);
     if (lane == 0 && hh < g) {
       mlw[hh] = st.m[hh];
       mlw[16 + hh] = ls;
@@ -840,10 +901,10 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
       }
     }
     float* ph = part0 + (int64_t)hh * a.n_splits * kPartStride;
-    part_store(ph + 2 + j, acc);
+    part_store(ph + j, acc);
     if (j == 0) {
-      part_store(ph, M);
-      part_store(ph + 1, lacc);
+      part_store(ph + kPartM, M);
+      part_store(ph + kPartL, lacc);
     }
   }
 
