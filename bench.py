@@ -114,6 +114,51 @@ def cpu_baseline(wl, alloc, bk, bv, T, budget_s=12.0):
     }
 
 
+def sources_digest() -> str:
+    """sha256 over the HIP/C++ sources of the library (which code a counter profile belongs to)."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "decode_attention_04_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attend launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size)
+    from the committed counter profile of this workload, if it was taken on these sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_attend_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("sources_sha256") != sources_digest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
+def copy_probe(mib: int):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counter readings."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 copies of {mib} MiB ({n * 4} bytes read and written each)")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,8 +167,14 @@ def main():
     ap.add_argument("--workload", default="llama-128k-2bpd")
     ap.add_argument("--replica-bytes", type=float, default=1.2e9, help="total bytes of rotated layer caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized device buffer 3 times (calibrates the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         raise SystemExit(2)
@@ -177,36 +228,77 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i):
         ck, cv = caches[i % n_rep]
         K.kv_append(lay, k_new, v_new, T, pk, pv, ck, cv)
-        if ev is not None:
-            ev[0].record(stream)
         K.kv_attend_decode(lay, q, T + 1, pk, pv, ck, cv, scale, out, ws)
-        if ev is not None:
-            ev[1].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ref_out = out.clone()
+
+    # each timed step replays a HIP graph of that step (one graph per layer cache), so
+    # that host launch latency does not sit between the kernels
+    graphs = []
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(n_rep):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for r in range(2):  # replays agree with the eager step, with eager work in between
+            for g in graphs:
+                out.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(out, ref_out), "graph replay differs from the eager step"
+            step(r)
+            torch.cuda.synchronize()
+    steps = args.steps
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
+    for i in range(steps):
+        if graphs:
+            graphs[i % n_rep].replay()
+        else:
+            step(i)
     stop.record(stream)
     torch.cuda.synchronize()
+    assert torch.equal(out, ref_out), "timed steps changed the output"
     total_ms = start.elapsed_time(stop)
-    att_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_step = total_ms / args.steps
-    att_avg = float(np.mean(att_ms))
+    ms_step = total_ms / steps
+
+    # the dominant kernel alone: back-to-back attend launches on the same stream
+    att_ms = []
+    for r in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n_rep * 4):
+            ck, cv = caches[i % n_rep]
+            K.kv_attend_decode(lay, q, T + 1, pk, pv, ck, cv, scale, out, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        att_ms.append(e0.elapsed_time(e1) / (n_rep * 4))
+    att_avg = float(np.median(att_ms))
     attend_bytes, append_bytes = step_bytes(wl, alloc, T + 1)
     gbs = (attend_bytes + append_bytes) / (ms_step * 1e-3) / 1e9
     att_gbs = attend_bytes / (att_avg * 1e-3) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us (attend {att_avg * 1e3:.1f} us, p10 {np.percentile(att_ms, 10) * 1e3:.1f} "
-        f"p90 {np.percentile(att_ms, 90) * 1e3:.1f}); {gbs:.1f} GB/s step, {att_gbs:.1f} GB/s attend "
-        f"({100 * att_gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
+    log(f"step {ms_step * 1e3:.1f} us over {steps} steps{' (graph replays)' if graphs else ''}; "
+        f"attend kernel {att_avg * 1e3:.1f} us (min {min(att_ms) * 1e3:.1f} max {max(att_ms) * 1e3:.1f}); "
+        f"{gbs:.1f} GB/s step, {att_gbs:.1f} GB/s attend ({100 * att_gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
+    traffic = measured_traffic(wl.name)
+    if traffic is not None:
+        log(f"HBM traffic per attend launch from the committed counter profile: {traffic / 1e6:.1f} MB "
+            f"(algorithmic {attend_bytes / 1e6:.1f} MB)")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -218,7 +310,7 @@ def main():
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
@@ -231,6 +323,7 @@ def main():
             "batch": B, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d, "context_tokens": T + 1,
             "allocation": [list(a) for a in alloc],
             "step": "kv_append (1 token) + kv_attend_decode",
+            "timing": "HIP graph replay per step" if graphs else "eager launches",
             "layer_caches_rotated": n_rep,
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "context_tokens_per_s": round(B * (T + 1) / (ms_step * 1e-3), 1),
@@ -244,7 +337,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(att_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
         },
         "cpu_baseline": cpu,
     }
