@@ -320,3 +320,47 @@ def test_end_to_end_encode_append_attend(K):
     err = H.rel_err_per_head(got, ref)
     say(f"  end-to-end max rel err {err:.3e}")
     assert err <= REL_TOL
+
+
+# ------------------------------------------------------------------ full size, sampled
+@pytest.mark.parametrize("bpd", [2.0, 0.5])
+def test_full_size_128k_sampled_units(K, bpd):
+    """The decode configuration at full size (4 sequences x 8 KV heads x 131073 tokens),
+    encoded on the GPU and attended with the default split, in the launch configuration
+    the benchmark times.  Sampled (sequence, KV head) units are re-encoded by the oracle
+    from the same inputs: their records must match (exact headers, codes off by one only
+    at rounding ties) and their query heads' outputs are checked against oracle attention."""
+    wl = W.llama_t128k(bpd)
+    T = wl.context + 1
+    B, hkv, hq, d, g = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.group
+    alloc, bk, bv = H.oracle_calibrate(wl)
+    say(f"full size {wl.name}: {alloc}")
+    lay = K.Layout(hkv, hq, B, T, alloc)
+    ck = torch.zeros(K.kv_cache_bytes(lay, 0) // 4, dtype=torch.int32, device="cuda")
+    cv = torch.zeros(K.kv_cache_bytes(lay, 1) // 4, dtype=torch.int32, device="cuda")
+    pk, pv = H.dev(codec.concat_bases(bk)), H.dev(codec.concat_bases(bv))
+    for t0 in range(0, T, 1 << 15):
+        n = min(1 << 15, T - t0)
+        K.kv_encode(lay, H.dev(W.kv_array(wl, "K", t0, n)), H.dev(W.kv_array(wl, "V", t0, n)), n, t0, pk, pv, ck, cv)
+    q = W.query_array(wl, 0)
+    out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(K.kv_workspace_bytes(lay, T) // 4, dtype=torch.float32, device="cuda")
+    K.kv_attend_decode(lay, H.dev(q), T, pk, pv, ck, cv, H.SCALE, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    gk, gv = H.u32_host(ck), H.u32_host(cv)
+    rk, bits_k, rv, bits_v = zip(*alloc)
+    for b, h in [(0, 0), (3, hkv - 1), (1, 3)]:
+        xk = W.tokens(wl, "K", b, h, 0, T)
+        xv = W.tokens(wl, "V", b, h, 0, T)
+        rec_k = np.concatenate([codec.encode_tokens(xk[i:i + 16384], bk[h], bits_k[h]) for i in range(0, T, 16384)])
+        rec_v = np.concatenate([codec.encode_tokens(xv[i:i + 16384], bv[h], bits_v[h]) for i in range(0, T, 16384)])
+        s0, s1, w = codec.record_slice(rk, bits_k, B, T, h, b, 0, T)
+        fk = _compare_records(gk[s0:s1].reshape(-1, w), rec_k, rk[h], bits_k[h], f"K b{b} h{h}")
+        s0, s1, w = codec.record_slice(rv, bits_v, B, T, h, b, 0, T)
+        fv = _compare_records(gv[s0:s1].reshape(-1, w), rec_v, rv[h], bits_v[h], f"V b{b} h{h}")
+        ref = attention.attend_head_records(q[b, h * g:(h + 1) * g].astype(np.float64), bk[h], rec_k, rk[h], bits_k[h],
+                                            bv[h], rec_v, rv[h], bits_v[h], H.SCALE)
+        err = H.rel_err_per_head(got[b, h * g:(h + 1) * g], ref)
+        say(f"  unit (b={b}, h={h}) {alloc[h]}: code mismatch K {fk:.1e} V {fv:.1e}, max rel err {err:.3e}")
+        assert err <= REL_TOL
