@@ -1,10 +1,12 @@
 """Decode-attention throughput over the transform-coded KV cache on one MI355X.
 
-One step = one decode step of one layer at 128K context: kv_append of the new
-token's key and value (encode: project -> quantize -> pack) followed by
-kv_attend_decode over the T+1 compressed records of every (sequence, KV head)
-(query projection, split-K attention over packed codes, log-sum-exp combine
-and value back-projection).  Inputs are resident in HBM before timing starts;
+One step = one decode step of one layer at 128K context, one launch of
+kv_append_attend_decode: the append of the new token's key and value (encode:
+project -> quantize -> pack) and the attention over the T+1 compressed records
+of every (sequence, KV head) (query projection, split-K attention over packed
+codes, log-sum-exp combine and value back-projection).  Before timing, the same
+step as two calls (kv_append, then kv_attend_decode) must give a bit-identical
+output.  Inputs are resident in HBM before timing starts;
 steps rotate over several layer caches (>= 1 GB in total) so that no step is
 served from the 256 MB Infinity Cache.
 
@@ -129,9 +131,9 @@ def sources_digest() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per attend launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size)
+    """HBM bytes per append + attend launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size)
     from the committed counter profile of this workload, if it was taken on these sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_attend_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"traffic_append_attend_{workload}.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -230,13 +232,20 @@ def main():
 
     def step(i):
         ck, cv = caches[i % n_rep]
+        K.kv_append_attend_decode(lay, k_new, v_new, q, T + 1, pk, pv, ck, cv, scale, out, ws)
+
+    # the step as two calls on every cache first: the fused launch must reproduce it bit for bit
+    for ck, cv in caches:
         K.kv_append(lay, k_new, v_new, T, pk, pv, ck, cv)
         K.kv_attend_decode(lay, q, T + 1, pk, pv, ck, cv, scale, out, ws)
-
-    for i in range(args.warmup):
+    torch.cuda.synchronize()
+    two_call_out = out.clone()
+    out.zero_()
+    for i in range(max(args.warmup, n_rep)):
         step(i)
     torch.cuda.synchronize()
     ref_out = out.clone()
+    assert torch.equal(ref_out, two_call_out), "fused append + attend differs from kv_append + kv_attend_decode"
 
     # each timed step replays a HIP graph of that step (one graph per layer cache), so
     # that host launch latency does not sit between the kernels
@@ -277,28 +286,28 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / steps
 
-    # the dominant kernel alone: back-to-back attend launches on the same stream
+    # the step's kernel alone: back-to-back launches on the same stream
     att_ms = []
     for r in range(5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(n_rep * 4):
             ck, cv = caches[i % n_rep]
-            K.kv_attend_decode(lay, q, T + 1, pk, pv, ck, cv, scale, out, ws)
+            K.kv_append_attend_decode(lay, k_new, v_new, q, T + 1, pk, pv, ck, cv, scale, out, ws)
         e1.record(stream)
         torch.cuda.synchronize()
         att_ms.append(e0.elapsed_time(e1) / (n_rep * 4))
     att_avg = float(np.median(att_ms))
     attend_bytes, append_bytes = step_bytes(wl, alloc, T + 1)
     gbs = (attend_bytes + append_bytes) / (ms_step * 1e-3) / 1e9
-    att_gbs = attend_bytes / (att_avg * 1e-3) / 1e9
+    att_gbs = (attend_bytes + append_bytes) / (att_avg * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us over {steps} steps{' (graph replays)' if graphs else ''}; "
-        f"attend kernel {att_avg * 1e3:.1f} us (min {min(att_ms) * 1e3:.1f} max {max(att_ms) * 1e3:.1f}); "
-        f"{gbs:.1f} GB/s step, {att_gbs:.1f} GB/s attend ({100 * att_gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
+        f"append+attend kernel {att_avg * 1e3:.1f} us (min {min(att_ms) * 1e3:.1f} max {max(att_ms) * 1e3:.1f}); "
+        f"{gbs:.1f} GB/s step, {att_gbs:.1f} GB/s kernel ({100 * att_gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
     traffic = measured_traffic(wl.name)
     if traffic is not None:
-        log(f"HBM traffic per attend launch from the committed counter profile: {traffic / 1e6:.1f} MB "
-            f"(algorithmic {attend_bytes / 1e6:.1f} MB)")
+        log(f"HBM traffic per launch from the committed counter profile: {traffic / 1e6:.1f} MB "
+            f"(algorithmic {(attend_bytes + append_bytes) / 1e6:.1f} MB)")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -322,7 +331,7 @@ def main():
             "workload": wl.name,
             "batch": B, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d, "context_tokens": T + 1,
             "allocation": [list(a) for a in alloc],
-            "step": "kv_append (1 token) + kv_attend_decode",
+            "step": "kv_append_attend_decode (append of 1 token fused with the attention)",
             "timing": "HIP graph replay per step" if graphs else "eager launches",
             "layer_caches_rotated": n_rep,
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -332,7 +341,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "kv_attend_decode",
+            "kernel": "kv_append_attend_decode",
             "achieved": round(att_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

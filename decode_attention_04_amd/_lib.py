@@ -20,7 +20,7 @@ KV_F32, KV_F16 = 0, 1
 EXPORTED = (
     "kv_record_words", "kv_cache_bytes", "kv_workspace_bytes", "kv_workspace_bytes_split",
     "kv_encode", "kv_append", "kv_attend_decode", "kv_attend_decode_split",
-    "kv_quantize_pack", "kv_unpack", "kv_last_error",
+    "kv_append_attend_decode", "kv_quantize_pack", "kv_unpack", "kv_last_error",
 )
 
 
@@ -66,6 +66,7 @@ def _load():
         "kv_append": (i32, [L, P, P, i32, i64, P, P, P, P, P]),
         "kv_attend_decode": (i32, [L, P, i32, i64, P, P, P, P, f32, P, P, sz, P]),
         "kv_attend_decode_split": (i32, [L, P, i32, i64, i64, P, P, P, P, f32, P, P, sz, P]),
+        "kv_append_attend_decode": (i32, [L, P, P, i32, P, i32, i64, i64, P, P, P, P, f32, P, P, sz, P]),
         "kv_quantize_pack": (i32, [P, i64, i32, i32, P, P]),
         "kv_unpack": (i32, [P, i64, i32, i32, P, P, P]),
         "kv_last_error": (ctypes.c_char_p, []),
@@ -180,6 +181,17 @@ def kv_attend_decode(layout, q, n_tokens, basis_k, basis_v, cache_k, cache_v, so
                                        _ptr(basis_k), _ptr(basis_v), _ptr(cache_k), _ptr(cache_v),
                                        float(softmax_scale), _ptr(out), _ptr(workspace), nbytes,
                                        _stream(stream)))
+
+
+def kv_append_attend_decode(layout, k1, v1, q, n_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale,
+                            out, workspace, split_tokens: int = 0, stream=None):
+    """Append k1, v1 [batch, n_kv_heads, head_dim] at position n_tokens - 1 and attend
+    over tokens 0 .. n_tokens-1 in one launch (workspace as for kv_attend_decode)."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.kv_append_attend_decode(layout.ref(), _ptr(k1), _ptr(v1), _dtype_code(k1), _ptr(q),
+                                        _dtype_code(q), n_tokens, split_tokens, _ptr(basis_k), _ptr(basis_v),
+                                        _ptr(cache_k), _ptr(cache_v), float(softmax_scale), _ptr(out),
+                                        _ptr(workspace), nbytes, _stream(stream)))
 
 
 def kv_quantize_pack(coords, rank, bits, records, stream=None):

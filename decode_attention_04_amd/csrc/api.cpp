@@ -143,6 +143,52 @@ kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Works
   return KV_OK;
 }
 
+kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_tokens, int64_t split_tokens,
+                      const float* basis_k, const float* basis_v, const uint32_t* cache_k, const uint32_t* cache_v,
+                      float softmax_scale, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                      const void* k1, const void* v1, kv_dtype kv_dt) {
+  if (dtype != KV_F32 && dtype != KV_F16) return fail(KV_ERR_INVALID, "dtype %d unknown", (int)dtype);
+  Workspace w;
+  kv_status s = plan_workspace(L, n_tokens, split_tokens, w);
+  if (s) return s;
+  if (!q || !basis_k || !basis_v || !cache_k || !cache_v || !out || !workspace)
+    return fail(KV_ERR_INVALID, "NULL query, basis, cache, output or workspace pointer");
+  const size_t esz = dtype == KV_F32 ? 4 : 2;
+  if (!aligned(q, esz) || !aligned(basis_k, 4) || !aligned(basis_v, 4) || !aligned(cache_k, 4) ||
+      !aligned(cache_v, 4) || !aligned(out, 4) || !aligned(workspace, 16))
+    return fail(KV_ERR_INVALID, "misaligned pointer");
+  if (workspace_bytes < (size_t)w.floats * 4u)
+    return fail(KV_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes,
+                (size_t)w.floats * 4u);
+  if (!(softmax_scale == softmax_scale)) return fail(KV_ERR_INVALID, "softmax_scale is NaN");
+  AttendArgs a{};
+  a.heads = L.table;
+  a.q = q;
+  a.basis_k = basis_k;
+  a.basis_v = basis_v;
+  a.cache_k = cache_k;
+  a.cache_v = cache_v;
+  a.out = out;
+  float* ws = (float*)workspace;
+  a.cnt = (uint32_t*)(ws + w.cnt);
+  a.part = ws + w.part;
+  a.n_tokens = n_tokens;
+  a.capacity = L.capacity;
+  a.split_tokens = w.split_tokens;
+  a.n_splits = w.n_splits;
+  a.n_kv_heads = L.n_kv;
+  a.n_q_heads = L.n_q;
+  a.group = L.group;
+  a.batch = L.batch;
+  a.dtype = dtype == KV_F32 ? 0 : 1;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.k1 = k1;
+  a.v1 = v1;
+  a.append_pos = k1 ? n_tokens - 1 : -1;
+  a.append_dtype = kv_dt == KV_F32 ? 0 : 1;
+  return device_status(launch_attend(a, (hipStream_t)stream), "attend launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,42 +276,25 @@ kv_status kv_attend_decode_split(const kv_layout* layout, const void* q, kv_dtyp
   Layout L;
   kv_status s = build_layout(layout, L);
   if (s) return s;
-  if (dtype != KV_F32 && dtype != KV_F16) return fail(KV_ERR_INVALID, "dtype %d unknown", (int)dtype);
-  Workspace w;
-  s = plan_workspace(L, n_tokens, split_tokens, w);
+  return attend_impl(L, q, dtype, n_tokens, split_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale, out,
+                     workspace, workspace_bytes, stream, nullptr, nullptr, KV_F32);
+}
+
+kv_status kv_append_attend_decode(const kv_layout* layout, const void* k1, const void* v1, kv_dtype kv_dt,
+                                  const void* q, kv_dtype q_dt, int64_t n_tokens, int64_t split_tokens,
+                                  const float* basis_k, const float* basis_v, uint32_t* cache_k,
+                                  uint32_t* cache_v, float softmax_scale, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Layout L;
+  kv_status s = build_layout(layout, L);
   if (s) return s;
-  if (!q || !basis_k || !basis_v || !cache_k || !cache_v || !out || !workspace)
-    return fail(KV_ERR_INVALID, "NULL query, basis, cache, output or workspace pointer");
-  const size_t esz = dtype == KV_F32 ? 4 : 2;
-  if (!aligned(q, esz) || !aligned(basis_k, 4) || !aligned(basis_v, 4) || !aligned(cache_k, 4) ||
-      !aligned(cache_v, 4) || !aligned(out, 4) || !aligned(workspace, 16))
-    return fail(KV_ERR_INVALID, "misaligned pointer");
-  if (workspace_bytes < (size_t)w.floats * 4u)
-    return fail(KV_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes,
-                (size_t)w.floats * 4u);
-  if (!(softmax_scale == softmax_scale)) return fail(KV_ERR_INVALID, "softmax_scale is NaN");
-  AttendArgs a{};
-  a.heads = L.table;
-  a.q = q;
-  a.basis_k = basis_k;
-  a.basis_v = basis_v;
-  a.cache_k = cache_k;
-  a.cache_v = cache_v;
-  a.out = out;
-  float* ws = (float*)workspace;
-  a.cnt = (uint32_t*)(ws + w.cnt);
-  a.part = ws + w.part;
-  a.n_tokens = n_tokens;
-  a.capacity = L.capacity;
-  a.split_tokens = w.split_tokens;
-  a.n_splits = w.n_splits;
-  a.n_kv_heads = L.n_kv;
-  a.n_q_heads = L.n_q;
-  a.group = L.group;
-  a.batch = L.batch;
-  a.dtype = dtype == KV_F32 ? 0 : 1;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  return device_status(launch_attend(a, (hipStream_t)stream), "attend launch");
+  if (kv_dt != KV_F32 && kv_dt != KV_F16) return fail(KV_ERR_INVALID, "dtype %d unknown", (int)kv_dt);
+  if (n_tokens < 1) return fail(KV_ERR_INVALID, "n_tokens %lld < 1: nothing to append", (long long)n_tokens);
+  if (!k1 || !v1) return fail(KV_ERR_INVALID, "NULL key or value to append");
+  const size_t esz = kv_dt == KV_F32 ? 4 : 2;
+  if (!aligned(k1, esz) || !aligned(v1, esz)) return fail(KV_ERR_INVALID, "misaligned pointer");
+  return attend_impl(L, q, q_dt, n_tokens, split_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale, out,
+                     workspace, workspace_bytes, stream, k1, v1, kv_dt);
 }
 
 kv_status kv_attend_decode(const kv_layout* layout, const void* q, kv_dtype dtype, int64_t n_tokens,

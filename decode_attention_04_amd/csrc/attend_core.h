@@ -4,6 +4,7 @@
 // generic kernel and by the kernels specialised per record format.
 #pragma once
 
+#include "encode_core.h"
 #include "kvtc_common.h"
 #include "kvtc_launch.h"
 
@@ -398,6 +399,12 @@ __host__ __device__ inline int tile_lds_words(int kbuf_words, int vbuf_words, in
 constexpr int kHeadStats = 3 * kMaxGroup;
 constexpr int kCommonWords = kWaves * 48 + 4 + kHeadStats;
 
+// The fused append encodes K and V with one EncodeScratch each in the score and
+// tile areas, which are at least this large for every group size.
+static_assert(2 * sizeof(EncodeScratch) <= sizeof(float) * kWaves * (size_t)(score_words(4) + 4 * kMaxRank),
+              "encode scratch does not fit the score and tile areas");
+static_assert(kCommonWords % 2 == 0, "encode scratch (float64) must start 8-byte aligned");
+
 // Dynamic LDS bytes of an attend workgroup.
 __host__ __device__ inline size_t attend_lds_bytes(int kbuf_words, int vbuf_words, int nbuf, int group) {
   const int gm = group <= 4 ? 4 : group <= 8 ? 8 : 16;
@@ -711,6 +718,19 @@ __device__ __attribute__((always_inline)) inline void init_state(WaveState<GM>& 
   for (int nt = 0; nt < 8; ++nt) st.acc2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Waves of a CU issue by age, so the workgroups resident first finish their splits
+// early and the last ones run their final tiles at lower occupancy.  Each wave
+// raises its issue priority with the share of its tiles still ahead of it, so the
+// waves that are behind catch up and all finish together.
+__device__ inline void progress_priority(int t0, int t_begin, int t_end) {
+  const int left = (t_end - t0 + kTileT - 1) / kTileT, total = (t_end - t_begin + kTileT - 1) / kTileT;
+  const int pr = (4 * left) / (total + 1);
+  if (pr >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+  else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Online softmax of one tile, one token per lane (branch-free over heads), after
 // the score phase has left S[token][GM]: s = min_K * sum(q~) + step_K 2^(24-E) S
 // (log2 units).  Each head keeps a reference M that bounds the log2 value weight
@@ -847,6 +867,26 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   c.stats = ml + kWaves * 48 + 4;
   c.g = g;
   c.unit = (int64_t)b * a.n_kv_heads + h;
+
+  // append fused with attention: the workgroup whose split holds the new token
+  // encodes its key and value (waves 0-1 and 2-3) before any of its tiles stream in
+  if (a.append_pos >= 0 && (int64_t)blockIdx.x == a.append_pos / a.split_tokens) {
+    EncodeScratch* scr = (EncodeScratch*)scores;  // score and tile areas are not in use yet
+    const int tensor = tid >> 7, t = tid & 127;
+    const int r = tensor ? hd.rv : hd.rk, bits = tensor ? hd.bv : hd.bk, W = tensor ? hd.wv : hd.wk;
+    const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
+    const int64_t xo = ((int64_t)b * a.n_kv_heads + h) * kHeadDim;
+    // the fused entry point hands writable caches (kv_append_attend_decode)
+    uint32_t* rec = const_cast<uint32_t*>(tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) +
+                    ((int64_t)b * a.capacity + a.append_pos) * W;
+    auto sync = [] { __syncthreads(); };
+    if (a.append_dtype == 0)
+      encode_token_128((const float*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, rec, scr[tensor], t, sync);
+    else
+      encode_token_128((const _Float16*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, rec, scr[tensor], t, sync);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the records are in L2 before any tile copy
+    __syncthreads();
+  }
 
   WaveState<GM> st;
   run(c, st);

@@ -84,6 +84,7 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
       tile_copy(c.rk_, (uint32_t)tn * 4u * wk, (uint32_t)nn * 4u * wk, c.ktile + sn * c.kbuf);
       tile_copy(c.rv_, (uint32_t)tn * 4u * wv, (uint32_t)nn * 4u * wv, c.vtile + sn * c.vbuf);
     }
+    progress_priority(t0, t_begin, t_end);
     if constexpr (GEN) {
       switch (bk) {
         KVTC_K_CASE(2) KVTC_K_CASE(3) KVTC_K_CASE(4) KVTC_K_CASE(5) KVTC_K_CASE(6) KVTC_K_CASE(7) KVTC_K_CASE(8)

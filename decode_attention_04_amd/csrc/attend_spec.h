@@ -95,6 +95,7 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
       sn = sn >= nbuf ? sn - nbuf : sn;
       issue_tile<WK, WV>(c, tn, t_end, sn);
     }
+    progress_priority(t0, t_begin, t_end);
     k_phase<BK, NKS, GM>(kt, WK, aq_hi, aq_lo, c.S);
     softmax_tile<GM>(kt, vt, WK, WV, nvalid, c.g, c.S, sq, kf, st);
 #pragma unroll

@@ -7,6 +7,7 @@
 // semantics (MI355X runs fp64 FMA at the fp32 VALU rate), so records are
 // bit-identical to an exact reference except where two float64 summation
 // orders of the projection land on different sides of a rounding boundary.
+#include "encode_core.h"
 #include "kvtc_common.h"
 #include "kvtc_launch.h"
 
@@ -82,12 +83,31 @@ __global__ __launch_bounds__(256) void encode_f64_kernel(EncodeArgs a) {
     xs[wave][lane + 64] = (double)(float)xt[lane + 64];
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // the fixed summation order of encode_core.h: four row groups, then their sums in order
     double c0 = 0.0, c1 = 0.0;
     if (lane < r) {
-      for (int i = 0; i < kHeadDim; ++i) c0 = fma(xs[wave][i], (double)P[i * r + lane], c0);
+      double g[kRowGroups];
+      for (int q = 0; q < kRowGroups; ++q) {
+        double acc = 0.0;
+        for (int k = 0; k < kGroupRows; ++k) {
+          const int i = q * kGroupRows + k;
+          acc = fma(xs[wave][i], (double)P[i * r + lane], acc);
+        }
+        g[q] = acc;
+      }
+      c0 = ((g[0] + g[1]) + g[2]) + g[3];
     }
     if (lane + 64 < r) {
-      for (int i = 0; i < kHeadDim; ++i) c1 = fma(xs[wave][i], (double)P[i * r + lane + 64], c1);
+      double g[kRowGroups];
+      for (int q = 0; q < kRowGroups; ++q) {
+        double acc = 0.0;
+        for (int k = 0; k < kGroupRows; ++k) {
+          const int i = q * kGroupRows + k;
+          acc = fma(xs[wave][i], (double)P[i * r + lane + 64], acc);
+        }
+        g[q] = acc;
+      }
+      c1 = ((g[0] + g[1]) + g[2]) + g[3];
     }
     double mn = lane < r ? c0 : __builtin_inf(), mx = lane < r ? c0 : -__builtin_inf();
     if (lane + 64 < r) { mn = fmin(mn, c1); mx = fmax(mx, c1); }
@@ -105,6 +125,22 @@ __global__ __launch_bounds__(256) void encode_f64_kernel(EncodeArgs a) {
     if (lane < W - 1) rec[1 + lane] = pack_word(codes_lds[wave], r, bits, lane);
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// ----------------------------------------------------------------- append
+// Grid (n_kv_heads, batch), 256 threads: waves 0-1 encode the sequence's new key,
+// waves 2-3 its new value, each with half of its basis loads in flight at once.
+template <typename T>
+__global__ __launch_bounds__(256) void append_kernel(EncodeArgs a) {
+  __shared__ EncodeScratch scr[2];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tensor = threadIdx.x >> 7, t = threadIdx.x & 127;
+  const HeadDesc& hd = a.heads.h[h];
+  const int r = tensor ? hd.rv : hd.rk, bits = tensor ? hd.bv : hd.bk, W = tensor ? hd.wv : hd.wk;
+  const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
+  const T* x = (const T*)(tensor ? a.v : a.k) + ((int64_t)b * a.n_kv_heads + h) * kHeadDim;
+  uint32_t* rec = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + ((int64_t)b * a.capacity + a.pos0) * W;
+  encode_token_128(x, P, r, bits, rec, scr[tensor], t, [] { __syncthreads(); });
 }
 
 // ----------------------------------------------------------------- launchers
@@ -127,6 +163,14 @@ hipError_t launch_unpack(const uint32_t* records, int64_t n, int r, int b, uint1
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
+  if (a.n_tokens == 1) {  // one token per (sequence, head): the append kernel
+    const dim3 grid((unsigned)a.n_kv_heads, (unsigned)a.batch);
+    if (a.dtype == 0)
+      hipLaunchKernelGGL(append_kernel<float>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(append_kernel<_Float16>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((a.n_tokens + 15) / 16), a.n_kv_heads, 2 * a.batch);
   if (a.dtype == 0)
     hipLaunchKernelGGL(encode_f64_kernel<float>, grid, dim3(256), 0, s, a);

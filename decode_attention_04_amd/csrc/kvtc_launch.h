@@ -44,6 +44,10 @@ struct AttendArgs {
   int32_t batch;
   int32_t dtype;
   float scale_log2;   // softmax_scale * log2(e)
+  const void* k1;      // [batch][n_kv_heads][head_dim] key and value appended at append_pos
+  const void* v1;      //   by the workgroup whose split holds it (append_pos < 0: no append)
+  int64_t append_pos;
+  int32_t append_dtype;  // 0 = f32, 1 = f16
   int32_t kbuf_words;  // LDS words per K / V record-tile buffer (set by launch_attend)
   int32_t vbuf_words;
   int32_t nbuf;        // tile buffers per wave: 2 (next tile streams in) or 1

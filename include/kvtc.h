@@ -148,6 +148,25 @@ kv_status kv_attend_decode_split(const kv_layout *layout, const void *q, kv_dtyp
                                  const uint32_t *cache_v, float softmax_scale, float *out,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* One decode step in one launch: append the new token of every (sequence, head)
+ * at position n_tokens - 1, then attend over records 0 .. n_tokens-1, the new
+ * one included.  k1, v1: [batch][n_kv_heads][head_dim] of `kv_dt` (KV_F32 or
+ * KV_F16); the other arguments, the workspace contract and the result are those
+ * of kv_attend_decode_split.  The records written are bit-identical to those of
+ * kv_append(pos = n_tokens - 1) and `out` equals that of kv_append followed by
+ * kv_attend_decode_split with the same split size: the workgroup whose split
+ * holds the new position encodes it before it reads that split.
+ * Errors: KV_ERR_INVALID if n_tokens < 1 or k1 / v1 is NULL; otherwise as
+ * kv_attend_decode_split.
+ * [KV-COBRA project page, "How KV-COBRA Works", Inference (each new key and
+ *  value is compressed as it is produced) and "Efficiency"] */
+kv_status kv_append_attend_decode(const kv_layout *layout, const void *k1, const void *v1,
+                                  kv_dtype kv_dt, const void *q, kv_dtype q_dt,
+                                  int64_t n_tokens, int64_t split_tokens, const float *basis_k,
+                                  const float *basis_v, uint32_t *cache_k, uint32_t *cache_v,
+                                  float softmax_scale, float *out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Quantize and pack n tokens of r float32 coordinates each (coords [n][r])
  * into records [n][kv_record_words(r, b)].  Same device code as the encoder's
  * quantize/pack stage; exposed to check the record format in isolation. */

@@ -279,6 +279,64 @@ def test_attention_workspace_reuse_across_calls(K):
     assert (cnt == 0).all()
 
 
+# ------------------------------------------------------------------ append fused with attention
+FUSED_CASES = [
+    # allocation, query heads per KV head, batch, capacity, tokens after the append, split, k1/v1 dtype
+    pytest.param([(128, 2, 128, 2), (64, 4, 32, 8)], 4, 2, 600, 1, 0, "f16", id="first-token"),
+    pytest.param([(128, 2, 128, 2), (64, 4, 32, 8)], 4, 2, 600, 256, 256, "f16", id="last-of-split"),
+    pytest.param([(128, 2, 128, 2), (64, 4, 32, 8)], 4, 2, 600, 257, 256, "f32", id="first-of-split"),
+    pytest.param(MIXED_ALLOC, 4, 2, 1600, 1500, 0, "f32", id="mixed-ragged"),
+    pytest.param([(32, 3, 64, 5), (16, 7, 128, 6)], 7, 1, 800, 777, 256, "f16", id="odd-widths-g7"),
+    pytest.param([(64, 4, 64, 4), (16, 8, 128, 4)], 8, 1, 600, 513, 512, "f16", id="g8"),
+]
+
+
+@pytest.mark.parametrize("alloc,g,B,cap,T,split,kvdt", FUSED_CASES)
+def test_fused_append_attend(K, alloc, g, B, cap, T, split, kvdt):
+    """kv_append_attend_decode against kv_append + kv_attend_decode on copies of one
+    cache (records and output bit-identical), and against the oracle (the new
+    record up to rounding ties, the output within the attention tolerance)."""
+    say(f"fused append+attend T={T} split={split} g={g} {kvdt}")
+    wl = W.LLAMA_T32K
+    hkv = len(alloc)
+    bk, bv = _mixed_bases(alloc, seed=41 + T)
+    kv = {(t, b, h): W.tokens(wl, t, b, h, 0, T, kvdt) for t in "KV" for b in range(B) for h in range(hkv)}
+    ck_h, cv_h = H.oracle_cache(wl, alloc, bk, bv, B, cap, T - 1, kv={key: x[: T - 1] for key, x in kv.items()})
+    lay = K.Layout(hkv, hkv * g, B, cap, alloc)
+    pk, pv = H.dev(codec.concat_bases(bk)), H.dev(codec.concat_bases(bv))
+    tdt = torch.float32 if kvdt == "f32" else torch.float16
+    k1 = H.dev(np.stack([np.stack([kv["K", b, h][T - 1] for h in range(hkv)]) for b in range(B)]), tdt)
+    v1 = H.dev(np.stack([np.stack([kv["V", b, h][T - 1] for h in range(hkv)]) for b in range(B)]), tdt)
+    q = H.dev(W.random_vectors(43 + T, (B, hkv * g, 128)).astype(np.float16), torch.float16)
+    ws = torch.zeros(K.kv_workspace_bytes(lay, T, split) // 4, dtype=torch.float32, device="cuda")
+
+    ck_f, cv_f = H.u32_dev(ck_h), H.u32_dev(cv_h)
+    out_f = torch.full((B, hkv * g, 128), float("nan"), dtype=torch.float32, device="cuda")
+    K.kv_append_attend_decode(lay, k1, v1, q, T, pk, pv, ck_f, cv_f, H.SCALE, out_f, ws, split_tokens=split)
+    ck_s, cv_s = H.u32_dev(ck_h), H.u32_dev(cv_h)
+    out_s = torch.full_like(out_f, float("nan"))
+    K.kv_append(lay, k1, v1, T - 1, pk, pv, ck_s, cv_s)
+    K.kv_attend_decode(lay, q, T, pk, pv, ck_s, cv_s, H.SCALE, out_s, ws, split_tokens=split)
+    torch.cuda.synchronize()
+    assert torch.equal(ck_f, ck_s) and torch.equal(cv_f, cv_s), "fused append wrote other records"
+    assert torch.equal(out_f, out_s), "fused output differs from append + attend"
+    assert (ws[: hkv * B].view(torch.int32) == 0).all()
+
+    ok_h, ov_h = H.oracle_cache(wl, alloc, bk, bv, B, cap, T, kv=kv)
+    gk, gv = H.u32_host(ck_f), H.u32_host(cv_f)
+    rk, bits_k, rv, bits_v = zip(*alloc)
+    for h in range(hkv):
+        for b in range(B):
+            for got, ref, ranks, bits, name in ((gk, ok_h, rk, bits_k, "K"), (gv, ov_h, rv, bits_v, "V")):
+                s0, s1, w = codec.record_slice(ranks, bits, B, cap, h, b, 0, T)
+                _compare_records(got[s0:s1].reshape(T, w), ref[s0:s1].reshape(T, w), ranks[h], bits[h],
+                                 f"{name} h{h} b{b}")
+    ref = attention.attend_cache(q.cpu().numpy().astype(np.float64), bk, bv, ok_h, ov_h, alloc, B, cap, T, H.SCALE)
+    err = H.rel_err_per_head(out_f.cpu().numpy(), ref)
+    say(f"  max rel err {err:.3e}")
+    assert err <= REL_TOL
+
+
 def test_attention_empty_context_is_zero(K):
     say("attention T=0")
     alloc = [(64, 4, 32, 8)]
