@@ -169,7 +169,8 @@ def main():
     ap.add_argument("--workload", default="llama-128k-2bpd")
     ap.add_argument("--replica-bytes", type=float, default=1.2e9, help="total bytes of rotated layer caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a captured HIP graph per step instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 3 times (calibrates the HBM byte counters)")
@@ -247,10 +248,10 @@ def main():
     ref_out = out.clone()
     assert torch.equal(ref_out, two_call_out), "fused append + attend differs from kv_append + kv_attend_decode"
 
-    # each timed step replays a HIP graph of that step (one graph per layer cache), so
-    # that host launch latency does not sit between the kernels
+    # with --graph each timed step replays a HIP graph of that step (one graph per layer
+    # cache); by default the step's single launch is issued eagerly, back to back
     graphs = []
-    if not args.no_graph:
+    if args.graph:
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -332,7 +333,7 @@ def main():
             "batch": B, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d, "context_tokens": T + 1,
             "allocation": [list(a) for a in alloc],
             "step": "kv_append_attend_decode (append of 1 token fused with the attention)",
-            "timing": "HIP graph replay per step" if graphs else "eager launches",
+            "timing": "HIP graph replay per step" if graphs else "one eager launch per step, back to back",
             "layer_caches_rotated": n_rep,
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "context_tokens_per_s": round(B * (T + 1) / (ms_step * 1e-3), 1),

@@ -243,6 +243,8 @@ kv_status kv_encode(const kv_layout* layout, const void* k, const void* v, kv_dt
   if (!aligned(k, esz) || !aligned(v, esz) || !aligned(basis_k, 4) || !aligned(basis_v, 4) ||
       !aligned(cache_k, 4) || !aligned(cache_v, 4))
     return fail(KV_ERR_INVALID, "misaligned pointer");
+  if (n_tokens > 1 && (!aligned(k, 16) || !aligned(v, 16)))
+    return fail(KV_ERR_INVALID, "k and v must be 16-byte aligned to encode more than one token");
   if (n_tokens > (int64_t)0x7FFFFFFF / 16 * 16)
     return fail(KV_ERR_UNSUPPORTED, "n_tokens %lld too large for one call", (long long)n_tokens);
   EncodeArgs a{};

@@ -1,12 +1,12 @@
-// Encode side of the codec for gfx950: project -> quantize -> pack, plus the
-// standalone quantize/pack and unpack kernels behind the test entry points.
+// Encode side of the codec for gfx950: the one-token append kernel, plus the
+// standalone quantize/pack and unpack kernels behind the test entry points
+// (the prefill encoder is in encode_mfma.hip).
 //
 // KV-COBRA project page, "How KV-COBRA Works" (Inference): each key is rotated
 // and truncated with the head's basis and quantized with its head's b-bit
 // quantizer.  The quantizer's rounding decisions are taken with float64
-// semantics (MI355X runs fp64 FMA at the fp32 VALU rate), so records are
-// bit-identical to an exact reference except where two float64 summation
-// orders of the projection land on different sides of a rounding boundary.
+// semantics (MI355X runs fp64 FMA at half the fp32 rate), from a float64
+// projection summed in one fixed order.
 #include "encode_core.h"
 #include "kvtc_common.h"
 #include "kvtc_launch.h"
@@ -57,76 +57,6 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict_
   }
 }
 
-// ----------------------------------------------------------------- encoder
-// Grid: x = token blocks of 16 (4 waves x 4 tokens), y = KV head, z = tensor * batch + b.
-// One wave per token: lanes own coordinates j = lane, lane + 64; the projection
-// c_j = sum_i x_i P_ij runs in float64 (x from LDS, P rows coalesced from L1/L2).
-template <typename T>
-__global__ __launch_bounds__(256) void encode_f64_kernel(EncodeArgs a) {
-  __shared__ double xs[4][kHeadDim];
-  __shared__ uint32_t codes_lds[4][kMaxRank];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int h = blockIdx.y;
-  const int tensor = blockIdx.z / a.batch, b = blockIdx.z % a.batch;
-  const HeadDesc& hd = a.heads.h[h];
-  const int r = tensor ? hd.rv : hd.rk;
-  const int bits = tensor ? hd.bv : hd.bk;
-  const int W = tensor ? hd.wv : hd.wk;
-  const float* P = (tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k);
-  const T* x = (const T*)(tensor ? a.v : a.k);
-  uint32_t* cache = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k);
-  for (int k = 0; k < 4; ++k) {
-    const int64_t t = ((int64_t)blockIdx.x * 4 + k) * 4 + wave;
-    if (t >= a.n_tokens) break;
-    const T* xt = x + (((int64_t)b * a.n_kv_heads + h) * a.n_tokens + t) * kHeadDim;
-    xs[wave][lane] = (double)(float)xt[lane];
-    xs[wave][lane + 64] = (double)(float)xt[lane + 64];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    // the fixed summation order of encode_core.h: four row groups, then their sums in order
-    double c0 = 0.0, c1 = 0.0;
-    if (lane < r) {
-      double g[kRowGroups];
-      for (int q = 0; q < kRowGroups; ++q) {
-        double acc = 0.0;
-        for (int k = 0; k < kGroupRows; ++k) {
-          const int i = q * kGroupRows + k;
-          acc = fma(xs[wave][i], (double)P[i * r + lane], acc);
-        }
-        g[q] = acc;
-      }
-      c0 = ((g[0] + g[1]) + g[2]) + g[3];
-    }
-    if (lane + 64 < r) {
-      double g[kRowGroups];
-      for (int q = 0; q < kRowGroups; ++q) {
-        double acc = 0.0;
-        for (int k = 0; k < kGroupRows; ++k) {
-          const int i = q * kGroupRows + k;
-          acc = fma(xs[wave][i], (double)P[i * r + lane + 64], acc);
-        }
-        g[q] = acc;
-      }
-      c1 = ((g[0] + g[1]) + g[2]) + g[3];
-    }
-    double mn = lane < r ? c0 : __builtin_inf(), mx = lane < r ? c0 : -__builtin_inf();
-    if (lane + 64 < r) { mn = fmin(mn, c1); mx = fmax(mx, c1); }
-    for (int o = 32; o > 0; o >>= 1) {
-      mn = fmin(mn, __shfl_xor(mn, o));
-      mx = fmax(mx, __shfl_xor(mx, o));
-    }
-    QuantHeader qh = quant_header(mn, mx, bits);
-    if (lane < r) codes_lds[wave][lane] = quant_code(c0, qh.mu, qh.sigma, bits);
-    if (lane + 64 < r) codes_lds[wave][lane + 64] = quant_code(c1, qh.mu, qh.sigma, bits);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    uint32_t* rec = cache + ((int64_t)b * a.capacity + a.pos0 + t) * W;
-    if (lane == 0) rec[0] = qh.word0;
-    if (lane < W - 1) rec[1 + lane] = pack_word(codes_lds[wave], r, bits, lane);
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
 // ----------------------------------------------------------------- append
 // Grid (n_kv_heads, batch), 256 threads: waves 0-1 encode the sequence's new key,
 // waves 2-3 its new value, each with half of its basis loads in flight at once.
@@ -171,12 +101,7 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(append_kernel<_Float16>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)((a.n_tokens + 15) / 16), a.n_kv_heads, 2 * a.batch);
-  if (a.dtype == 0)
-    hipLaunchKernelGGL(encode_f64_kernel<float>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(encode_f64_kernel<_Float16>, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_encode_mfma(a, s);
 }
 
 }  // namespace kvtc

@@ -102,8 +102,9 @@ __device__ inline uint32_t quant_code(double c, double mu, double sigma, int b) 
 }
 
 // Word w (0-based among the code words) of the little-endian code stream,
-// gathered from codes[0..r) held in LDS.
-__device__ inline uint32_t pack_word(const uint32_t* codes, int r, int b, int w) {
+// gathered from codes[0..r) held in LDS (32-bit or 8-bit code elements).
+template <typename C>
+__device__ inline uint32_t pack_word(const C* codes, int r, int b, int w) {
   const int lo = 32 * w;
   int j0 = lo / b;
   int j1 = (lo + 31) / b;
@@ -111,7 +112,7 @@ __device__ inline uint32_t pack_word(const uint32_t* codes, int r, int b, int w)
   uint32_t word = 0u;
   for (int j = j0; j <= j1; ++j) {
     int off = j * b - lo;
-    uint32_t c = codes[j];
+    uint32_t c = (uint32_t)codes[j];
     word |= off >= 0 ? (c << off) : (c >> (-off));
   }
   return word;

@@ -61,7 +61,8 @@ hipError_t launch_quantize_pack(const float* coords, int64_t n, int r, int b, ui
                                 hipStream_t s);
 hipError_t launch_unpack(const uint32_t* records, int64_t n, int r, int b, uint16_t* min_step,
                          uint8_t* codes, hipStream_t s);
-hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);       // one token: append kernel, else the below
+hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s);  // prefill: k, v 16-byte aligned
 // How a layout's decode attention runs: the specialised kernel class (-1: the
 // generic kernel), LDS tile buffers per wave and resident workgroups per CU.
 struct AttendPlan {

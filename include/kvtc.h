@@ -97,11 +97,16 @@ kv_status kv_cache_bytes(const kv_layout *layout, int32_t which, size_t *bytes);
 kv_status kv_workspace_bytes(const kv_layout *layout, int64_t n_tokens, size_t *bytes);
 
 /* Prefill encode.  k, v: [batch][n_kv_heads][n_tokens][head_dim] of `dtype`
- * (KV_F32 or KV_F16), contiguous.  Writes records pos0 .. pos0+n_tokens-1 of
- * every (sequence, head) into cache_k / cache_v (other records untouched).
- * basis_k / basis_v: concatenated float32 bases (layout above).
+ * (KV_F32 or KV_F16), contiguous, 16-byte aligned when n_tokens > 1; float32
+ * inputs must lie inside the fp16 range (|x| < 65504).  Writes records
+ * pos0 .. pos0+n_tokens-1 of every (sequence, head) into cache_k / cache_v
+ * (other records untouched).  basis_k / basis_v: concatenated float32 bases
+ * (layout above).  The projection runs on the matrix cores; every rounding
+ * decision it cannot settle within its error bound is taken from the float64
+ * projection, so the records are those of kv_append token by token.
  * Errors: KV_ERR_CAPACITY if pos0 < 0 or pos0 + n_tokens > capacity;
- * n_tokens == 0 launches nothing and returns KV_OK.
+ * KV_ERR_INVALID for misaligned inputs; n_tokens == 0 launches nothing and
+ * returns KV_OK.
  * [KV-COBRA project page, "How KV-COBRA Works", Inference; the projection
  *  d -> r is a dense T x d by d x r contraction per head] */
 kv_status kv_encode(const kv_layout *layout, const void *k, const void *v, kv_dtype dtype,

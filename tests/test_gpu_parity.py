@@ -158,6 +158,68 @@ def test_encode_mixed_allocation_matches_oracle(K, dtype):
                  2, 1100, 37, 1001, dtype)
 
 
+@pytest.mark.parametrize("n", [2, 15, 16, 17, 63, 65, 129, 257, 513])
+def test_encode_ragged_token_counts(K, n):
+    """Token counts around the encoder's 16-token blocks and 64/128-token tiles; nothing
+    outside positions pos0 .. pos0+n-1 is written."""
+    say(f"encode n={n}")
+    wl = W.LLAMA_T32K
+    alloc = [(128, 2, 16, 8), (64, 5, 32, 3)]
+    bk, bv = _mixed_bases(alloc, seed=7)
+    _encode_case(K, lambda t, b, h, n_: W.tokens(wl, t, b, h, 11, n_), alloc, bk, bv, 2, n + 9, 9, n, "f16")
+
+
+def _near_basis_nullspace(P, n, seed, dtype):
+    """Tokens almost orthogonal to the span of P: coordinates of the order of the
+    float32 error bound, so that most header and code decisions are near a boundary
+    at float32 precision (the exact float64 decisions are ordinary)."""
+    rng = np.random.default_rng(seed)
+    P = np.asarray(P, np.float64)
+    z = rng.standard_normal((n, P.shape[0])) * 3.0
+    x = z - (z @ P) @ P.T + (rng.standard_normal((n, P.shape[1])) * 1e-4) @ P.T
+    return x.astype(np.float16 if dtype == "f16" else np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_prefill_records_equal_append_records(K, dtype):
+    """kv_encode (matrix-core projection, exact recomputation near rounding boundaries)
+    writes the same records, bit for bit, as kv_append (float64 projection) token by
+    token, for every rank and bit width, on ordinary tokens and on tokens whose
+    coordinates sit within the float32 error bound of each other."""
+    say(f"prefill records == append records {dtype}")
+    wl = W.LLAMA_T32K
+    alloc = MIXED_ALLOC
+    hkv, B, n, pos0 = len(alloc), 2, 320, 5
+    bk, bv = _mixed_bases(alloc, seed=11)
+    lay = K.Layout(hkv, hkv, B, pos0 + n, alloc)
+    tdt = torch.float32 if dtype == "f32" else torch.float16
+    x = {}
+    for t, bases in (("K", bk), ("V", bv)):
+        x[t] = np.stack([np.stack([np.concatenate([W.tokens(wl, t, b, h, 0, n - 96, dtype),
+                                                   _near_basis_nullspace(bases[h], 96, 100 * b + h, dtype)])
+                                   for h in range(hkv)]) for b in range(B)])
+    pk, pv = H.dev(codec.concat_bases(bk)), H.dev(codec.concat_bases(bv))
+    kd, vd = H.dev(x["K"], tdt), H.dev(x["V"], tdt)
+    nk, nv = K.kv_cache_bytes(lay, 0) // 4, K.kv_cache_bytes(lay, 1) // 4
+    ck_e = torch.zeros(nk, dtype=torch.int32, device="cuda")
+    cv_e = torch.zeros(nv, dtype=torch.int32, device="cuda")
+    ck_a, cv_a = torch.zeros_like(ck_e), torch.zeros_like(cv_e)
+    K.kv_encode(lay, kd, vd, n, pos0, pk, pv, ck_e, cv_e)
+    for t in range(n):
+        K.kv_append(lay, kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), pos0 + t, pk, pv, ck_a, cv_a)
+    gk, gv = H.u32_host(ck_e), H.u32_host(cv_e)
+    ak, av = H.u32_host(ck_a), H.u32_host(cv_a)
+    assert np.array_equal(gk, ak), f"K records differ at {np.flatnonzero(gk != ak)[:8]}"
+    assert np.array_equal(gv, av), f"V records differ at {np.flatnonzero(gv != av)[:8]}"
+    rk, bits_k, rv, bits_v = zip(*alloc)
+    for tensor, got_all, ranks, bits, bases in (("K", gk, rk, bits_k, bk), ("V", gv, rv, bits_v, bv)):
+        for h in range(hkv):
+            for b in range(B):
+                s0, s1, w = codec.record_slice(ranks, bits, B, pos0 + n, h, b, pos0, pos0 + n)
+                ref = codec.encode_tokens(x[tensor][b, h].astype(np.float64), bases[h], bits[h])
+                _compare_records(got_all[s0:s1].reshape(n, w), ref, ranks[h], bits[h], f"{tensor} h{h} b{b}")
+
+
 def test_append_matches_oracle(K):
     say("append mixed allocation")
     wl = W.QWEN_T128K
