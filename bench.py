@@ -80,6 +80,48 @@ def step_bytes(wl, alloc, T):
     return attend, append
 
 
+def encode_rate(K, wl, block=2048, reps=5):
+    """kv_encode of the workload's prefill chunk (every sequence and KV head at once).
+
+    Inputs: the workload's generated keys and values for the first `block` tokens,
+    repeated along the token axis to the chunk length on the GPU (same per-token
+    statistics, so the same share of coordinates near a rounding boundary)."""
+    import torch
+
+    alloc, bk, bv = calibrate(wl)
+    T = wl.encode_tokens or wl.context
+    B, H, d = wl.batch, wl.n_kv_heads, wl.head_dim
+    lay = K.Layout(H, wl.n_q_heads, B, T, alloc)
+    dev = torch.device("cuda:0")
+    pk = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bk])).to(dev)
+    pv = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bv])).to(dev)
+    nb = min(block, T)
+    reps_t = (T + nb - 1) // nb
+    kx = torch.from_numpy(W.kv_array(wl, "K", 0, nb)).to(dev).repeat(1, 1, reps_t, 1)[:, :, :T].contiguous()
+    vx = torch.from_numpy(W.kv_array(wl, "V", 0, nb)).to(dev).repeat(1, 1, reps_t, 1)[:, :, :T].contiguous()
+    ck = torch.empty(K.kv_cache_bytes(lay, 0) // 4, dtype=torch.int32, device=dev)
+    cv = torch.empty(K.kv_cache_bytes(lay, 1) // 4, dtype=torch.int32, device=dev)
+    K.kv_encode(lay, kx, vx, T, 0, pk, pv, ck, cv)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        K.kv_encode(lay, kx, vx, T, 0, pk, pv, ck, cv)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    in_bytes = 2 * B * H * T * d * kx.element_size()
+    out_bytes = (ck.numel() + cv.numel()) * 4
+    del kx, vx, ck, cv
+    torch.cuda.empty_cache()
+    return {"tokens_per_seq": T, "batch": B, "allocation": [list(a) for a in alloc], "ms": round(ms, 4),
+            "input_GB_per_s": round(in_bytes / ms / 1e6, 1),
+            "hbm_GB_per_s": round((in_bytes + out_bytes) / ms / 1e6, 1),
+            "pct_of_hbm_peak": round(100 * (in_bytes + out_bytes) / ms / 1e6 / HBM_PEAK_GBS, 2)}
+
+
 def cpu_baseline(wl, alloc, bk, bv, T, budget_s=12.0):
     """The oracle (float64 numpy, one BLAS thread) on whole (sequence, KV head) units of the same workload."""
     from threadpoolctl import threadpool_limits
@@ -169,6 +211,8 @@ def main():
     ap.add_argument("--workload", default="llama-128k-2bpd")
     ap.add_argument("--replica-bytes", type=float, default=1.2e9, help="total bytes of rotated layer caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-encode-rates", action="store_true",
+                    help="skip the prefill encode measurements of the prefill workloads")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a captured HIP graph per step instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -310,6 +354,13 @@ def main():
         log(f"HBM traffic per launch from the committed counter profile: {traffic / 1e6:.1f} MB "
             f"(algorithmic {(attend_bytes + append_bytes) / 1e6:.1f} MB)")
 
+    enc_rates = None
+    if not args.no_encode_rates:
+        enc_rates = {}
+        for ewl in (W.llama_prefill(32, 8), W.llama_prefill(64, 4), W.QWEN_T128K):
+            enc_rates[ewl.name] = encode_rate(K, ewl)
+            log(f"encode {ewl.name}: {enc_rates[ewl.name]}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, alloc, bk, bv, T + 1, args.cpu_seconds)
@@ -339,6 +390,7 @@ def main():
             "context_tokens_per_s": round(B * (T + 1) / (ms_step * 1e-3), 1),
             "bytes_per_step": attend_bytes + append_bytes,
             "encode_prefill_ms": round(enc_ms, 4),
+            "encode_rates": enc_rates,
         },
         "roofline": {
             "bound": "hbm",

@@ -8,20 +8,24 @@
 //
 // Arithmetic.  Each basis element (fp32) is split into two fp16 parts,
 // P = Ph + Pl + e with |e| <= 2^-22 |P| + 2^-25, and fp32 inputs the same way
-// (fp16 inputs are exact operands).  v_mfma_f32_16x16x32_f16 forms the products
-// exactly and accumulates in fp32, rounding to nearest.  With at most 256
-// rounded additions of terms whose magnitudes sum to S_j = sum_i |x_i P_ij| <=
-// ||x||_2 (the columns of P are orthonormal), the computed coordinate c~_j is within
-//     E = 1.3125 * 2^-16 * ||x||_2
-// of the exact one (the split remainders add less than 2^-20.5 ||x||_2; fp32
-// inputs take three products per term, 384 additions, and E = 1.6875 * 2^-16 *
-// ||x||_2 + 2^-21, the last term for inputs split below the fp16 normal range;
-// they must lie inside the fp16 range, |x| < 65504).  The
-// header (fp16 min and step) and the codes are monotone functions of the
-// coordinates, so a decision that takes the same value at c~ - E and c~ + E is
-// the exact decision.  The others are recomputed from the float64 projection in
-// the fixed summation order every encode path uses (four groups of 32 rows, then
-// the group sums in order):
+// (fp16 inputs are exact operands).  On gfx950, v_mfma_f32_16x16x32_f16 forms
+// its 32 products exactly, sums them exactly, adds the accumulator aligned to
+// 2^-24 of the largest product and rounds the result to nearest once (measured
+// on constructed operands: sub-ulp products survive the sum, cancellations are
+// exact, an accumulator bit 25 places below the largest product is dropped).
+// Per instruction the error is then at most u |D| + 2u max|p| (u = 2^-24), and
+// over the 8 chained instructions of a coordinate, with S_j = sum_i |x_i P_ij|
+// <= ||x||_2 (the columns of P are orthonormal), at most 24u S_j; the split
+// remainders add at most 4u S_j + 2^-25 ||x||_1 <= 4u S_j + 11.4u ||x||_2.  The
+// encoder uses
+//     E = 48u ||x||_2
+// (fp32 inputs: three products per term, 24 instructions, E = 96u ||x||_2 +
+// 2^-21, the last term for inputs split below the fp16 normal range; they must
+// lie inside the fp16 range, |x| < 65504).  The header (fp16 min and step) and
+// the codes are monotone functions of the coordinates, so a decision that takes
+// the same value at c~ - E and c~ + E is the exact decision.  The others are
+// recomputed from the float64 projection in the fixed summation order every
+// encode path uses (four groups of 32 rows, then the group sums in order):
 //   * a token whose fp16 min or step could round either way gets the exact
 //     values of its extreme candidates (c~ within 2E of the approximate min or
 //     max), which contain the exact extremes, and its header from them;
@@ -45,14 +49,6 @@ __device__ inline enc_f32x4 mma(enc_half8 a, enc_u32x4 b, enc_f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(enc_half8, b), c, 0, 0, 0);
 }
 
-// Float index, in the staged basis, of P[k][j]: the A operand (P^T, 16 coordinates
-// x 32 rows) of coordinate block j/16 and row block k/32 in lane order, split in
-// two planes of four rows so that every lane reads 16 contiguous bytes.
-__device__ inline int basis_slot(int k, int j) {
-  const int mb = j >> 4, m = j & 15, ks = k >> 5, G = (k >> 3) & 3, i = k & 7;
-  return ((((mb * 4 + ks) * 2 + (i >> 2)) * 64 + 16 * G + m) << 2) + (i & 3);
-}
-
 // Eight consecutive input elements as floats.
 __device__ inline void load8(const _Float16* p, float (&f)[8]) {
   const enc_half8 h = *(const enc_half8*)p;
@@ -67,48 +63,123 @@ __device__ inline void load8(const float* p, float (&f)[8]) {
 
 // Exact (float64) coordinate j of the token whose 128 inputs start at `row`,
 // summed in the fixed order of the encoder (rows 32q .. 32q+31 in order, q = 0..3,
-// then ((g0 + g1) + g2) + g3); P is read from the staged basis.
+// then ((g0 + g1) + g2) + g3), with the basis P (128 x R, fp32) from memory.
 template <typename T>
-__device__ inline double exact_coord(const T* row, const float* pb, int j) {
+__device__ inline double exact_coord(const T* row, const float* P, int R, int j) {
   double g[kRowGroups];
 #pragma unroll 1
   for (int q = 0; q < kRowGroups; ++q) {
     double acc = 0.0;
-#pragma unroll
+#pragma unroll 1
     for (int c8 = 0; c8 < 4; ++c8) {
       float xv[8];
       load8(row + 32 * q + 8 * c8, xv);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc = fma((double)xv[i], (double)pb[basis_slot(32 * q + 8 * c8 + i, j)], acc);
+      for (int i = 0; i < 8; ++i) acc = fma((double)xv[i], (double)P[(32 * q + 8 * c8 + i) * R + j], acc);
     }
     g[q] = acc;
   }
   return ((g[0] + g[1]) + g[2]) + g[3];
 }
 
-// Dynamic LDS: the basis (R x 128 floats, operand order), then per wave the codes
-// of one 16-token block (16 x R bytes) and its 16 header words.
-__host__ __device__ constexpr int enc_wave_bytes(int R) { return 16 * R + 64; }
+__device__ inline uint32_t h16_bits(float x) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x); }
+
+// Four codes (bytes of v, codes < 16) as one 16-bit field, and (codes < 4) as one byte.
+__device__ inline uint32_t compact4(uint32_t v) {
+  v = (v | (v >> 4)) & 0x00FF00FFu;
+  return (v | (v >> 8)) & 0xFFFFu;
+}
+__device__ inline uint32_t compact2(uint32_t v) {
+  v = (v | (v >> 6)) & 0x000F000Fu;
+  return (v | (v >> 12)) & 0xFFu;
+}
+
+// LDS ordering among the lanes of one wave.
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Exclusive prefix sum of v over the wave's lanes; the sum over all lanes in total.
+__device__ inline int wave_prefix(int v, int lane, int& total) {
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  total = __shfl(x, 63);
+  return x - v;
+}
+
+// A coordinate to recompute: token 16nt + n of the wave, coordinate 16(s/4) + 4G + s%4.
+__device__ inline uint32_t item_code(int nt, int n, int G, int s) {
+  return ((uint32_t)(16 * nt + n) << 8) | (uint32_t)(16 * (s >> 2) + 4 * G + (s & 3));
+}
+
+constexpr int kRepairList = 64;  // items one wave recomputes together (more: lane by lane)
+
+// Exact values of the `cnt` listed coordinates (cnt <= kRepairList), four lanes per
+// item, lane 4i + q summing rows 32q .. 32q+31 of item i in order; the group sums
+// are added in the fixed order, so each value equals exact_coord's.
+template <typename T>
+__device__ inline void coop_exact(const uint32_t* items, double* res, int cnt, const T* xu, int64_t wtok0,
+                                  const float* P, int R, int lane) {
+  wave_sync();
+  const int q = lane & 3, l0 = lane & ~3;
+#pragma unroll 1
+  for (int base = 0; base < cnt; base += 16) {
+    const int it = base + (lane >> 2);
+    double g = 0.0;
+    if (it < cnt) {
+      const uint32_t e = items[it];
+      const T* row = xu + (wtok0 + (int64_t)(e >> 8)) * kHeadDim + 32 * q;
+      const float* pc = P + 32 * q * R + (int)(e & 255u);
+#pragma unroll 1
+      for (int c8 = 0; c8 < 4; ++c8) {
+        float xv[8];
+        load8(row + 8 * c8, xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g = fma((double)xv[i], (double)pc[(8 * c8 + i) * R], g);
+      }
+    }
+    const double g0 = __shfl(g, l0), g1 = __shfl(g, l0 + 1), g2 = __shfl(g, l0 + 2), g3 = __shfl(g, l0 + 3);
+    if (q == 0 && it < cnt) res[it] = ((g0 + g1) + g2) + g3;
+  }
+  wave_sync();
+}
+
+// Dynamic LDS: the basis as fp16 hi/lo A operands (R x 128 x 4 bytes), then per
+// wave one 16-token block: the records being assembled ([16][W] words, header
+// first) for b = 2, 4, 8, or the codes ([16][R] bytes) and headers for other b;
+// and the list of coordinates to recompute with their exact values.
+__host__ __device__ constexpr int enc_wave_bytes(int R) { return 16 * R + 128 + kRepairList * 12; }
 __host__ __device__ constexpr int enc_lds_bytes(int R) { return R * kHeadDim * 4 + kEncWaves * enc_wave_bytes(R); }
 
 // Grid: x = groups of `tiles_per_wg` token tiles, y = the (head, tensor) units of
 // rank R (keys of the heads in mask_k, then values of the heads in mask_v), z =
-// sequence.  Each wave projects 16*NT tokens per tile: A = P^T from LDS (split
-// into fp16 hi/lo on the fly), B = the tokens' inputs straight from HBM, one
-// 16 x 16 coordinate-by-token accumulator per (coordinate block, token block).
-template <typename T, int R, int NT>
-__global__ __launch_bounds__(256, 2) void encode_mfma_kernel(EncodeArgs a, uint64_t mask_k, uint64_t mask_v,
-                                                             int tiles_per_wg) {
+// sequence.  Each wave projects 16*NT tokens per tile: A = P^T (hi and lo parts)
+// from LDS, B = the tokens' inputs straight from HBM, one 16 x 16
+// coordinate-by-token accumulator per (coordinate block, token block).  Lane
+// (n, G) = (lane % 16, lane / 16) ends with coordinates 16mb + 4G + i of token n.
+template <typename T, int R, int NT, bool PF, int OCC>
+__global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uint64_t mask_k, uint64_t mask_v,
+                                                               int tiles_per_wg) {
   constexpr int MB = R / 16;
+  constexpr int NS = MB * 4;  // coordinates per lane and token
   constexpr bool kF32 = sizeof(T) == 4;
   constexpr int kWaveTok = 16 * NT;
   constexpr int kTileTok = kEncWaves * kWaveTok;
   extern __shared__ float enc_lds[];
-  float* pb = enc_lds;
+  uint8_t* ab = (uint8_t*)enc_lds;
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, G = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint8_t* codes = (uint8_t*)(pb + R * kHeadDim) + wave * enc_wave_bytes(R);
-  uint32_t* hdrw = (uint32_t*)(codes + 16 * R);
+  uint8_t* wb = ab + R * kHeadDim * 4 + wave * enc_wave_bytes(R);
+  uint32_t* recw = (uint32_t*)wb;                  // b = 2, 4, 8: [16][W] words
+  uint32_t* hdrw = (uint32_t*)(wb + 16 * R + 64);  // other b: header words
+  double* res = (double*)(wb + 16 * R + 128);       // exact values of the listed coordinates
+  uint32_t* items = (uint32_t*)(res + kRepairList);
 
   // the unit: blockIdx.y-th set bit of mask_k, then of mask_v
   const int nk = __popcll(mask_k);
@@ -132,42 +203,67 @@ __global__ __launch_bounds__(256, 2) void encode_mfma_kernel(EncodeArgs a, uint6
   const T* xu = (const T*)(tensor ? a.v : a.k) + ((int64_t)b * a.n_kv_heads + h) * a.n_tokens * kHeadDim;
   uint32_t* cu = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + ((int64_t)b * a.capacity + a.pos0) * W;
 
-  // stage the basis in operand order (four rows of one column per thread and step)
-  for (int q = tid; q < R * 32; q += 256) {
-    const int ln = q & 63, hf = (q >> 6) & 1, ks = (q >> 7) & 3, mb = q >> 9;
-    const int k0 = 32 * ks + 8 * (ln >> 4) + 4 * hf, j = 16 * mb + (ln & 15);
-    float4 v;
-    v.x = P[(k0 + 0) * R + j];
-    v.y = P[(k0 + 1) * R + j];
-    v.z = P[(k0 + 2) * R + j];
-    v.w = P[(k0 + 3) * R + j];
-    *(float4*)(pb + 4 * q) = v;
+  // stage the basis as A operands: for (mb, ks, lane) the eight rows 32ks + 8G ..
+  // of column 16mb + m, hi parts then (64 lanes later) lo parts
+  for (int q = tid; q < R * 16; q += 256) {
+    const int ln = q & 63, ks = (q >> 6) & 3, mb = q >> 8;
+    const int k0 = 32 * ks + 8 * (ln >> 4), j = 16 * mb + (ln & 15);
+    enc_half8 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = P[(k0 + i) * R + j];
+      hi[i] = (_Float16)p;
+      lo[i] = (_Float16)(p - (float)hi[i]);
+    }
+    uint8_t* dst = ab + (((mb * 4 + ks) * 2 * 64 + ln) << 4);
+    *(enc_half8*)dst = hi;
+    *(enc_half8*)(dst + 1024) = lo;
   }
   __syncthreads();
 
   const float top = (float)((1 << bits) - 1);
+  const float kinv = 1.0f / top;
+  const bool pow2 = (bits & (bits - 1)) == 0;
+  const uint32_t wmagic = (uint32_t)((0x100000000ull + W - 1) / W);
   const int64_t n_tiles = (a.n_tokens + kTileTok - 1) / kTileTok;
+  // B operands: lane (n, G) holds dims 32ks + 8G .. +7 of token 16nt + n.  fp16
+  // inputs are the operands as loaded; the next tile's are loaded while this
+  // tile's coordinates are quantized.
+  enc_u32x4 bh[4][NT], bl[4][NT];
+  auto load_f16 = [&](int64_t tile_) {
+    const int64_t t0 = tile_ * kTileTok + wave * kWaveTok;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t tok = t0 + 16 * nt + n;
+      const T* row = xu + tok * kHeadDim + 8 * G;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        enc_u32x4 v = {0u, 0u, 0u, 0u};
+        if (tok < a.n_tokens) v = *(const enc_u32x4*)(row + 32 * ks);
+        bh[ks][nt] = v;
+      }
+    }
+  };
+  if constexpr (!kF32 && PF) {
+    if ((int64_t)blockIdx.x * tiles_per_wg < n_tiles) load_f16((int64_t)blockIdx.x * tiles_per_wg);
+  }
 #pragma unroll 1
   for (int it = 0; it < tiles_per_wg; ++it) {
     const int64_t tile = (int64_t)blockIdx.x * tiles_per_wg + it;
     if (tile >= n_tiles) break;
     const int64_t wtok0 = tile * kTileTok + wave * kWaveTok;
+    if constexpr (!kF32 && !PF) load_f16(tile);
 
-    // ---- B operands: lane (n, G) holds dims 32ks + 8G .. +7 of token 16nt + n
-    enc_u32x4 bh[4][NT], bl[4][NT];
     float ss[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int64_t tok = wtok0 + 16 * nt + n;
-      ss[nt] = 0.f;
-      const T* row = xu + tok * kHeadDim + 8 * G;
+    for (int nt = 0; nt < NT; ++nt) ss[nt] = 0.f;
+    if constexpr (kF32) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if constexpr (!kF32) {
-          enc_u32x4 v = {0u, 0u, 0u, 0u};
-          if (tok < a.n_tokens) v = *(const enc_u32x4*)(row + 32 * ks);
-          bh[ks][nt] = v;
-        } else {
+      for (int nt = 0; nt < NT; ++nt) {
+        const int64_t tok = wtok0 + 16 * nt + n;
+        const T* row = xu + tok * kHeadDim + 8 * G;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
           float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
           if (tok < a.n_tokens) load8(row + 32 * ks, f);
           enc_half8 hi, lo;
@@ -181,8 +277,7 @@ __global__ __launch_bounds__(256, 2) void encode_mfma_kernel(EncodeArgs a, uint6
           bl[ks][nt] = __builtin_bit_cast(enc_u32x4, lo);
         }
       }
-    }
-    if constexpr (!kF32) {
+    } else {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -204,15 +299,8 @@ __global__ __launch_bounds__(256, 2) void encode_mfma_kernel(EncodeArgs a, uint6
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const float* pa = pb + ((((mb * 4 + ks) * 2) * 64 + lane) << 2);
-        const float4 p0 = *(const float4*)pa, p1 = *(const float4*)(pa + 256);
-        const float pf[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        enc_half8 ah, al;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ah[i] = (_Float16)pf[i];
-          al[i] = (_Float16)(pf[i] - (float)ah[i]);
-        }
+        const uint8_t* src = ab + (((mb * 4 + ks) * 2 * 64 + lane) << 4);
+        const enc_half8 ah = *(const enc_half8*)src, al = *(const enc_half8*)(src + 1024);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           acc[mb][nt] = mma(ah, bh[ks][nt], acc[mb][nt]);
@@ -220,144 +308,202 @@ __global__ __launch_bounds__(256, 2) void encode_mfma_kernel(EncodeArgs a, uint6
           if constexpr (kF32) acc[mb][nt] = mma(ah, bl[ks][nt], acc[mb][nt]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);  // keeps the operand reads of later row blocks from piling up
+    }
+    if constexpr (!kF32 && PF) {
+      if (it + 1 < tiles_per_wg && tile + 1 < n_tiles) load_f16(tile + 1);
     }
 
-    // ---- per 16-token block: header, codes, exact recomputation near boundaries, pack
-#pragma unroll 1
+    // ---- headers of the wave's 16*NT tokens from the approximate extremes, if every
+    // value within E gives the same fp16 min and step (fp32 interval ends, hardware
+    // round-to-nearest-even: the interval is many fp32 ulps wide, so it settles the
+    // float64 decision too); the others from the exact values of their candidates
+    float Ev[NT];
+    uint32_t w0[NT], cand[NT];
+    bool hbad[NT];
+#pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float c[MB * 4];
-      float s2 = 0.f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        if (t == nt) {
-          s2 = ss[t];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) c[mb * 4 + i] = acc[mb][t][i];
-        }
-      const int64_t tok = wtok0 + 16 * nt + n;
-      const bool valid = tok < a.n_tokens;
-      const T* row = xu + tok * kHeadDim;
+      const bool valid = wtok0 + 16 * nt + n < a.n_tokens;
+      float s2 = ss[nt];
       s2 += __shfl_xor(s2, 16);
       s2 += __shfl_xor(s2, 32);
-      float mn = c[0], mx = c[0];
+      float mn = acc[0][nt][0], mx = acc[0][nt][0];
 #pragma unroll
-      for (int s = 1; s < MB * 4; ++s) {
-        mn = fminf(mn, c[s]);
-        mx = fmaxf(mx, c[s]);
+      for (int s = 1; s < NS; ++s) {
+        mn = fminf(mn, acc[s >> 2][nt][s & 3]);
+        mx = fmaxf(mx, acc[s >> 2][nt][s & 3]);
       }
       mn = fminf(mn, __shfl_xor(mn, 16));
       mn = fminf(mn, __shfl_xor(mn, 32));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // error bound of the coordinates: 256 (fp16 inputs) or 384 (fp32 inputs, three
-      // products per term) rounded additions, plus the split remainders; an fp32
-      // input below the fp16 normal range keeps an absolute split error of up to
-      // 2^-25 per element, at most 2^-25 * ||P_j||_1 <= 2^-21.5 per coordinate
-      const float E = kF32 ? 0x1.bp-16f * __builtin_sqrtf(s2) + 0x1p-21f : 0x1.5p-16f * __builtin_sqrtf(s2);
-
-      // header from the approximate extremes, if no value within E changes it
-      uint32_t w0;
-      bool hok;
-      {
-        const double ed = (double)E, kq = (double)((1 << bits) - 1);
-        const uint32_t m_lo = f64_to_f16_rne((double)mn - ed), m_hi = f64_to_f16_rne((double)mn + ed);
-        const double mu = f16_bits_to_f64(m_lo);
-        double r_lo = (double)mx - ed - mu, r_hi = (double)mx + ed - mu;
-        if (!(r_lo > 0.0)) r_lo = 0.0;
-        if (!(r_hi > 0.0)) r_hi = 0.0;
-        const uint32_t s_lo = f64_to_f16_rne(r_lo / kq), s_hi = f64_to_f16_rne(r_hi / kq);
-        hok = m_lo == m_hi && s_lo == s_hi;
-        w0 = m_lo | (s_lo << 16);
-      }
-      const bool hbad = valid && !hok;
-      if (__ballot(hbad)) {
-        uint32_t cand = 0u;
-        if (hbad) {
+      // error bound of the coordinates (see the top of the file); an fp32 input below
+      // the fp16 normal range keeps an absolute split error of up to 2^-25 per
+      // element, at most 2^-25 * ||P_j||_1 <= 2^-21.5 per coordinate
+      const float E = kF32 ? 0x1.8p-18f * __builtin_sqrtf(s2) + 0x1p-21f : 0x1.8p-19f * __builtin_sqrtf(s2);
+      Ev[nt] = E;
+      const uint32_t m_lo = h16_bits(mn - E), m_hi = h16_bits(mn + E);
+      const float muf0 = f16_bits_to_f32(m_lo);
+      const uint32_t s_lo = h16_bits(fmaxf(mx - E - muf0, 0.f) * kinv);
+      const uint32_t s_hi = h16_bits(fmaxf(mx + E - muf0, 0.f) * kinv);
+      w0[nt] = m_lo | (s_lo << 16);
+      hbad[nt] = valid && (m_lo != m_hi || s_lo != s_hi);
+      cand[nt] = 0u;
+      if (hbad[nt]) {
 #pragma unroll
-          for (int s = 0; s < MB * 4; ++s)
-            if (c[s] <= mn + 2.f * E || c[s] >= mx - 2.f * E) cand |= 1u << s;
+        for (int s = 0; s < NS; ++s) {
+          const float c = acc[s >> 2][nt][s & 3];
+          if (c <= mn + 2.f * E || c >= mx - 2.f * E) cand[nt] |= 1u << s;
         }
-        double emin = __builtin_inf(), emax = -__builtin_inf();
-        while (__ballot(cand != 0u)) {
-          if (cand) {
-            const int s = __builtin_ctz(cand);
-            cand &= cand - 1u;
-            const double v = exact_coord(row, pb, 16 * (s >> 2) + 4 * G + (s & 3));
+      }
+    }
+    {
+      int mine = 0;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) mine += __popc(cand[nt]);
+      if (__ballot(mine != 0)) {
+        int total;
+        const int off = wave_prefix(mine, lane, total);
+        const bool coop = total <= kRepairList;
+        if (coop) {
+          int k = off;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            for (uint32_t m = cand[nt]; m; m &= m - 1u) items[k++] = item_code(nt, n, G, __builtin_ctz(m));
+          coop_exact(items, res, total, xu, wtok0, P, R, lane);
+        }
+        int k = off;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          double emin = __builtin_inf(), emax = -__builtin_inf();
+          const T* row = xu + (wtok0 + 16 * nt + n) * kHeadDim;
+          for (uint32_t m = cand[nt]; m; m &= m - 1u) {
+            const int s = __builtin_ctz(m);
+            const double v = coop ? res[k] : exact_coord(row, P, R, 16 * (s >> 2) + 4 * G + (s & 3));
+            ++k;
             emin = fmin(emin, v);
             emax = fmax(emax, v);
           }
+          emin = fmin(emin, __shfl_xor(emin, 16));
+          emin = fmin(emin, __shfl_xor(emin, 32));
+          emax = fmax(emax, __shfl_xor(emax, 16));
+          emax = fmax(emax, __shfl_xor(emax, 32));
+          if (hbad[nt]) w0[nt] = quant_header(emin, emax, bits).word0;
         }
-        emin = fmin(emin, __shfl_xor(emin, 16));
-        emin = fmin(emin, __shfl_xor(emin, 32));
-        emax = fmax(emax, __shfl_xor(emax, 16));
-        emax = fmax(emax, __shfl_xor(emax, 32));
-        if (hbad) w0 = quant_header(emin, emax, bits).word0;
+        wave_sync();
       }
-      if (G == 0) hdrw[n] = w0;
+    }
 
-      // codes from the approximate coordinates, if no value within E changes them
-      const float muf = f16_bits_to_f32(w0 & 0xFFFFu), sgf = f16_bits_to_f32(w0 >> 16);
-      const bool sig_pos = sgf > 0.f;
-      const float inv = sig_pos ? 1.0f / sgf : 0.f;
-      const float tol = E * inv * 1.0001f + 0x1p-13f;
-      uint32_t flags = 0u;
+    // ---- per 16-token block: codes, exact codes near rounding boundaries, store
 #pragma unroll
-      for (int s = 0; s < MB * 4; ++s) {
-        const float u = (c[s] - muf) * inv;
-        const float lo = fminf(fmaxf(__builtin_floorf(u - tol + 0.5f), 0.f), top);
-        const float hi = fminf(fmaxf(__builtin_floorf(u + tol + 0.5f), 0.f), top);
-        codes[n * R + 16 * (s >> 2) + 4 * G + (s & 3)] = (uint8_t)lo;
-        if (valid && sig_pos && lo != hi) flags |= 1u << s;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t tok = wtok0 + 16 * nt + n;
+      const bool valid = tok < a.n_tokens;
+      const T* row = xu + tok * kHeadDim;
+      // q = (c - min) / step + 1/2, code = floor(q) clamped, unless q is within tol
+      // of an integer (tol: the coordinate bound E, and 4u (2^b) for the fp32 steps)
+      const float muf = f16_bits_to_f32(w0[nt] & 0xFFFFu), sgf = f16_bits_to_f32(w0[nt] >> 16);
+      const bool sig_pos = valid && sgf > 0.f;
+      const float inv = sgf > 0.f ? 1.0f / sgf : 0.f;
+      const float tol = Ev[nt] * inv * 1.0001f + (top + 1.f) * 0x1p-22f;
+      uint32_t fl = 0u;
+      uint32_t* rec = recw + n * W;
+      if (G == 0) {
+        if (pow2) rec[0] = w0[nt];
+        else hdrw[n] = w0[nt];
       }
-      if (__ballot(flags != 0u)) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        uint32_t v = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float q = fmaf(acc[mb][nt][i] - muf, inv, 0.5f);
+          const float fr = __builtin_amdgcn_fractf(q);
+          if (__builtin_fabsf(fr - 0.5f) > 0.5f - tol) fl |= 1u << (4 * mb + i);
+          v = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(q - fr, 0.f, top), i, v);
+        }
+        const int j0 = 16 * mb + 4 * G;  // first of the four coordinates
+        if (bits == 8) rec[1 + (j0 >> 2)] = v;
+        else if (bits == 4) ((uint16_t*)(rec + 1))[j0 >> 2] = (uint16_t)compact4(v);
+        else if (bits == 2) ((uint8_t*)(rec + 1))[j0 >> 2] = (uint8_t)compact2(v);
+        else *(uint32_t*)(wb + n * R + j0) = v;
+      }
+      if (!sig_pos) fl = 0u;
+      if (__ballot(fl != 0u)) {  // exact codes of the flagged coordinates
+        int total;
+        const int off = wave_prefix(__popc(fl), lane, total);
+        const bool coop = total <= kRepairList;
+        if (coop) {
+          int k = off;
+          for (uint32_t m = fl; m; m &= m - 1u) items[k++] = item_code(nt, n, G, __builtin_ctz(m));
+          coop_exact(items, res, total, xu, wtok0, P, R, lane);
+        }
         const double mu = (double)muf, sg = (double)sgf;
-        while (__ballot(flags != 0u)) {
-          if (flags) {
-            const int s = __builtin_ctz(flags);
-            flags &= flags - 1u;
-            const int j = 16 * (s >> 2) + 4 * G + (s & 3);
-            codes[n * R + j] = (uint8_t)quant_code(exact_coord(row, pb, j), mu, sg, bits);
+        int k = off;
+        for (uint32_t m = fl; m; m &= m - 1u) {
+          const int s = __builtin_ctz(m);
+          const int j = 16 * (s >> 2) + 4 * G + (s & 3);
+          const uint32_t code = quant_code(coop ? res[k] : exact_coord(row, P, R, j), mu, sg, bits);
+          ++k;
+          if (pow2) {  // codes of other lanes share the word: atomic field update
+            const int bit = j * bits;
+            const uint32_t sh = bit & 31, fm = ((1u << bits) - 1u) << sh;
+            atomicAnd(rec + 1 + (bit >> 5), ~fm);
+            atomicOr(rec + 1 + (bit >> 5), code << sh);
+          } else {
+            wb[n * R + j] = (uint8_t)code;
           }
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_sync();
 
-      // pack and store the block's records (consecutive tokens are contiguous)
+      // store the block's records (consecutive tokens are contiguous); f / W as a
+      // multiply-high by ceil(2^32 / W), exact for f < 2^16
       const int64_t btok0 = wtok0 + 16 * nt;
       for (int f = lane; f < 16 * W; f += 64) {
-        const int tn = f / W, w = f - tn * W;
-        if (btok0 + tn < a.n_tokens) cu[btok0 * W + f] = w == 0 ? hdrw[tn] : pack_word(codes + tn * R, R, bits, w - 1);
+        const int tn = (int)__umulhi((uint32_t)f, wmagic), w = f - tn * W;
+        if (btok0 + tn < a.n_tokens) {
+          uint32_t word;
+          if (pow2) word = recw[f];
+          else word = w == 0 ? hdrw[tn] : pack_word(wb + tn * R, R, bits, w - 1);
+          cu[btok0 * W + f] = word;
+        }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_sync();
     }
   }
 }
 
-template <typename T, int R, int NT>
+// Launch shapes per (input type, rank), from measurements of the 128K-context
+// allocations: 16-token blocks per wave (NT), whether the next tile's inputs are
+// loaded during quantization (PF), and workgroups per CU (OCC, bounds registers).
+template <typename T, int R>
+struct EncShape {
+  static constexpr bool kF32 = sizeof(T) == 4;
+  static constexpr int NT = kF32 ? (R == 128 ? 1 : 2) : (R == 16 ? 4 : 2);
+  static constexpr bool PF = !kF32 && R == 32;
+  static constexpr int OCC = (!kF32 && R <= 64) ? 3 : 2;
+};
+
+template <typename T, int R>
 hipError_t launch_rank(const EncodeArgs& a, uint64_t mask_k, uint64_t mask_v, hipStream_t s) {
+  using S = EncShape<T, R>;
   const int units = __builtin_popcountll(mask_k) + __builtin_popcountll(mask_v);
   if (units == 0) return hipSuccess;
-  constexpr int kTileTok = kEncWaves * 16 * NT;
+  constexpr int kTileTok = kEncWaves * 16 * S::NT;
   const int64_t n_tiles = (a.n_tokens + kTileTok - 1) / kTileTok;
   // about 2048 workgroups or more in flight, each staging the basis once for its tiles
   const int64_t per_tile_row = (int64_t)units * a.batch;
   int64_t tpw = (n_tiles * per_tile_row) / 2048;
   tpw = tpw < 1 ? 1 : (tpw > 8 ? 8 : tpw);
   const dim3 grid((unsigned)((n_tiles + tpw - 1) / tpw), (unsigned)units, (unsigned)a.batch);
-  hipLaunchKernelGGL((encode_mfma_kernel<T, R, NT>), grid, dim3(256), enc_lds_bytes(R), s, a, mask_k, mask_v,
-                     (int)tpw);
+  hipLaunchKernelGGL((encode_mfma_kernel<T, R, S::NT, S::PF, S::OCC>), grid, dim3(256), enc_lds_bytes(R), s, a,
+                     mask_k, mask_v, (int)tpw);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_all_ranks(const EncodeArgs& a, int n_heads, hipStream_t s) {
-  constexpr bool kF32 = sizeof(T) == 4;
   uint64_t mk[4] = {0, 0, 0, 0}, mv[4] = {0, 0, 0, 0};
   for (int h = 0; h < n_heads; ++h) {
     const int ik = __builtin_ctz((unsigned)a.heads.h[h].rk) - 4, iv = __builtin_ctz((unsigned)a.heads.h[h].rv) - 4;
@@ -365,10 +511,10 @@ hipError_t launch_all_ranks(const EncodeArgs& a, int n_heads, hipStream_t s) {
     mv[iv] |= 1ull << h;
   }
   hipError_t e;
-  if ((e = launch_rank<T, 16, kF32 ? 2 : 4>(a, mk[0], mv[0], s)) != hipSuccess) return e;
-  if ((e = launch_rank<T, 32, kF32 ? 2 : 4>(a, mk[1], mv[1], s)) != hipSuccess) return e;
-  if ((e = launch_rank<T, 64, kF32 ? 2 : 4>(a, mk[2], mv[2], s)) != hipSuccess) return e;
-  return launch_rank<T, 128, 2>(a, mk[3], mv[3], s);
+  if ((e = launch_rank<T, 16>(a, mk[0], mv[0], s)) != hipSuccess) return e;
+  if ((e = launch_rank<T, 32>(a, mk[1], mv[1], s)) != hipSuccess) return e;
+  if ((e = launch_rank<T, 64>(a, mk[2], mv[2], s)) != hipSuccess) return e;
+  return launch_rank<T, 128>(a, mk[3], mv[3], s);
 }
 
 }  // namespace
