@@ -412,7 +412,7 @@ __host__ __device__ inline size_t attend_lds_bytes(int kbuf_words, int vbuf_word
          sizeof(float);
 }
 
-// ----------------------------------------------------------------- split merge + back-projection
+// ----------------------------------------------------------------- split merge
 // Split partials cross workgroups (and XCDs, whose L2 caches are not coherent with
 // each other): they are written and read as relaxed device-scope atomics, which
 // bypass the non-coherent cache level, and ordered by the arrival counter after
@@ -430,38 +430,31 @@ __device__ inline void part_load2(const float* p, float& x, float& y) {
   x = __builtin_bit_cast(float, (uint32_t)v);
   y = __builtin_bit_cast(float, (uint32_t)(v >> 32));
 }
-// Offsets in a split partial: o~[0, r_V), then m and l.
+// Offsets in a split partial: o[0, 128) (the back-projected P_V o~ of the split,
+// unnormalised), then m and l.
 constexpr int kPartM = kMaxRank, kPartL = kMaxRank + 1;
 
 constexpr int kMergeChunk = 8;  // splits whose loads one merging thread has in flight
 
 // Run by the last workgroup of a (sequence, KV head) to finish its split partials.
-// Work item = (head, 4 consecutive codes); with at most 128 items two threads share
-// one, each taking every other kMergeChunk splits.  A thread issues the coherent
-// loads of kMergeChunk splits (o~ quad, m and l) at once and folds them into a
-// running log-sum-exp, with its half row of P_V already loading;
-// the two halves combine through a lane exchange, o~ / l goes to LDS, then
-// o = P_V o~ (thread pair per output row, half the codes each).  `w` is LDS scratch
-// of 16 * 128 floats.  The arrival counter is left at zero for the next call.
-__device__ inline void merge_splits(const AttendArgs& a, int h, int b, float* w) {
+// Work item = (head, 4 consecutive output dimensions); with at most 128 items two
+// threads share one, each taking every other kMergeChunk splits.  A thread issues
+// the coherent loads of kMergeChunk splits (output quad, m and l) at once and folds
+// them into a running log-sum-exp; the two halves combine through a lane exchange
+// and o / l is the output (the back-projection already happened in each split's
+// workgroup, since it commutes with the weighted sum).  The arrival counter is left
+// at zero for the next call.
+__device__ inline void merge_splits(const AttendArgs& a, int h, int b) {
   const int tid = threadIdx.x;
-  const HeadDesc& hd = a.heads.h[h];
-  const int g = a.group, rv = hd.rv, ns = a.n_splits;
+  const int g = a.group, ns = a.n_splits;
   const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
-  float* ot = w;  // [16][128] normalised o~
-  // this thread's half row of P_V for the back-projection, in flight during the merge
-  const int i = tid >> 1, half = tid & 1, jh = rv / 2;
-  const float* row = a.basis_v + hd.boff_v + (int64_t)i * rv + half * jh;
-  float4 pv[kMaxRank / 8];
-#pragma unroll
-  for (int k = 0; k < kMaxRank / 8; ++k)
-    if (4 * k < jh) pv[k] = *(const float4*)(row + 4 * k);
-  const int nq = rv / 4, items = g * nq;
+  // item = (query head, four output dimensions); two threads per item when they fit
+  const int items = g * (kHeadDim / 4);
   const int tpi = items <= 128 ? 2 : 1;
   for (int t0 = 0; t0 < items * tpi; t0 += 256) {
     const int t = t0 + tid;
     const int item = t / tpi, sp = t % tpi;  // sp: which splits of the item this thread takes
-    const int hh = item / nq, jq = item % nq;
+    const int hh = item / (kHeadDim / 4), jq = item % (kHeadDim / 4);
     const bool act = item < items;
     const float* part = a.part + (bq0 + (act ? hh : 0)) * ns * (int64_t)kPartStride + 4 * jq;
     float M = -__builtin_inff(), L = 0.0f, A0 = 0.0f, A1 = 0.0f, A2 = 0.0f, A3 = 0.0f;
@@ -518,30 +511,7 @@ __device__ inline void merge_splits(const AttendArgs& a, int h, int b, float* w)
     }
     if (act && sp == 0) {
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      *(f32x4*)(ot + hh * kMaxRank + 4 * jq) = f32x4{A0 * inv, A1 * inv, A2 * inv, A3 * inv};
-    }
-  }
-  __syncthreads();
-  float acc[kMaxGroup];
-#pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) acc[hh] = 0.0f;
-#pragma unroll
-  for (int k = 0; k < kMaxRank / 8; ++k) {
-    if (4 * k < jh) {
-#pragma unroll
-      for (int hh = 0; hh < kMaxGroup; ++hh) {
-        if (hh < g) {
-          const float* o = &ot[hh * kMaxRank + half * jh + 4 * k];
-          acc[hh] = fmaf(pv[k].x, o[0], fmaf(pv[k].y, o[1], fmaf(pv[k].z, o[2], fmaf(pv[k].w, o[3], acc[hh]))));
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) {
-    if (hh < g) {
-      const float v = acc[hh] + __shfl_xor(acc[hh], 1);
-      if (half == 0) a.out[(bq0 + hh) * kHeadDim + i] = v;
+      *(f32x4*)(a.out + (bq0 + hh) * kHeadDim + 4 * jq) = f32x4{A0 * inv, A1 * inv, A2 * inv, A3 * inv};
     }
   }
   if (tid == 0)
@@ -892,6 +862,15 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   run(c, st);
   wait_tiles();
 
+  // this thread's half row of P_V for the back-projection of the workgroup's partial,
+  // in flight during the wave merge
+  const int bi = tid >> 1, bhalf = tid & 1, jh = rv / 2;
+  const float* prow = a.basis_v + hd.boff_v + (int64_t)bi * rv + bhalf * jh;
+  float4 pv[kMaxRank / 8];
+#pragma unroll
+  for (int k = 0; k < kMaxRank / 8; ++k)
+    if (4 * k < jh) pv[k] = *(const float4*)(prow + 4 * k);
+
   // ---- wave partial: m, l, sum of p*min (per head), o~[head][j] in natural code order
   const int n = lane & 15, G = lane >> 4;
   float* mlw = ml + wave * 48;
@@ -922,8 +901,10 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   }
   __syncthreads();
 
-  // ---- merge the four wave partials, one partial per query head
+  // ---- merge the four wave partials, one partial o~[head][r_V] per query head (in
+  // the score area, free after the token loop), then its back-projection P_V o~
   float* part0 = a.part + (bq0 * a.n_splits + blockIdx.x) * (int64_t)kPartStride;
+  float* ot = scores;  // [g][kMaxRank]
   for (int o = tid; o < g * rv; o += 256) {
     const int hh = o / rv, j = o % rv;
     float M = -__builtin_inff();
@@ -940,11 +921,36 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
         lacc = fmaf(wgt, ml[w * 48 + 16 + hh], lacc);
       }
     }
-    float* ph = part0 + (int64_t)hh * a.n_splits * kPartStride;
-    part_store(ph + j, acc);
+    ot[hh * kMaxRank + j] = acc;
     if (j == 0) {
+      float* ph = part0 + (int64_t)hh * a.n_splits * kPartStride;
       part_store(ph + kPartM, M);
       part_store(ph + kPartL, lacc);
+    }
+  }
+  __syncthreads();
+  {
+    float accb[GM];
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh) accb[hh] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxRank / 8; ++k) {
+      if (4 * k < jh) {
+#pragma unroll
+        for (int hh = 0; hh < GM; ++hh) {
+          if (hh < g) {
+            const f32x4 o4 = *(const f32x4*)(ot + hh * kMaxRank + bhalf * jh + 4 * k);
+            accb[hh] = fmaf(pv[k].x, o4[0], fmaf(pv[k].y, o4[1], fmaf(pv[k].z, o4[2], fmaf(pv[k].w, o4[3], accb[hh]))));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh) {
+      if (hh < g) {
+        const float v = accb[hh] + __shfl_xor(accb[hh], 1);
+        if (bhalf == 0) part_store(part0 + (int64_t)hh * a.n_splits * kPartStride + bi, v);
+      }
     }
   }
 
@@ -958,7 +964,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   }
   __syncthreads();
   if (*flag == 0u) return;
-  merge_splits(a, h, b, areas);
+  merge_splits(a, h, b);
 }
 
 }  // namespace kvtc
