@@ -818,8 +818,16 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   float* wl = areas + wave * WA;
 
   WaveCtx c;
-  const int wq = (int)(a.split_tokens / kWaves);
-  c.t_begin = (int)blockIdx.x * (int)a.split_tokens + wave * wq;
+  // split x covers the 256-token quanta [x nq / ns, (x + 1) nq / ns) of the nq in the
+  // context: the splits differ by at most one quantum, so the XCDs (which take the
+  // splits round-robin) stream equal shares
+  const int nq = (int)((a.n_tokens + kSplitQuantum - 1) / kSplitQuantum);
+  const int q0 = (int)(((int64_t)blockIdx.x * nq) / a.n_splits);
+  const int q1 = (int)(((int64_t)blockIdx.x * nq + nq) / a.n_splits);
+  const int s_begin = q0 * kSplitQuantum;
+  const int s_end = q1 * kSplitQuantum < (int)a.n_tokens ? q1 * kSplitQuantum : (int)a.n_tokens;
+  const int wq = (q1 - q0) * (kSplitQuantum / kWaves);
+  c.t_begin = s_begin + wave * wq;
   c.t_end = c.t_begin + wq;
   if (c.t_end > (int)a.n_tokens) c.t_end = (int)a.n_tokens;
   const int wk = hd.wk, wv = hd.wv;
@@ -840,7 +848,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
 
   // append fused with attention: the workgroup whose split holds the new token
   // encodes its key and value (waves 0-1 and 2-3) before any of its tiles stream in
-  if (a.append_pos >= 0 && (int64_t)blockIdx.x == a.append_pos / a.split_tokens) {
+  if (a.append_pos >= s_begin && a.append_pos < s_end) {
     EncodeScratch* scr = (EncodeScratch*)scores;  // score and tile areas are not in use yet
     const int tensor = tid >> 7, t = tid & 127;
     const int r = tensor ? hd.rv : hd.rk, bits = tensor ? hd.bv : hd.bk, W = tensor ? hd.wv : hd.wk;
@@ -910,12 +918,12 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     float M = -__builtin_inff();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
-      if ((int)blockIdx.x * (int)a.split_tokens + w * wq < (int)a.n_tokens) M = fmaxf(M, ml[w * 48 + hh]);
+      if (s_begin + w * wq < (int)a.n_tokens) M = fmaxf(M, ml[w * 48 + hh]);
     const float mu = M == -__builtin_inff() ? 0.0f : M;
     float acc = 0.0f, lacc = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      if ((int)blockIdx.x * (int)a.split_tokens + w * wq < (int)a.n_tokens) {
+      if (s_begin + w * wq < (int)a.n_tokens) {
         const float wgt = exp2f(ml[w * 48 + hh] - mu);
         acc = fmaf(wgt, areas[w * WA + hh * rv + j], acc);
         lacc = fmaf(wgt, ml[w * 48 + 16 + hh], lacc);

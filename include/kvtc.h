@@ -141,8 +141,10 @@ kv_status kv_attend_decode(const kv_layout *layout, const void *q, kv_dtype dtyp
                            const uint32_t *cache_v, float softmax_scale, float *out, void *workspace,
                            size_t workspace_bytes, void *stream);
 
-/* As kv_attend_decode with an explicit number of context tokens per split-K
- * work unit (a positive multiple of 256; 0 picks the default).  The result is
+/* As kv_attend_decode with an explicit maximum number of context tokens per
+ * split-K work unit (a positive multiple of 256; 0 picks the default): the
+ * context is divided into ceil(n_tokens / split_tokens) splits of whole
+ * 256-token blocks whose sizes differ by at most one block.  The result is
  * the same up to float rounding for every split size.  The workspace must
  * hold kv_workspace_bytes_split(layout, n_tokens, split_tokens) bytes. */
 kv_status kv_workspace_bytes_split(const kv_layout *layout, int64_t n_tokens, int64_t split_tokens,
