@@ -818,12 +818,15 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   float* wl = areas + wave * WA;
 
   WaveCtx c;
-  // split x covers the 256-token quanta [x nq / ns, (x + 1) nq / ns) of the nq in the
-  // context: the splits differ by at most one quantum, so the XCDs (which take the
-  // splits round-robin) stream equal shares
+  // split x covers the 256-token quanta [q(x), q(x + 1)) of the nq in the context,
+  // q(x) = min(nq, x ne / ns): the splits differ by at most one quantum, so the XCDs
+  // (which take the splits round-robin) stream equal shares.  With the append fused
+  // in, its encode counts as one more quantum (ne = nq + 1) of the last split, the
+  // one that holds the new token.
   const int nq = (int)((a.n_tokens + kSplitQuantum - 1) / kSplitQuantum);
-  const int q0 = (int)(((int64_t)blockIdx.x * nq) / a.n_splits);
-  const int q1 = (int)(((int64_t)blockIdx.x * nq + nq) / a.n_splits);
+  const int ne = nq + (a.append_pos >= 0 ? 1 : 0);
+  const int q0 = min(nq, (int)(((int64_t)blockIdx.x * ne) / a.n_splits));
+  const int q1 = min(nq, (int)(((int64_t)blockIdx.x * ne + ne) / a.n_splits));
   const int s_begin = q0 * kSplitQuantum;
   const int s_end = q1 * kSplitQuantum < (int)a.n_tokens ? q1 * kSplitQuantum : (int)a.n_tokens;
   const int wq = (q1 - q0) * (kSplitQuantum / kWaves);
