@@ -819,12 +819,13 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
 
   WaveCtx c;
   // split x covers the 256-token quanta [q(x), q(x + 1)) of the nq in the context,
-  // q(x) = min(nq, x ne / ns): the splits differ by at most one quantum, so the XCDs
-  // (which take the splits round-robin) stream equal shares.  With the append fused
-  // in, its encode counts as one more quantum (ne = nq + 1) of the last split, the
-  // one that holds the new token.
+  // q(x) = min(nq, x ne / ns) with ne = nq + 1: the splits differ by at most one
+  // quantum, so the XCDs (which take the splits round-robin) stream equal shares,
+  // and the last split (which holds the newest token, the one a fused append
+  // encodes) is one quantum lighter.  Both entry points use the same splits, so
+  // appending in the same launch leaves the result bit for bit unchanged.
   const int nq = (int)((a.n_tokens + kSplitQuantum - 1) / kSplitQuantum);
-  const int ne = nq + (a.append_pos >= 0 ? 1 : 0);
+  const int ne = nq + 1;
   const int q0 = min(nq, (int)(((int64_t)blockIdx.x * ne) / a.n_splits));
   const int q1 = min(nq, (int)(((int64_t)blockIdx.x * ne + ne) / a.n_splits));
   const int s_begin = q0 * kSplitQuantum;
