@@ -196,7 +196,8 @@ hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
       case 0: return launch_attend_spec0(a, s);
       case 1: return launch_attend_spec1(a, s);
       case 2: return launch_attend_spec2(a, s);
-      default: return launch_attend_spec3(a, s);
+      case 3: return launch_attend_spec3(a, s);
+      default: return launch_attend_spec4(a, s);
     }
   }
   // the generic kernel; all power-of-two widths skip the general-width paths

@@ -8,8 +8,9 @@
 // copy wait counts are constants, and each tile is one straight instruction
 // sequence.  The formats compiled are the ones the per-head bit allocation picks
 // under one budget of bits per vector (every rank of the allocation search with
-// b = min(8, floor(budget / r)) >= 2), all (K, V) pairs of a class; a layout
-// outside one class runs the generic kernel.
+// b = min(8, floor(budget / r)) >= 2), all (K, V) pairs of a class, and those of
+// the mixed full-rank / low-rank layout; a layout outside one class runs the
+// generic kernel.
 #pragma once
 
 #include "attend_core.h"
@@ -28,7 +29,11 @@ namespace kvtc {
 // 512-bit budget per vector (C1 picks b = min(8, floor(budget / r)))
 #define KVTC_SPEC_CLASS3(X) X(0, 16, 8, 16, 8) X(1, 16, 8, 32, 8) X(2, 16, 8, 64, 8) X(3, 16, 8, 128, 4) X(4, 32, 8, 16, 8) X(5, 32, 8, 32, 8) X(6, 32, 8, 64, 8) X(7, 32, 8, 128, 4) X(8, 64, 8, 16, 8) X(9, 64, 8, 32, 8) X(10, 64, 8, 64, 8) X(11, 64, 8, 128, 4) X(12, 128, 4, 16, 8) X(13, 128, 4, 32, 8) X(14, 128, 4, 64, 8) X(15, 128, 4, 128, 4)
 
-constexpr int kSpecClasses = 4;
+// Mixed fixed-width layout: full-rank r = 128 at 2 bits beside r = 16 at 6 bits
+// (half of the heads each), every (K, V) pair of the two formats
+#define KVTC_SPEC_CLASS4(X) X(0, 128, 2, 128, 2) X(1, 128, 2, 16, 6) X(2, 16, 6, 128, 2) X(3, 16, 6, 16, 6)
+
+constexpr int kSpecClasses = 5;
 
 // Index of (rk, bk, rv, bv) in class `cls`, or -1.
 __host__ inline int spec_index(int cls, int rk, int bk, int rv, int bv) {
@@ -40,6 +45,7 @@ __host__ inline int spec_index(int cls, int rk, int bk, int rv, int bv) {
     case 1: KVTC_SPEC_CLASS1(KVTC_SPEC_FIND) break;
     case 2: KVTC_SPEC_CLASS2(KVTC_SPEC_FIND) break;
     case 3: KVTC_SPEC_CLASS3(KVTC_SPEC_FIND) break;
+    case 4: KVTC_SPEC_CLASS4(KVTC_SPEC_FIND) break;
     default: break;
   }
 #undef KVTC_SPEC_FIND

@@ -77,5 +77,6 @@ hipError_t launch_attend_spec0(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec1(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec2(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec3(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_spec4(const AttendArgs& a, hipStream_t s);
 
 }  // namespace kvtc

@@ -443,14 +443,19 @@ def test_end_to_end_encode_append_attend(K):
 
 
 # ------------------------------------------------------------------ full size, sampled
-@pytest.mark.parametrize("bpd", [2.0, 0.5])
-def test_full_size_128k_sampled_units(K, bpd):
-    """The decode configuration at full size (4 sequences x 8 KV heads x 131073 tokens),
-    encoded on the GPU and attended with the default split, in the launch configuration
-    the benchmark times.  Sampled (sequence, KV head) units are re-encoded by the oracle
-    from the same inputs: their records must match (exact headers, codes off by one only
-    at rounding ties) and their query heads' outputs are checked against oracle attention."""
-    wl = W.llama_t128k(bpd)
+FULL_SIZE = {"llama-2bpd": lambda: W.llama_t128k(2.0), "llama-0.5bpd": lambda: W.llama_t128k(0.5),
+             "qwen-mixed": lambda: W.QWEN_T128K}
+
+
+@pytest.mark.parametrize("name", list(FULL_SIZE))
+def test_full_size_128k_sampled_units(K, name):
+    """The 128K decode configurations at full size (LLaMA shape: 4 sequences x 8 KV heads,
+    Qwen shape: 8 sequences x 4 KV heads, 131073 tokens), encoded on the GPU and attended
+    with the default split, in the launch configuration the benchmark times.  Sampled
+    (sequence, KV head) units are re-encoded by the oracle from the same inputs: their
+    records must match (exact headers, codes off by one only at rounding ties) and their
+    query heads' outputs are checked against oracle attention."""
+    wl = FULL_SIZE[name]()
     T = wl.context + 1
     B, hkv, hq, d, g = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.group
     alloc, bk, bv = H.oracle_calibrate(wl)
@@ -470,7 +475,7 @@ def test_full_size_128k_sampled_units(K, bpd):
     got = out.cpu().numpy()
     gk, gv = H.u32_host(ck), H.u32_host(cv)
     rk, bits_k, rv, bits_v = zip(*alloc)
-    for b, h in [(0, 0), (3, hkv - 1), (1, 3)]:
+    for b, h in [(0, 0), (B - 1, hkv - 1), (1, hkv // 2)]:
         xk = W.tokens(wl, "K", b, h, 0, T)
         xv = W.tokens(wl, "V", b, h, 0, T)
         rec_k = np.concatenate([codec.encode_tokens(xk[i:i + 16384], bk[h], bits_k[h]) for i in range(0, T, 16384)])
