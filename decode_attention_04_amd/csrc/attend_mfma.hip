@@ -53,6 +53,9 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
   const int NT = rv / 16;
   const int t_begin = c.t_begin, t_end = c.t_end, nbuf = c.nbuf;
   const int lane = threadIdx.x & 63;
+  u32x4 aq_hi[4], aq_lo[4];
+  float sq[GM], kf[GM];
+  project_query<GM, 0>(a, c, rk, aq_hi, aq_lo, sq, kf);  // before the copies: in-order memory counter
   for (int t = 0; t < (nbuf > 1 ? nbuf - 1 : 1); ++t) {  // the first tiles
     const int t0 = t_begin + t * kTileT;
     if (t0 < t_end) {
@@ -61,9 +64,6 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
       tile_copy(c.rv_, (uint32_t)t0 * 4u * wv, (uint32_t)nn * 4u * wv, c.vtile + t * c.vbuf);
     }
   }
-  u32x4 aq_hi[4], aq_lo[4];
-  float sq[GM], kf[GM];
-  project_query<GM, 0>(a, c, rk, aq_hi, aq_lo, sq, kf);
   init_state(st);
   float* S = c.S;
   f32x4 (&acc2)[8] = st.acc2;
