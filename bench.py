@@ -206,8 +206,10 @@ def copy_probe(mib: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    # a few hundred back-to-back launches bring the GPU to its sustained clocks (the
+    # first ~100 decode launches run up to 10% slower); 200 steps take about 16 ms
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="llama-128k-2bpd")
     ap.add_argument("--replica-bytes", type=float, default=1.2e9, help="total bytes of rotated layer caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
