@@ -128,6 +128,36 @@ def test_attend_validation_happens_before_launch():
     assert L.kv_attend_decode_split(*args(-1, need)) == lib_mod.KV_ERR_INVALID
 
 
+def test_prefill_requires_16_byte_aligned_inputs():
+    lay = _layout()
+    ref = lay.ref()
+    # more than one token: the matrix-core encoder loads 16-byte operands
+    assert L.kv_encode(ref, 18, 16, 1, 10, 0, 16, 16, 16, 16, None) == lib_mod.KV_ERR_INVALID
+    assert L.kv_encode(ref, 16, 20, 1, 10, 0, 16, 16, 16, 16, None) == lib_mod.KV_ERR_INVALID
+    assert "16-byte" in L.kv_last_error().decode()
+
+
+def test_fused_append_attend_validation_happens_before_launch():
+    lay = _layout()
+    ref = lay.ref()
+    need = lib_mod.kv_workspace_bytes(lay, 500)
+    f16 = lib_mod.KV_F16
+
+    def call(T=500, k1=16, v1=16, kvdt=f16, ws_bytes=need, q=16, out=16):
+        return L.kv_append_attend_decode(ref, k1, v1, kvdt, q, f16, T, 0, 16, 16, 16, 16, 0.1, out, 16, ws_bytes,
+                                         None)
+
+    assert call(T=0) == lib_mod.KV_ERR_INVALID          # nothing to append
+    assert call(T=1001) == lib_mod.KV_ERR_CAPACITY      # the new token past the capacity
+    assert call(k1=0) == lib_mod.KV_ERR_INVALID
+    assert call(v1=0) == lib_mod.KV_ERR_INVALID
+    assert call(k1=17) == lib_mod.KV_ERR_INVALID        # misaligned fp16 key
+    assert call(kvdt=5) == lib_mod.KV_ERR_INVALID
+    assert call(ws_bytes=need - 4) == lib_mod.KV_ERR_INVALID
+    assert call(q=0) == lib_mod.KV_ERR_INVALID
+    assert call(out=0) == lib_mod.KV_ERR_INVALID
+
+
 def test_pack_validation():
     assert L.kv_quantize_pack(16, 10, 48, 4, 16, None) == lib_mod.KV_ERR_UNSUPPORTED
     assert L.kv_quantize_pack(16, 10, 16, 9, 16, None) == lib_mod.KV_ERR_UNSUPPORTED
