@@ -6,26 +6,27 @@
 // is rotated and truncated with its head's basis and quantized with its head's
 // b-bit quantizer; at prefill that projection is one dense contraction per head.
 //
-// Arithmetic.  Each basis element (fp32) is split into two fp16 parts,
-// P = Ph + Pl + e with |e| <= 2^-22 |P| + 2^-25, and fp32 inputs the same way
-// (fp16 inputs are exact operands).  On gfx950, v_mfma_f32_16x16x32_f16 forms
-// its 32 products exactly, sums them exactly, adds the accumulator aligned to
-// 2^-24 of the largest product and rounds the result to nearest once (measured
-// on constructed operands: sub-ulp products survive the sum, cancellations are
-// exact, an accumulator bit 25 places below the largest product is dropped).
-// Per instruction the error is then at most u |D| + 2u max|p| (u = 2^-24), and
-// over the 8 chained instructions of a coordinate, with S_j = sum_i |x_i P_ij|
-// <= ||x||_2 (the columns of P are orthonormal), at most 24u S_j; the split
-// remainders add at most 4u S_j + 2^-25 ||x||_1 <= 4u S_j + 11.4u ||x||_2.  The
-// encoder uses
-//     E = 48u ||x||_2
-// (fp32 inputs: three products per term, 24 instructions, E = 96u ||x||_2 +
-// 2^-21, the last term for inputs split below the fp16 normal range; they must
-// lie inside the fp16 range, |x| < 65504).  The header (fp16 min and step) and
-// the codes are monotone functions of the coordinates, so a decision that takes
-// the same value at c~ - E and c~ + E is the exact decision.  The others are
-// recomputed from the float64 projection in the fixed summation order every
-// encode path uses (four groups of 32 rows, then the group sums in order):
+// Arithmetic.  Each basis element (fp32), scaled by 2^8, is split into two fp16
+// parts, 2^8 P = Ph + Pl + e with |e| <= 2^-22 |2^8 P| + 2^-25, and fp32 inputs the
+// same way (fp16 inputs are exact operands); the sums are scaled back by 2^-8,
+// exactly.  On gfx950, v_mfma_f32_16x16x32_f16 forms its 32 products exactly, sums
+// them exactly, adds the accumulator aligned to 2^-24 of the largest product and
+// rounds the result to nearest once (measured on constructed operands: sub-ulp
+// products survive the sum, cancellations are exact, an accumulator bit 25 places
+// below the largest product is dropped).  Per instruction the error is then at
+// most u |D| + u max|p| (u = 2^-24); over the 8 chained instructions of a
+// coordinate, with S_j = sum_i |x_i P_ij| <= ||x||_2 (the columns of P are
+// orthonormal), at most 9u S_j, and the split remainders add 4u S_j (the absolute
+// part, 2^-33 ||x||_1, is negligible).  The encoder uses
+//     E = 20u ||x||_2
+// for fp16 inputs (fp32 inputs: three products per term, 24 instructions, and the
+// absolute split error of inputs below the fp16 normal range: E = 96u ||x||_2 +
+// 2^-21; they must lie inside the fp16 range, |x| < 65504).  The header (fp16 min
+// and step) and the codes are monotone functions of the coordinates, so a
+// decision that takes the same value at c~ - E and c~ + E is the exact decision.
+// The others are recomputed from the float64 projection in the fixed summation
+// order every encode path uses (four groups of 32 rows, then the group sums in
+// order):
 //   * a token whose fp16 min or step could round either way gets the exact
 //     values of its extreme candidates (c~ within 2E of the approximate min or
 //     max), which contain the exact extremes, and its header from them;
@@ -204,14 +205,16 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
   uint32_t* cu = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + ((int64_t)b * a.capacity + a.pos0) * W;
 
   // stage the basis as A operands: for (mb, ks, lane) the eight rows 32ks + 8G ..
-  // of column 16mb + m, hi parts then (64 lanes later) lo parts
+  // of column 16mb + m, hi parts then (64 lanes later) lo parts; the basis is scaled
+  // by 2^8 (undone exactly on the sums) so that the lo parts of its elements stay in
+  // the fp16 normal range down to |P| = 2^-11
   for (int q = tid; q < R * 16; q += 256) {
     const int ln = q & 63, ks = (q >> 6) & 3, mb = q >> 8;
     const int k0 = 32 * ks + 8 * (ln >> 4), j = 16 * mb + (ln & 15);
     enc_half8 hi, lo;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p = P[(k0 + i) * R + j];
+      const float p = P[(k0 + i) * R + j] * 0x1p8f;
       hi[i] = (_Float16)p;
       lo[i] = (_Float16)(p - (float)hi[i]);
     }
@@ -310,6 +313,10 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
       }
       __builtin_amdgcn_sched_barrier(0);  // keeps the operand reads of later row blocks from piling up
     }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mb][nt] *= 0x1p-8f;  // the basis scale, exactly
     if constexpr (!kF32 && PF) {
       if (it + 1 < tiles_per_wg && tile + 1 < n_tiles) load_f16(tile + 1);
     }
@@ -340,7 +347,7 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
       // error bound of the coordinates (see the top of the file); an fp32 input below
       // the fp16 normal range keeps an absolute split error of up to 2^-25 per
       // element, at most 2^-25 * ||P_j||_1 <= 2^-21.5 per coordinate
-      const float E = kF32 ? 0x1.8p-18f * __builtin_sqrtf(s2) + 0x1p-21f : 0x1.8p-19f * __builtin_sqrtf(s2);
+      const float E = kF32 ? 0x1.8p-18f * __builtin_sqrtf(s2) + 0x1p-21f : 0x1.4p-20f * __builtin_sqrtf(s2);
       Ev[nt] = E;
       const uint32_t m_lo = h16_bits(mn - E), m_hi = h16_bits(mn + E);
       const float muf0 = f16_bits_to_f32(m_lo);
