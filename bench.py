@@ -122,6 +122,59 @@ def encode_rate(K, wl, block=2048, reps=5):
             "pct_of_hbm_peak": round(100 * (in_bytes + out_bytes) / ms / 1e6 / HBM_PEAK_GBS, 2)}
 
 
+def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9):
+    """Sustained kv_append_attend_decode throughput of another decode layout at its full size.
+
+    The caches hold the workload's generated keys and values of the first `block` tokens
+    repeated along the token axis (same per-token statistics), encoded on the GPU; enough
+    layer caches rotate to exceed the Infinity Cache.  Not checked against anything here:
+    the GPU parity tests cover these layouts."""
+    import torch
+
+    alloc, bk, bv = calibrate(wl)
+    T = wl.context + 1
+    B, H, hq, d = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim
+    lay = K.Layout(H, hq, B, T, alloc)
+    dev = torch.device("cuda:0")
+    pk = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bk])).to(dev)
+    pv = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bv])).to(dev)
+    reps_t = (T - 1 + block - 1) // block
+    kx = torch.from_numpy(W.kv_array(wl, "K", 0, block)).to(dev).repeat(1, 1, reps_t, 1)[:, :, :T - 1].contiguous()
+    vx = torch.from_numpy(W.kv_array(wl, "V", 0, block)).to(dev).repeat(1, 1, reps_t, 1)[:, :, :T - 1].contiguous()
+    ck = torch.zeros(K.kv_cache_bytes(lay, 0) // 4, dtype=torch.int32, device=dev)
+    cv = torch.zeros(K.kv_cache_bytes(lay, 1) // 4, dtype=torch.int32, device=dev)
+    K.kv_encode(lay, kx, vx, T - 1, 0, pk, pv, ck, cv)
+    k1 = kx[:, :, -1].contiguous()
+    v1 = vx[:, :, -1].contiguous()
+    del kx, vx
+    cache_bytes = (ck.numel() + cv.numel()) * 4
+    n_rep = max(2, int(math.ceil(min_bytes / cache_bytes)))
+    caches = [(ck, cv)] + [(ck.clone(), cv.clone()) for _ in range(n_rep - 1)]
+    q = torch.from_numpy(W.query_array(wl, 0)).to(dev)
+    out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+    ws = torch.zeros(K.kv_workspace_bytes(lay, T) // 4, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    for i in range(warmup):
+        ck_, cv_ = caches[i % n_rep]
+        K.kv_append_attend_decode(lay, k1, v1, q, T, pk, pv, ck_, cv_, scale, out, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        ck_, cv_ = caches[i % n_rep]
+        K.kv_append_attend_decode(lay, k1, v1, q, T, pk, pv, ck_, cv_, scale, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    attend_bytes, append_bytes = step_bytes(wl, alloc, T)
+    gbs = (attend_bytes + append_bytes) / (us * 1e-6) / 1e9
+    del caches, ck, cv
+    torch.cuda.empty_cache()
+    return {"batch": B, "n_q_heads": hq, "n_kv_heads": H, "context_tokens": T,
+            "allocation": [list(a) for a in alloc], "us_per_step": round(us, 2), "GB_per_s": round(gbs, 1),
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "layer_caches_rotated": n_rep}
+
+
 def cpu_baseline(wl, alloc, bk, bv, T, budget_s=12.0):
     """The oracle (float64 numpy, one BLAS thread) on whole (sequence, KV head) units of the same workload."""
     from threadpoolctl import threadpool_limits
@@ -213,6 +266,8 @@ def main():
     ap.add_argument("--workload", default="llama-128k-2bpd")
     ap.add_argument("--replica-bytes", type=float, default=1.2e9, help="total bytes of rotated layer caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-rates", action="store_true",
+                    help="skip the decode measurements of the other 128K layouts")
     ap.add_argument("--no-encode-rates", action="store_true",
                     help="skip the prefill encode measurements of the prefill workloads")
     ap.add_argument("--graph", action="store_true",
@@ -363,6 +418,13 @@ def main():
             enc_rates[ewl.name] = encode_rate(K, ewl)
             log(f"encode {ewl.name}: {enc_rates[ewl.name]}")
 
+    dec_rates = None
+    if not args.no_decode_rates:
+        dec_rates = {}
+        for dwl in (W.llama_t128k(0.5), W.llama_t128k(1.0), W.llama_t128k(4.0), W.QWEN_T128K):
+            dec_rates[dwl.name] = decode_rate(K, dwl)
+            log(f"decode {dwl.name}: {dec_rates[dwl.name]}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, alloc, bk, bv, T + 1, args.cpu_seconds)
@@ -393,6 +455,7 @@ def main():
             "bytes_per_step": attend_bytes + append_bytes,
             "encode_prefill_ms": round(enc_ms, 4),
             "encode_rates": enc_rates,
+            "other_decode_layouts": dec_rates,
         },
         "roofline": {
             "bound": "hbm",
