@@ -120,14 +120,16 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // Copy `nbytes` starting at byte `src` of the region to LDS `dst` in 16-byte
 // chunks (up to 12 bytes past the end are copied too); issues copy_insts(nbytes)
 // vector-memory instructions.
-__device__ inline void tile_copy(rsrc_t r, uint32_t src, uint32_t nbytes, uint32_t* dst) {
+__device__ inline void tile_copy(rsrc_t r, uint32_t src, uint32_t nbytes, uint32_t base) {
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t n16 = (nbytes + 15u) >> 4;
-  const uint32_t base = lds_addr(dst);
   uint32_t c = 0;
   for (; c + 64 <= n16; c += 64) dma16(r, base + 16u * c, src + 16u * (c + lane));
   if (c + lane < n16)  // tail: only the lanes whose 16 bytes belong to the tile
     dma16(r, base + 16u * c, src + 16u * (c + lane));
+}
+__device__ inline void tile_copy(rsrc_t r, uint32_t src, uint32_t nbytes, uint32_t* dst) {
+  tile_copy(r, src, nbytes, lds_addr(dst));
 }
 
 // tile_copy of a compile-time size: the 64-lane chunks unrolled, then the tail.
@@ -434,7 +436,7 @@ __device__ inline void part_load2(const float* p, float& x, float& y) {
 // unnormalised), then m and l.
 constexpr int kPartM = kMaxRank, kPartL = kMaxRank + 1;
 
-constexpr int kMergeChunk = 8;  // splits whose loads one merging thread has in flight
+constexpr int kMergeChunk = 16;  // splits whose loads one merging thread has in flight (one round up to 32 splits)
 
 // Run by the last workgroup of a (sequence, KV head) to finish its split partials.
 // Work item = (head, 4 consecutive output dimensions); with at most 128 items two
@@ -460,18 +462,19 @@ __device__ inline void merge_splits(const AttendArgs& a, int h, int b) {
     float M = -__builtin_inff(), L = 0.0f, A0 = 0.0f, A1 = 0.0f, A2 = 0.0f, A3 = 0.0f;
     for (int s0 = kMergeChunk * sp; s0 < ns; s0 += kMergeChunk * tpi) {
       float o[kMergeChunk][4], mv[kMergeChunk], lv[kMergeChunk];
+      // every load unconditional (splits past the last one re-read it and get weight
+      // 0), so that all of them are in flight before the first wait
 #pragma unroll
       for (int k = 0; k < kMergeChunk; ++k) {
-        mv[k] = -__builtin_inff();
-        lv[k] = 0.0f;
-        o[k][0] = o[k][1] = o[k][2] = o[k][3] = 0.0f;
-        if (act && s0 + k < ns) {
-          const float* ps = part + (int64_t)(s0 + k) * kPartStride;
-          part_load2(ps, o[k][0], o[k][1]);
-          part_load2(ps + 2, o[k][2], o[k][3]);
-          part_load2(ps - 4 * jq + kPartM, mv[k], lv[k]);
-        }
+        const int sk = s0 + k < ns ? s0 + k : ns - 1;
+        const float* ps = part + (int64_t)sk * kPartStride;
+        part_load2(ps, o[k][0], o[k][1]);
+        part_load2(ps + 2, o[k][2], o[k][3]);
+        part_load2(ps - 4 * jq + kPartM, mv[k], lv[k]);
       }
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k)
+        if (s0 + k >= ns) mv[k] = -__builtin_inff();
       float mc = M;
 #pragma unroll
       for (int k = 0; k < kMergeChunk; ++k) mc = fmaxf(mc, mv[k]);
@@ -571,16 +574,21 @@ __device__ inline void aq_slot(const float* qt, const float* E_h, int g, int rk,
 
 // The g query heads of this KV head projected into its key basis by the whole
 // workgroup, q~ = scale * log2(e) * P_K^T q (the inverse key transform folded into
-// the query), while the first record tiles stream in.  Wave w owns columns
+// the query), while the first record tiles stream in: the queries and the basis
+// columns are requested first, then `issue` starts the first tile copies, then the
+// arithmetic waits for its loads (the memory counter completes in order, so only
+// the last basis loads also wait for the copies, which were issued right behind
+// them).  Wave w owns columns
 // [w r_K / 4, (w+1) r_K / 4) of P_K; its lanes split the 128 rows into groups
 // (each lane loads its column segment once and serves all g heads), and the row
 // groups are summed across lanes.  Then per head the exponent E (max |q~| 2^E <
 // 2^14), sum(q~) and 2^(24-E), and each wave's MFMA A operands of q~ (B: the key
 // code width as unpacked by the score phase, 0 to read it from the head at run time).
-template <int GM, int B>
+template <int GM, int B, class Issue>
 __device__ __attribute__((always_inline)) inline void project_query(const AttendArgs& a, const WaveCtx& c, int rk,
                                                                     u32x4 (&aq_hi)[4], u32x4 (&aq_lo)[4],
-                                                                    float (&sq)[GM], float (&kf)[GM]) {
+                                                                    float (&sq)[GM], float (&kf)[GM],
+                                                                    Issue&& issue) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.y, b = blockIdx.z, g = c.g;
@@ -594,11 +602,8 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
   const int jj = lane % cw, rgi = lane / cw;
   const int j = wave * cw + jj;
   const float* col = a.basis_k + hd.boff_k + (int64_t)(rgi * rpg) * rk + j;
-  // every load in flight before the first use: the column segment, then the queries
-  float pk[kMaxRank / 2];
-#pragma unroll
-  for (int k = 0; k < kMaxRank / 2; ++k)
-    if (k < rpg) pk[k] = col[(int64_t)k * rk];
+  // every load in flight before the first use: the queries (used first), then the
+  // column segment, then the first tile copies
   constexpr int kQ = GM * kHeadDim / 256;
   float qv[kQ];
 #pragma unroll
@@ -610,6 +615,11 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
       qv[k] = a.dtype == 0 ? ((const float*)a.q)[off] : (float)((const _Float16*)a.q)[off];
     }
   }
+  float pk[kMaxRank / 2];
+#pragma unroll
+  for (int k = 0; k < kMaxRank / 2; ++k)
+    if (k < rpg) pk[k] = col[(int64_t)k * rk];
+  issue();
 #pragma unroll
   for (int k = 0; k < kQ; ++k) {
     const int idx = tid + 256 * k;  // head idx / 128, dimension idx % 128

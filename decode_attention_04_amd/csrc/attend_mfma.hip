@@ -55,15 +55,17 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
   const int lane = threadIdx.x & 63;
   u32x4 aq_hi[4], aq_lo[4];
   float sq[GM], kf[GM];
-  project_query<GM, 0>(a, c, rk, aq_hi, aq_lo, sq, kf);  // before the copies: in-order memory counter
-  for (int t = 0; t < (nbuf > 1 ? nbuf - 1 : 1); ++t) {  // the first tiles
-    const int t0 = t_begin + t * kTileT;
-    if (t0 < t_end) {
-      const int nn = (t_end - t0) < kTileT ? (t_end - t0) : kTileT;
-      tile_copy(c.rk_, (uint32_t)t0 * 4u * wk, (uint32_t)nn * 4u * wk, c.ktile + t * c.kbuf);
-      tile_copy(c.rv_, (uint32_t)t0 * 4u * wv, (uint32_t)nn * 4u * wv, c.vtile + t * c.vbuf);
+  const uint32_t kl = lds_addr(c.ktile), vl = lds_addr(c.vtile);
+  project_query<GM, 0>(a, c, rk, aq_hi, aq_lo, sq, kf, [&] {  // the first tiles, behind the projection loads
+    for (int t = 0; t < (nbuf > 1 ? nbuf - 1 : 1); ++t) {
+      const int t0 = t_begin + t * kTileT;
+      if (t0 < t_end) {
+        const int nn = (t_end - t0) < kTileT ? (t_end - t0) : kTileT;
+        tile_copy(c.rk_, (uint32_t)t0 * 4u * wk, (uint32_t)nn * 4u * wk, kl + 4u * (uint32_t)(t * c.kbuf));
+        tile_copy(c.rv_, (uint32_t)t0 * 4u * wv, (uint32_t)nn * 4u * wv, vl + 4u * (uint32_t)(t * c.vbuf));
+      }
     }
-  }
+  });
   init_state(st);
   float* S = c.S;
   f32x4 (&acc2)[8] = st.acc2;

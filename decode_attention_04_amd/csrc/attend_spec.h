@@ -77,14 +77,14 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
   static_assert(KI + VI <= 63, "vmcnt range");
   const int t_begin = c.t_begin, t_end = c.t_end, nbuf = c.nbuf;
   const int lane = threadIdx.x & 63;
-  // the query projection first: its loads would otherwise wait behind the first tile
-  // copies (the memory counter is in order), then the first nbuf - 1 tiles (one with
-  // a single buffer) start streaming
+  // the first nbuf - 1 tiles (one with a single buffer) start streaming behind the
+  // loads of the query projection
   u32x4 aq_hi[4], aq_lo[4];
   float sq[GM], kf[GM];
-  project_query<GM, BK>(a, c, RK, aq_hi, aq_lo, sq, kf);
-  for (int t = 0; t < (nbuf > 1 ? nbuf - 1 : 1); ++t)
-    if (t_begin + t * kTileT < t_end) issue_tile<WK, WV>(c, t_begin + t * kTileT, t_end, t);
+  project_query<GM, BK>(a, c, RK, aq_hi, aq_lo, sq, kf, [&] {
+    for (int t = 0; t < (nbuf > 1 ? nbuf - 1 : 1); ++t)
+      if (t_begin + t * kTileT < t_end) issue_tile<WK, WV>(c, t_begin + t * kTileT, t_end, t);
+  });
   init_state(st);
   if (lane < 4) ((uint32_t*)c.S)[GM * 64 + lane] = 0u;  // zero slot
   int slot = 0;
