@@ -884,15 +884,6 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   run(c, st);
   wait_tiles();
 
-  // this thread's half row of P_V for the back-projection of the workgroup's partial,
-  // in flight during the wave merge
-  const int bi = tid >> 1, bhalf = tid & 1, jh = rv / 2;
-  const float* prow = a.basis_v + hd.boff_v + (int64_t)bi * rv + bhalf * jh;
-  float4 pv[kMaxRank / 8];
-#pragma unroll
-  for (int k = 0; k < kMaxRank / 8; ++k)
-    if (4 * k < jh) pv[k] = *(const float4*)(prow + 4 * k);
-
   // ---- wave partial: m, l, sum of p*min (per head), o~[head][j] in natural code order
   const int n = lane & 15, G = lane >> 4;
   float* mlw = ml + wave * 48;
@@ -921,30 +912,45 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
       }
     }
   }
+
+  // this thread's half row of P_V for the back-projection of the workgroup's partial,
+  // in flight during the wave merge (issued once the value accumulators are free):
+  // segment [bhalf jh, bhalf jh + jh) of row bi, jh = r_V / 2, in float4 steps;
+  // steps past the segment re-read its first one and meet zeros in the staged
+  // partial, so that no load or product is conditional (a data-dependent branch
+  // here costs a full memory wait per step)
+  const int bi = tid >> 1, bhalf = tid & 1, jh = rv / 2;
+  const float* prow = a.basis_v + hd.boff_v + (int64_t)bi * rv + bhalf * jh;
+  float4 pv[kMaxRank / 8];
+#pragma unroll
+  for (int k = 0; k < kMaxRank / 8; ++k) pv[k] = *(const float4*)(prow + (4 * k < jh ? 4 * k : 0));
   __syncthreads();
 
-  // ---- merge the four wave partials, one partial o~[head][r_V] per query head (in
-  // the score area, free after the token loop), then its back-projection P_V o~
+  // ---- merge the four wave partials into one partial o~ per query head, staged
+  // in the score area (free after the token loop) as ot[head][half][64]: half h of
+  // head row holds o~[bhalf jh .. bhalf jh + jh) and zeros after it, rows >= g are
+  // zero.  Waves without tokens carry m = -1e30, l = 0 and a zero partial, so
+  // their weight is 0.  Then the back-projection P_V o~.
   float* part0 = a.part + (bq0 * a.n_splits + blockIdx.x) * (int64_t)kPartStride;
-  float* ot = scores;  // [g][kMaxRank]
-  for (int o = tid; o < g * rv; o += 256) {
-    const int hh = o / rv, j = o % rv;
+  float* ot = scores;  // [GM][2][64]
+#pragma unroll
+  for (int i = 0; i < GM / 2; ++i) {
+    const int o = tid + 256 * i;
+    const int hh = o >> 7, half = (o >> 6) & 1, m = o & 63;
+    const bool on = hh < g && m < jh;
+    const int hc = hh < g ? hh : 0, j = half * jh + (m < jh ? m : 0);
     float M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (s_begin + w * wq < (int)a.n_tokens) M = fmaxf(M, ml[w * 48 + hh]);
-    const float mu = M == -__builtin_inff() ? 0.0f : M;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[w * 48 + hc]);
     float acc = 0.0f, lacc = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      if (s_begin + w * wq < (int)a.n_tokens) {
-        const float wgt = exp2f(ml[w * 48 + hh] - mu);
-        acc = fmaf(wgt, areas[w * WA + hh * rv + j], acc);
-        lacc = fmaf(wgt, ml[w * 48 + 16 + hh], lacc);
-      }
+      const float wgt = exp2f(ml[w * 48 + hc] - M);
+      acc = fmaf(wgt, areas[w * WA + hc * rv + j], acc);
+      lacc = fmaf(wgt, ml[w * 48 + 16 + hc], lacc);
     }
-    ot[hh * kMaxRank + j] = acc;
-    if (j == 0) {
+    ot[o] = on ? acc : 0.0f;
+    if (on && o == hh * 128) {
       float* ph = part0 + (int64_t)hh * a.n_splits * kPartStride;
       part_store(ph + kPartM, M);
       part_store(ph + kPartL, lacc);
@@ -955,24 +961,24 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     float accb[GM];
 #pragma unroll
     for (int hh = 0; hh < GM; ++hh) accb[hh] = 0.0f;
+    // one step per float4 of the row segment: the staged reads of a step are issued
+    // together (the uniform bound keeps the scheduler from hoisting all of them,
+    // which would not fit the register budget)
 #pragma unroll
     for (int k = 0; k < kMaxRank / 8; ++k) {
       if (4 * k < jh) {
+        f32x4 o4[GM];
 #pragma unroll
-        for (int hh = 0; hh < GM; ++hh) {
-          if (hh < g) {
-            const f32x4 o4 = *(const f32x4*)(ot + hh * kMaxRank + bhalf * jh + 4 * k);
-            accb[hh] = fmaf(pv[k].x, o4[0], fmaf(pv[k].y, o4[1], fmaf(pv[k].z, o4[2], fmaf(pv[k].w, o4[3], accb[hh]))));
-          }
-        }
+        for (int hh = 0; hh < GM; ++hh) o4[hh] = *(const f32x4*)(ot + hh * 128 + bhalf * 64 + 4 * k);
+#pragma unroll
+        for (int hh = 0; hh < GM; ++hh)
+          accb[hh] = fmaf(pv[k].x, o4[hh][0], fmaf(pv[k].y, o4[hh][1], fmaf(pv[k].z, o4[hh][2], fmaf(pv[k].w, o4[hh][3], accb[hh]))));
       }
     }
 #pragma unroll
     for (int hh = 0; hh < GM; ++hh) {
-      if (hh < g) {
-        const float v = accb[hh] + __shfl_xor(accb[hh], 1);
-        if (bhalf == 0) part_store(part0 + (int64_t)hh * a.n_splits * kPartStride + bi, v);
-      }
+      const float v = accb[hh] + __shfl_xor(accb[hh], 1);
+      if (hh < g && bhalf == 0) part_store(part0 + (int64_t)hh * a.n_splits * kPartStride + bi, v);
     }
   }
 
