@@ -876,7 +876,9 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
       encode_token_128((const float*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, rec, scr[tensor], t, sync);
     else
       encode_token_128((const _Float16*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, rec, scr[tensor], t, sync);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the records are in L2 before any tile copy
+    // the records are in L2 before any tile copy (the builtin, unlike an asm wait, also
+    // tells the compiler that no store of the encoder is outstanding any more)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
   }
 
@@ -983,7 +985,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   }
 
   // ---- arrival: the last workgroup of this (sequence, KV head) merges all splits
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores have completed
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores have completed
   __syncthreads();
   uint32_t* flag = (uint32_t*)(ml + kWaves * 48);
   if (tid == 0) {
