@@ -267,7 +267,7 @@ def main():
     ap.add_argument("--replica-bytes", type=float, default=1.2e9, help="total bytes of rotated layer caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-rates", action="store_true",
-                    help="skip the decode measurements of the other 128K layouts")
+                    help="skip the decode measurements of the other layouts (128K budgets, Qwen, 32K batch 16)")
     ap.add_argument("--no-encode-rates", action="store_true",
                     help="skip the prefill encode measurements of the prefill workloads")
     ap.add_argument("--graph", action="store_true",
@@ -421,7 +421,8 @@ def main():
     dec_rates = None
     if not args.no_decode_rates:
         dec_rates = {}
-        for dwl in (W.llama_t128k(0.5), W.llama_t128k(1.0), W.llama_t128k(4.0), W.QWEN_T128K):
+        for dwl in (W.llama_t128k(0.5), W.llama_t128k(1.0), W.llama_t128k(4.0), W.QWEN_T128K,
+                    W.llama_prefill(32, 8), W.llama_prefill(64, 4)):
             dec_rates[dwl.name] = decode_rate(K, dwl)
             log(f"decode {dwl.name}: {dec_rates[dwl.name]}")
 

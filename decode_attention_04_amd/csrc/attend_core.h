@@ -700,14 +700,15 @@ __device__ __attribute__((always_inline)) inline void init_state(WaveState<GM>& 
 
 // Waves of a CU issue by age, so the workgroups resident first finish their splits
 // early and the last ones run their final tiles at lower occupancy.  Each wave
-// raises its issue priority with the share of its tiles still ahead of it, so the
-// waves that are behind catch up and all finish together.
+// raises its issue priority with the share of its tokens still ahead of it (3 in
+// the first quarter, then 2, 1, 0), so the waves that are behind catch up and all
+// finish together.  Comparisons only: a division here costs ~25 scalar
+// instructions per tile.
 __device__ inline void progress_priority(int t0, int t_begin, int t_end) {
-  const int left = (t_end - t0 + kTileT - 1) / kTileT, total = (t_end - t_begin + kTileT - 1) / kTileT;
-  const int pr = (4 * left) / (total + 1);
-  if (pr >= 3) __builtin_amdgcn_s_setprio(3);
-  else if (pr == 2) __builtin_amdgcn_s_setprio(2);
-  else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+  const int q = t_end - t_begin, d = t0 - t_begin;
+  if (4 * d < q) __builtin_amdgcn_s_setprio(3);
+  else if (2 * d < q) __builtin_amdgcn_s_setprio(2);
+  else if (4 * d < 3 * q) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
 }
 
