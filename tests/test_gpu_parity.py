@@ -295,6 +295,16 @@ def test_attention_short_and_ragged_contexts(K, T):
     _attention_case(K, alloc, bk, bv, 2, 3, T, T, [0])
 
 
+@pytest.mark.parametrize("g", [1, 2, 3, 5, 8, 12])
+def test_attention_group_sizes(K, g):
+    """GQA groups below, at and above the specialised kernels' row blocks (4, 8; 12
+    runs the generic kernel): query-head rows past g stay out of every sum."""
+    say(f"attention g={g}")
+    alloc = [(64, 4, 128, 2), (32, 8, 16, 8)]
+    bk, bv = _mixed_bases(alloc, seed=41 + g)
+    _attention_case(K, alloc, bk, bv, 2, g, 900, 873, [0, 256])
+
+
 def _budget_formats(budget_bits):
     """(rank, bits) the per-head search can pick under one budget of bits per vector:
     b = min(8, floor(budget / r)) for every rank with b >= 2."""
