@@ -308,9 +308,11 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
 
 // One 32-token value step (tile tokens 32*kk .. 32*kk+31): for each N-tile of 16
 // codes the B operand (lane n owns codes [n*NT, (n+1)*NT) of the 8 tokens of its
-// lane group, one aligned field of NT*B bits for power-of-two widths) and its two
-// MFMAs with A = p*step_V (hi, lo).
-template <int B, int NT>
+// lane group, one aligned field of NT*B bits for power-of-two widths) and its MFMAs
+// with A = p*step_V.  PACK (g <= 8): the hi and lo fp16 parts of A sit in rows
+// [0, GM) and [GM, 2 GM) of one operand, one MFMA per N-tile, and the two row
+// blocks of the accumulator are added at the end; otherwise two MFMAs (hi, lo).
+template <int B, int NT, bool PACK>
 __device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt, int wv, int kk,
                                                               u32x4 ahi, u32x4 alo, f32x4 (&acc2)[8]) {
   // tokens past the tile's last record carry p = 0 in A, so their (finite) codes add nothing
@@ -354,8 +356,10 @@ __device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt
       }
       acc2[n2] = mfma(ahi, bop[0], acc2[n2]);
       if (n2 + 1 < NT) acc2[n2 + 1] = mfma(ahi, bop[1], acc2[n2 + 1]);
-      acc2[n2] = mfma(alo, bop[0], acc2[n2]);
-      if (n2 + 1 < NT) acc2[n2 + 1] = mfma(alo, bop[1], acc2[n2 + 1]);
+      if constexpr (!PACK) {
+        acc2[n2] = mfma(alo, bop[0], acc2[n2]);
+        if (n2 + 1 < NT) acc2[n2 + 1] = mfma(alo, bop[1], acc2[n2 + 1]);
+      }
     }
   } else {
     constexpr uint32_t M = (1u << B) - 1u;
@@ -370,7 +374,7 @@ __device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt
         bop[p] = ca | (cb << 16);
       }
       acc2[nt] = mfma(ahi, bop, acc2[nt]);
-      acc2[nt] = mfma(alo, bop, acc2[nt]);
+      if constexpr (!PACK) acc2[nt] = mfma(alo, bop, acc2[nt]);
     }
   }
 }
@@ -396,7 +400,8 @@ __device__ inline int v_shift(int B, int nt) {
 __host__ __device__ constexpr int score_words(int gm) { return 64 * gm + 4; }
 __host__ __device__ inline int tile_lds_words(int kbuf_words, int vbuf_words, int nbuf, int gm) {
   const int w = nbuf * (kbuf_words + vbuf_words);
-  return w > gm * kMaxRank ? w : gm * kMaxRank;
+  const int part = (gm <= 8 ? 2 : 1) * gm * kMaxRank;  // the wave's value partial (hi and lo rows when packed)
+  return w > part ? w : part;
 }
 constexpr int kHeadStats = 3 * kMaxGroup;
 constexpr int kCommonWords = kWaves * 48 + 4 + kHeadStats;
@@ -773,7 +778,10 @@ __device__ __attribute__((always_inline)) inline void softmax_tile(const uint32_
       for (int hh = 0; hh < GM; ++hh) S[hh] = alpha[hh];
     }
     lds_fence();
-    const f32x4 f = 4 * G < GM ? *(const f32x4*)(S + 4 * G) : f32x4{1.f, 1.f, 1.f, 1.f};
+    // lane group G holds accumulator rows 4G..4G+3: heads 4G.. (hi), or with packed
+    // value operands (GM <= 8) rows GM..2GM-1 are the lo parts of heads 0..GM-1
+    constexpr int kRows = GM <= 8 ? 2 * GM : GM;
+    const f32x4 f = 4 * G < kRows ? *(const f32x4*)(S + ((4 * G) & (GM - 1))) : f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) st.acc2[nt] *= f;
     lds_fence();
@@ -792,14 +800,21 @@ __device__ __attribute__((always_inline)) inline void softmax_tile(const uint32_
   lds_fence();
 }
 
-// A operands of value step kk: P rows (hi, lo) for tokens 32kk + 8G .. +7; rows >= GM
-// read the zero slot.
+// A operands of value step kk for tokens 32kk + 8G .. +7.  GM <= 8: one operand
+// whose rows [0, GM) are the hi parts and rows [GM, 2 GM) the lo parts (P stores the
+// lo rows right after the hi rows); GM = 16: hi and lo operands.  Other rows read
+// the zero slot.
 template <int GM>
 __device__ __attribute__((always_inline)) inline void p_operands(const float* S, int kk, u32x4& ahi, u32x4& alo) {
   const int lane = threadIdx.x & 63, n = lane & 15, G = lane >> 4;
   const _Float16* P = (const _Float16*)S;
-  ahi = *(const u32x4*)(P + (n < GM ? n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
-  alo = *(const u32x4*)(P + (n < GM ? GM * 64 + n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
+  if constexpr (GM <= 8) {
+    ahi = *(const u32x4*)(P + (n < 2 * GM ? n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
+    alo = ahi;
+  } else {
+    ahi = *(const u32x4*)(P + (n < GM ? n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
+    alo = *(const u32x4*)(P + (n < GM ? GM * 64 + n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
+  }
 }
 
 // ----------------------------------------------------------------- kernel body
@@ -901,7 +916,10 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     }
   }
   lds_fence();
-  if (4 * G < GM) {
+  // accumulator row 4G + e: head (4G + e) mod GM, the lo part of the packed value
+  // operand for rows >= GM (GM <= 8); the sum p*min joins the hi row
+  constexpr int kRows = GM <= 8 ? 2 * GM : GM;
+  if (4 * G < kRows) {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       if (nt < NT) {
@@ -909,8 +927,8 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
         const int j = n * NT + nt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int hh = 4 * G + e;
-          if (hh < g) wl[hh * rv + j] = fmaf(st.acc2[nt][e], f, mlw[32 + hh]);
+          const int row = 4 * G + e, hh = row & (GM - 1);
+          if (hh < g) wl[row * rv + j] = fmaf(st.acc2[nt][e], f, row < GM ? mlw[32 + hh] : 0.0f);
         }
       }
     }
@@ -949,7 +967,8 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float wgt = exp2f(ml[w * 48 + hc] - M);
-      acc = fmaf(wgt, areas[w * WA + hc * rv + j], acc);
+      const float* aw = areas + w * WA + hc * rv + j;
+      acc = fmaf(wgt, GM <= 8 ? aw[0] + aw[GM * rv] : aw[0], acc);
       lacc = fmaf(wgt, ml[w * 48 + 16 + hc], lacc);
     }
     ot[o] = on ? acc : 0.0f;

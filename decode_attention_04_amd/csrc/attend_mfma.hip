@@ -33,10 +33,10 @@ namespace kvtc {
     break;
 #define KVTC_V_CASE(B)                                                              \
   case B:                                                                           \
-    if (NT == 1) v_phase<B, 1>(vt, wv, kk, ahi, alo, acc2);                         \
-    else if (NT == 2) v_phase<B, 2>(vt, wv, kk, ahi, alo, acc2);                    \
-    else if (NT == 4) v_phase<B, 4>(vt, wv, kk, ahi, alo, acc2);                    \
-    else v_phase<B, 8>(vt, wv, kk, ahi, alo, acc2);                                 \
+    if (NT == 1) v_phase<B, 1, (GM <= 8)>(vt, wv, kk, ahi, alo, acc2);                         \
+    else if (NT == 2) v_phase<B, 2, (GM <= 8)>(vt, wv, kk, ahi, alo, acc2);                    \
+    else if (NT == 4) v_phase<B, 4, (GM <= 8)>(vt, wv, kk, ahi, alo, acc2);                    \
+    else v_phase<B, 8, (GM <= 8)>(vt, wv, kk, ahi, alo, acc2);                                 \
     break;
 
 // ----------------------------------------------------------------- generic tile loop

@@ -110,7 +110,7 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
     for (int kk = 0; kk < 2; ++kk) {
       u32x4 ahi, alo;
       p_operands<GM>(c.S, kk, ahi, alo);
-      v_phase<BV, NT>(vt, WV, kk, ahi, alo, st.acc2);
+      v_phase<BV, NT, (GM <= 8)>(vt, WV, kk, ahi, alo, st.acc2);
     }
     lds_fence();
     if (nbuf == 1) {
