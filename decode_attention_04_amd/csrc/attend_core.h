@@ -19,6 +19,12 @@ typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 constexpr int kWaves = 4;       // waves per workgroup
 constexpr int kTileT = 64;      // tokens per wave iteration
 
+// With GM = 4 the score MFMA packs the hi and lo query parts into rows [0, 4) and
+// [4, 8) of one operand and leaves S[token][8] (hi sums, then lo sums).
+__host__ __device__ constexpr bool kpack(int gm) { return gm == 4; }
+__host__ __device__ constexpr int score_floats(int gm) { return 64 * (kpack(gm) ? 2 * gm : gm); }
+__host__ __device__ constexpr int score_words(int gm) { return score_floats(gm) + 4; }  // + the zero slot
+
 __device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
                                                 __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
@@ -276,8 +282,10 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_hi[ks], bop[tt], acc[tt]);
+      if constexpr (!kpack(GM)) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_lo[ks], bop[tt], acc[tt]);
+        for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_lo[ks], bop[tt], acc[tt]);
+      }
     }
   } else {
     constexpr uint32_t M = (1u << B) - 1u;
@@ -295,14 +303,18 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_hi[ks], bop[tt], acc[tt]);
+      if constexpr (!kpack(GM)) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_lo[ks], bop[tt], acc[tt]);
+        for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_lo[ks], bop[tt], acc[tt]);
+      }
     }
   }
-  // S[token][GM]: the lanes of head rows >= GM (all zero) store nothing
-  if (4 * G < GM) {
+  // S[token][GM] (GM = 4: S[token][2][4], the hi rows then the lo rows): the lanes
+  // of the all-zero rows store nothing
+  constexpr int kRows = kpack(GM) ? 2 * GM : GM;
+  if (4 * G < kRows) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) *(f32x4*)(S + (tt * 16 + n) * GM + 4 * G) = acc[tt];
+    for (int tt = 0; tt < 4; ++tt) *(f32x4*)(S + (tt * 16 + n) * kRows + 4 * G) = acc[tt];
   }
 }
 
@@ -391,13 +403,13 @@ __device__ inline int v_shift(int B, int nt) {
 
 // LDS of an attend workgroup, in 32-bit words:
 //   common: per wave m[16] l[16] c[16]; a flag word (padded); per head E, sum(q~), 2^(24-E)
-//   scores: per wave S[64][GM] (fp32), overwritten by the probabilities
+//   scores: per wave S[64][GM] (fp32; S[64][2][4] hi and lo sums for GM = 4),
+//           overwritten by the probabilities
 //           P[2][GM][64] (fp16, hi then lo) once read, and a 4-word zero slot read
 //           as the A rows >= GM; before the tile loop the whole region holds the
 //           query staging of the projection (q[g][128], q~[g][128])
 //   tiles:  per wave nbuf K and nbuf V record tiles; at the end the wave's value
 //           partial o~[g][r_V], then the split merge's o~[g][128]
-__host__ __device__ constexpr int score_words(int gm) { return 64 * gm + 4; }
 __host__ __device__ inline int tile_lds_words(int kbuf_words, int vbuf_words, int nbuf, int gm) {
   const int w = nbuf * (kbuf_words + vbuf_words);
   const int part = (gm <= 8 ? 2 : 1) * gm * kMaxRank;  // the wave's value partial (hi and lo rows when packed)
@@ -551,12 +563,16 @@ struct WaveCtx {
 };
 
 // Key operand (A of the score MFMA) for one (K-step, lane): row = head (lane % 16),
-// element of pair slot = q~_j * 2^(E_head - s), split into fp16 hi + lo.
-// B = 0: the width bk is known only at run time.
-template <int B>
+// element of pair slot = q~_j * 2^(E_head - s), split into fp16 hi + lo.  PACK
+// (GM = 4): one operand, rows [0, 4) the hi and rows [4, 8) the lo parts (returned
+// in `hi`).  B = 0: the width bk is known only at run time.
+template <int B, bool PACK>
 __device__ inline void aq_slot(const float* qt, const float* E_h, int g, int rk, int bk, int ks, int lane,
                                u32x4& hi, u32x4& lo) {
-  const int i = lane & 15, G = lane >> 4;
+  const int r16 = lane & 15, G = lane >> 4;
+  const int i = PACK ? (r16 & 3) : r16;           // the head of this row
+  const bool row_on = PACK ? r16 < 8 : true;
+  const bool lo_row = PACK && r16 >= 4;
   const int nks = rk >= 32 ? rk / 32 : 1;
   const int E = i < g ? (int)E_h[i] : 0;
 #pragma unroll
@@ -566,14 +582,15 @@ __device__ inline void aq_slot(const float* qt, const float* E_h, int g, int rk,
     if constexpr (B == 0) k_slot_rt(bk, G, nks, ks, p, rk, valid, jl, jh, sh);
     else k_slot<B>(G, nks, ks, p, rk, valid, jl, jh, sh);
     float xl = 0.0f, xh = 0.0f;
-    if (valid && i < g && ks < nks) {
+    if (valid && row_on && i < g && ks < nks) {
       xl = ldexpf(qt[i * kMaxRank + jl], E - sh);
       xh = ldexpf(qt[i * kMaxRank + jh], E - sh);
     }
     const _Float16 hl = (_Float16)xl, hh = (_Float16)xh;
     const _Float16 ll = (_Float16)(xl - (float)hl), lh = (_Float16)(xh - (float)hh);
-    hi[p] = h2u(hl) | (h2u(hh) << 16);
-    lo[p] = h2u(ll) | (h2u(lh) << 16);
+    const uint32_t hw = h2u(hl) | (h2u(hh) << 16), lw = h2u(ll) | (h2u(lh) << 16);
+    hi[p] = lo_row ? lw : hw;
+    lo[p] = lw;
   }
 }
 
@@ -676,7 +693,7 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (ks < nks) {
-      aq_slot<B>(qt, Eh, g, rk, hd.bk, ks, lane, aq_hi[ks], aq_lo[ks]);
+      aq_slot<B, kpack(GM)>(qt, Eh, g, rk, hd.bk, ks, lane, aq_hi[ks], aq_lo[ks]);
     } else {
       aq_hi[ks] = u32x4{0u, 0u, 0u, 0u};
       aq_lo[ks] = u32x4{0u, 0u, 0u, 0u};
@@ -748,7 +765,13 @@ __device__ __attribute__((always_inline)) inline void softmax_tile(const uint32_
   float s[GM], u[GM];
 #pragma unroll
   for (int q4 = 0; q4 < GM / 4; ++q4) {
-    const f32x4 d = *(const f32x4*)(S + lane * GM + 4 * q4);
+    f32x4 d;
+    if constexpr (kpack(GM)) {  // hi sums + lo sums
+      const f32x4 dh = *(const f32x4*)(S + lane * 2 * GM), dl = *(const f32x4*)(S + lane * 2 * GM + GM);
+      d = dh + dl;
+    } else {
+      d = *(const f32x4*)(S + lane * GM + 4 * q4);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int hh = 4 * q4 + e;
@@ -808,12 +831,13 @@ template <int GM>
 __device__ __attribute__((always_inline)) inline void p_operands(const float* S, int kk, u32x4& ahi, u32x4& alo) {
   const int lane = threadIdx.x & 63, n = lane & 15, G = lane >> 4;
   const _Float16* P = (const _Float16*)S;
+  constexpr int kZero = 2 * score_floats(GM);  // the zero slot, in halves
   if constexpr (GM <= 8) {
-    ahi = *(const u32x4*)(P + (n < 2 * GM ? n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
+    ahi = *(const u32x4*)(P + (n < 2 * GM ? n * 64 + 32 * kk + 8 * G : kZero));
     alo = ahi;
   } else {
-    ahi = *(const u32x4*)(P + (n < GM ? n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
-    alo = *(const u32x4*)(P + (n < GM ? GM * 64 + n * 64 + 32 * kk + 8 * G : 2 * GM * 64));
+    ahi = *(const u32x4*)(P + (n < GM ? n * 64 + 32 * kk + 8 * G : kZero));
+    alo = *(const u32x4*)(P + (n < GM ? GM * 64 + n * 64 + 32 * kk + 8 * G : kZero));
   }
 }
 

@@ -69,7 +69,7 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
   init_state(st);
   float* S = c.S;
   f32x4 (&acc2)[8] = st.acc2;
-  if (lane < 4) ((uint32_t*)S)[GM * 64 + lane] = 0u;  // zero slot
+  if (lane < 4) ((uint32_t*)S)[score_floats(GM) + lane] = 0u;  // zero slot
   int slot = 0;
   lds_fence();
   for (int t0 = t_begin; t0 < t_end; t0 += kTileT) {

@@ -86,7 +86,7 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
       if (t_begin + t * kTileT < t_end) issue_tile<WK, WV>(c, t_begin + t * kTileT, t_end, t);
   });
   init_state(st);
-  if (lane < 4) ((uint32_t*)c.S)[GM * 64 + lane] = 0u;  // zero slot
+  if (lane < 4) ((uint32_t*)c.S)[score_floats(GM) + lane] = 0u;  // zero slot
   int slot = 0;
   lds_fence();
   for (int t0 = t_begin; t0 < t_end; t0 += kTileT) {
