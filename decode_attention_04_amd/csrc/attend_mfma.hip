@@ -14,8 +14,10 @@
 // VALU op.  The matrix cores take subnormal fp16 inputs exactly, and the 2^(o-24)
 // factor is folded into the other operand (keys) or the partial (values).
 //
-// Precision: q~ and p*step are split into fp16 hi + lo parts (two MFMAs each), so
-// products carry ~22 significant bits and accumulate in fp32.
+// Precision: q~ and p*step are split into fp16 hi + lo parts, so products carry
+// ~22 significant bits and accumulate in fp32.  For small GQA groups the two parts
+// share one MFMA (hi in the first rows of the operand, lo in the next ones: values
+// for g <= 8, scores for g <= 4); otherwise each part takes its own MFMA.
 //
 // Pages: KV-COBRA project page, "Efficiency" (dequantization and inverse rotation
 // in one pass over packed codes); pith.science NOVA-KV verdict, forward
