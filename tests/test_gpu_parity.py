@@ -409,6 +409,31 @@ def test_fused_append_attend(K, alloc, g, B, cap, T, split, kvdt):
     assert err <= REL_TOL
 
 
+@pytest.mark.parametrize("alloc", [MIXED_ALLOC, [(64, 4, 128, 2), (32, 8, 64, 4)]], ids=["generic", "specialised"])
+def test_attention_repeatable_bit_for_bit(K, alloc):
+    """The fixed split boundaries, tile-to-wave assignment and summation orders make
+    the output a function of the inputs alone: repeated calls, and calls on a copy
+    of the cache at another address, give the same bits."""
+    say(f"attention: repeated calls are bit-identical {alloc}")
+    wl = W.LLAMA_T32K
+    bk, bv = _mixed_bases(alloc, seed=53)
+    B, g, T = 2, 4, 5000
+    hkv = len(alloc)
+    ck_h, cv_h = H.oracle_cache(wl, alloc, bk, bv, B, T, T,
+                                kv={(t, b, h): W.tokens(wl, t, b, h % wl.n_kv_heads, 0, T)
+                                    for t in "KV" for b in range(B) for h in range(hkv)})
+    q = W.random_vectors(59, (B, hkv * g, 128)).astype(np.float16)
+    lay = K.Layout(hkv, hkv * g, B, T, alloc)
+    ck, cv = H.u32_dev(ck_h), H.u32_dev(cv_h)
+    outs = [_attend(K, lay, q, T, bk, bv, ck, cv) for _ in range(3)]
+    ck2, cv2 = ck.clone(), cv.clone()
+    outs.append(_attend(K, lay, q, T, bk, bv, ck2, cv2))
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    ref = attention.attend_cache(q.astype(np.float64), bk, bv, ck_h, cv_h, alloc, B, T, T, H.SCALE)
+    assert H.rel_err_per_head(outs[0], ref) <= REL_TOL
+
+
 def test_attention_empty_context_is_zero(K):
     say("attention T=0")
     alloc = [(64, 4, 32, 8)]
