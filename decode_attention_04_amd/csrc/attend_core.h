@@ -872,13 +872,14 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
 
   WaveCtx c;
   // split x covers the 256-token quanta [q(x), q(x + 1)) of the nq in the context,
-  // q(x) = min(nq, x ne / ns) with ne = nq + 1: the splits differ by at most one
+  // q(x) = min(nq, x ne / ns) with ne = nq + 2: the splits differ by at most one
   // quantum, so the XCDs (which take the splits round-robin) stream equal shares,
   // and the last split (which holds the newest token, the one a fused append
-  // encodes) is one quantum lighter.  Both entry points use the same splits, so
-  // appending in the same launch leaves the result bit for bit unchanged.
+  // encodes first) is about two quanta lighter, roughly the time that encode
+  // takes.  Both entry points use the same splits, so appending in the same
+  // launch leaves the result bit for bit unchanged.
   const int nq = (int)((a.n_tokens + kSplitQuantum - 1) / kSplitQuantum);
-  const int ne = nq + 1;
+  const int ne = nq + 2;
   const int q0 = min(nq, (int)(((int64_t)blockIdx.x * ne) / a.n_splits));
   const int q1 = min(nq, (int)(((int64_t)blockIdx.x * ne + ne) / a.n_splits));
   const int s_begin = q0 * kSplitQuantum;
