@@ -280,7 +280,7 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the decode step is measured on one GPU; --gpus must be 1 (a sharded layout splits the KV heads across GPUs, each running this same kernel on its share)"}))
         raise SystemExit(2)
 
     import torch
