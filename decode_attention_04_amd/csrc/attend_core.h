@@ -19,8 +19,10 @@ typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
 constexpr int kWaves = 4;       // waves per workgroup
 constexpr int kTileT = 64;      // tokens per wave iteration
 
-// With GM = 4 the score MFMA packs the hi and lo query parts into rows [0, 4) and
-// [4, 8) of one operand and leaves S[token][8] (hi sums, then lo sums).
+// With GM = 4 the score MFMA packs the hi and lo query parts into rows [0, GM) and
+// [GM, 2 GM) of one operand and leaves S[token][2 GM] (hi sums, then lo sums).  The
+// code handles GM = 8 too, but the doubled score area then leaves room for only two
+// workgroups per CU on the mixed Qwen-shaped layout (137 µs against 88 µs).
 __host__ __device__ constexpr bool kpack(int gm) { return gm == 4; }
 __host__ __device__ constexpr int score_floats(int gm) { return 64 * (kpack(gm) ? 2 * gm : gm); }
 __host__ __device__ constexpr int score_words(int gm) { return score_floats(gm) + 4; }  // + the zero slot
@@ -312,7 +314,7 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
       }
     }
   }
-  // S[token][GM] (GM = 4: S[token][2][4], the hi rows then the lo rows): the lanes
+  // S[token][GM] (GM = 4: S[token][2][GM], the hi rows then the lo rows): the lanes
   // of the all-zero rows store nothing
   constexpr int kRows = kpack(GM) ? 2 * GM : GM;
   if (4 * G < kRows) {
@@ -406,7 +408,7 @@ __device__ inline int v_shift(int B, int nt) {
 
 // LDS of an attend workgroup, in 32-bit words:
 //   common: per wave m[16] l[16] c[16]; a flag word (padded); per head E, sum(q~), 2^(24-E)
-//   scores: per wave S[64][GM] (fp32; S[64][2][4] hi and lo sums for GM = 4),
+//   scores: per wave S[64][GM] (fp32; S[64][2][GM] hi and lo sums for GM = 4),
 //           overwritten by the probabilities
 //           P[2][GM][64] (fp16, hi then lo) once read, and a 4-word zero slot read
 //           as the A rows >= GM; before the tile loop the whole region holds the
@@ -566,16 +568,17 @@ struct WaveCtx {
 };
 
 // Key operand (A of the score MFMA) for one (K-step, lane): row = head (lane % 16),
-// element of pair slot = q~_j * 2^(E_head - s), split into fp16 hi + lo.  PACK
-// (GM = 4): one operand, rows [0, 4) the hi and rows [4, 8) the lo parts (returned
-// in `hi`).  B = 0: the width bk is known only at run time.
-template <int B, bool PACK>
+// element of pair slot = q~_j * 2^(E_head - s), split into fp16 hi + lo.  PACK =
+// GM (GM <= 8): one operand, rows [0, GM) the hi and rows [GM, 2 GM) the lo parts
+// (returned in `hi`); PACK = 0: separate hi and lo operands.  B = 0: the width bk
+// is known only at run time.
+template <int B, int PACK>
 __device__ inline void aq_slot(const float* qt, const float* E_h, int g, int rk, int bk, int ks, int lane,
                                u32x4& hi, u32x4& lo) {
   const int r16 = lane & 15, G = lane >> 4;
-  const int i = PACK ? (r16 & 3) : r16;           // the head of this row
-  const bool row_on = PACK ? r16 < 8 : true;
-  const bool lo_row = PACK && r16 >= 4;
+  const int i = PACK ? (r16 & (PACK - 1)) : r16;  // the head of this row
+  const bool row_on = PACK ? r16 < 2 * PACK : true;
+  const bool lo_row = PACK && r16 >= PACK;
   const int nks = rk >= 32 ? rk / 32 : 1;
   const int E = i < g ? (int)E_h[i] : 0;
 #pragma unroll
@@ -696,7 +699,7 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (ks < nks) {
-      aq_slot<B, kpack(GM)>(qt, Eh, g, rk, hd.bk, ks, lane, aq_hi[ks], aq_lo[ks]);
+      aq_slot<B, kpack(GM) ? GM : 0>(qt, Eh, g, rk, hd.bk, ks, lane, aq_hi[ks], aq_lo[ks]);
     } else {
       aq_hi[ks] = u32x4{0u, 0u, 0u, 0u};
       aq_lo[ks] = u32x4{0u, 0u, 0u, 0u};
@@ -770,7 +773,8 @@ __device__ __attribute__((always_inline)) inline void softmax_tile(const uint32_
   for (int q4 = 0; q4 < GM / 4; ++q4) {
     f32x4 d;
     if constexpr (kpack(GM)) {  // hi sums + lo sums
-      const f32x4 dh = *(const f32x4*)(S + lane * 2 * GM), dl = *(const f32x4*)(S + lane * 2 * GM + GM);
+      const f32x4 dh = *(const f32x4*)(S + lane * 2 * GM + 4 * q4);
+      const f32x4 dl = *(const f32x4*)(S + lane * 2 * GM + GM + 4 * q4);
       d = dh + dl;
     } else {
       d = *(const f32x4*)(S + lane * GM + 4 * q4);

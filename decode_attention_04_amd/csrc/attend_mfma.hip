@@ -167,12 +167,18 @@ AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group) {
   // tile buffers: 64 records plus the 16-byte copy granule and one word read past the last record
   p.kbuf_words = ((64 * wkm + 4 + 3) / 4) * 4;
   p.vbuf_words = ((64 * wvm + 4 + 3) / 4) * 4;
-  const size_t kLds = 160 * 1024;
+  // LDS per CU, and the hardware's allocation granule (a workgroup's LDS is rounded
+  // up to it; 1280 bytes bounds the gfx950 granule from above)
+  const size_t kLds = 160 * 1024, kGranule = 1280;
+  auto fits = [&](int wpc, int nb) {
+    const size_t per_wg = (attend_lds_bytes(p.kbuf_words, p.vbuf_words, nb, group) + kGranule - 1) / kGranule * kGranule;
+    return (size_t)wpc * per_wg <= kLds;
+  };
   const int max_wpc = p.spec_class >= 0 ? 3 : 2;
   p.nbuf = 0;
   for (int wpc = max_wpc; wpc >= 1 && p.nbuf == 0; --wpc) {
     for (int nb = 3; nb >= (wpc == 1 ? 1 : 2) && p.nbuf == 0; --nb) {
-      if ((size_t)wpc * attend_lds_bytes(p.kbuf_words, p.vbuf_words, nb, group) <= kLds) {
+      if (fits(wpc, nb)) {
         p.nbuf = nb;
         p.wg_per_cu = wpc;
       }
