@@ -479,13 +479,18 @@ def test_end_to_end_encode_append_attend(K):
 
 # ------------------------------------------------------------------ full size, sampled
 FULL_SIZE = {"llama-2bpd": lambda: W.llama_t128k(2.0), "llama-0.5bpd": lambda: W.llama_t128k(0.5),
-             "qwen-mixed": lambda: W.QWEN_T128K}
+             "llama-1bpd": lambda: W.llama_t128k(1.0), "llama-4bpd": lambda: W.llama_t128k(4.0),
+             "qwen-mixed": lambda: W.QWEN_T128K,
+             "llama-B16-T32K-r32b8": lambda: W.llama_prefill(32, 8),
+             "llama-B16-T32K-r64b4": lambda: W.llama_prefill(64, 4)}
 
 
 @pytest.mark.parametrize("name", list(FULL_SIZE))
 def test_full_size_128k_sampled_units(K, name):
-    """The 128K decode configurations at full size (LLaMA shape: 4 sequences x 8 KV heads,
-    Qwen shape: 8 sequences x 4 KV heads, 131073 tokens), encoded on the GPU and attended
+    """The decode configurations at full size (LLaMA shape at 128K: 4 sequences x 8 KV
+    heads at 0.5, 1, 2 and 4 bits per dimension; Qwen shape: 8 sequences x 4 KV heads;
+    both with 131073 tokens; LLaMA shape at 32K: 16 sequences x 8 KV heads, 32769
+    tokens, uniform r = 32 b = 8 or r = 64 b = 4), encoded on the GPU and attended
     with the default split, in the launch configuration the benchmark times.  Sampled
     (sequence, KV head) units are re-encoded by the oracle from the same inputs: their
     records must match (exact headers, codes off by one only at rounding ties) and their
