@@ -20,12 +20,28 @@ constexpr int kWaves = 4;       // waves per workgroup
 constexpr int kTileT = 64;      // tokens per wave iteration
 
 // With GM = 4 the score MFMA packs the hi and lo query parts into rows [0, GM) and
-// [GM, 2 GM) of one operand and leaves S[token][2 GM] (hi sums, then lo sums).  The
-// code handles GM = 8 too, but the doubled score area then leaves room for only two
-// workgroups per CU on the mixed Qwen-shaped layout (137 µs against 88 µs).
+// [GM, 2 GM) of one operand and leaves S[token][2 GM] (hi sums, then lo sums).  A
+// doubled score area at GM = 8 would leave room for only two workgroups per CU on
+// the mixed Qwen-shaped layout (137 µs against 88 µs), so GM = 8 puts the hi parts
+// in rows [0, 8) and the lo parts in rows [8, 16), which land in lanes 32..63 of the
+// result, and a lane swap across the two wave halves adds them to the hi sums
+// before the store.
 __host__ __device__ constexpr bool kpack(int gm) { return gm == 4; }
+__host__ __device__ constexpr bool k_packed(int gm) { return gm <= 8; }
+__host__ __device__ constexpr int k_lo_row(int gm) { return kpack(gm) ? gm : (k_packed(gm) ? 8 : 0); }
 __host__ __device__ constexpr int score_floats(int gm) { return 64 * (kpack(gm) ? 2 * gm : gm); }
 __host__ __device__ constexpr int score_words(int gm) { return score_floats(gm) + 4; }  // + the zero slot
+
+// One v_permlane32_swap folds two values: lane l < 32 returns x[l] + x[l + 32] and
+// lane l >= 32 returns y[l - 32] + y[l].  The empty asm hands the builtin opaque
+// scalars: fed straight from vector elements, this compiler lowers every such swap
+// on element 0 of the vector.
+__device__ inline float fold_halves(float x, float y) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = __builtin_bit_cast(uint32_t, y);
+  asm volatile("" : "+v"(a), "+v"(b));
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
 
 __device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
@@ -287,7 +303,7 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_hi[ks], bop[tt], acc[tt]);
-      if constexpr (!kpack(GM)) {
+      if constexpr (!k_packed(GM)) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_lo[ks], bop[tt], acc[tt]);
       }
@@ -308,11 +324,23 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_hi[ks], bop[tt], acc[tt]);
-      if constexpr (!kpack(GM)) {
+      if constexpr (!k_packed(GM)) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_lo[ks], bop[tt], acc[tt]);
       }
     }
+  }
+  if constexpr (k_packed(GM) && !kpack(GM)) {
+    // S[token][8]: tiles 2u and 2u + 1 folded together, the low wave half storing
+    // tile 2u and the high half tile 2u + 1
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = fold_halves(acc[2 * u][e], acc[2 * u + 1][e]);
+      *(f32x4*)(S + ((2 * u + (G >> 1)) * 16 + n) * GM + 4 * (G & 1)) = r;
+    }
+    return;
   }
   // S[token][GM] (GM = 4: S[token][2][GM], the hi rows then the lo rows): the lanes
   // of the all-zero rows store nothing
@@ -699,7 +727,7 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (ks < nks) {
-      aq_slot<B, kpack(GM) ? GM : 0>(qt, Eh, g, rk, hd.bk, ks, lane, aq_hi[ks], aq_lo[ks]);
+      aq_slot<B, k_lo_row(GM)>(qt, Eh, g, rk, hd.bk, ks, lane, aq_hi[ks], aq_lo[ks]);
     } else {
       aq_hi[ks] = u32x4{0u, 0u, 0u, 0u};
       aq_lo[ks] = u32x4{0u, 0u, 0u, 0u};
