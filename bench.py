@@ -46,6 +46,7 @@ def pick_workload(name: str) -> W.Workload:
     }
     for bpd in W.ALL_BUDGETS:
         table[f"llama-128k-{bpd:g}bpd"] = W.llama_t128k(bpd)
+        table[f"llama-128k-{bpd:g}bpd-c2"] = W.llama_t128k_c2(bpd)
     if name not in table:
         raise SystemExit(f"unknown workload {name}; choose from {sorted(table)}")
     return table[name]
@@ -54,6 +55,12 @@ def pick_workload(name: str) -> W.Workload:
 def calibrate(wl: W.Workload):
     from decode_attention_04_amd import calib
 
+    if wl.allocation[0] == "c2":
+        n = wl.n_kv_heads
+        return calib.calibrate_layer(
+            [W.covariance(wl, "K", h) for h in range(n)], [W.covariance(wl, "V", h) for h in range(n)],
+            lambda h, r: W.hadamard_signs(wl, "K", h, r), lambda h, r: W.hadamard_signs(wl, "V", h, r),
+            wl.allocation, [W.query_covariance(wl, h) for h in range(n)], head_dim=wl.head_dim)
     alloc, bk, bv = [], [], []
     for h in range(wl.n_kv_heads):
         fixed = wl.allocation[1][h] if wl.allocation[0] == "fixed" else None
@@ -422,7 +429,7 @@ def main():
     if not args.no_decode_rates:
         dec_rates = {}
         for dwl in (W.llama_t128k(0.5), W.llama_t128k(1.0), W.llama_t128k(4.0), W.QWEN_T128K,
-                    W.llama_prefill(32, 8), W.llama_prefill(64, 4)):
+                    W.llama_prefill(32, 8), W.llama_prefill(64, 4), W.llama_t128k_c2(2.0)):
             dec_rates[dwl.name] = decode_rate(K, dwl)
             log(f"decode {dwl.name}: {dec_rates[dwl.name]}")
 

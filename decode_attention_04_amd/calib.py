@@ -13,6 +13,12 @@ KV-COBRA project page, "How KV-COBRA Works":
   b = min(8, floor(B / r)) (ranks with B / r < 2 are infeasible) and keep the
   smallest D(r, b) = sum_{i>r} w_i + q(b) sum_{i<=r} w_i, q(b) = 2^(-2b)/12;
   ties go to fewer bits, then the smaller rank.
+* C2, across heads -- budget moves between heads until their marginal
+  distortions are equal.  That condition holds at the split of the total budget
+  with the smallest summed distortion, which `c2_allocate` finds exactly (a
+  multiple-choice knapsack over each head's (r, b) options, solved by dynamic
+  programming over the bits spent).  The K heads and the V heads form one pool
+  each, or one joint pool (the abstract's joint K+V allocation).
 
 Calibration runs once, offline, on the host (float64 numpy); the kernels take
 its output as plain arrays.  The random signs are an input (drawn by the caller).
@@ -76,6 +82,81 @@ def c1_search(weights: np.ndarray, budget_bits: int, ranks: Sequence[int]) -> Tu
     if best is None:
         raise ValueError("no (rank, bits) fits the budget")
     return best
+
+
+def c2_allocate(weights: Sequence[np.ndarray], total_bits: int,
+                ranks: Sequence[int] = (16, 32, 64, 128)) -> Tuple[List[Tuple[int, int]], float]:
+    """C2: one (rank, bits) per item with the smallest summed D(r, b) within ``total_bits`` code bits.
+
+    weights: one decreasing weight vector per item.  Returns the pairs and the total
+    distortion; among equal distortions the allocation spending fewer bits wins.
+    """
+    items = []
+    for w in weights:
+        w = np.asarray(w, np.float64)
+        csum = np.concatenate([[0.0], np.cumsum(w)])
+        rs, bs = np.meshgrid(np.array([r for r in ranks if r <= w.size], np.int64),
+                             np.arange(BITS_MIN, BITS_MAX + 1, dtype=np.int64), indexing="ij")
+        rs, bs = rs.reshape(-1), bs.reshape(-1)
+        if rs.size == 0:
+            raise ValueError("no rank fits the head dimension")
+        dist = (csum[-1] - csum[rs]) + csum[rs] * np.power(2.0, -2.0 * bs) / 12.0
+        items.append((rs, bs, rs * bs, dist))
+    unit = int(np.gcd.reduce(np.concatenate([it[2] for it in items])))
+    n = int(total_bits) // unit
+    best = np.full(n + 1, np.inf)      # best[u]: least total D of the items so far spending exactly u units
+    best[0] = 0.0
+    picks = []
+    for rs, bs, cost, dist in items:
+        cu = cost // unit
+        cand = np.full((cost.size, n + 1), np.inf)
+        for j in range(cost.size):
+            if cu[j] <= n:
+                cand[j, cu[j]:] = best[:n + 1 - cu[j]] + dist[j]
+        pick = np.argmin(cand, axis=0)
+        best = cand[pick, np.arange(n + 1)]
+        picks.append(pick)
+    if not np.isfinite(best).any():
+        raise ValueError("the total budget is below the smallest allocation")
+    u = int(np.argmin(best))             # first minimum: the fewest units among equal totals
+    total = float(best[u])
+    out = []
+    for (rs, bs, cost, dist), pick in zip(reversed(items), reversed(picks)):
+        j = int(pick[u])
+        out.append((int(rs[j]), int(bs[j])))
+        u -= int(cost[j]) // unit
+    return out[::-1], total
+
+
+def calibrate_layer(covs_k, covs_v, signs_k_for, signs_v_for, policy, query_covs=None,
+                    ranks: Sequence[int] = (16, 32, 64, 128), head_dim: int = 128):
+    """Allocation and bases of every KV head of a layer under C2.
+
+    policy: ("c2", bits_per_dim, "mse"|"kl", "split"|"joint"): a total of
+    bits_per_dim * head_dim code bits per vector on average, shared among the K heads
+    and among the V heads ("split") or among all of them ("joint").
+    signs_k_for / signs_v_for: callables (head, r) -> +-1 vector of length r.
+    Returns (allocations [(rk, bk, rv, bv), ...], bases_k, bases_v).
+    """
+    if policy[0] != "c2":
+        raise ValueError(f"calibrate_layer takes a c2 policy, not {policy[0]}")
+    n = len(covs_k)
+    kl = policy[2] == "kl"
+    dk = [sorted_directions(covs_k[h], query_covs[h] if kl else None) for h in range(n)]
+    dv = [sorted_directions(covs_v[h]) for h in range(n)]
+    per_vector = int(round(policy[1] * head_dim))
+    if policy[3] == "joint":
+        pairs, _ = c2_allocate([w for w, _ in dk] + [w for w, _ in dv], per_vector * 2 * n, ranks)
+        ak, av = pairs[:n], pairs[n:]
+    elif policy[3] == "split":
+        ak, _ = c2_allocate([w for w, _ in dk], per_vector * n, ranks)
+        av, _ = c2_allocate([w for w, _ in dv], per_vector * n, ranks)
+    else:
+        raise ValueError(f"unknown C2 pooling {policy[3]}")
+    alloc = [(ak[h][0], ak[h][1], av[h][0], av[h][1]) for h in range(n)]
+    bases_k = [fold(dk[h][1], ak[h][0], signs_k_for(h, ak[h][0])) for h in range(n)]
+    bases_v = [fold(dv[h][1], av[h][0], signs_v_for(h, av[h][0])) for h in range(n)]
+    return alloc, bases_k, bases_v
 
 
 def calibrate_head(cov_k, cov_v, signs_k_for, signs_v_for, policy, query_cov=None,

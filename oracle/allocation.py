@@ -14,6 +14,8 @@ ties go to the smaller D, then fewer bits r * b, then the smaller r.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 from .quantizer import q_noise
@@ -43,3 +45,60 @@ def c1(w, budget_bits: int, ranks=None):
     if best is None:
         raise ValueError("no feasible (rank, bits) within the budget")
     return best[1], best[2], best[0][0]
+
+
+def options(w, ranks):
+    """Every (r, b) a head can take -- r from ``ranks``, b in [2, 8] -- as (bits r*b, D(r, b), r, b)."""
+    out = []
+    for r in ranks:
+        if r > len(w):
+            continue
+        for b in range(B_MIN, B_MAX + 1):
+            out.append((r * b, distortion(w, r, b), r, b))
+    return out
+
+
+def c2(weights, total_bits: int, ranks=None):
+    """C2 across heads: one (r, b) per item minimising the summed distortion within a total budget.
+
+    Pages: KV-COBRA project page, "How KV-COBRA Works", C2 across heads (budget is
+    moved between heads, C1 serving as each head's oracle, until their marginal
+    distortions are equal: the water-filling condition), and the abstract (the same
+    allocator applied jointly to the K and V heads).
+
+    Reading: the allocation that condition characterises is the one with the smallest
+    total distortion sum_i D_i(r_i, b_i) subject to sum_i r_i b_i <= total_bits (C1's
+    budget counting: code bits only).  A head given budget B_i takes C1's pair, the
+    smallest-D option with r b <= B_i, so searching over the heads' (r, b) options
+    directly is the same as searching over budget splits.  The pages' damped update
+    is one way to reach it; here it is computed exactly by dynamic programming over
+    the bits spent, item by item.  ``weights``: one decreasing weight vector per item
+    (a KV head's key or value spectrum).  Returns ([(r, b), ...], total D).
+    Ties: the smaller total D, then fewer bits spent.
+    """
+    opts = [options(np.asarray(w, np.float64), ranks if ranks is not None else range(2, len(w) + 1, 2))
+            for w in weights]
+    if any(not o for o in opts):
+        raise ValueError("an item has no (rank, bits) option")
+    unit = 0
+    for o in opts:
+        for bits, _, _, _ in o:
+            unit = math.gcd(unit, bits)
+    n_units = int(total_bits) // unit
+    # table[u] = (total D, choices) over the items so far, spending exactly u units
+    table = {0: (0.0, [])}
+    for o in opts:
+        nxt = {}
+        for spent, (dist, picks) in table.items():
+            for bits, dj, r, b in o:
+                u = spent + bits // unit
+                if u > n_units:
+                    continue
+                cand = (dist + dj, picks + [(r, b)])
+                if u not in nxt or cand[0] < nxt[u][0]:
+                    nxt[u] = cand
+        table = nxt
+    if not table:
+        raise ValueError("the total budget is below the smallest allocation")
+    best_u = min(table, key=lambda u: (table[u][0], u))
+    return table[best_u][1], table[best_u][0]

@@ -16,15 +16,26 @@ SCALE = 1.0 / np.sqrt(128.0)
 def oracle_calibrate(wl: W.Workload):
     """(alloc, bases_k, bases_v) of a workload built with the oracle's calibration."""
     alloc, bk, bv = [], [], []
+    pol = wl.allocation
+    dirs = []
     for h in range(wl.n_kv_heads):
-        cov_k = W.covariance(wl, "K", h)
-        cov_v = W.covariance(wl, "V", h)
-        pol = wl.allocation
-        qcov = W.query_covariance(wl, h) if (pol[0] == "c1" and pol[2] == "kl") else None
-        wk, vk = transform.ordered_basis(cov_k, qcov)
-        wv, vv = transform.ordered_basis(cov_v)
+        qcov = W.query_covariance(wl, h) if (pol[0] in ("c1", "c2") and pol[2] == "kl") else None
+        dirs.append((transform.ordered_basis(W.covariance(wl, "K", h), qcov),
+                     transform.ordered_basis(W.covariance(wl, "V", h))))
+    if pol[0] == "c2":
+        n, per = wl.n_kv_heads, int(round(pol[1] * wl.head_dim))
+        if pol[3] == "joint":
+            pairs, _ = allocation.c2([d[0][0] for d in dirs] + [d[1][0] for d in dirs], per * 2 * n, W.C1_RANKS)
+            pk_, pv_ = pairs[:n], pairs[n:]
+        else:
+            pk_, _ = allocation.c2([d[0][0] for d in dirs], per * n, W.C1_RANKS)
+            pv_, _ = allocation.c2([d[1][0] for d in dirs], per * n, W.C1_RANKS)
+    for h in range(wl.n_kv_heads):
+        (wk, vk), (wv, vv) = dirs[h]
         if pol[0] == "fixed":
             a = pol[1][h]
+        elif pol[0] == "c2":
+            a = (pk_[h][0], pk_[h][1], pv_[h][0], pv_[h][1])
         else:
             budget = int(round(pol[1] * wl.head_dim))
             rk, b_k, _ = allocation.c1(wk, budget, W.C1_RANKS)

@@ -1,4 +1,4 @@
-"""Host-side calibration of the package (basis, Hadamard fold, C1) against the oracle (no GPU)."""
+"""Host-side calibration of the package (basis, Hadamard fold, C1, C2) against the oracle (no GPU)."""
 import numpy as np
 import pytest
 
@@ -45,3 +45,61 @@ def test_calibrate_head_c1_kl():
                                      wl.allocation, W.query_covariance(wl, 3))
     assert a[0] * a[1] <= 128 and a[2] * a[3] <= 128
     assert pk.shape == (128, a[0]) and pv.shape == (128, a[2]) and pk.dtype == np.float32
+
+
+def _spectra(wl):
+    wk = [transform.ordered_basis(W.covariance(wl, "K", h), W.query_covariance(wl, h))[0] for h in range(wl.n_kv_heads)]
+    wv = [transform.ordered_basis(W.covariance(wl, "V", h))[0] for h in range(wl.n_kv_heads)]
+    return wk, wv
+
+
+def _check_c2(ws, total, ranks):
+    got, dg = calib.c2_allocate(ws, total, ranks)
+    exp, de = allocation.c2(ws, total, ranks)
+    assert dg == pytest.approx(de, rel=1e-9)
+    assert sum(r * b for r, b in got) <= total
+    assert sum(allocation.distortion(w, r, b) for w, (r, b) in zip(ws, got)) == pytest.approx(dg, rel=1e-12)
+    return got, exp
+
+
+def test_c2_matches_oracle_on_random_heads():
+    for seed in range(6):
+        ws = [W.random_weights(40 * seed + i, 128) for i in range(5)]
+        for per_head in (32, 64, 128, 200, 256, 512):
+            got, exp = _check_c2(ws, per_head * len(ws), W.C1_RANKS)
+            assert got == exp
+        got, exp = _check_c2(ws[:3], 300, (2, 8, 30, 64))   # ranks that are not multiples of 16
+        assert got == exp
+    with pytest.raises(ValueError):
+        calib.c2_allocate([W.random_weights(1, 128)] * 3, 3 * 31, W.C1_RANKS)
+
+
+@pytest.mark.parametrize("bpd", W.ALL_BUDGETS)
+def test_c2_matches_oracle_on_the_llama_heads(bpd):
+    wk, wv = _spectra(W.llama_t128k(bpd))
+    per = int(bpd * 128)
+    for ws, total in ((wk, per * 8), (wv, per * 8), (wk + wv, per * 16)):
+        got, exp = _check_c2(ws, total, W.C1_RANKS)
+        assert got == exp
+
+
+@pytest.mark.parametrize("pool", ["split", "joint"])
+def test_calibrate_layer_c2(pool):
+    wl = W.llama_t128k(2.0)
+    n = wl.n_kv_heads
+    alloc, pk, pv = calib.calibrate_layer(
+        [W.covariance(wl, "K", h) for h in range(n)], [W.covariance(wl, "V", h) for h in range(n)],
+        lambda h, r: W.hadamard_signs(wl, "K", h, r), lambda h, r: W.hadamard_signs(wl, "V", h, r),
+        ("c2", 2.0, "kl", pool), [W.query_covariance(wl, h) for h in range(n)])
+    wk, wv = _spectra(wl)
+    if pool == "split":
+        ek, _ = allocation.c2(wk, 256 * n, W.C1_RANKS)
+        ev, _ = allocation.c2(wv, 256 * n, W.C1_RANKS)
+    else:
+        e, _ = allocation.c2(wk + wv, 256 * 2 * n, W.C1_RANKS)
+        ek, ev = e[:n], e[n:]
+    assert alloc == [(ek[h][0], ek[h][1], ev[h][0], ev[h][1]) for h in range(n)]
+    assert sum(a[0] * a[1] + a[2] * a[3] for a in alloc) <= 256 * 2 * n
+    for h in range(n):
+        assert pk[h].shape == (128, alloc[h][0]) and pv[h].shape == (128, alloc[h][2])
+        assert np.abs(pk[h].astype(np.float64).T @ pk[h] - np.eye(alloc[h][0])).max() < 1e-5

@@ -482,7 +482,8 @@ FULL_SIZE = {"llama-2bpd": lambda: W.llama_t128k(2.0), "llama-0.5bpd": lambda: W
              "llama-1bpd": lambda: W.llama_t128k(1.0), "llama-4bpd": lambda: W.llama_t128k(4.0),
              "qwen-mixed": lambda: W.QWEN_T128K,
              "llama-B16-T32K-r32b8": lambda: W.llama_prefill(32, 8),
-             "llama-B16-T32K-r64b4": lambda: W.llama_prefill(64, 4)}
+             "llama-B16-T32K-r64b4": lambda: W.llama_prefill(64, 4),
+             "llama-2bpd-c2": lambda: W.llama_t128k_c2(2.0)}
 
 
 @pytest.mark.parametrize("name", list(FULL_SIZE))

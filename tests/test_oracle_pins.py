@@ -337,6 +337,75 @@ def test_c1_on_generated_heads_uses_the_budget():
         assert r * b <= 256 and (r, b) in {(16, 8), (32, 8), (64, 4), (128, 2)}
 
 
+def _c2_brute_force(ws, total, ranks):
+    """Every combination of the items' (r, b) options: the least summed distortion within the bits."""
+    opts = [[(r, b) for r in ranks if r <= len(w) for b in range(2, 9)] for w in ws]
+    best = None
+    for combo in itertools.product(*opts):
+        bits = sum(r * b for r, b in combo)
+        if bits > total:
+            continue
+        dist = sum(sum(w[r:]) + sum(w[:r]) / (12 * 4 ** b) for w, (r, b) in zip(ws, combo))
+        if best is None or (dist, bits) < best[0]:
+            best = ((dist, bits), list(combo))
+    return best
+
+
+def test_c2_equals_brute_force():
+    ranks = (2, 4, 8)
+    for seed in range(3):
+        ws = [list(W.random_weights(seed * 7 + i, 8)) for i in range(3)]
+        for total in range(0, 3 * 64 + 1, 5):
+            bf = _c2_brute_force(ws, total, ranks)
+            if bf is None:
+                with pytest.raises(ValueError):
+                    allocation.c2(ws, total, ranks)
+                continue
+            picks, dist = allocation.c2(ws, total, ranks)
+            assert picks == bf[1], (seed, total)
+            assert dist == pytest.approx(bf[0][0], rel=1e-12)
+
+
+def test_c2_of_one_head_is_c1():
+    for seed in range(8):
+        w = W.random_weights(100 + seed, 128)
+        for budget in (32, 64, 100, 128, 256, 300, 512, 1024):
+            r, b, d1 = allocation.c1(w, budget, W.C1_RANKS)
+            picks, d2 = allocation.c2([w], budget, W.C1_RANKS)
+            assert picks == [(r, b)] and d2 == pytest.approx(d1, rel=1e-15)
+
+
+def test_c2_lagrangian_allocations_are_optimal():
+    """Everett's theorem: the choice minimising sum_i D_i + mu * bits_i, made item by
+    item, has the least total D among all allocations spending no more bits than it."""
+    for seed in range(4):
+        ws = [W.random_weights(200 + 10 * seed + i, 128) for i in range(6)]
+        for mu in (1e-5, 1e-4, 1e-3, 1e-2):
+            combo, bits, dist = [], 0, 0.0
+            for w in ws:
+                cands = [(allocation.distortion(w, r, b) + mu * r * b, r * b, r, b)
+                         for r in W.C1_RANKS for b in range(2, 9)]
+                _, cb, r, b = min(cands)
+                combo.append((r, b))
+                bits += cb
+                dist += allocation.distortion(w, r, b)
+            picks, d2 = allocation.c2(ws, bits, W.C1_RANKS)
+            assert d2 == pytest.approx(dist, rel=1e-12), (seed, mu)
+
+
+def test_c2_monotone_in_budget_and_no_worse_than_uniform_c1():
+    ws = [W.random_weights(300 + i, 128) for i in range(8)]
+    prev = None
+    for per_head in (32, 64, 96, 128, 192, 256, 384, 512):
+        picks, dist = allocation.c2(ws, per_head * len(ws), W.C1_RANKS)
+        assert sum(r * b for r, b in picks) <= per_head * len(ws)
+        uniform = sum(allocation.c1(w, per_head, W.C1_RANKS)[2] for w in ws)
+        assert dist <= uniform * (1 + 1e-12)
+        if prev is not None:
+            assert dist <= prev * (1 + 1e-12)
+        prev = dist
+
+
 # ---------------------------------------------------------------- layout
 def test_region_offsets_and_record_slices():
     rk, bk = [16, 128, 16], [4, 2, 6]

@@ -60,6 +60,7 @@ class Workload:
     # allocation policy, as plain data:
     #   ("fixed", ((rk, bk, rv, bv), ...))  one tuple per KV head
     #   ("c1", budget_bits_per_dim, key_weights)  key_weights in {"mse", "kl"}; values use "mse"
+    #   ("c2", budget_bits_per_dim, key_weights, "split"|"joint")  budget shared across heads
     allocation: tuple = ()
     decode_steps: int = 1        # decode steps the workload runs (append + attend each)
     encode_tokens: int = 0       # prefill chunk encoded per sequence (0: none)
@@ -91,6 +92,14 @@ def llama_t128k(bpd: float) -> Workload:
         head_dim=128, context=131072, dtype="f16", alpha=(1.0, 2.5), query_cov=True,
         allocation=("c1", float(bpd), "kl"),
         note="C1 with attention-KL key weights from generated query variances")
+
+
+def llama_t128k_c2(bpd: float) -> Workload:
+    """The 128K LLaMA-shaped layer (same generated data) with the budget shared across heads."""
+    return dataclasses.replace(
+        llama_t128k(bpd), name=f"llama8b-layer-B4-T128K-{bpd:g}bpd-c2",
+        allocation=("c2", float(bpd), "kl", "split"),
+        note="C2 across the K heads and across the V heads, attention-KL key weights")
 
 
 def llama_prefill(rank: int, bits: int) -> Workload:
