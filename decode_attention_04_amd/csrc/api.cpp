@@ -119,9 +119,20 @@ int64_t default_split_tokens(const Layout& L, int64_t T) {
 
 struct Workspace {
   int64_t cnt = 0, part = 0, floats = 0;  // offsets in 4-byte words
-  int32_t n_splits = 1;
-  int64_t split_tokens = 0;
+  int32_t n_splits = 1;                   // the largest per-head count
+  int64_t split_tokens = 0;               // given by the caller, else 0
+  int32_t ns[kMaxKvHeads] = {};           // splits per (sequence, head) unit of each head
+  int32_t wg_per_row = 0;                 // sum of ns over the heads
 };
+
+// Splits of a unit of T tokens when each split takes about st tokens (a multiple of
+// the quantum), as the kernel cuts them.
+static int64_t splits_for(int64_t T, int64_t st) { return T > 0 ? (T + st - 1) / st : 1; }
+static int64_t quantum_split(int64_t T, int64_t ns) {
+  int64_t st = (T + ns - 1) / ns;
+  st = ((st + kSplitQuantum - 1) / kSplitQuantum) * kSplitQuantum;
+  return st < kSplitQuantum ? kSplitQuantum : st;
+}
 
 kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Workspace& w) {
   if (T < 0) return fail(KV_ERR_INVALID, "n_tokens %lld < 0", (long long)T);
@@ -130,13 +141,64 @@ kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Works
   if (split_tokens < 0 || split_tokens % kSplitQuantum != 0)
     return fail(KV_ERR_INVALID, "split_tokens %lld is not a non-negative multiple of %d", (long long)split_tokens,
                 kSplitQuantum);
-  if (split_tokens == 0) split_tokens = default_split_tokens(L, T);
-  int64_t ns = T > 0 ? (T + split_tokens - 1) / split_tokens : 1;
-  if (ns > 65535) return fail(KV_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)ns);
+  // A given split size applies to every head.  By default the splits of a head
+  // are in proportion to the cost of one of its tokens, modelled as its record
+  // words (K + V) plus 6 words per query row of the group block (the per-token
+  // softmax and operand work, which does not depend on the widths; measured on the
+  // mixed layouts: bytes alone, or equal counts, left the widest or the narrowest
+  // heads finishing last).  The layout's total of workgroups (one per resident
+  // slot) is shared among the heads by that weight, then each head's count is
+  // rounded to whole 256-token quanta.  Equal widths give every head the same
+  // count.
+  w.split_tokens = split_tokens;
+  if (split_tokens != 0) {
+    const int64_t ns = splits_for(T, split_tokens);
+    for (int h = 0; h < L.n_kv; ++h) w.ns[h] = (int32_t)(ns > 65535 ? 65536 : ns);
+  } else {
+    const int64_t st_uniform = default_split_tokens(L, T);
+    const int64_t ns_uniform = splits_for(T, st_uniform);
+    // largest-remainder apportionment of ns_uniform * n_kv splits, at least one per
+    // head, so that the layout never launches more workgroups than with equal counts
+    const int64_t total = ns_uniform * L.n_kv;
+    const int64_t row_words = 6 * (L.group <= 4 ? 4 : L.group <= 8 ? 8 : 16);
+    int64_t wsum = 0, given = 0;
+    int64_t nh[kMaxKvHeads], rem[kMaxKvHeads];
+    for (int h = 0; h < L.n_kv; ++h) wsum += L.table.h[h].wk + L.table.h[h].wv + row_words;
+    for (int h = 0; h < L.n_kv; ++h) {
+      const int64_t wh = L.table.h[h].wk + L.table.h[h].wv + row_words;
+      nh[h] = total * wh / wsum;
+      rem[h] = total * wh % wsum;
+      if (nh[h] < 1) {
+        nh[h] = 1;
+        rem[h] = -1;
+      }
+      given += nh[h];
+    }
+    for (; given < total; ++given) {
+      int best = 0;
+      for (int h = 1; h < L.n_kv; ++h)
+        if (rem[h] > rem[best]) best = h;
+      ++nh[best];
+      rem[best] = -1;
+    }
+    for (int h = 0; h < L.n_kv; ++h) {
+      const int64_t ns = splits_for(T, quantum_split(T, nh[h]));
+      w.ns[h] = (int32_t)(ns > 65535 ? 65536 : ns);
+    }
+  }
+  int64_t per_row = 0, ns_max = 1;
+  for (int h = 0; h < L.n_kv; ++h) {
+    if (w.ns[h] > 65535) return fail(KV_ERR_UNSUPPORTED, "too many splits (%d)", (int)w.ns[h]);
+    per_row += w.ns[h];
+    ns_max = w.ns[h] > ns_max ? w.ns[h] : ns_max;
+  }
+  if (per_row > 65535) return fail(KV_ERR_UNSUPPORTED, "too many workgroups per sequence (%lld)", (long long)per_row);
+  if (per_row * L.batch > 0x7FFFFFFF) return fail(KV_ERR_UNSUPPORTED, "grid too large");
   const int64_t nbq = (int64_t)L.batch * L.n_q;
   const int64_t units = (int64_t)L.batch * L.n_kv;
-  w.split_tokens = split_tokens;
+  const int64_t ns = ns_max;
   w.n_splits = (int32_t)ns;
+  w.wg_per_row = (int32_t)per_row;
   w.cnt = 0;
   w.part = ((units + 3) / 4) * 4;
   w.floats = w.part + nbq * ns * kPartStride;
@@ -176,6 +238,12 @@ kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_
   a.capacity = L.capacity;
   a.split_tokens = w.split_tokens;
   a.n_splits = w.n_splits;
+  a.wg_per_row = w.wg_per_row;
+  for (int h = 0, wg = 0; h < L.n_kv; ++h) {
+    a.heads.h[h].ns = w.ns[h];
+    a.wg0[h] = (uint16_t)wg;
+    wg += w.ns[h];
+  }
   a.n_kv_heads = L.n_kv;
   a.n_q_heads = L.n_q;
   a.group = L.group;

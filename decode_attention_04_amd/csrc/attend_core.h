@@ -498,7 +498,7 @@ constexpr int kMergeChunk = 16;  // splits whose loads one merging thread has in
 // at zero for the next call.
 __device__ inline void merge_splits(const AttendArgs& a, int h, int b) {
   const int tid = threadIdx.x;
-  const int g = a.group, ns = a.n_splits;
+  const int g = a.group, ns = a.heads.h[h].ns;
   const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
   // item = (query head, four output dimensions); two threads per item when they fit
   const int items = g * (kHeadDim / 4);
@@ -508,7 +508,7 @@ __device__ inline void merge_splits(const AttendArgs& a, int h, int b) {
     const int item = t / tpi, sp = t % tpi;  // sp: which splits of the item this thread takes
     const int hh = item / (kHeadDim / 4), jq = item % (kHeadDim / 4);
     const bool act = item < items;
-    const float* part = a.part + (bq0 + (act ? hh : 0)) * ns * (int64_t)kPartStride + 4 * jq;
+    const float* part = a.part + (bq0 + (act ? hh : 0)) * a.n_splits * (int64_t)kPartStride + 4 * jq;
     float M = -__builtin_inff(), L = 0.0f, A0 = 0.0f, A1 = 0.0f, A2 = 0.0f, A3 = 0.0f;
     for (int s0 = kMergeChunk * sp; s0 < ns; s0 += kMergeChunk * tpi) {
       float o[kMergeChunk][4], mv[kMergeChunk], lv[kMergeChunk];
@@ -592,6 +592,7 @@ struct WaveCtx {
   int kbuf, vbuf, nbuf;
   int t_begin, t_end;       // this wave's tokens
   int g;
+  int h, b;                 // KV head and sequence of this workgroup
   int64_t unit;             // sequence * n_kv_heads + KV head
 };
 
@@ -647,7 +648,7 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
                                                                     Issue&& issue) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.y, b = blockIdx.z, g = c.g;
+  const int h = c.h, b = c.b, g = c.g;
   const HeadDesc& hd = a.heads.h[h];
   const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
   float* qs = c.stage;                    // [128][GM] raw queries, row-major over the head dimension
@@ -877,9 +878,11 @@ __device__ __attribute__((always_inline)) inline void p_operands(const float* S,
 }
 
 // ----------------------------------------------------------------- kernel body
-// Grid (n_splits, n_kv_heads, batch), 256 threads; GM bounds the GQA group (g <= GM).
-// Workgroup x covers tokens [x*split_tokens, (x+1)*split_tokens), a quarter per
-// wave; `run(ctx, state)` streams the wave's records and runs its online softmax.
+// One-dimensional grid of 256-thread workgroups; GM bounds the GQA group (g <= GM).
+// Sequence b takes workgroups [b W, (b + 1) W) with W = wg_per_row: head h the
+// heads.h[h].ns of them from wg0[h] on, one per split of its (b, h) unit, each
+// split a quarter per wave; `run(ctx, state)` streams the wave's records and runs
+// its online softmax.
 // The four wave states are merged in LDS into one partial (m, l, o~[r_V]) per
 // query head and split, and the last workgroup of the (sequence, KV head) to
 // finish merges the splits and writes the output.
@@ -887,10 +890,15 @@ template <int GM, class Run>
 __device__ __attribute__((always_inline)) inline void attend_body(const AttendArgs& a, Run&& run) {
   extern __shared__ float lds[];
   const int WA = tile_lds_words(a.kbuf_words, a.vbuf_words, a.nbuf, GM);
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int b = (int)blockIdx.x / a.wg_per_row;
+  const int wr = (int)blockIdx.x - b * a.wg_per_row;
+  int h = 0;
+  while (h + 1 < a.n_kv_heads && (int)a.wg0[h + 1] <= wr) ++h;
+  const int split = wr - (int)a.wg0[h];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the token loop scalar
   const HeadDesc& hd = a.heads.h[h];
+  const int ns = hd.ns;
   const int g = __builtin_amdgcn_readfirstlane(a.group);
   const int rv = __builtin_amdgcn_readfirstlane(hd.rv);
   const int bv = __builtin_amdgcn_readfirstlane(hd.bv);
@@ -912,8 +920,8 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   // launch leaves the result bit for bit unchanged.
   const int nq = (int)((a.n_tokens + kSplitQuantum - 1) / kSplitQuantum);
   const int ne = nq + 2;
-  const int q0 = min(nq, (int)(((int64_t)blockIdx.x * ne) / a.n_splits));
-  const int q1 = min(nq, (int)(((int64_t)blockIdx.x * ne + ne) / a.n_splits));
+  const int q0 = min(nq, (int)(((int64_t)split * ne) / ns));
+  const int q1 = min(nq, (int)(((int64_t)split * ne + ne) / ns));
   const int s_begin = q0 * kSplitQuantum;
   const int s_end = q1 * kSplitQuantum < (int)a.n_tokens ? q1 * kSplitQuantum : (int)a.n_tokens;
   const int wq = (q1 - q0) * (kSplitQuantum / kWaves);
@@ -934,6 +942,8 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   c.stage = scores;
   c.stats = ml + kWaves * 48 + 4;
   c.g = g;
+  c.h = h;
+  c.b = b;
   c.unit = (int64_t)b * a.n_kv_heads + h;
 
   // append fused with attention: the workgroup whose split holds the new token
@@ -1012,7 +1022,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   // head row holds o~[bhalf jh .. bhalf jh + jh) and zeros after it, rows >= g are
   // zero.  Waves without tokens carry m = -1e30, l = 0 and a zero partial, so
   // their weight is 0.  Then the back-projection P_V o~.
-  float* part0 = a.part + (bq0 * a.n_splits + blockIdx.x) * (int64_t)kPartStride;
+  float* part0 = a.part + (bq0 * a.n_splits + split) * (int64_t)kPartStride;
   float* ot = scores;  // [GM][2][64]
 #pragma unroll
   for (int i = 0; i < GM / 2; ++i) {
@@ -1070,7 +1080,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   uint32_t* flag = (uint32_t*)(ml + kWaves * 48);
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(a.cnt + c.unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = prev + 1u == (uint32_t)a.n_splits ? 1u : 0u;
+    *flag = prev + 1u == (uint32_t)ns ? 1u : 0u;
   }
   __syncthreads();
   if (*flag == 0u) return;

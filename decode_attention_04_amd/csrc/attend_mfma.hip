@@ -47,7 +47,7 @@ namespace kvtc {
 template <int GM, bool GEN>
 __device__ __attribute__((always_inline)) inline void generic_tiles(const AttendArgs& a, const WaveCtx& c,
                                                                     WaveState<GM>& st) {
-  const HeadDesc& hd = a.heads.h[blockIdx.y];
+  const HeadDesc& hd = a.heads.h[c.h];
   const int rk = __builtin_amdgcn_readfirstlane(hd.rk), rv = __builtin_amdgcn_readfirstlane(hd.rv);
   const int bk = __builtin_amdgcn_readfirstlane(hd.bk), bv = __builtin_amdgcn_readfirstlane(hd.bv);
   const int wk = hd.wk, wv = hd.wv;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
 template <int GM, bool GEN>
 static hipError_t launch_gm(const AttendArgs& a, hipStream_t s) {
   const size_t lds = attend_lds_bytes(a.kbuf_words, a.vbuf_words, a.nbuf, a.group);
-  const dim3 grid((unsigned)a.n_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch);
+  const dim3 grid((unsigned)(a.wg_per_row * a.batch));
   hipLaunchKernelGGL((attend_mfma_kernel<GM, GEN>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
@@ -207,7 +207,8 @@ hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
       case 1: return launch_attend_spec1(a, s);
       case 2: return launch_attend_spec2(a, s);
       case 3: return launch_attend_spec3(a, s);
-      default: return launch_attend_spec4(a, s);
+      case 4: return launch_attend_spec4(a, s);
+      default: return launch_attend_spec5(a, s);
     }
   }
   // the generic kernel; all power-of-two widths skip the general-width paths

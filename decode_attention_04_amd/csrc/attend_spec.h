@@ -8,9 +8,9 @@
 // copy wait counts are constants, and each tile is one straight instruction
 // sequence.  The formats compiled are the ones the per-head bit allocation picks
 // under one budget of bits per vector (every rank of the allocation search with
-// b = min(8, floor(budget / r)) >= 2), all (K, V) pairs of a class, and those of
-// the mixed full-rank / low-rank layout; a layout outside one class runs the
-// generic kernel.
+// b = min(8, floor(budget / r)) >= 2), all (K, V) pairs of a class, and the pairs
+// of frozen per-layer allocations (the mixed full-rank / low-rank layout, a
+// cross-head allocation); a layout outside one class runs the generic kernel.
 #pragma once
 
 #include "attend_core.h"
@@ -33,7 +33,12 @@ namespace kvtc {
 // (half of the heads each), every (K, V) pair of the two formats
 #define KVTC_SPEC_CLASS4(X) X(0, 128, 2, 128, 2) X(1, 128, 2, 16, 6) X(2, 16, 6, 128, 2) X(3, 16, 6, 16, 6)
 
-constexpr int kSpecClasses = 5;
+// A frozen cross-head (C2) allocation: the LLaMA-shaped layer of 8 KV heads at 2
+// bits per dimension on average, K heads and V heads each sharing their budget
+// (attention-KL key weights), as (r_K, b_K, r_V, b_V) per head
+#define KVTC_SPEC_CLASS5(X) X(0, 64, 4, 128, 3) X(1, 128, 4, 128, 3) X(2, 32, 5, 16, 5) X(3, 128, 3, 16, 5) X(4, 128, 4, 32, 4) X(5, 16, 4, 128, 3) X(6, 16, 5, 128, 4) X(7, 16, 5, 32, 3)
+
+constexpr int kSpecClasses = 6;
 
 // Index of (rk, bk, rv, bv) in class `cls`, or -1.
 __host__ inline int spec_index(int cls, int rk, int bk, int rv, int bv) {
@@ -46,6 +51,7 @@ __host__ inline int spec_index(int cls, int rk, int bk, int rv, int bv) {
     case 2: KVTC_SPEC_CLASS2(KVTC_SPEC_FIND) break;
     case 3: KVTC_SPEC_CLASS3(KVTC_SPEC_FIND) break;
     case 4: KVTC_SPEC_CLASS4(KVTC_SPEC_FIND) break;
+    case 5: KVTC_SPEC_CLASS5(KVTC_SPEC_FIND) break;
     default: break;
   }
 #undef KVTC_SPEC_FIND
@@ -128,14 +134,14 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
   template <int GM>                                                                                  \
   __global__ __launch_bounds__(256, 3) void attend_spec##CLS##_kernel(AttendArgs a) {               \
     attend_body<GM>(a, [&](const WaveCtx& c, WaveState<GM>& st) {                                    \
-      switch (__builtin_amdgcn_readfirstlane(a.heads.h[blockIdx.y].spec)) {                          \
+      switch (__builtin_amdgcn_readfirstlane(a.heads.h[c.h].spec)) {                                \
         KVTC_SPEC_CLASS##CLS(KVTC_SPEC_CASE) default : break;                                        \
       }                                                                                              \
     });                                                                                              \
   }                                                                                                  \
   hipError_t launch_attend_spec##CLS(const AttendArgs& a, hipStream_t s) {                          \
     const size_t lds = attend_lds_bytes(a.kbuf_words, a.vbuf_words, a.nbuf, a.group);                \
-    const dim3 grid((unsigned)a.n_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch);               \
+    const dim3 grid((unsigned)(a.wg_per_row * a.batch));                                          \
     if (a.group <= 4)                                                                                \
       hipLaunchKernelGGL(attend_spec##CLS##_kernel<4>, grid, dim3(256), lds, s, a);                 \
     else                                                                                             \

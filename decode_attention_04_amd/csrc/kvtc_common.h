@@ -31,7 +31,8 @@ struct HeadDesc {
   int32_t wk, wv;           // record words
   int32_t boff_k, boff_v;   // float offset of the head's basis
   int64_t base_k, base_v;   // word offset of the head's cache region
-  int32_t spec, pad_;       // index of the format in the specialised kernel's class (set at launch)
+  int32_t spec;             // index of the format in the specialised kernel's class (set at launch)
+  int32_t ns;               // splits of each of the head's (sequence, head) units (set at launch)
 };
 
 struct HeadTable {

@@ -33,11 +33,13 @@ struct AttendArgs {
   const uint32_t* cache_v;
   float* out;
   uint32_t* cnt; // [batch][n_kv_heads] split arrival counters: zero on entry, left zero
-  float* part;   // [batch][n_q_heads][n_splits][kPartStride]
+  float* part;   // [batch][n_q_heads][n_splits][kPartStride] (head h fills its first heads.h[h].ns)
   int64_t n_tokens;
   int64_t capacity;
   int64_t split_tokens;
-  int32_t n_splits;
+  int32_t n_splits;    // the largest per-head split count: the stride of `part`
+  int32_t wg_per_row;  // workgroups per sequence: the sum of the heads' split counts
+  uint16_t wg0[kMaxKvHeads];  // first workgroup of head h within a sequence's run
   int32_t n_kv_heads;
   int32_t n_q_heads;
   int32_t group;
@@ -72,11 +74,12 @@ struct AttendPlan {
 };
 AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
-// Decode attention specialised for the record formats of one budget class (group <= 8).
+// Decode attention specialised for the record formats of one class (group <= 8).
 hipError_t launch_attend_spec0(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec1(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec2(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec3(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec4(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_spec5(const AttendArgs& a, hipStream_t s);
 
 }  // namespace kvtc

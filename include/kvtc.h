@@ -143,9 +143,13 @@ kv_status kv_attend_decode(const kv_layout *layout, const void *q, kv_dtype dtyp
 
 /* As kv_attend_decode with an explicit maximum number of context tokens per
  * split-K work unit (a positive multiple of 256; 0 picks the default): the
- * context is divided into ceil(n_tokens / split_tokens) splits of whole
- * 256-token blocks whose sizes differ by at most one block.  The result is
- * the same up to float rounding for every split size.  The workspace must
+ * context of every KV head is divided into ceil(n_tokens / split_tokens)
+ * splits of whole 256-token blocks whose sizes differ by at most one block.
+ * The default gives each KV head a number of splits in proportion to the
+ * cost of its tokens (record words per token, key plus value, plus a fixed
+ * per-token share for the softmax), so that heads of different widths finish
+ * together.  The result is the same up to float rounding for every
+ * split size.  The workspace must
  * hold kv_workspace_bytes_split(layout, n_tokens, split_tokens) bytes. */
 kv_status kv_workspace_bytes_split(const kv_layout *layout, int64_t n_tokens, int64_t split_tokens,
                                    size_t *bytes);

@@ -103,3 +103,21 @@ def test_calibrate_layer_c2(pool):
     for h in range(n):
         assert pk[h].shape == (128, alloc[h][0]) and pv[h].shape == (128, alloc[h][2])
         assert np.abs(pk[h].astype(np.float64).T @ pk[h] - np.eye(alloc[h][0])).max() < 1e-5
+
+
+def test_frozen_c2_kernel_class_matches_the_calibration():
+    """The specialised kernel class compiled for the LLaMA-shaped C2 layout at 2 bits/dim
+    lists exactly the per-head formats its calibration picks (else the layout would
+    silently fall back to the generic kernel)."""
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(calib.__file__), "csrc", "attend_spec.h")).read()
+    body = re.search(r"#define KVTC_SPEC_CLASS5\(X\)(.*)", src).group(1)
+    listed = [tuple(int(v) for v in m[1:]) for m in re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+)\)", body)]
+    wl = W.llama_t128k_c2(2.0)
+    n = wl.n_kv_heads
+    alloc, _, _ = calib.calibrate_layer(
+        [W.covariance(wl, "K", h) for h in range(n)], [W.covariance(wl, "V", h) for h in range(n)],
+        lambda h, r: W.hadamard_signs(wl, "K", h, r), lambda h, r: W.hadamard_signs(wl, "V", h, r),
+        wl.allocation, [W.query_covariance(wl, h) for h in range(n)])
+    assert sorted(set(alloc)) == sorted(set(listed))

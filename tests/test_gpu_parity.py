@@ -322,6 +322,19 @@ def test_attention_every_format_pair_of_a_budget(K, budget, g):
     _attention_case(K, alloc, bk, bv, 1, g, 800, 777, [0, 256])
 
 
+# the frozen cross-head (C2) allocation of the LLaMA-shaped layer at 2 bits/dim (odd widths)
+C2_LLAMA_2BPD = [(64, 4, 128, 3), (128, 4, 128, 3), (32, 5, 16, 5), (128, 3, 16, 5),
+                 (128, 4, 32, 4), (16, 4, 128, 3), (16, 5, 128, 4), (16, 5, 32, 3)]
+
+
+@pytest.mark.parametrize("g", [4, 7])
+def test_attention_frozen_cross_head_allocation(K, g):
+    """The eight per-head format pairs of a frozen C2 allocation in one layout."""
+    say(f"attention C2 allocation, g={g}")
+    bk, bv = _mixed_bases(C2_LLAMA_2BPD, seed=61 + g)
+    _attention_case(K, C2_LLAMA_2BPD, bk, bv, 2, g, 1100, 1037, [0, 256])
+
+
 def test_attention_workspace_reuse_across_calls(K):
     """One zero-filled workspace serves consecutive calls with different split counts:
     every call leaves its split arrival counters at zero for the next."""
