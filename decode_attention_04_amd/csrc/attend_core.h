@@ -206,6 +206,33 @@ __device__ inline uint32_t lds_window(const uint32_t* rec, int bit) {
   return __builtin_amdgcn_alignbit(p[1], p[0], bit & 31);
 }
 
+// General widths: the NA words of a lane's code span that starts at stream bit
+// `sb` (p: the record's first code word), read once and shifted so that the span
+// begins at bit 0 of a[0].  ALIGNED: sb is a multiple of 32 for every lane.
+template <int NA, bool ALIGNED>
+__device__ __attribute__((always_inline)) inline void span_words(const uint32_t* p, int sb, uint32_t (&a)[NA]) {
+  const uint32_t* q = p + (sb >> 5);
+  if constexpr (ALIGNED) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) a[i] = q[i];
+  } else {
+    uint32_t w[NA + 1];
+#pragma unroll
+    for (int i = 0; i <= NA; ++i) w[i] = q[i];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) a[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], sb & 31);
+  }
+}
+
+// Code c (B bits at bit c B) of a span held in registers; c is a constant once the
+// callers' loops are unrolled, so the word index and shift fold away.
+template <int B, int NA>
+__device__ __attribute__((always_inline)) inline uint32_t span_code(const uint32_t (&a)[NA], int c) {
+  const int bit = c * B, wd = bit >> 5, off = bit & 31;
+  if (off + B <= 32) return (a[wd] >> off) & ((1u << B) - 1u);
+  return __builtin_amdgcn_alignbit(a[wd + 1 < NA ? wd + 1 : wd], a[wd], off) & ((1u << B) - 1u);
+}
+
 // ----------------------------------------------------------------- code fields
 // Power-of-two widths (2, 4, 8): a pair operand holds the codes at the same
 // offset of the two 16-bit halves of a word; offsets whose field would reach the
@@ -309,18 +336,20 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
       }
     }
   } else {
-    constexpr uint32_t M = (1u << B) - 1u;
+    // lane group G holds codes [8 NKS G, 8 NKS (G + 1)) of each token: read once
+    constexpr int SPAN = 8 * NKS * B;
+    constexpr int NA = (SPAN + 31) / 32;
+    uint32_t a[4][NA];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) span_words<NA, SPAN % 32 == 0>(rec0 + tt * 16 * wk + 1, G * SPAN, a[tt]);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       u32x4 bop[4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int pi = G * NKS * 4 + ks * 4 + p;
-          const uint32_t f = lds_window(rec0 + tt * 16 * wk, 2 * pi * B);
-          bop[tt][p] = (f & M) | (((f >> B) & M) << 16);
-        }
+        for (int p = 0; p < 4; ++p)
+          bop[tt][p] = span_code<B>(a[tt], 8 * ks + 2 * p) | (span_code<B>(a[tt], 8 * ks + 2 * p + 1) << 16);
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_hi[ks], bop[tt], acc[tt]);
@@ -407,17 +436,17 @@ __device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt
       }
     }
   } else {
-    constexpr uint32_t M = (1u << B) - 1u;
+    // lane column block n holds codes [n NT, (n + 1) NT) of each of its 8 tokens: read once
+    constexpr int FS = NT * B;
+    constexpr int NA = (FS + 31) / 32;
+    uint32_t a[8][NA];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) span_words<NA, FS % 32 == 0>(rec0 + e * wv, n * FS, a[e]);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int bit = (n * NT + nt) * B;
       u32x4 bop;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t ca = lds_window(rec0 - 1 + (2 * p) * wv, bit) & M;
-        const uint32_t cb = lds_window(rec0 - 1 + (2 * p + 1) * wv, bit) & M;
-        bop[p] = ca | (cb << 16);
-      }
+      for (int p = 0; p < 4; ++p) bop[p] = span_code<B>(a[2 * p], nt) | (span_code<B>(a[2 * p + 1], nt) << 16);
       acc2[nt] = mfma(ahi, bop, acc2[nt]);
       if constexpr (!PACK) acc2[nt] = mfma(alo, bop, acc2[nt]);
     }
