@@ -62,6 +62,30 @@ def test_workspace_grows_with_context_and_split_count():
     assert lib_mod.kv_workspace_bytes(lay, 1000, 256) >= lib_mod.kv_workspace_bytes(lay, 1000, 512)
 
 
+def _max_splits(lay, batch, n_q, n_kv, T, split=0):
+    """The largest per-head split count, read back from the workspace size
+    (split counters, then batch x n_q x splits partials of 132 floats)."""
+    words = lib_mod.kv_workspace_bytes(lay, T, split) // 4
+    return (words - (batch * n_kv + 3) // 4 * 4) // (batch * n_q * 132)
+
+
+def test_default_splits_follow_the_heads_token_cost():
+    """Equal widths keep one split count for every head (here 24: 768 resident
+    workgroups over 32 units); a head with much wider records than the others gets
+    the largest share of the workgroups; a given split size applies to every head."""
+    T = 131073
+    uni = lib_mod.Layout(8, 32, 4, T, [(64, 4, 64, 4)] * 8)
+    assert _max_splits(uni, 4, 32, 8, T) == 24
+    wide = lib_mod.Layout(8, 32, 4, T, [(128, 4, 128, 4)] * 8)
+    ns_equal = _max_splits(wide, 4, 32, 8, T)
+    # same tile buffers (the widest record sets them), one wide head among narrow ones:
+    # its weight W_K + W_V + 24 = 58 against 30 for each (16, 4) head
+    mixed = lib_mod.Layout(8, 32, 4, T, [(128, 4, 128, 4)] + [(16, 4, 16, 4)] * 7)
+    ns_wide = _max_splits(mixed, 4, 32, 8, T)
+    assert ns_wide >= 1.5 * ns_equal
+    assert _max_splits(mixed, 4, 32, 8, T, 4096) == (T + 4095) // 4096
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), lib_mod.KV_ERR_UNSUPPORTED),
     (dict(n_q_heads=13), lib_mod.KV_ERR_INVALID),
