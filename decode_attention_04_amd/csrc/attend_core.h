@@ -225,7 +225,9 @@ __device__ __attribute__((always_inline)) inline void span_words(const uint32_t*
 }
 
 // Code c (B bits at bit c B) of a span held in registers; c is a constant once the
-// callers' loops are unrolled, so the word index and shift fold away.
+// callers' loops are unrolled, so the word index and shift fold away.  No code of
+// a span reaches past its last word (the span is a whole number of codes), so the
+// clamp of the second index only keeps the untaken branch in range.
 template <int B, int NA>
 __device__ __attribute__((always_inline)) inline uint32_t span_code(const uint32_t (&a)[NA], int c) {
   const int bit = c * B, wd = bit >> 5, off = bit & 31;
