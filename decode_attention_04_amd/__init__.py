@@ -11,7 +11,7 @@ it has not been built (there is no fallback implementation).
 """
 _BINDING = (
     "KV_ERR_CAPACITY", "KV_ERR_DEVICE", "KV_ERR_INVALID", "KV_ERR_UNSUPPORTED", "KV_OK", "KvError",
-    "Layout", "kv_append", "kv_append_attend_decode", "kv_attend_decode", "kv_cache_bytes", "kv_encode", "kv_quantize_pack",
+    "Layout", "kv_append", "kv_append_attend_decode", "kv_attend_decode", "kv_attend_decode_ragged", "kv_cache_bytes", "kv_encode", "kv_quantize_pack",
     "kv_record_words", "kv_unpack", "kv_workspace_bytes",
 )
 

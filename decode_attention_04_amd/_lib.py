@@ -20,7 +20,7 @@ KV_F32, KV_F16 = 0, 1
 EXPORTED = (
     "kv_record_words", "kv_cache_bytes", "kv_workspace_bytes", "kv_workspace_bytes_split",
     "kv_encode", "kv_append", "kv_attend_decode", "kv_attend_decode_split",
-    "kv_append_attend_decode", "kv_quantize_pack", "kv_unpack", "kv_last_error",
+    "kv_append_attend_decode", "kv_attend_decode_ragged", "kv_quantize_pack", "kv_unpack", "kv_last_error",
 )
 
 
@@ -67,6 +67,7 @@ def _load():
         "kv_attend_decode": (i32, [L, P, i32, i64, P, P, P, P, f32, P, P, sz, P]),
         "kv_attend_decode_split": (i32, [L, P, i32, i64, i64, P, P, P, P, f32, P, P, sz, P]),
         "kv_append_attend_decode": (i32, [L, P, P, i32, P, i32, i64, i64, P, P, P, P, f32, P, P, sz, P]),
+        "kv_attend_decode_ragged": (i32, [L, P, i32, P, i64, P, P, P, P, f32, P, P, sz, P]),
         "kv_quantize_pack": (i32, [P, i64, i32, i32, P, P]),
         "kv_unpack": (i32, [P, i64, i32, i32, P, P, P]),
         "kv_last_error": (ctypes.c_char_p, []),
@@ -181,6 +182,18 @@ def kv_attend_decode(layout, q, n_tokens, basis_k, basis_v, cache_k, cache_v, so
                                        _ptr(basis_k), _ptr(basis_v), _ptr(cache_k), _ptr(cache_v),
                                        float(softmax_scale), _ptr(out), _ptr(workspace), nbytes,
                                        _stream(stream)))
+
+
+def kv_attend_decode_ragged(layout, q, lengths, max_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale,
+                            out, workspace, stream=None):
+    """Decode attention with per-sequence lengths: lengths is a device int32 tensor
+    [batch] (sequence b attends over its tokens 0 .. lengths[b]-1, clamped to
+    [0, max_tokens]); workspace as for kv_attend_decode at max_tokens."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.kv_attend_decode_ragged(layout.ref(), _ptr(q), _dtype_code(q), _ptr(lengths), max_tokens,
+                                        _ptr(basis_k), _ptr(basis_v), _ptr(cache_k), _ptr(cache_v),
+                                        float(softmax_scale), _ptr(out), _ptr(workspace), nbytes,
+                                        _stream(stream)))
 
 
 def kv_append_attend_decode(layout, k1, v1, q, n_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale,

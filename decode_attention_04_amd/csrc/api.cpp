@@ -208,7 +208,7 @@ kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Works
 kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_tokens, int64_t split_tokens,
                       const float* basis_k, const float* basis_v, const uint32_t* cache_k, const uint32_t* cache_v,
                       float softmax_scale, float* out, void* workspace, size_t workspace_bytes, void* stream,
-                      const void* k1, const void* v1, kv_dtype kv_dt) {
+                      const void* k1, const void* v1, kv_dtype kv_dt, const int32_t* lengths = nullptr) {
   if (dtype != KV_F32 && dtype != KV_F16) return fail(KV_ERR_INVALID, "dtype %d unknown", (int)dtype);
   Workspace w;
   kv_status s = plan_workspace(L, n_tokens, split_tokens, w);
@@ -235,6 +235,7 @@ kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_
   a.cnt = (uint32_t*)(ws + w.cnt);
   a.part = ws + w.part;
   a.n_tokens = n_tokens;
+  a.lengths = lengths;
   a.capacity = L.capacity;
   a.split_tokens = w.split_tokens;
   a.n_splits = w.n_splits;
@@ -348,6 +349,19 @@ kv_status kv_attend_decode_split(const kv_layout* layout, const void* q, kv_dtyp
   if (s) return s;
   return attend_impl(L, q, dtype, n_tokens, split_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale, out,
                      workspace, workspace_bytes, stream, nullptr, nullptr, KV_F32);
+}
+
+kv_status kv_attend_decode_ragged(const kv_layout* layout, const void* q, kv_dtype dtype, const int32_t* lengths,
+                                  int64_t max_tokens, const float* basis_k, const float* basis_v,
+                                  const uint32_t* cache_k, const uint32_t* cache_v, float softmax_scale,
+                                  float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  Layout L;
+  kv_status s = build_layout(layout, L);
+  if (s) return s;
+  if (!lengths) return fail(KV_ERR_INVALID, "NULL lengths");
+  if (!aligned(lengths, 4)) return fail(KV_ERR_INVALID, "misaligned lengths");
+  return attend_impl(L, q, dtype, max_tokens, 0, basis_k, basis_v, cache_k, cache_v, softmax_scale, out, workspace,
+                     workspace_bytes, stream, nullptr, nullptr, KV_F32, lengths);
 }
 
 kv_status kv_append_attend_decode(const kv_layout* layout, const void* k1, const void* v1, kv_dtype kv_dt,

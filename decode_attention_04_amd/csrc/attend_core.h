@@ -949,16 +949,22 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   // encodes first) is about two quanta lighter, roughly the time that encode
   // takes.  Both entry points use the same splits, so appending in the same
   // launch leaves the result bit for bit unchanged.
-  const int nq = (int)((a.n_tokens + kSplitQuantum - 1) / kSplitQuantum);
+  // this sequence's context: n_tokens, or its own length (clamped to [0, n_tokens])
+  int n_tok = (int)a.n_tokens;
+  if (a.lengths) {
+    const int lb = a.lengths[b];
+    n_tok = lb < 0 ? 0 : (lb < n_tok ? lb : n_tok);
+  }
+  const int nq = (n_tok + kSplitQuantum - 1) / kSplitQuantum;
   const int ne = nq + 2;
   const int q0 = min(nq, (int)(((int64_t)split * ne) / ns));
   const int q1 = min(nq, (int)(((int64_t)split * ne + ne) / ns));
   const int s_begin = q0 * kSplitQuantum;
-  const int s_end = q1 * kSplitQuantum < (int)a.n_tokens ? q1 * kSplitQuantum : (int)a.n_tokens;
+  const int s_end = q1 * kSplitQuantum < n_tok ? q1 * kSplitQuantum : n_tok;
   const int wq = (q1 - q0) * (kSplitQuantum / kWaves);
   c.t_begin = s_begin + wave * wq;
   c.t_end = c.t_begin + wq;
-  if (c.t_end > (int)a.n_tokens) c.t_end = (int)a.n_tokens;
+  if (c.t_end > n_tok) c.t_end = n_tok;
   const int wk = hd.wk, wv = hd.wv;
   const uint32_t* kreg = a.cache_k + hd.base_k + (int64_t)b * a.capacity * wk;
   const uint32_t* vreg = a.cache_v + hd.base_v + (int64_t)b * a.capacity * wv;

@@ -35,6 +35,7 @@ struct AttendArgs {
   uint32_t* cnt; // [batch][n_kv_heads] split arrival counters: zero on entry, left zero
   float* part;   // [batch][n_q_heads][n_splits][kPartStride] (head h fills its first heads.h[h].ns)
   int64_t n_tokens;
+  const int32_t* lengths;  // [batch] per-sequence context lengths (device), or null: n_tokens for all
   int64_t capacity;
   int64_t split_tokens;
   int32_t n_splits;    // the largest per-head split count: the stride of `part`

@@ -171,6 +171,21 @@ kv_status kv_attend_decode_split(const kv_layout *layout, const void *q, kv_dtyp
  * kv_attend_decode_split.
  * [KV-COBRA project page, "How KV-COBRA Works", Inference (each new key and
  *  value is compressed as it is produced) and "Efficiency"] */
+/* Decode attention over sequences of different lengths: sequence b attends over
+ * its tokens 0 .. lengths[b]-1.  lengths: DEVICE int32 [batch], read by the
+ * kernel on `stream` (so it can be written by earlier work on that stream), each
+ * value clamped to [0, max_tokens]; max_tokens <= capacity sets the split plan
+ * and the workspace size (kv_workspace_bytes(layout, max_tokens)).  A sequence
+ * of length 0 gets an all-zero output.  Otherwise as kv_attend_decode.  Errors
+ * as kv_attend_decode, plus KV_ERR_INVALID for a NULL or misaligned lengths.
+ * [KV-COBRA project page, "Efficiency" (the decode attention over the packed
+ *  cache), for a batch of requests at different positions] */
+kv_status kv_attend_decode_ragged(const kv_layout *layout, const void *q, kv_dtype dtype,
+                                  const int32_t *lengths, int64_t max_tokens, const float *basis_k,
+                                  const float *basis_v, const uint32_t *cache_k, const uint32_t *cache_v,
+                                  float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 kv_status kv_append_attend_decode(const kv_layout *layout, const void *k1, const void *v1,
                                   kv_dtype kv_dt, const void *q, kv_dtype q_dt,
                                   int64_t n_tokens, int64_t split_tokens, const float *basis_k,

@@ -161,6 +161,18 @@ def test_prefill_requires_16_byte_aligned_inputs():
     assert "16-byte" in L.kv_last_error().decode()
 
 
+def test_ragged_attend_validation_happens_before_launch():
+    lay = _layout()
+    need = lib_mod.kv_workspace_bytes(lay, 500)
+    # NULL or misaligned lengths, and a maximum past the capacity, fail before any launch
+    assert L.kv_attend_decode_ragged(lay.ref(), 16, 1, None, 500, 16, 16, 16, 16, 0.1, 16, 16, need, None) \
+        == lib_mod.KV_ERR_INVALID
+    assert L.kv_attend_decode_ragged(lay.ref(), 16, 1, 18, 500, 16, 16, 16, 16, 0.1, 16, 16, need, None) \
+        == lib_mod.KV_ERR_INVALID
+    assert L.kv_attend_decode_ragged(lay.ref(), 16, 1, 16, 5000, 16, 16, 16, 16, 0.1, 16, 16, need, None) \
+        == lib_mod.KV_ERR_CAPACITY
+
+
 def test_fused_append_attend_validation_happens_before_launch():
     lay = _layout()
     ref = lay.ref()

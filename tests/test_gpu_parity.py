@@ -335,6 +335,46 @@ def test_attention_frozen_cross_head_allocation(K, g):
     _attention_case(K, C2_LLAMA_2BPD, bk, bv, 2, g, 1100, 1037, [0, 256])
 
 
+def test_attention_ragged_lengths(K):
+    """kv_attend_decode_ragged: each sequence against the oracle over its own tokens
+    (a zero length gives zeros, a length past max_tokens is clamped to it), and with
+    every length equal to max_tokens the output equals kv_attend_decode's bit for bit."""
+    alloc = [(64, 4, 32, 8), (16, 6, 128, 3)]
+    bk, bv = _mixed_bases(alloc, seed=71)
+    batch, g, cap, T = 4, 4, 3200, 3100
+    lens = [1000, 0, 257, 5000]
+    say(f"attention ragged lengths {lens}, max {T}")
+    hkv, wl = len(alloc), W.LLAMA_T32K
+    ck_h, cv_h = H.oracle_cache(wl, alloc, bk, bv, batch, cap, T,
+                                kv={(t, b, h): W.tokens(wl, t, b, h, 0, T)
+                                    for t in "KV" for b in range(batch) for h in range(hkv)})
+    q = W.random_vectors(3, (batch, hkv * g, 128)).astype(np.float16)
+    lay = K.Layout(hkv, hkv * g, batch, cap, alloc)
+    ck, cv = H.u32_dev(ck_h), H.u32_dev(cv_h)
+    pk, pv = H.dev(codec.concat_bases(bk)), H.dev(codec.concat_bases(bv))
+    ws = torch.zeros(K.kv_workspace_bytes(lay, T) // 4, dtype=torch.float32, device="cuda")
+    out = torch.full((batch, hkv * g, 128), float("nan"), dtype=torch.float32, device="cuda")
+    qd = H.dev(q, torch.float16)
+    K.kv_attend_decode_ragged(lay, qd, torch.tensor(lens, dtype=torch.int32, device="cuda"), T, pk, pv, ck, cv,
+                              H.SCALE, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b, lb in enumerate(lens):
+        tb = min(max(lb, 0), T)
+        if tb == 0:
+            assert (got[b] == 0).all()
+            continue
+        ref = attention.attend_cache(q.astype(np.float64), bk, bv, ck_h, cv_h, alloc, batch, cap, tb, H.SCALE)
+        err = H.rel_err_per_head(got[b:b + 1], ref[b:b + 1])
+        say(f"  sequence {b} length {tb}: max rel err {err:.3e}")
+        assert err <= REL_TOL
+    K.kv_attend_decode_ragged(lay, qd, torch.full((batch,), T, dtype=torch.int32, device="cuda"), T, pk, pv, ck, cv,
+                              H.SCALE, out, ws)
+    torch.cuda.synchronize()
+    same = _attend(K, lay, q, T, bk, bv, ck, cv)
+    assert np.array_equal(out.cpu().numpy(), same)
+
+
 def test_attention_workspace_reuse_across_calls(K):
     """One zero-filled workspace serves consecutive calls with different split counts:
     every call leaves its split arrival counters at zero for the next."""
