@@ -129,13 +129,14 @@ def encode_rate(K, wl, block=2048, reps=5):
             "pct_of_hbm_peak": round(100 * (in_bytes + out_bytes) / ms / 1e6 / HBM_PEAK_GBS, 2)}
 
 
-def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9):
+def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragged=None):
     """Sustained kv_append_attend_decode throughput of another decode layout at its full size.
 
     The caches hold the workload's generated keys and values of the first `block` tokens
     repeated along the token axis (same per-token statistics), encoded on the GPU; enough
     layer caches rotate to exceed the Infinity Cache.  Not checked against anything here:
-    the GPU parity tests cover these layouts."""
+    the GPU parity tests cover these layouts.  ragged: fractions of the context, one per
+    sequence, timed as kv_attend_decode_ragged (attention only) over those lengths."""
     import torch
 
     alloc, bk, bv = calibrate(wl)
@@ -161,23 +162,36 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9):
     out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
     ws = torch.zeros(K.kv_workspace_bytes(lay, T) // 4, dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(d)
-    for i in range(warmup):
+    lens = [int(T * f) for f in ragged] if ragged else None
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=dev) if ragged else None
+
+    def step(i):
         ck_, cv_ = caches[i % n_rep]
-        K.kv_append_attend_decode(lay, k1, v1, q, T, pk, pv, ck_, cv_, scale, out, ws)
+        if ragged:
+            K.kv_attend_decode_ragged(lay, q, lens_d, T, pk, pv, ck_, cv_, scale, out, ws)
+        else:
+            K.kv_append_attend_decode(lay, k1, v1, q, T, pk, pv, ck_, cv_, scale, out, ws)
+
+    for i in range(warmup):
+        step(i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for i in range(steps):
-        ck_, cv_ = caches[i % n_rep]
-        K.kv_append_attend_decode(lay, k1, v1, q, T, pk, pv, ck_, cv_, scale, out, ws)
+        step(i)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     attend_bytes, append_bytes = step_bytes(wl, alloc, T)
+    if ragged:  # the records of each sequence's own tokens, no append
+        rec = attend_bytes - step_bytes(wl, alloc, 0)[0]
+        attend_bytes = attend_bytes - rec + rec * sum(lens) // (B * T)
+        append_bytes = 0
     gbs = (attend_bytes + append_bytes) / (us * 1e-6) / 1e9
     del caches, ck, cv
     torch.cuda.empty_cache()
-    return {"batch": B, "n_q_heads": hq, "n_kv_heads": H, "context_tokens": T,
+    extra = {"lengths": lens, "step": "kv_attend_decode_ragged (no append)"} if ragged else {}
+    return {**extra, "batch": B, "n_q_heads": hq, "n_kv_heads": H, "context_tokens": T,
             "allocation": [list(a) for a in alloc], "us_per_step": round(us, 2), "GB_per_s": round(gbs, 1),
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "layer_caches_rotated": n_rep}
 
@@ -432,6 +446,9 @@ def main():
                     W.llama_prefill(32, 8), W.llama_prefill(64, 4), W.llama_t128k_c2(2.0)):
             dec_rates[dwl.name] = decode_rate(K, dwl)
             log(f"decode {dwl.name}: {dec_rates[dwl.name]}")
+        name = W.llama_t128k(2.0).name + "-ragged"
+        dec_rates[name] = decode_rate(K, W.llama_t128k(2.0), ragged=(1.0, 0.75, 0.5, 0.25))
+        log(f"decode {name}: {dec_rates[name]}")
 
     cpu = None
     if not args.no_cpu_baseline:
