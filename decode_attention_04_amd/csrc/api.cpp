@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <chrono>
 #include <string>
 
 #include "kvtc.h"
@@ -36,6 +37,22 @@ kv_status device_status(hipError_t e, const char* what) {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Tag of one attention call, stored in every split partial it writes, so that a
+// merge never folds a partial some earlier call left in the workspace: a mix
+// (splitmix64 finaliser) of the monotonic clock in nanoseconds and the calling
+// thread's stack address, never zero.  Computed per call; nothing is kept.
+uint32_t call_nonce() {
+  int here = 0;
+  uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+               ((uint64_t)(uintptr_t)&here << 20);
+  z += 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  const uint32_t n = (uint32_t)z ^ (uint32_t)(z >> 32);
+  return n ? n : 1u;
+}
 
 struct Layout {
   int n_kv = 0, n_q = 0, batch = 0, group = 0;
@@ -234,6 +251,7 @@ kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_
   float* ws = (float*)workspace;
   a.cnt = (uint32_t*)(ws + w.cnt);
   a.part = ws + w.part;
+  a.nonce = call_nonce();
   a.n_tokens = n_tokens;
   a.lengths = lengths;
   a.capacity = L.capacity;

@@ -504,6 +504,9 @@ __host__ __device__ inline size_t attend_lds_bytes(int kbuf_words, int vbuf_word
 __device__ inline void part_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ inline void part_store_u32(float* p, uint32_t v) {
+  __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ inline float part_load(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -514,20 +517,29 @@ __device__ inline void part_load2(const float* p, float& x, float& y) {
   y = __builtin_bit_cast(float, (uint32_t)(v >> 32));
 }
 // Offsets in a split partial: o[0, 128) (the back-projected P_V o~ of the split,
-// unnormalised), then m and l.
-constexpr int kPartM = kMaxRank, kPartL = kMaxRank + 1;
+// unnormalised), then m, l and the tag of the call that wrote it (the call's
+// nonce, stored with m and l before the split's arrival is counted).
+constexpr int kPartM = kMaxRank, kPartL = kMaxRank + 1, kPartTag = kMaxRank + 2;
+static_assert(kPartTag + 1 < kPartStride, "split partial layout");
 
 constexpr int kMergeChunk = 16;  // splits whose loads one merging thread has in flight (one round up to 32 splits)
 
-// Run by the last workgroup of a (sequence, KV head) to finish its split partials.
-// Work item = (head, 4 consecutive output dimensions); with at most 128 items two
-// threads share one, each taking every other kMergeChunk splits.  A thread issues
-// the coherent loads of kMergeChunk splits (output quad, m and l) at once and folds
-// them into a running log-sum-exp; the two halves combine through a lane exchange
-// and o / l is the output (the back-projection already happened in each split's
-// workgroup, since it commutes with the weighted sum).  The arrival counter is left
-// at zero for the next call.
-__device__ inline void merge_splits(const AttendArgs& a, int h, int b) {
+// Run by a workgroup that arrived as the last of the ns splits of a (sequence, KV
+// head), or later (only with a counter that was not zero on entry), to finish the
+// split partials.  Work item = (head, 4 consecutive output dimensions); with at
+// most 128 items two threads share one, each taking every other kMergeChunk
+// splits.  A thread issues the coherent loads of kMergeChunk splits (output quad,
+// m, l and tag) at once and folds them into a running log-sum-exp; the two halves
+// combine through a lane exchange and o / l is the output (the back-projection
+// already happened in each split's workgroup, since it commutes with the weighted
+// sum).  An item for which any split's tag is not this call's nonce (a partial
+// not yet written by this call: possible only when the counter started above
+// zero, so that a workgroup counted as last before every split had arrived) gets
+// NaN instead.  Every merge of an item over the same partials writes the same
+// bits, so the output is correct or NaN, never a fold of a stale partial.  The
+// workgroup that arrived exactly ns-th (reset = true) leaves the counter at zero
+// for the next call.
+__device__ inline void merge_splits(const AttendArgs& a, int h, int b, bool reset) {
   const int tid = threadIdx.x;
   const int g = a.group, ns = a.heads.h[h].ns;
   const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
@@ -541,8 +553,10 @@ __device__ inline void merge_splits(const AttendArgs& a, int h, int b) {
     const bool act = item < items;
     const float* part = a.part + (bq0 + (act ? hh : 0)) * a.n_splits * (int64_t)kPartStride + 4 * jq;
     float M = -__builtin_inff(), L = 0.0f, A0 = 0.0f, A1 = 0.0f, A2 = 0.0f, A3 = 0.0f;
+    bool stale = false;
     for (int s0 = kMergeChunk * sp; s0 < ns; s0 += kMergeChunk * tpi) {
       float o[kMergeChunk][4], mv[kMergeChunk], lv[kMergeChunk];
+      uint32_t tg[kMergeChunk];
       // every load unconditional (splits past the last one re-read it and get weight
       // 0), so that all of them are in flight before the first wait
 #pragma unroll
@@ -552,10 +566,14 @@ __device__ inline void merge_splits(const AttendArgs& a, int h, int b) {
         part_load2(ps, o[k][0], o[k][1]);
         part_load2(ps + 2, o[k][2], o[k][3]);
         part_load2(ps - 4 * jq + kPartM, mv[k], lv[k]);
+        tg[k] = __hip_atomic_load((uint32_t*)const_cast<float*>(ps - 4 * jq + kPartTag), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
-      for (int k = 0; k < kMergeChunk; ++k)
+      for (int k = 0; k < kMergeChunk; ++k) {
+        stale |= tg[k] != a.nonce;
         if (s0 + k >= ns) mv[k] = -__builtin_inff();
+      }
       float mc = M;
 #pragma unroll
       for (int k = 0; k < kMergeChunk; ++k) mc = fmaxf(mc, mv[k]);
@@ -592,13 +610,16 @@ __device__ inline void merge_splits(const AttendArgs& a, int h, int b) {
       A1 += __shfl_xor(A1, 1);
       A2 += __shfl_xor(A2, 1);
       A3 += __shfl_xor(A3, 1);
+      stale |= __shfl_xor((int)stale, 1) != 0;
     }
     if (act && sp == 0) {
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      *(f32x4*)(a.out + (bq0 + hh) * kHeadDim + 4 * jq) = f32x4{A0 * inv, A1 * inv, A2 * inv, A3 * inv};
+      const float nan = __builtin_nanf("");
+      const f32x4 r = stale ? f32x4{nan, nan, nan, nan} : f32x4{A0 * inv, A1 * inv, A2 * inv, A3 * inv};
+      *(f32x4*)(a.out + (bq0 + hh) * kHeadDim + 4 * jq) = r;
     }
   }
-  if (tid == 0)
+  if (tid == 0 && reset)
     __hip_atomic_store(a.cnt + (int64_t)b * a.n_kv_heads + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1083,6 +1104,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
       float* ph = part0 + (int64_t)hh * a.n_splits * kPartStride;
       part_store(ph + kPartM, M);
       part_store(ph + kPartL, lacc);
+      part_store_u32(ph + kPartTag, a.nonce);
     }
   }
   __syncthreads();
@@ -1111,17 +1133,21 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     }
   }
 
-  // ---- arrival: the last workgroup of this (sequence, KV head) merges all splits
+  // ---- arrival: the last workgroup of this (sequence, KV head) merges all splits.
+  // A counter that was not zero on entry makes later arrivals (count past ns) merge
+  // too; the partial tags keep any of those merges from folding a stale partial.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores have completed
   __syncthreads();
   uint32_t* flag = (uint32_t*)(ml + kWaves * 48);
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(a.cnt + c.unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = prev + 1u == (uint32_t)ns ? 1u : 0u;
+    const uint64_t arrived = (uint64_t)prev + 1u;
+    *flag = arrived == (uint64_t)ns ? 1u : (arrived > (uint64_t)ns ? 2u : 0u);
   }
   __syncthreads();
-  if (*flag == 0u) return;
-  merge_splits(a, h, b);
+  const uint32_t fl = *flag;
+  if (fl == 0u) return;
+  merge_splits(a, h, b, fl == 1u);
 }
 
 }  // namespace kvtc

@@ -18,7 +18,7 @@ constexpr int kMinBits = 2;
 constexpr int kMaxBits = 8;
 constexpr int kMaxWords = 1 + (kMaxRank * kMaxBits + 31) / 32;  // 33
 constexpr int kSplitQuantum = 256;  // split-K sizes are multiples of this
-constexpr int kPartStride = 132;    // floats per split partial: m, l, o~[128], pad
+constexpr int kPartStride = 132;    // floats per split partial: o[128], m, l, tag, pad
 
 __host__ __device__ inline int record_words(int r, int b) { return 1 + (r * b + 31) / 32; }
 
@@ -94,11 +94,13 @@ __device__ inline QuantHeader quant_header(double cmin, double cmax, int b) {
 }
 
 // code = clamp(rint((c - mu) / sigma), 0, 2^b - 1), all zero when sigma == 0.
+// An undefined argument (NaN: only for inputs beyond the supported range, whose
+// fp16 min or step overflowed) gives code 0 rather than a NaN-to-integer cast.
 __device__ inline uint32_t quant_code(double c, double mu, double sigma, int b) {
   if (!(sigma > 0.0)) return 0u;
   double u = __builtin_rint((c - mu) / sigma);
   double top = (double)((1 << b) - 1);
-  u = u < 0.0 ? 0.0 : (u > top ? top : u);
+  u = !(u > 0.0) ? 0.0 : (u > top ? top : u);
   return (uint32_t)u;
 }
 

@@ -34,6 +34,7 @@ struct AttendArgs {
   float* out;
   uint32_t* cnt; // [batch][n_kv_heads] split arrival counters: zero on entry, left zero
   float* part;   // [batch][n_q_heads][n_splits][kPartStride] (head h fills its first heads.h[h].ns)
+  uint32_t nonce;  // non-zero tag of this call, stored in every split partial it writes
   int64_t n_tokens;
   const int32_t* lengths;  // [batch] per-sequence context lengths (device), or null: n_tokens for all
   int64_t capacity;

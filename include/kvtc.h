@@ -97,8 +97,11 @@ kv_status kv_cache_bytes(const kv_layout *layout, int32_t which, size_t *bytes);
 kv_status kv_workspace_bytes(const kv_layout *layout, int64_t n_tokens, size_t *bytes);
 
 /* Prefill encode.  k, v: [batch][n_kv_heads][n_tokens][head_dim] of `dtype`
- * (KV_F32 or KV_F16), contiguous, 16-byte aligned when n_tokens > 1; float32
- * inputs must lie inside the fp16 range (|x| < 65504).  Writes records
+ * (KV_F32 or KV_F16), contiguous, 16-byte aligned when n_tokens > 1; every
+ * token must have ||x||_2 <= 65504 (its coordinates, bounded by the norm since
+ * the basis columns are orthonormal, then keep the fp16 min and step finite;
+ * outside that range the records are unspecified but the call stays defined).
+ * Writes records
  * pos0 .. pos0+n_tokens-1 of every (sequence, head) into cache_k / cache_v
  * (other records untouched).  basis_k / basis_v: concatenated float32 bases
  * (layout above).  The projection runs on the matrix cores; every rounding
@@ -127,11 +130,18 @@ kv_status kv_append(const kv_layout *layout, const void *k1, const void *v1, kv_
  *   softmax_scale: multiplies q . k (1/sqrt(head_dim) for standard attention)
  *   workspace: at least kv_workspace_bytes(layout, n_tokens) bytes, 16-byte
  *              aligned, caller-owned.  Its first 4 * batch * n_kv_heads bytes
- *              are split arrival counters: they must be zero before the first
- *              call (zero-fill a new workspace, and again after using it for
- *              anything else) and every completed call leaves them zero; the
- *              rest is scratch whose contents on entry are ignored.  Calls that
- *              share a workspace must not overlap in time.
+ *              are split arrival counters, one per (sequence, KV head): zero-fill
+ *              a new workspace (and again after using it for anything else);
+ *              every completed call leaves them zero.  The rest is scratch whose
+ *              contents on entry are ignored.  A counter that is not zero on
+ *              entry (a workspace that was not zero-filled, or one left by an
+ *              aborted launch) never makes the output wrong: every split
+ *              partial carries a tag of the call that wrote it, and a merge
+ *              that would fold a partial this call has not written writes NaN
+ *              instead, so that unit's output elements are each either NaN or
+ *              the correct value.  A counter at or above the unit's split count
+ *              is not reset by the call.  Calls that share a workspace must not
+ *              overlap in time.
  * n_tokens == 0 writes zeros to `out`.  Errors: KV_ERR_CAPACITY if
  * n_tokens > capacity; KV_ERR_INVALID if the workspace is too small.
  * [KV-COBRA project page, "Efficiency"; pith.science NOVA-KV verdict,
@@ -141,16 +151,21 @@ kv_status kv_attend_decode(const kv_layout *layout, const void *q, kv_dtype dtyp
                            const uint32_t *cache_v, float softmax_scale, float *out, void *workspace,
                            size_t workspace_bytes, void *stream);
 
-/* As kv_attend_decode with an explicit maximum number of context tokens per
- * split-K work unit (a positive multiple of 256; 0 picks the default): the
- * context of every KV head is divided into ceil(n_tokens / split_tokens)
- * splits of whole 256-token blocks whose sizes differ by at most one block.
- * The default gives each KV head a number of splits in proportion to the
- * cost of its tokens (record words per token, key plus value, plus a fixed
- * per-token share for the softmax), so that heads of different widths finish
- * together.  The result is the same up to float rounding for every
- * split size.  The workspace must
- * hold kv_workspace_bytes_split(layout, n_tokens, split_tokens) bytes. */
+/* As kv_attend_decode with an explicit split-K size (a positive multiple of
+ * 256; 0 picks the default).  The context of every (sequence, KV head) is cut
+ * into ns = ceil(n_tokens / split_tokens) splits of whole 256-token blocks:
+ * with nq = ceil(n_tokens / 256) blocks, split x takes blocks [q(x), q(x+1))
+ * where q(x) = min(nq, floor(x * (nq + 2) / ns)).  Consecutive splits differ
+ * by at most one block, and the last splits are about two blocks lighter (the
+ * newest token's split also encodes it in kv_append_attend_decode); with few
+ * blocks per split a split may be larger than split_tokens and the last ones
+ * may be empty (n_tokens = 512, split_tokens = 256: 512 and 0 tokens).  The
+ * default gives each KV head a number of splits in proportion to the cost of
+ * its tokens (record words per token, key plus value, plus a fixed per-token
+ * share for the softmax), so that heads of different widths finish together.
+ * The result is the same up to float rounding for every split size.  The
+ * workspace must hold kv_workspace_bytes_split(layout, n_tokens, split_tokens)
+ * bytes. */
 kv_status kv_workspace_bytes_split(const kv_layout *layout, int64_t n_tokens, int64_t split_tokens,
                                    size_t *bytes);
 kv_status kv_attend_decode_split(const kv_layout *layout, const void *q, kv_dtype dtype,
@@ -159,18 +174,6 @@ kv_status kv_attend_decode_split(const kv_layout *layout, const void *q, kv_dtyp
                                  const uint32_t *cache_v, float softmax_scale, float *out,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
-/* One decode step in one launch: append the new token of every (sequence, head)
- * at position n_tokens - 1, then attend over records 0 .. n_tokens-1, the new
- * one included.  k1, v1: [batch][n_kv_heads][head_dim] of `kv_dt` (KV_F32 or
- * KV_F16); the other arguments, the workspace contract and the result are those
- * of kv_attend_decode_split.  The records written are bit-identical to those of
- * kv_append(pos = n_tokens - 1) and `out` equals that of kv_append followed by
- * kv_attend_decode_split with the same split size: the workgroup whose split
- * holds the new position encodes it before it reads that split.
- * Errors: KV_ERR_INVALID if n_tokens < 1 or k1 / v1 is NULL; otherwise as
- * kv_attend_decode_split.
- * [KV-COBRA project page, "How KV-COBRA Works", Inference (each new key and
- *  value is compressed as it is produced) and "Efficiency"] */
 /* Decode attention over sequences of different lengths: sequence b attends over
  * its tokens 0 .. lengths[b]-1.  lengths: DEVICE int32 [batch], read by the
  * kernel on `stream` (so it can be written by earlier work on that stream), each
@@ -186,6 +189,18 @@ kv_status kv_attend_decode_ragged(const kv_layout *layout, const void *q, kv_dty
                                   float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
+/* One decode step in one launch: append the new token of every (sequence, head)
+ * at position n_tokens - 1, then attend over records 0 .. n_tokens-1, the new
+ * one included.  k1, v1: [batch][n_kv_heads][head_dim] of `kv_dt` (KV_F32 or
+ * KV_F16); the other arguments, the workspace contract and the result are those
+ * of kv_attend_decode_split.  The records written are bit-identical to those of
+ * kv_append(pos = n_tokens - 1) and `out` equals that of kv_append followed by
+ * kv_attend_decode_split with the same split size: the workgroup whose split
+ * holds the new position encodes it before it reads that split.
+ * Errors: KV_ERR_INVALID if n_tokens < 1 or k1 / v1 is NULL; otherwise as
+ * kv_attend_decode_split.
+ * [KV-COBRA project page, "How KV-COBRA Works", Inference (each new key and
+ *  value is compressed as it is produced) and "Efficiency"] */
 kv_status kv_append_attend_decode(const kv_layout *layout, const void *k1, const void *v1,
                                   kv_dtype kv_dt, const void *q, kv_dtype q_dt,
                                   int64_t n_tokens, int64_t split_tokens, const float *basis_k,

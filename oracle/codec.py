@@ -41,11 +41,6 @@ def region_offsets(ranks, bits, batch: int, capacity: int) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
 
 
-def basis_offsets(ranks, d: int) -> np.ndarray:
-    """Float offset of each head's d x r basis in the concatenated basis array, plus the total."""
-    return np.concatenate([[0], np.cumsum([d * r for r in ranks])]).astype(np.int64)
-
-
 def record_slice(ranks, bits, batch, capacity, h, b, t0, t1):
     """(start, stop, W) word range of records t0..t1-1 of head h, sequence b."""
     off = region_offsets(ranks, bits, batch, capacity)

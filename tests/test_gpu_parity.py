@@ -18,7 +18,6 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 REL_TOL = 2e-3        # attention output, max relative error per (sequence, query head)
-TIE_FRACTION = 1e-5   # codes allowed to differ (by one) at rounding ties
 
 
 @pytest.fixture(scope="module")
@@ -101,19 +100,6 @@ def _mixed_bases(alloc, seed=0):
     return bk, bv
 
 
-def _compare_records(got, ref, r, b, what):
-    """Headers exact; codes equal except at rounding ties (<= TIE_FRACTION, off by one)."""
-    g_mu, g_sg, g_c = packing.unpack(got, r, b)
-    r_mu, r_sg, r_c = packing.unpack(ref, r, b)
-    hdr_bad = int(((g_mu != r_mu) | (g_sg != r_sg)).sum())
-    diff = np.abs(g_c - r_c)
-    assert hdr_bad == 0, f"{what}: {hdr_bad} headers differ"
-    assert diff.max(initial=0) <= 1, f"{what}: code off by {diff.max()}"
-    frac = (diff > 0).mean() if diff.size else 0.0
-    assert frac <= TIE_FRACTION, f"{what}: {frac:.2e} of codes differ"
-    return frac
-
-
 def _encode_case(K, wl_tokens, alloc, bases_k, bases_v, batch, cap, pos0, n, dtype):
     hkv = len(alloc)
     lay = K.Layout(hkv, hkv, batch, cap, alloc)
@@ -134,7 +120,8 @@ def _encode_case(K, wl_tokens, alloc, bases_k, bases_v, batch, cap, pos0, n, dty
             for b in range(batch):
                 s0, s1, w = codec.record_slice(ranks, bits, batch, cap, h, b, pos0, pos0 + n)
                 ref = codec.encode_tokens(x[b, h].astype(np.float64), bases[h], bits[h])
-                _compare_records(got_all[s0:s1].reshape(n, w), ref, ranks[h], bits[h], f"{tensor} h{h} b{b}")
+                H.compare_records(got_all[s0:s1].reshape(n, w), ref, ranks[h], bits[h], f"{tensor} h{h} b{b}",
+                                 x[b, h], bases[h])
                 a0, _, _ = codec.record_slice(ranks, bits, batch, cap, h, b, 0, 0)
                 a1, _, _ = codec.record_slice(ranks, bits, batch, cap, h, b, cap, cap)
                 outside = np.concatenate([got_all[a0:s0], got_all[s1:a1]])
@@ -217,7 +204,8 @@ def test_prefill_records_equal_append_records(K, dtype):
             for b in range(B):
                 s0, s1, w = codec.record_slice(ranks, bits, B, pos0 + n, h, b, pos0, pos0 + n)
                 ref = codec.encode_tokens(x[tensor][b, h].astype(np.float64), bases[h], bits[h])
-                _compare_records(got_all[s0:s1].reshape(n, w), ref, ranks[h], bits[h], f"{tensor} h{h} b{b}")
+                H.compare_records(got_all[s0:s1].reshape(n, w), ref, ranks[h], bits[h], f"{tensor} h{h} b{b}",
+                                 x[tensor][b, h], bases[h])
 
 
 def test_append_matches_oracle(K):
@@ -404,6 +392,136 @@ def test_attention_workspace_reuse_across_calls(K):
     assert (cnt == 0).all()
 
 
+def _n_splits(K, lay, T, split=0):
+    """Largest per-head split count of a launch, read back from its workspace size."""
+    units = lay.batch * lay.n_kv_heads
+    words = K.kv_workspace_bytes(lay, T, split) // 4 - (units + 3) // 4 * 4
+    return words // (lay.batch * lay.n_q_heads * 132)
+
+
+@pytest.mark.parametrize("g", [2, 4, 8])
+def test_attention_more_than_32_splits(K, g):
+    """66 splits per (sequence, KV head): the split merge's multi-round path (two
+    threads per output quad for g <= 4, each folding three rounds of up to 16
+    splits and then exchanging; one thread and five rounds for g = 8)."""
+    alloc = [(64, 4, 32, 8), (32, 8, 64, 4)]
+    bk, bv = _mixed_bases(alloc, seed=83 + g)
+    T = 16700
+    lay = K.Layout(len(alloc), len(alloc) * g, 1, T, alloc)
+    ns = _n_splits(K, lay, T, 256)
+    say(f"attention g={g}, T={T}, split 256: {ns} splits per unit")
+    assert ns > 32
+    _attention_case(K, alloc, bk, bv, 1, g, T, T, [256, 0])
+
+
+def test_attention_dirty_workspace_is_nan_or_correct(K):
+    """Split arrival counters that are not zero on entry (above, at and below the
+    split count, and an all-ones word) and stale partials: every output element is
+    NaN or bit-equal to the output of a zero-filled workspace, on this call and the
+    next; a zero-filled workspace afterwards gives the exact output again, and the
+    kernel exits normally throughout."""
+    alloc = [(64, 4, 64, 4), (128, 2, 32, 8)]
+    bk, bv = _mixed_bases(alloc, seed=89)
+    B, g, T, split = 2, 4, 3000, 256
+    hkv = len(alloc)
+    wl = W.LLAMA_T32K
+    ck_h, cv_h = H.oracle_cache(wl, alloc, bk, bv, B, T, T,
+                                kv={(t, b, h): W.tokens(wl, t, b, h, 0, T) for t in "KV" for b in range(B)
+                                    for h in range(hkv)})
+    q = W.random_vectors(97, (B, hkv * g, 128)).astype(np.float16)
+    lay = K.Layout(hkv, hkv * g, B, T, alloc)
+    ns = _n_splits(K, lay, T, split)
+    say(f"dirty workspace: {ns} splits per unit")
+    ck, cv = H.u32_dev(ck_h), H.u32_dev(cv_h)
+    pk, pv = H.dev(codec.concat_bases(bk)), H.dev(codec.concat_bases(bv))
+    qd = H.dev(q, torch.float16)
+    nw = K.kv_workspace_bytes(lay, T, split) // 4
+    clean = torch.zeros(nw, dtype=torch.float32, device="cuda")
+    ref = torch.empty((B, hkv * g, 128), dtype=torch.float32, device="cuda")
+    K.kv_attend_decode(lay, qd, T, pk, pv, ck, cv, H.SCALE, ref, clean, split_tokens=split)
+    torch.cuda.synchronize()
+    assert (clean[: B * hkv].view(torch.int32) == 0).all()
+    oracle = attention.attend_cache(q.astype(np.float64), bk, bv, ck_h, cv_h, alloc, B, T, T, H.SCALE)
+    assert H.rel_err_per_head(ref.cpu().numpy(), oracle) <= REL_TOL
+    ref_bits = ref.cpu().numpy().view(np.uint32)
+    # partials left by the clean call (another call's tags), counters preset
+    dirty = clean.clone()
+    cnt = np.array([0xFFFFFFFF, ns + 7, ns, ns - 1], np.uint32)[: B * hkv]
+    dirty[: B * hkv] = torch.from_numpy(cnt.view(np.int32)).cuda().view(torch.float32)
+    n_nan = 0
+    for rep in range(2):
+        out = torch.full_like(ref, 7.0)
+        K.kv_attend_decode(lay, qd, T, pk, pv, ck, cv, H.SCALE, out, dirty, split_tokens=split)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        nan = np.isnan(got)
+        same = got.view(np.uint32) == ref_bits
+        assert (nan | same).all(), f"call {rep}: {(~(nan | same)).sum()} elements neither NaN nor correct"
+        n_nan += int(nan.sum())
+        say(f"  call {rep}: {int(nan.sum())} NaN elements, the rest exact; counters "
+            f"{dirty[: B * hkv].view(torch.int32).cpu().numpy().view(np.uint32).tolist()}")
+    dirty.zero_()
+    out = torch.empty_like(ref)
+    K.kv_attend_decode(lay, qd, T, pk, pv, ck, cv, H.SCALE, out, dirty, split_tokens=split)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref_bits)
+
+
+def test_full_size_llama_b1_t32k_fused_step(K):
+    """The LLaMA-shaped single-sequence layer at its own size: 32 query heads over 8 KV
+    heads, C1 at 2 bits per dimension with MSE weights, a 32768-token prefill encoded
+    on the GPU, then one decode step (the append of token 32768 fused with attention
+    over all 32769 tokens) with the default split plan (more than 32 splits per unit).
+    The fused step equals kv_append + kv_attend_decode bit for bit; every unit's
+    records match the oracle's (exact headers, codes only at classified ties) and all
+    32 query heads' outputs match oracle attention."""
+    wl = W.LLAMA_T32K
+    T = wl.context + 1
+    B, hkv, hq, g = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.group
+    alloc, bk, bv = H.oracle_calibrate(wl)
+    lay = K.Layout(hkv, hq, B, T, alloc)
+    ns = _n_splits(K, lay, T)
+    say(f"full size {wl.name}: {alloc}, {ns} splits per unit")
+    assert ns > 32
+    kx = W.kv_array(wl, "K", 0, T)
+    vx = W.kv_array(wl, "V", 0, T)
+    pk, pv = H.dev(codec.concat_bases(bk)), H.dev(codec.concat_bases(bv))
+    ck = torch.zeros(K.kv_cache_bytes(lay, 0) // 4, dtype=torch.int32, device="cuda")
+    cv = torch.zeros(K.kv_cache_bytes(lay, 1) // 4, dtype=torch.int32, device="cuda")
+    K.kv_encode(lay, H.dev(kx[:, :, :T - 1]), H.dev(vx[:, :, :T - 1]), T - 1, 0, pk, pv, ck, cv)
+    k1, v1 = H.dev(kx[:, :, T - 1]), H.dev(vx[:, :, T - 1])
+    q = W.query_array(wl, 0)
+    qd = H.dev(q)
+    ws = torch.zeros(K.kv_workspace_bytes(lay, T) // 4, dtype=torch.float32, device="cuda")
+    ck2, cv2 = ck.clone(), cv.clone()
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    K.kv_append_attend_decode(lay, k1, v1, qd, T, pk, pv, ck, cv, H.SCALE, out, ws)
+    out2 = torch.empty_like(out)
+    K.kv_append(lay, k1, v1, T - 1, pk, pv, ck2, cv2)
+    K.kv_attend_decode(lay, qd, T, pk, pv, ck2, cv2, H.SCALE, out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ck, ck2) and torch.equal(cv, cv2), "fused append wrote other records"
+    assert torch.equal(out, out2), "fused step differs from append + attend"
+    assert (ws[: B * hkv].view(torch.int32) == 0).all()
+    got = out.cpu().numpy()
+    gk, gv = H.u32_host(ck), H.u32_host(cv)
+    rk, bits_k, rv, bits_v = zip(*alloc)
+    worst = 0.0
+    for h in range(hkv):
+        rec_k = codec.encode_tokens(kx[0, h], bk[h], bits_k[h])
+        rec_v = codec.encode_tokens(vx[0, h], bv[h], bits_v[h])
+        s0, s1, w = codec.record_slice(rk, bits_k, B, T, h, 0, 0, T)
+        H.compare_records(gk[s0:s1].reshape(-1, w), rec_k, rk[h], bits_k[h], f"K h{h}", kx[0, h], bk[h])
+        s0, s1, w = codec.record_slice(rv, bits_v, B, T, h, 0, 0, T)
+        H.compare_records(gv[s0:s1].reshape(-1, w), rec_v, rv[h], bits_v[h], f"V h{h}", vx[0, h], bv[h])
+        ref = attention.attend_head_records(q[0, h * g:(h + 1) * g].astype(np.float64), bk[h], rec_k, rk[h],
+                                            bits_k[h], bv[h], rec_v, rv[h], bits_v[h], H.SCALE)
+        err = H.rel_err_per_head(got[0, h * g:(h + 1) * g], ref)
+        worst = max(worst, err)
+        assert err <= REL_TOL, f"KV head {h}: max rel err {err:.3e}"
+    say(f"  all 8 units: records match, max rel err {worst:.3e}")
+
+
 # ------------------------------------------------------------------ append fused with attention
 FUSED_CASES = [
     # allocation, query heads per KV head, batch, capacity, tokens after the append, split, k1/v1 dtype
@@ -452,10 +570,10 @@ def test_fused_append_attend(K, alloc, g, B, cap, T, split, kvdt):
     rk, bits_k, rv, bits_v = zip(*alloc)
     for h in range(hkv):
         for b in range(B):
-            for got, ref, ranks, bits, name in ((gk, ok_h, rk, bits_k, "K"), (gv, ov_h, rv, bits_v, "V")):
+            for got, ref, ranks, bits, name, bases in ((gk, ok_h, rk, bits_k, "K", bk), (gv, ov_h, rv, bits_v, "V", bv)):
                 s0, s1, w = codec.record_slice(ranks, bits, B, cap, h, b, 0, T)
-                _compare_records(got[s0:s1].reshape(T, w), ref[s0:s1].reshape(T, w), ranks[h], bits[h],
-                                 f"{name} h{h} b{b}")
+                H.compare_records(got[s0:s1].reshape(T, w), ref[s0:s1].reshape(T, w), ranks[h], bits[h],
+                                 f"{name} h{h} b{b}", kv[name, b, h], bases[h])
     ref = attention.attend_cache(q.cpu().numpy().astype(np.float64), bk, bv, ok_h, ov_h, alloc, B, cap, T, H.SCALE)
     err = H.rel_err_per_head(out_f.cpu().numpy(), ref)
     say(f"  max rel err {err:.3e}")
@@ -521,9 +639,11 @@ def test_end_to_end_encode_append_attend(K):
     rk, bits_k, rv, bits_v = zip(*alloc)
     for h in range(wl.n_kv_heads):
         s0, s1, w = codec.record_slice(rk, bits_k, B, T + 1, h, 0, 0, T + 1)
-        _compare_records(gk[s0:s1].reshape(-1, w), ck_h[s0:s1].reshape(-1, w), rk[h], bits_k[h], f"K h{h}")
+        H.compare_records(gk[s0:s1].reshape(-1, w), ck_h[s0:s1].reshape(-1, w), rk[h], bits_k[h], f"K h{h}",
+                         kx[0, h], bk[h])
         s0, s1, w = codec.record_slice(rv, bits_v, B, T + 1, h, 0, 0, T + 1)
-        _compare_records(gv[s0:s1].reshape(-1, w), cv_h[s0:s1].reshape(-1, w), rv[h], bits_v[h], f"V h{h}")
+        H.compare_records(gv[s0:s1].reshape(-1, w), cv_h[s0:s1].reshape(-1, w), rv[h], bits_v[h], f"V h{h}",
+                         vx[0, h], bv[h])
     ref = attention.attend_cache(q.astype(np.float64), bk, bv, ck_h, cv_h, alloc, B, T + 1, T + 1, H.SCALE)
     err = H.rel_err_per_head(got, ref)
     say(f"  end-to-end max rel err {err:.3e}")
@@ -575,9 +695,9 @@ def test_full_size_128k_sampled_units(K, name):
         rec_k = np.concatenate([codec.encode_tokens(xk[i:i + 16384], bk[h], bits_k[h]) for i in range(0, T, 16384)])
         rec_v = np.concatenate([codec.encode_tokens(xv[i:i + 16384], bv[h], bits_v[h]) for i in range(0, T, 16384)])
         s0, s1, w = codec.record_slice(rk, bits_k, B, T, h, b, 0, T)
-        fk = _compare_records(gk[s0:s1].reshape(-1, w), rec_k, rk[h], bits_k[h], f"K b{b} h{h}")
+        fk = H.compare_records(gk[s0:s1].reshape(-1, w), rec_k, rk[h], bits_k[h], f"K b{b} h{h}", xk, bk[h])
         s0, s1, w = codec.record_slice(rv, bits_v, B, T, h, b, 0, T)
-        fv = _compare_records(gv[s0:s1].reshape(-1, w), rec_v, rv[h], bits_v[h], f"V b{b} h{h}")
+        fv = H.compare_records(gv[s0:s1].reshape(-1, w), rec_v, rv[h], bits_v[h], f"V b{b} h{h}", xv, bv[h])
         ref = attention.attend_head_records(q[b, h * g:(h + 1) * g].astype(np.float64), bk[h], rec_k, rk[h], bits_k[h],
                                             bv[h], rec_v, rv[h], bits_v[h], H.SCALE)
         err = H.rel_err_per_head(got[b, h * g:(h + 1) * g], ref)
