@@ -20,7 +20,8 @@ KV_F32, KV_F16 = 0, 1
 EXPORTED = (
     "kv_record_words", "kv_cache_bytes", "kv_workspace_bytes", "kv_workspace_bytes_split",
     "kv_encode", "kv_append", "kv_attend_decode", "kv_attend_decode_split",
-    "kv_append_attend_decode", "kv_attend_decode_ragged", "kv_quantize_pack", "kv_unpack", "kv_last_error",
+    "kv_append_attend_decode", "kv_attend_decode_ragged", "kv_append_attend_decode_noalloc",
+    "kv_quantize_pack", "kv_unpack", "kv_last_error",
 )
 
 
@@ -68,6 +69,7 @@ def _load():
         "kv_attend_decode_split": (i32, [L, P, i32, i64, i64, P, P, P, P, f32, P, P, sz, P]),
         "kv_append_attend_decode": (i32, [L, P, P, i32, P, i32, i64, i64, P, P, P, P, f32, P, P, sz, P]),
         "kv_attend_decode_ragged": (i32, [L, P, i32, P, i64, P, P, P, P, f32, P, P, sz, P]),
+        "kv_append_attend_decode_noalloc": (i32, [L, P, P, i32, P, i32, i64, i64, P, P, P, P, f32, P, P]),
         "kv_quantize_pack": (i32, [P, i64, i32, i32, P, P]),
         "kv_unpack": (i32, [P, i64, i32, i32, P, P, P]),
         "kv_last_error": (ctypes.c_char_p, []),
@@ -205,6 +207,16 @@ def kv_append_attend_decode(layout, k1, v1, q, n_tokens, basis_k, basis_v, cache
                                         _dtype_code(q), n_tokens, split_tokens, _ptr(basis_k), _ptr(basis_v),
                                         _ptr(cache_k), _ptr(cache_v), float(softmax_scale), _ptr(out),
                                         _ptr(workspace), nbytes, _stream(stream)))
+
+
+def kv_append_attend_decode_noalloc(layout, k1, v1, q, n_tokens, basis_k, basis_v, cache_k, cache_v,
+                                    softmax_scale, out, split_tokens: int = 0, stream=None):
+    """kv_append_attend_decode with the split scratch in the library's static device
+    array (no workspace argument; calls on one GPU must not overlap)."""
+    _check(_lib.kv_append_attend_decode_noalloc(layout.ref(), _ptr(k1), _ptr(v1), _dtype_code(k1), _ptr(q),
+                                                _dtype_code(q), n_tokens, split_tokens, _ptr(basis_k),
+                                                _ptr(basis_v), _ptr(cache_k), _ptr(cache_v), float(softmax_scale),
+                                                _ptr(out), _stream(stream)))
 
 
 def kv_quantize_pack(coords, rank, bits, records, stream=None):

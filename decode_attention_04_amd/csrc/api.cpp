@@ -4,7 +4,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <chrono>
+#include <mutex>
 #include <string>
 
 #include "kvtc.h"
@@ -222,24 +224,99 @@ kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Works
   return KV_OK;
 }
 
+// ---------------------------------------------------------------- static split scratch
+// The split-merge scratch of kv_append_attend_decode_noalloc, one copy per GPU
+// (device globals are zero when the code object loads): arrival counters in the
+// first kStaticCounterWords words (a fixed region, so no call's partials ever land
+// on a counter, and every completed call leaves its counters at zero), split
+// partials after them.  Host code never names the array itself (its host-side
+// name is not a device address): the device address comes from
+// hipGetSymbolAddress, taken once per device and kept for the process.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+constexpr int64_t kStaticCounterWords = 4096;
+constexpr int kStaticMaxDevices = 64;
+static __device__ __align__(256) uint32_t scratch[kStaticScratchBytes / 4];
+
+std::mutex g_scratch_mu;
+std::atomic<uint32_t*> g_scratch_ptr[kStaticMaxDevices];
+
+// The device address of `scratch` on the current device (looked up on the first
+// call on that device, under a lock; later calls read the cached address).
+kv_status static_scratch(void* stream, uint32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kStaticMaxDevices)
+    return fail(KV_ERR_UNSUPPORTED, "device %d beyond the %d devices of the static scratch table", dev,
+                kStaticMaxDevices);
+  if (stream) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess) return device_status(e, "hipStreamGetDevice");
+    if ((int)sdev != dev)
+      return fail(KV_ERR_INVALID, "stream belongs to device %d, the current device is %d", (int)sdev, dev);
+  }
+  uint32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return device_status(e, "hipGetSymbolAddress(scratch)");
+      p = (uint32_t*)addr;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return KV_OK;
+}
+
+// Where a call's split counters and partials live: the caller's workspace, or
+// (static_ws) the library's static scratch.
 kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_tokens, int64_t split_tokens,
                       const float* basis_k, const float* basis_v, const uint32_t* cache_k, const uint32_t* cache_v,
                       float softmax_scale, float* out, void* workspace, size_t workspace_bytes, void* stream,
-                      const void* k1, const void* v1, kv_dtype kv_dt, const int32_t* lengths = nullptr) {
+                      const void* k1, const void* v1, kv_dtype kv_dt, const int32_t* lengths = nullptr,
+                      bool static_ws = false) {
   if (dtype != KV_F32 && dtype != KV_F16) return fail(KV_ERR_INVALID, "dtype %d unknown", (int)dtype);
   Workspace w;
   kv_status s = plan_workspace(L, n_tokens, split_tokens, w);
   if (s) return s;
-  if (!q || !basis_k || !basis_v || !cache_k || !cache_v || !out || !workspace)
+  if (!q || !basis_k || !basis_v || !cache_k || !cache_v || !out || (!static_ws && !workspace))
     return fail(KV_ERR_INVALID, "NULL query, basis, cache, output or workspace pointer");
   const size_t esz = dtype == KV_F32 ? 4 : 2;
   if (!aligned(q, esz) || !aligned(basis_k, 4) || !aligned(basis_v, 4) || !aligned(cache_k, 4) ||
-      !aligned(cache_v, 4) || !aligned(out, 4) || !aligned(workspace, 16))
+      !aligned(cache_v, 4) || !aligned(out, 4) || (!static_ws && !aligned(workspace, 16)))
     return fail(KV_ERR_INVALID, "misaligned pointer");
-  if (workspace_bytes < (size_t)w.floats * 4u)
+  const int64_t part_floats = w.floats - w.part;
+  if (static_ws) {
+    const int64_t units = (int64_t)L.batch * L.n_kv;
+    if (units > kStaticCounterWords)
+      return fail(KV_ERR_CAPACITY, "batch x n_kv_heads = %lld exceeds the static scratch's %lld counters",
+                  (long long)units, (long long)kStaticCounterWords);
+    const int64_t room = (int64_t)(kStaticScratchBytes / 4) - kStaticCounterWords;
+    if (part_floats > room)
+      return fail(KV_ERR_CAPACITY, "split partials of %lld bytes exceed the static scratch's %lld bytes "
+                  "(fewer splits: a larger split_tokens)", (long long)part_floats * 4, (long long)room * 4);
+  } else if (workspace_bytes < (size_t)w.floats * 4u) {
     return fail(KV_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes,
                 (size_t)w.floats * 4u);
+  }
   if (!(softmax_scale == softmax_scale)) return fail(KV_ERR_INVALID, "softmax_scale is NaN");
+  uint32_t* cnt = nullptr;
+  float* part = nullptr;
+  if (static_ws) {
+    uint32_t* sp = nullptr;
+    s = static_scratch(stream, &sp);
+    if (s) return s;
+    cnt = sp;
+    part = (float*)(sp + kStaticCounterWords);
+  } else {
+    float* ws = (float*)workspace;
+    cnt = (uint32_t*)(ws + w.cnt);
+    part = ws + w.part;
+  }
   AttendArgs a{};
   a.heads = L.table;
   a.q = q;
@@ -248,9 +325,8 @@ kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_
   a.cache_k = cache_k;
   a.cache_v = cache_v;
   a.out = out;
-  float* ws = (float*)workspace;
-  a.cnt = (uint32_t*)(ws + w.cnt);
-  a.part = ws + w.part;
+  a.cnt = cnt;
+  a.part = part;
   a.nonce = call_nonce();
   a.n_tokens = n_tokens;
   a.lengths = lengths;
@@ -397,6 +473,22 @@ kv_status kv_append_attend_decode(const kv_layout* layout, const void* k1, const
   if (!aligned(k1, esz) || !aligned(v1, esz)) return fail(KV_ERR_INVALID, "misaligned pointer");
   return attend_impl(L, q, q_dt, n_tokens, split_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale, out,
                      workspace, workspace_bytes, stream, k1, v1, kv_dt);
+}
+
+kv_status kv_append_attend_decode_noalloc(const kv_layout* layout, const void* k1, const void* v1, kv_dtype kv_dt,
+                                          const void* q, kv_dtype q_dt, int64_t n_tokens, int64_t split_tokens,
+                                          const float* basis_k, const float* basis_v, uint32_t* cache_k,
+                                          uint32_t* cache_v, float softmax_scale, float* out, void* stream) {
+  Layout L;
+  kv_status s = build_layout(layout, L);
+  if (s) return s;
+  if (kv_dt != KV_F32 && kv_dt != KV_F16) return fail(KV_ERR_INVALID, "dtype %d unknown", (int)kv_dt);
+  if (n_tokens < 1) return fail(KV_ERR_INVALID, "n_tokens %lld < 1: nothing to append", (long long)n_tokens);
+  if (!k1 || !v1) return fail(KV_ERR_INVALID, "NULL key or value to append");
+  const size_t esz = kv_dt == KV_F32 ? 4 : 2;
+  if (!aligned(k1, esz) || !aligned(v1, esz)) return fail(KV_ERR_INVALID, "misaligned pointer");
+  return attend_impl(L, q, q_dt, n_tokens, split_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale, out,
+                     nullptr, 0, stream, k1, v1, kv_dt, nullptr, true);
 }
 
 kv_status kv_attend_decode(const kv_layout* layout, const void* q, kv_dtype dtype, int64_t n_tokens,

@@ -208,6 +208,29 @@ kv_status kv_append_attend_decode(const kv_layout *layout, const void *k1, const
                                   float softmax_scale, float *out, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* kv_append_attend_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that must
+ * not allocate, harnesses that forbid it).  The split counters and partials live
+ * in a static device array of the library, 16 MiB per GPU (held until the
+ * process ends): its first 4096 words are arrival counters, the rest partials.
+ * The call itself calls no allocating routine.  Arguments, records and output
+ * are those of kv_append_attend_decode with the same split size.
+ * The counters are zero when the library's code loads on a device and every
+ * completed call leaves them zero; a counter that is not (a launch that did not
+ * complete) gives NaN or correct outputs, as for kv_attend_decode.  Every call
+ * on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (on different streams, or from several threads) race and must not be issued.
+ * `stream` must belong to the current device.
+ * Errors: KV_ERR_CAPACITY if batch * n_kv_heads > 4096 or the split partials
+ * (4 * 132 bytes per sequence, query head and split) exceed 16 MiB - 16 KiB;
+ * KV_ERR_INVALID if `stream` is on another device; otherwise as
+ * kv_append_attend_decode. */
+kv_status kv_append_attend_decode_noalloc(const kv_layout *layout, const void *k1, const void *v1,
+                                          kv_dtype kv_dt, const void *q, kv_dtype q_dt,
+                                          int64_t n_tokens, int64_t split_tokens, const float *basis_k,
+                                          const float *basis_v, uint32_t *cache_k, uint32_t *cache_v,
+                                          float softmax_scale, float *out, void *stream);
+
 /* Quantize and pack n tokens of r float32 coordinates each (coords [n][r])
  * into records [n][kv_record_words(r, b)].  Same device code as the encoder's
  * quantize/pack stage; exposed to check the record format in isolation. */
