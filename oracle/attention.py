@@ -17,7 +17,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codec import decode_records
+from .codec import decode_records, decode_records_static
 
 
 def softmax(s: np.ndarray) -> np.ndarray:
@@ -39,18 +39,22 @@ def attend_coords(q, basis_k, ck, basis_v, cv, scale: float) -> np.ndarray:
     return np.asarray(basis_v, np.float64) @ ot
 
 
-def attend_head_records(qs, basis_k, rec_k, rk, bk, basis_v, rec_v, rv, bv, scale):
-    """Query heads qs [g, d] of one KV head over its records [T, W] -> [g, d]."""
-    ck = decode_records(rec_k, rk, bk)
-    cv = decode_records(rec_v, rv, bv)
+def attend_head_records(qs, basis_k, rec_k, rk, bk, basis_v, rec_v, rv, bv, scale, static_k=None, static_v=None):
+    """Query heads qs [g, d] of one KV head over its records [T, W] -> [g, d].
+
+    static_k / static_v: the head's fixed (min, step) when its records are header-free."""
+    ck = decode_records(rec_k, rk, bk) if static_k is None else decode_records_static(rec_k, rk, bk, *static_k)
+    cv = decode_records(rec_v, rv, bv) if static_v is None else decode_records_static(rec_v, rv, bv, *static_v)
     return np.stack([attend_coords(q, basis_k, ck, basis_v, cv, scale) for q in np.atleast_2d(qs)])
 
 
-def attend_cache(q, bases_k, bases_v, cache_k, cache_v, alloc, batch, capacity, T, scale):
+def attend_cache(q, bases_k, bases_v, cache_k, cache_v, alloc, batch, capacity, T, scale,
+                 static_k=None, static_v=None):
     """Full decode attention: q [B, Hq, d] over records 0..T-1 of every head -> [B, Hq, d].
 
     ``alloc`` lists (r_K, b_K, r_V, b_V) per KV head; ``bases_k/v`` list the
     d x r bases; ``cache_k/v`` are the flat uint32 caches in the head-major layout.
+    static_k / static_v: per-head fixed (min, step) of header-free K / V records (or None).
     """
     from .codec import record_slice
 
@@ -62,15 +66,18 @@ def attend_cache(q, bases_k, bases_v, cache_k, cache_v, alloc, batch, capacity, 
     bk = [a[1] for a in alloc]
     rv = [a[2] for a in alloc]
     bv = [a[3] for a in alloc]
+    fk = [static_k is not None] * hkv
+    fv = [static_v is not None] * hkv
     out = np.zeros((B, hq, d))
     for b in range(B):
         for h in range(hkv):
-            s0, s1, wk = record_slice(rk, bk, batch, capacity, h, b, 0, T)
-            v0, v1, wv = record_slice(rv, bv, batch, capacity, h, b, 0, T)
+            s0, s1, wk = record_slice(rk, bk, batch, capacity, h, b, 0, T, fk)
+            v0, v1, wv = record_slice(rv, bv, batch, capacity, h, b, 0, T, fv)
             recs_k = np.asarray(cache_k[s0:s1]).reshape(T, wk)
             recs_v = np.asarray(cache_v[v0:v1]).reshape(T, wv)
             out[b, h * g:(h + 1) * g] = attend_head_records(
                 q[b, h * g:(h + 1) * g], bases_k[h], recs_k, rk[h], bk[h],
-                bases_v[h], recs_v, rv[h], bv[h], scale)
+                bases_v[h], recs_v, rv[h], bv[h], scale,
+                None if static_k is None else static_k[h], None if static_v is None else static_v[h])
     return out
 

@@ -10,6 +10,9 @@ packed b-bit codes.  Record of one token (r coordinates, b bits each):
   Codes may straddle two words; unused high bits of the last word are zero.
 
 W = 1 + ceil(r * b / 32) 32-bit words.
+
+A header-free record (the head's quantizer fixed at calibration) is the same
+record without word 0: ceil(r * b / 32) words of codes.
 """
 from __future__ import annotations
 
@@ -67,3 +70,17 @@ def padding_is_zero(records, r: int, b: int) -> bool:
     shifts = np.arange(32, dtype=np.uint64)
     bits = ((rec[..., 1:, None] >> shifts) & np.uint64(1)).reshape(rec.shape[:-1] + (-1,))
     return not bits[..., used:].any()
+
+
+def pack_codes(codes, b: int) -> np.ndarray:
+    """Header-free record: the code words of ``pack`` (its word 0 dropped)."""
+    codes = np.asarray(codes, np.int64)
+    z = np.zeros(codes.shape[:-1])
+    return pack(z, z, codes, b)[..., 1:]
+
+
+def unpack_codes(words, r: int, b: int) -> np.ndarray:
+    """Inverse of ``pack_codes``: code words [..., W - 1] -> codes [..., r]."""
+    words = np.asarray(words, np.uint32)
+    full = np.concatenate([np.zeros(words.shape[:-1] + (1,), np.uint32), words], axis=-1)
+    return unpack(full, r, b)[2]

@@ -413,3 +413,122 @@ def test_region_offsets_and_record_slices():
     assert off.tolist() == [0, 2 * 8 * 3, 2 * 8 * 3 + 2 * 8 * 9, 2 * 8 * 3 + 2 * 8 * 9 + 2 * 8 * 4]
     s0, s1, w = codec.record_slice(rk, bk, 2, 8, 1, 1, 2, 5)
     assert w == 9 and s0 == 48 + (1 * 8 + 2) * 9 and s1 == s0 + 3 * 9
+
+
+# ------------------------------------------------------------------ header-free records (one static quantizer per head)
+def test_static_quantizer_hand_worked_example():
+    """min 0, step 0.5, b = 2: (c - min) / step = 0, 0.5, 1, 2, 2.4, -0.2, 7 -> rint (half to
+    even) 0, 0, 1, 2, 2, -0, 7 -> clamped to [0, 3]: 0, 0, 1, 2, 2, 0, 3."""
+    c = np.array([0.0, 0.25, 0.5, 1.0, 1.2, -0.1, 3.5])
+    assert quantizer.quantize_static(c, 2, 0.0, 0.5).tolist() == [0, 0, 1, 2, 2, 0, 3]
+
+
+@pytest.mark.parametrize("b", [2, 4, 8])
+def test_static_quantizer_noise_on_its_range_is_step_squared_over_12(b):
+    """Inputs uniform over the grid's span [min, min + (2^b - 1) step): every error is
+    uniform over half a step or a whole cell, so E[MSE] = step^2 / 12 exactly (step 2^-b,
+    exact in fp16)."""
+    rng = np.random.default_rng(b)
+    step = 2.0 ** -b
+    c = rng.random(1_000_000) * ((1 << b) - 1) * step
+    codes = quantizer.quantize_static(c, b, 0.0, step)
+    mse = np.mean((c - step * codes) ** 2)
+    assert abs(mse / (step * step / 12.0) - 1.0) < 0.01
+
+
+@pytest.mark.parametrize("b", range(2, 9))
+def test_gaussian_uniform_mse_closed_form_matches_monte_carlo(b):
+    """The closed form of the clamped endpoint grid's error on N(0, 1) against the
+    mean squared error of quantize_static on 2e6 samples, at the optimal clip and at
+    half and twice it."""
+    rng = np.random.default_rng(100 + b)
+    x = rng.standard_normal(2_000_000)
+    L = (1 << b) - 1
+    k_opt = quantizer.optimal_clip(b)
+    for k in (k_opt, 0.5 * k_opt, 2.0 * k_opt):
+        step = 2.0 * k / L
+        xh = -k + step * quantizer.quantize_static(x, b, -k, step)
+        mc = np.mean((x - xh) ** 2)
+        assert abs(mc / float(quantizer.gaussian_uniform_mse(k, b)) - 1.0) < 0.01
+
+
+def test_optimal_clip_is_a_minimum_and_grows_with_bits():
+    prev_k, prev_d = 0.0, np.inf
+    for b in range(2, 9):
+        k = quantizer.optimal_clip(b)
+        d = float(quantizer.gaussian_uniform_mse(k, b))
+        for delta in (1e-3, 1e-2, 1e-1):
+            assert d <= float(quantizer.gaussian_uniform_mse(k + delta, b))
+            assert d <= float(quantizer.gaussian_uniform_mse(k - delta, b))
+        assert k > prev_k and d < prev_d
+        prev_k, prev_d = k, d
+    # fine grids: the error splits into the granular step^2 / 12 inside the range and
+    # the overload 2 int_kappa^inf (x - kappa)^2 phi = 2 ((1 + k^2) Q(k) - k phi(k))
+    from scipy.special import ndtr
+    k8 = quantizer.optimal_clip(8)
+    step = 2 * k8 / 255
+    tail = 1.0 - ndtr(k8)
+    dens = np.exp(-k8 * k8 / 2) / np.sqrt(2 * np.pi)
+    overload = 2 * ((1 + k8 * k8) * tail - k8 * dens)
+    granular = step * step / 12 * (1 - 2 * tail)
+    d8 = float(quantizer.gaussian_uniform_mse(k8, 8))
+    assert abs((granular + overload) / d8 - 1.0) < 0.01
+
+
+@pytest.mark.parametrize("r", [16, 64])
+def test_hadamard_fold_equalises_coordinate_variances(r):
+    """With the random-sign Hadamard folded in, every retained coordinate of a head
+    has the same variance trace(P^T Sigma P) / r (the mean of the retained
+    eigenvalues): one static quantizer per head fits all of them."""
+    cov = W.random_covariance(7, 128)
+    lam, vecs = transform.eigenbasis(cov)
+    P = transform.folded_basis(vecs, r, W.random_basis_signs(3, r))
+    var = np.diag(P.T @ cov @ P)
+    assert np.allclose(var, lam[:r].mean(), rtol=1e-12, atol=0)
+
+
+def test_static_scale_uses_the_clipped_range():
+    s, b = 0.75, 3
+    k = quantizer.optimal_clip(b)
+    mu, sg = quantizer.static_scale(s, b)
+    assert mu == float(quantizer.fp16_round(-k * s))
+    assert sg == float(quantizer.fp16_round((k * s - mu) / 7))
+    assert quantizer.fp16_bits(mu) is not None and quantizer.fp16_bits(sg) is not None
+
+
+@pytest.mark.parametrize("r", [16, 32, 64, 128])
+@pytest.mark.parametrize("b", range(2, 9))
+def test_header_free_records_round_trip(r, b):
+    codes = W.random_codes(r * 10 + b, 50, r, b)
+    words = packing.pack_codes(codes, b)
+    assert words.shape == (50, packing.record_words(r, b) - 1)
+    assert np.array_equal(words, packing.pack(np.zeros(50), np.zeros(50), codes, b)[:, 1:])
+    assert np.array_equal(packing.unpack_codes(words, r, b), codes)
+
+
+def test_header_free_attention_on_exact_grid_is_textbook_attention():
+    """Full rank, identity basis, coordinates on the static grid: the header-free cache
+    holds the keys and values exactly, and decode attention over it equals textbook
+    softmax(q K^T / sqrt(d)) V computed directly."""
+    rng = np.random.default_rng(11)
+    T, d, b = 300, 128, 4
+    mu, sg = -2.0, 0.25
+    P = np.eye(d)
+    k = mu + sg * rng.integers(0, 16, (T, d))
+    v = mu + sg * rng.integers(0, 16, (T, d))
+    q = rng.standard_normal((2, d))
+    rk = codec.encode_tokens_static(k, P, b, mu, sg)
+    rv = codec.encode_tokens_static(v, P, b, mu, sg)
+    got = attention.attend_head_records(q, P, rk, d, b, P, rv, d, b, 1 / np.sqrt(d), (mu, sg), (mu, sg))
+    s = q @ k.T / np.sqrt(d)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    ref = (p / p.sum(axis=1, keepdims=True)) @ v
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_header_free_region_offsets():
+    ranks, bits = [16, 64], [4, 4]
+    off = codec.region_offsets(ranks, bits, 2, 10, [True, False])
+    assert off.tolist() == [0, 2 * 10 * 2, 2 * 10 * 2 + 2 * 10 * 9]
+    s0, s1, w = codec.record_slice(ranks, bits, 2, 10, 0, 1, 3, 5, [True, False])
+    assert (s0, s1, w) == (10 * 2 + 3 * 2, 10 * 2 + 5 * 2, 2)
