@@ -74,13 +74,14 @@ def calibrate(wl: W.Workload):
     return alloc, bk, bv
 
 
-def step_bytes(wl, alloc, T):
-    """Algorithmic HBM bytes of one decode step: attention part and append part."""
+def step_bytes(wl, alloc, T, static=False):
+    """Algorithmic HBM bytes of one decode step: attention part and append part
+    (static: header-free records, one word fewer each)."""
     from decode_attention_04_amd import kv_record_words
 
     B, hq, d = wl.batch, wl.n_q_heads, wl.head_dim
     esz = 4 if wl.dtype == "f32" else 2
-    rec = sum(4 * (kv_record_words(a[0], a[1]) + kv_record_words(a[2], a[3])) for a in alloc)
+    rec = sum(4 * (kv_record_words(a[0], a[1]) + kv_record_words(a[2], a[3]) - (2 if static else 0)) for a in alloc)
     basis = sum(4 * d * (a[0] + a[2]) for a in alloc)
     attend = B * T * rec + B * hq * d * esz + basis + B * hq * d * 4
     append = B * wl.n_kv_heads * 2 * d * esz + B * rec + basis
@@ -129,20 +130,27 @@ def encode_rate(K, wl, block=2048, reps=5):
             "pct_of_hbm_peak": round(100 * (in_bytes + out_bytes) / ms / 1e6 / HBM_PEAK_GBS, 2)}
 
 
-def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragged=None):
+def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragged=None, static=False):
     """Sustained kv_append_attend_decode throughput of another decode layout at its full size.
 
     The caches hold the workload's generated keys and values of the first `block` tokens
     repeated along the token axis (same per-token statistics), encoded on the GPU; enough
     layer caches rotate to exceed the Infinity Cache.  Not checked against anything here:
     the GPU parity tests cover these layouts.  ragged: fractions of the context, one per
-    sequence, timed as kv_attend_decode_ragged (attention only) over those lengths."""
+    sequence, timed as kv_attend_decode_ragged (attention only) over those lengths.
+    static: header-free records with each head's fixed quantizer from calibration."""
     import torch
+
+    from decode_attention_04_amd import calib
 
     alloc, bk, bv = calibrate(wl)
     T = wl.context + 1
     B, H, hq, d = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim
-    lay = K.Layout(H, hq, B, T, alloc)
+    scales = {}
+    if static:
+        scales = {"scale_k": [calib.static_scale_word(W.covariance(wl, "K", h), bk[h], alloc[h][1]) for h in range(H)],
+                  "scale_v": [calib.static_scale_word(W.covariance(wl, "V", h), bv[h], alloc[h][3]) for h in range(H)]}
+    lay = K.Layout(H, hq, B, T, alloc, **scales)
     dev = torch.device("cuda:0")
     pk = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bk])).to(dev)
     pv = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bv])).to(dev)
@@ -182,7 +190,7 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
-    attend_bytes, append_bytes = step_bytes(wl, alloc, T)
+    attend_bytes, append_bytes = step_bytes(wl, alloc, T, static)
     if ragged:  # the records of each sequence's own tokens, no append
         rec = attend_bytes - step_bytes(wl, alloc, 0)[0]
         attend_bytes = attend_bytes - rec + rec * sum(lens) // (B * T)
@@ -191,6 +199,8 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
     del caches, ck, cv
     torch.cuda.empty_cache()
     extra = {"lengths": lens, "step": "kv_attend_decode_ragged (no append)"} if ragged else {}
+    if static:
+        extra["records"] = "header-free (one fixed quantizer per head)"
     return {**extra, "batch": B, "n_q_heads": hq, "n_kv_heads": H, "context_tokens": T,
             "allocation": [list(a) for a in alloc], "us_per_step": round(us, 2), "GB_per_s": round(gbs, 1),
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "layer_caches_rotated": n_rep}
@@ -508,9 +518,14 @@ def main():
     if not args.no_decode_rates:
         dec_rates = {}
         for dwl in (W.llama_t128k(0.5), W.llama_t128k(1.0), W.llama_t128k(4.0), W.QWEN_T128K,
-                    W.llama_prefill(32, 8), W.llama_prefill(64, 4), W.llama_t128k_c2(2.0)):
+                    W.llama_prefill(32, 8), W.llama_prefill(64, 4), W.llama_t128k_c2(2.0),
+                    W.llama_t128k_c2(2.0, "joint"), W.LLAMA_T32K):
             dec_rates[dwl.name] = decode_rate(K, dwl)
             log(f"decode {dwl.name}: {dec_rates[dwl.name]}")
+        for bpd in (0.5, 1.0):
+            name = W.llama_t128k(bpd).name + "-header-free"
+            dec_rates[name] = decode_rate(K, W.llama_t128k(bpd), static=True)
+            log(f"decode {name}: {dec_rates[name]}")
         name = W.llama_t128k(2.0).name + "-ragged"
         dec_rates[name] = decode_rate(K, W.llama_t128k(2.0), ragged=(1.0, 0.75, 0.5, 0.25))
         log(f"decode {name}: {dec_rates[name]}")

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Sequence, Tuple
+from typing import Optional, Sequence, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvtc.so")
@@ -21,7 +21,7 @@ EXPORTED = (
     "kv_record_words", "kv_cache_bytes", "kv_workspace_bytes", "kv_workspace_bytes_split",
     "kv_encode", "kv_append", "kv_attend_decode", "kv_attend_decode_split",
     "kv_append_attend_decode", "kv_attend_decode_ragged", "kv_append_attend_decode_noalloc",
-    "kv_quantize_pack", "kv_unpack", "kv_last_error",
+    "kv_decode", "kv_quantize_pack", "kv_unpack", "kv_last_error",
 )
 
 
@@ -42,6 +42,8 @@ class _Layout(ctypes.Structure):
         ("bits_k", ctypes.POINTER(ctypes.c_int32)),
         ("rank_v", ctypes.POINTER(ctypes.c_int32)),
         ("bits_v", ctypes.POINTER(ctypes.c_int32)),
+        ("scale_k", ctypes.POINTER(ctypes.c_uint32)),
+        ("scale_v", ctypes.POINTER(ctypes.c_uint32)),
     ]
 
 
@@ -70,6 +72,7 @@ def _load():
         "kv_append_attend_decode": (i32, [L, P, P, i32, P, i32, i64, i64, P, P, P, P, f32, P, P, sz, P]),
         "kv_attend_decode_ragged": (i32, [L, P, i32, P, i64, P, P, P, P, f32, P, P, sz, P]),
         "kv_append_attend_decode_noalloc": (i32, [L, P, P, i32, P, i32, i64, i64, P, P, P, P, f32, P, P]),
+        "kv_decode": (i32, [L, i32, i64, i64, P, P, P, P]),
         "kv_quantize_pack": (i32, [P, i64, i32, i32, P, P]),
         "kv_unpack": (i32, [P, i64, i32, i32, P, P, P]),
         "kv_last_error": (ctypes.c_char_p, []),
@@ -92,11 +95,15 @@ def _check(status: int):
 class Layout:
     """Shape and per-head (rank, bits) allocation of one layer's compressed cache.
 
-    ``alloc`` lists (rank_k, bits_k, rank_v, bits_v) per KV head.
+    ``alloc`` lists (rank_k, bits_k, rank_v, bits_v) per KV head.  ``scale_k`` /
+    ``scale_v``: None (records with per-token headers) or one 32-bit word per KV
+    head, the head's fixed quantizer for header-free records (fp16 bits of the min
+    in bits 0-15, of the step in bits 16-31).
     """
 
     def __init__(self, n_kv_heads: int, n_q_heads: int, batch: int, capacity: int,
-                 alloc: Sequence[Tuple[int, int, int, int]], head_dim: int = 128):
+                 alloc: Sequence[Tuple[int, int, int, int]], head_dim: int = 128,
+                 scale_k: Optional[Sequence[int]] = None, scale_v: Optional[Sequence[int]] = None):
         if len(alloc) != n_kv_heads:
             raise ValueError("alloc needs one (rank_k, bits_k, rank_v, bits_v) per KV head")
         self.head_dim, self.n_kv_heads, self.n_q_heads = head_dim, n_kv_heads, n_q_heads
@@ -107,8 +114,18 @@ class Layout:
         self._bk = arr(*[a[1] for a in self.alloc])
         self._rv = arr(*[a[2] for a in self.alloc])
         self._bv = arr(*[a[3] for a in self.alloc])
+        u32 = ctypes.c_uint32 * n_kv_heads
+        for name, sc in (("scale_k", scale_k), ("scale_v", scale_v)):
+            if sc is not None and len(sc) != n_kv_heads:
+                raise ValueError(f"{name} needs one word per KV head")
+        self.scale_k = None if scale_k is None else [int(x) for x in scale_k]
+        self.scale_v = None if scale_v is None else [int(x) for x in scale_v]
+        self._sk = None if scale_k is None else u32(*self.scale_k)
+        self._sv = None if scale_v is None else u32(*self.scale_v)
         self._c = _Layout(head_dim, n_kv_heads, n_q_heads, batch, capacity,
-                          self._rk, self._bk, self._rv, self._bv)
+                          self._rk, self._bk, self._rv, self._bv,
+                          ctypes.cast(self._sk, ctypes.POINTER(ctypes.c_uint32)) if self._sk else None,
+                          ctypes.cast(self._sv, ctypes.POINTER(ctypes.c_uint32)) if self._sv else None)
 
     @property
     def group(self) -> int:
@@ -217,6 +234,13 @@ def kv_append_attend_decode_noalloc(layout, k1, v1, q, n_tokens, basis_k, basis_
                                                 _dtype_code(q), n_tokens, split_tokens, _ptr(basis_k),
                                                 _ptr(basis_v), _ptr(cache_k), _ptr(cache_v), float(softmax_scale),
                                                 _ptr(out), _stream(stream)))
+
+
+def kv_decode(layout, which, n_tokens, pos0, basis, cache, out, stream=None):
+    """Reconstruct records pos0 .. pos0+n_tokens-1 of tensor `which` (0 = K, 1 = V):
+    out float32 [batch, n_kv_heads, n_tokens, head_dim] = P (min + step * code)."""
+    _check(_lib.kv_decode(layout.ref(), which, n_tokens, pos0, _ptr(basis), _ptr(cache), _ptr(out),
+                          _stream(stream)))
 
 
 def kv_quantize_pack(coords, rank, bits, records, stream=None):

@@ -20,11 +20,19 @@ KV-COBRA project page, "How KV-COBRA Works":
   programming over the bits spent).  The K heads and the V heads form one pool
   each, or one joint pool (the abstract's joint K+V allocation).
 
+* Header-free records -- with the Hadamard rotation one uniform quantizer per
+  head suffices (KV-COBRA, Hadamard rotation) and no per-token header is stored
+  (abstract).  Each retained coordinate of a head has the variance
+  s^2 = trace(P^T Sigma P) / r (equal for all of them once the rotation is folded
+  in); `static_scale_word` fixes the range [-kappa s, kappa s] with the kappa
+  that minimises the b-bit endpoint grid's squared error on a Gaussian.
+
 Calibration runs once, offline, on the host (float64 numpy); the kernels take
 its output as plain arrays.  The random signs are an input (drawn by the caller).
 """
 from __future__ import annotations
 
+import math
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -183,3 +191,58 @@ def calibrate_head(cov_k, cov_v, signs_k_for, signs_v_for, policy, query_cov=Non
 def concat(bases: Sequence[np.ndarray]) -> np.ndarray:
     """Concatenate per-head d x r float32 bases into the library's flat basis array."""
     return np.concatenate([np.ascontiguousarray(b, np.float32).reshape(-1) for b in bases])
+
+
+def _grid_mse(kappa: float, bits: int) -> float:
+    """Squared error of the 2^bits-level endpoint grid on [-kappa, kappa] (inputs beyond
+    the ends clamped) for a standard normal input: per level c with cell [lo, hi],
+    (1 + c^2) dP - [x pdf] + 2 c d(pdf), from the Gaussian moments."""
+    n = (1 << bits) - 1
+    step = 2.0 * kappa / n
+    sq2 = math.sqrt(2.0)
+
+    def cdf(x):
+        return 0.5 * math.erfc(-x / sq2)
+
+    def pdf(x):
+        return math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+    total = 0.0
+    for k in range(n + 1):
+        c = -kappa + k * step
+        lo, hi = c - 0.5 * step, c + 0.5 * step
+        p_lo, f_lo, xf_lo = (0.0, 0.0, 0.0) if k == 0 else (cdf(lo), pdf(lo), lo * pdf(lo))
+        p_hi, f_hi, xf_hi = (1.0, 0.0, 0.0) if k == n else (cdf(hi), pdf(hi), hi * pdf(hi))
+        total += (1.0 + c * c) * (p_hi - p_lo) - (xf_hi - xf_lo) + 2.0 * c * (f_hi - f_lo)
+    return total
+
+
+def gaussian_clip(bits: int) -> float:
+    """kappa minimising _grid_mse, by golden-section search on [0.5, 6] (the error is
+    unimodal in kappa: overload falls and granular noise grows with it)."""
+    lo, hi = 0.5, 6.0
+    g = (math.sqrt(5.0) - 1.0) / 2.0
+    a, b = hi - g * (hi - lo), lo + g * (hi - lo)
+    fa, fb = _grid_mse(a, bits), _grid_mse(b, bits)
+    while hi - lo > 1e-9:
+        if fa < fb:
+            hi, b, fb = b, a, fa
+            a = hi - g * (hi - lo)
+            fa = _grid_mse(a, bits)
+        else:
+            lo, a, fa = a, b, fb
+            b = lo + g * (hi - lo)
+            fb = _grid_mse(b, bits)
+    return 0.5 * (lo + hi)
+
+
+def static_scale_word(cov: np.ndarray, basis: np.ndarray, bits: int) -> int:
+    """The fixed quantizer of a head's header-free records as the layout's 32-bit word:
+    fp16 bits of min = -kappa s, then of step = (kappa s - min) / (2^bits - 1), with
+    s^2 = trace(P^T Sigma P) / r the retained coordinates' common variance."""
+    P = np.asarray(basis, np.float64)
+    s = math.sqrt(float(np.trace(P.T @ np.asarray(cov, np.float64) @ P)) / P.shape[1])
+    k = gaussian_clip(bits)
+    mu = np.float16(-k * s)
+    step = np.float16((k * s - float(mu)) / ((1 << bits) - 1))
+    return int(mu.view(np.uint16)) | (int(step.view(np.uint16)) << 16)

@@ -91,13 +91,25 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
       return fail(KV_ERR_UNSUPPORTED, "head %d: rank (%d, %d) not in {16, 32, 64, 128}", h, rk, rv);
     if (!supported_bits(bk) || !supported_bits(bv))
       return fail(KV_ERR_UNSUPPORTED, "head %d: bits (%d, %d) not in [2, 8]", h, bk, bv);
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t* sc = t ? L->scale_v : L->scale_k;
+      if (!sc) continue;
+      const uint32_t mu = sc[h] & 0xFFFFu, st = sc[h] >> 16;
+      if ((mu & 0x7C00u) == 0x7C00u || (st & 0x7C00u) == 0x7C00u || (st & 0x8000u) || st == 0u)
+        return fail(KV_ERR_INVALID, "head %d: static %s scale 0x%08x needs a finite fp16 min and a finite step > 0", h,
+                    t ? "value" : "key", sc[h]);
+    }
     HeadDesc& d = out.table.h[h];
     d.rk = rk;
     d.bk = bk;
     d.rv = rv;
     d.bv = bv;
-    d.wk = record_words(rk, bk);
-    d.wv = record_words(rv, bv);
+    d.hk = L->scale_k ? 0 : 1;
+    d.hv = L->scale_v ? 0 : 1;
+    d.sk = L->scale_k ? L->scale_k[h] : 0u;
+    d.sv = L->scale_v ? L->scale_v[h] : 0u;
+    d.wk = record_words(rk, bk, d.hk);
+    d.wv = record_words(rv, bv, d.hv);
     d.boff_k = (int32_t)bk_total;
     d.boff_v = (int32_t)bv_total;
     d.base_k = wk_total;
@@ -523,6 +535,34 @@ kv_status kv_unpack(const uint32_t* records, int64_t n, int32_t rank, int32_t bi
   if (n * rank > (int64_t)0x7FFFFFFF * 64) return fail(KV_ERR_UNSUPPORTED, "n too large");
   return device_status(launch_unpack(records, n, rank, bits, min_step, codes, (hipStream_t)stream),
                        "unpack launch");
+}
+
+kv_status kv_decode(const kv_layout* layout, int32_t which, int64_t n_tokens, int64_t pos0, const float* basis,
+                    const uint32_t* cache, float* out, void* stream) {
+  Layout L;
+  kv_status s = build_layout(layout, L);
+  if (s) return s;
+  if (which != 0 && which != 1) return fail(KV_ERR_INVALID, "which must be 0 (K) or 1 (V)");
+  if (n_tokens < 0) return fail(KV_ERR_INVALID, "n_tokens %lld < 0", (long long)n_tokens);
+  if (pos0 < 0 || pos0 + n_tokens > L.capacity)
+    return fail(KV_ERR_CAPACITY, "positions [%lld, %lld) outside capacity %lld", (long long)pos0,
+                (long long)(pos0 + n_tokens), (long long)L.capacity);
+  if (n_tokens == 0) return ok();
+  if (!basis || !cache || !out) return fail(KV_ERR_INVALID, "NULL basis, cache or output pointer");
+  if (!aligned(basis, 4) || !aligned(cache, 4) || !aligned(out, 4)) return fail(KV_ERR_INVALID, "misaligned pointer");
+  if (n_tokens > (int64_t)0x7FFFFFFF * 16) return fail(KV_ERR_UNSUPPORTED, "n_tokens too large");
+  DecodeArgs a{};
+  a.heads = L.table;
+  a.basis = basis;
+  a.cache = cache;
+  a.out = out;
+  a.n_tokens = n_tokens;
+  a.pos0 = pos0;
+  a.capacity = L.capacity;
+  a.n_kv_heads = L.n_kv;
+  a.batch = L.batch;
+  a.which = which;
+  return device_status(launch_decode(a, (hipStream_t)stream), "decode launch");
 }
 
 const char* kv_last_error(void) { return g_error.c_str(); }

@@ -829,20 +829,23 @@ __device__ inline void progress_priority(int t0, int t_begin, int t_end) {
 // hi + lo) neither overflows nor, for tokens within 2^-28 of the heaviest one,
 // leaves the normal fp16 range.  M moves lazily: only when a token exceeds it, and
 // then to the tile's maximum plus kLazyMargin, so that later tiles rarely move it.
-// p = 2^(s - M) <= 2^24 feeds the fp32 sums l and c.
+// p = 2^(s - M) <= 2^24 feeds the fp32 sums l and c.  hk / hv = 0: the key /
+// value records are header-free and every token takes the head's fixed min and
+// step sk / sv (fp16 min | fp16 step << 16).
 constexpr int kPScale = 14;
 constexpr float kLazyMargin = 8.0f;
 
 template <int GM>
 __device__ __attribute__((always_inline)) inline void softmax_tile(const uint32_t* kt, const uint32_t* vt, int wk,
-                                                                   int wv, int nvalid, int g, float* S,
+                                                                   int wv, int hk, int hv, uint32_t sk, uint32_t sv,
+                                                                   int nvalid, int g, float* S,
                                                                    const float (&sq)[GM], const float (&kf)[GM],
                                                                    WaveState<GM>& st) {
   const int lane = threadIdx.x & 63, G = lane >> 4;
   _Float16* P = (_Float16*)S;
   const bool valid = lane < nvalid;
-  const uint32_t kh = kt[lane * wk];
-  const uint32_t vh = vt[lane * wv];
+  const uint32_t kh = hk ? kt[lane * wk] : sk;
+  const uint32_t vh = hv ? vt[lane * wv] : sv;
   const float muk = f16_bits_to_f32(kh & 0xFFFFu), sgk = f16_bits_to_f32(kh >> 16);
   const float muv = valid ? f16_bits_to_f32(vh & 0xFFFFu) : 0.0f;
   const float sgv = valid ? f16_bits_to_f32(vh >> 16) : 0.0f;
@@ -1010,6 +1013,8 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     EncodeScratch* scr = (EncodeScratch*)scores;  // score and tile areas are not in use yet
     const int tensor = tid >> 7, t = tid & 127;
     const int r = tensor ? hd.rv : hd.rk, bits = tensor ? hd.bv : hd.bk, W = tensor ? hd.wv : hd.wk;
+    const int hdr = tensor ? hd.hv : hd.hk;
+    const uint32_t sw = tensor ? hd.sv : hd.sk;
     const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
     const int64_t xo = ((int64_t)b * a.n_kv_heads + h) * kHeadDim;
     // the fused entry point hands writable caches (kv_append_attend_decode)
@@ -1017,9 +1022,9 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
                     ((int64_t)b * a.capacity + a.append_pos) * W;
     auto sync = [] { __syncthreads(); };
     if (a.append_dtype == 0)
-      encode_token_128((const float*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, rec, scr[tensor], t, sync);
+      encode_token_128((const float*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, hdr, sw, rec, scr[tensor], t, sync);
     else
-      encode_token_128((const _Float16*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, rec, scr[tensor], t, sync);
+      encode_token_128((const _Float16*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, hdr, sw, rec, scr[tensor], t, sync);
     // the records are in L2 before any tile copy (the builtin, unlike an asm wait, also
     // tells the compiler that no store of the encoder is outstanding any more)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)

@@ -27,18 +27,20 @@
 
 namespace kvtc {
 
+// ktc / vtc: the tile shifted so that the codes of record n start at word n * w + 1
+// (one word earlier than the tile for header-free records)
 #define KVTC_K_CASE(B)                                                              \
   case B:                                                                           \
-    if (nks == 1) k_phase<B, 1, GM>(kt, wk, aq_hi, aq_lo, S);                       \
-    else if (nks == 2) k_phase<B, 2, GM>(kt, wk, aq_hi, aq_lo, S);                  \
-    else k_phase<B, 4, GM>(kt, wk, aq_hi, aq_lo, S);                                \
+    if (nks == 1) k_phase<B, 1, GM>(ktc, wk, aq_hi, aq_lo, S);                      \
+    else if (nks == 2) k_phase<B, 2, GM>(ktc, wk, aq_hi, aq_lo, S);                 \
+    else k_phase<B, 4, GM>(ktc, wk, aq_hi, aq_lo, S);                               \
     break;
 #define KVTC_V_CASE(B)                                                              \
   case B:                                                                           \
-    if (NT == 1) v_phase<B, 1, (GM <= 8)>(vt, wv, kk, ahi, alo, acc2);                         \
-    else if (NT == 2) v_phase<B, 2, (GM <= 8)>(vt, wv, kk, ahi, alo, acc2);                    \
-    else if (NT == 4) v_phase<B, 4, (GM <= 8)>(vt, wv, kk, ahi, alo, acc2);                    \
-    else v_phase<B, 8, (GM <= 8)>(vt, wv, kk, ahi, alo, acc2);                                 \
+    if (NT == 1) v_phase<B, 1, (GM <= 8)>(vtc, wv, kk, ahi, alo, acc2);                        \
+    else if (NT == 2) v_phase<B, 2, (GM <= 8)>(vtc, wv, kk, ahi, alo, acc2);                   \
+    else if (NT == 4) v_phase<B, 4, (GM <= 8)>(vtc, wv, kk, ahi, alo, acc2);                   \
+    else v_phase<B, 8, (GM <= 8)>(vtc, wv, kk, ahi, alo, acc2);                                \
     break;
 
 // ----------------------------------------------------------------- generic tile loop
@@ -51,6 +53,8 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
   const int rk = __builtin_amdgcn_readfirstlane(hd.rk), rv = __builtin_amdgcn_readfirstlane(hd.rv);
   const int bk = __builtin_amdgcn_readfirstlane(hd.bk), bv = __builtin_amdgcn_readfirstlane(hd.bv);
   const int wk = hd.wk, wv = hd.wv;
+  const int hk = __builtin_amdgcn_readfirstlane(hd.hk), hv = __builtin_amdgcn_readfirstlane(hd.hv);
+  const uint32_t skw = __builtin_amdgcn_readfirstlane(hd.sk), svw = __builtin_amdgcn_readfirstlane(hd.sv);
   const int nks = rk >= 32 ? rk / 32 : 1;
   const int NT = rv / 16;
   const int t_begin = c.t_begin, t_end = c.t_end, nbuf = c.nbuf;
@@ -79,6 +83,8 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
     const int t1 = t0 + kTileT;
     const uint32_t* kt = c.ktile + slot * c.kbuf;
     const uint32_t* vt = c.vtile + slot * c.vbuf;
+    const uint32_t* ktc = kt + hk - 1;
+    const uint32_t* vtc = vt + hv - 1;
     wait_tiles();  // this tile is in LDS (the next one is issued below)
     const int tn = t0 + (nbuf - 1) * kTileT;
     if (nbuf >= 2 && tn < t_end) {
@@ -96,7 +102,7 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
     } else {
       switch (bk) { KVTC_K_CASE(2) KVTC_K_CASE(4) KVTC_K_CASE(8) }
     }
-    softmax_tile<GM>(kt, vt, wk, wv, nvalid, c.g, S, sq, kf, st);
+    softmax_tile<GM>(kt, vt, wk, wv, hk, hv, skw, svw, nvalid, c.g, S, sq, kf, st);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       u32x4 ahi, alo;
@@ -159,7 +165,7 @@ AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group) {
       bool all = true;
       for (int h = 0; h < n_kv_heads && all; ++h) {
         const HeadDesc& d = heads.h[h];
-        all = spec_index(cls, d.rk, d.bk, d.rv, d.bv) >= 0;
+        all = spec_index(cls, d.rk, d.bk, d.rv, d.bv) >= 0 && d.hk == spec_header(cls) && d.hv == spec_header(cls);
       }
       if (all) p.spec_class = cls;
     }
@@ -208,7 +214,9 @@ hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
       case 2: return launch_attend_spec2(a, s);
       case 3: return launch_attend_spec3(a, s);
       case 4: return launch_attend_spec4(a, s);
-      default: return launch_attend_spec5(a, s);
+      case 5: return launch_attend_spec5(a, s);
+      case 6: return launch_attend_spec6(a, s);
+      default: return launch_attend_spec7(a, s);
     }
   }
   // the generic kernel; all power-of-two widths skip the general-width paths

@@ -38,7 +38,14 @@ namespace kvtc {
 // (attention-KL key weights), as (r_K, b_K, r_V, b_V) per head
 #define KVTC_SPEC_CLASS5(X) X(0, 64, 4, 128, 3) X(1, 128, 4, 128, 3) X(2, 32, 5, 16, 5) X(3, 128, 3, 16, 5) X(4, 128, 4, 32, 4) X(5, 16, 4, 128, 3) X(6, 16, 5, 128, 4) X(7, 16, 5, 32, 3)
 
-constexpr int kSpecClasses = 6;
+// Header-free records (one fixed quantizer per head) of the 64- and 128-bit budget formats
+#define KVTC_SPEC_CLASS6(X) KVTC_SPEC_CLASS0(X)
+#define KVTC_SPEC_CLASS7(X) KVTC_SPEC_CLASS1(X)
+
+constexpr int kSpecClasses = 8;
+
+// Header words of every record a class reads: 1 (per-token min and step) or 0.
+__host__ __device__ constexpr int spec_header(int cls) { return cls >= 6 ? 0 : 1; }
 
 // Index of (rk, bk, rv, bv) in class `cls`, or -1.
 __host__ inline int spec_index(int cls, int rk, int bk, int rv, int bv) {
@@ -52,6 +59,8 @@ __host__ inline int spec_index(int cls, int rk, int bk, int rv, int bv) {
     case 3: KVTC_SPEC_CLASS3(KVTC_SPEC_FIND) break;
     case 4: KVTC_SPEC_CLASS4(KVTC_SPEC_FIND) break;
     case 5: KVTC_SPEC_CLASS5(KVTC_SPEC_FIND) break;
+    case 6: KVTC_SPEC_CLASS6(KVTC_SPEC_FIND) break;
+    case 7: KVTC_SPEC_CLASS7(KVTC_SPEC_FIND) break;
     default: break;
   }
 #undef KVTC_SPEC_FIND
@@ -73,16 +82,19 @@ __device__ __attribute__((always_inline)) inline void issue_tile(const WaveCtx& 
   }
 }
 
-// The tile loop of one wave for records of (RK, BK) keys and (RV, BV) values.
-template <int GM, int RK, int BK, int RV, int BV>
+// The tile loop of one wave for records of (RK, BK) keys and (RV, BV) values, with
+// (HDR = 1) or without (HDR = 0, the head's fixed min and step) per-token headers.
+template <int GM, int RK, int BK, int RV, int BV, int HDR>
 __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArgs& a, const WaveCtx& c,
                                                                  WaveState<GM>& st) {
-  constexpr int WK = 1 + (RK * BK + 31) / 32, WV = 1 + (RV * BV + 31) / 32;
+  constexpr int WK = HDR + (RK * BK + 31) / 32, WV = HDR + (RV * BV + 31) / 32;
   constexpr int NKS = RK >= 32 ? RK / 32 : 1, NT = RV / 16;
   constexpr int KI = (16 * WK + 63) / 64, VI = (16 * WV + 63) / 64;  // copy instructions of a full tile
   static_assert(KI + VI <= 63, "vmcnt range");
   const int t_begin = c.t_begin, t_end = c.t_end, nbuf = c.nbuf;
   const int lane = threadIdx.x & 63;
+  const uint32_t sk = HDR ? 0u : __builtin_amdgcn_readfirstlane(a.heads.h[c.h].sk);
+  const uint32_t sv = HDR ? 0u : __builtin_amdgcn_readfirstlane(a.heads.h[c.h].sv);
   // the first nbuf - 1 tiles (one with a single buffer) start streaming behind the
   // loads of the query projection
   u32x4 aq_hi[4], aq_lo[4];
@@ -110,13 +122,14 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
       issue_tile<WK, WV>(c, tn, t_end, sn);
     }
     progress_priority(t0, t_begin, t_end);
-    k_phase<BK, NKS, GM>(kt, WK, aq_hi, aq_lo, c.S);
-    softmax_tile<GM>(kt, vt, WK, WV, nvalid, c.g, c.S, sq, kf, st);
+    // codes of record n start at word n * W + HDR: the phases take the tile shifted to n * W + 1
+    k_phase<BK, NKS, GM>(kt + HDR - 1, WK, aq_hi, aq_lo, c.S);
+    softmax_tile<GM>(kt, vt, WK, WV, HDR, HDR, sk, sv, nvalid, c.g, c.S, sq, kf, st);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       u32x4 ahi, alo;
       p_operands<GM>(c.S, kk, ahi, alo);
-      v_phase<BV, NT, (GM <= 8)>(vt, WV, kk, ahi, alo, st.acc2);
+      v_phase<BV, NT, (GM <= 8)>(vt + HDR - 1, WV, kk, ahi, alo, st.acc2);
     }
     lds_fence();
     if (nbuf == 1) {
@@ -128,11 +141,12 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
 }
 
 #define KVTC_SPEC_CASE(I, RK, BK, RV, BV) \
-  case I: spec_tiles<GM, RK, BK, RV, BV>(a, c, st); break;
+  case I: spec_tiles<GM, RK, BK, RV, BV, kHdr>(a, c, st); break;
 
 #define KVTC_DEFINE_SPEC_CLASS(CLS)                                                                  \
   template <int GM>                                                                                  \
   __global__ __launch_bounds__(256, 3) void attend_spec##CLS##_kernel(AttendArgs a) {               \
+    constexpr int kHdr = spec_header(CLS);                                                           \
     attend_body<GM>(a, [&](const WaveCtx& c, WaveState<GM>& st) {                                    \
       switch (__builtin_amdgcn_readfirstlane(a.heads.h[c.h].spec)) {                                \
         KVTC_SPEC_CLASS##CLS(KVTC_SPEC_CASE) default : break;                                        \

@@ -1,0 +1,7 @@
+// Decode attention kernels for header-free records (one fixed quantizer per head)
+// of the formats of the 128-bit per-vector budget.
+#include "attend_spec.h"
+
+namespace kvtc {
+KVTC_DEFINE_SPEC_CLASS(7)
+}  // namespace kvtc

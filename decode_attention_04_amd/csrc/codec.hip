@@ -67,13 +67,60 @@ __global__ __launch_bounds__(256) void append_kernel(EncodeArgs a) {
   const int tensor = threadIdx.x >> 7, t = threadIdx.x & 127;
   const HeadDesc& hd = a.heads.h[h];
   const int r = tensor ? hd.rv : hd.rk, bits = tensor ? hd.bv : hd.bk, W = tensor ? hd.wv : hd.wk;
+  const int hdr = tensor ? hd.hv : hd.hk;
+  const uint32_t sw = tensor ? hd.sv : hd.sk;
   const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
   const T* x = (const T*)(tensor ? a.v : a.k) + ((int64_t)b * a.n_kv_heads + h) * kHeadDim;
   uint32_t* rec = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + ((int64_t)b * a.capacity + a.pos0) * W;
-  encode_token_128(x, P, r, bits, rec, scr[tensor], t, [] { __syncthreads(); });
+  encode_token_128(x, P, r, bits, hdr, sw, rec, scr[tensor], t, [] { __syncthreads(); });
+}
+
+// ----------------------------------------------------------------- reconstruction
+// Grid (token blocks of 16, n_kv_heads, batch), 256 threads.  The block's
+// dequantized coordinates min + step * code go to LDS (one thread per (token,
+// coordinate)), then each thread forms outputs x^_i = sum_j P_ij c^_j of its
+// (token, i) pairs in float32, over j in order.
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  __shared__ float ch[16][kMaxRank];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const HeadDesc& hd = a.heads.h[h];
+  const int r = a.which ? hd.rv : hd.rk, bits = a.which ? hd.bv : hd.bk;
+  const int W = a.which ? hd.wv : hd.wk, hdr = a.which ? hd.hv : hd.hk;
+  const uint32_t sw = a.which ? hd.sv : hd.sk;
+  const float* P = a.basis + (a.which ? hd.boff_v : hd.boff_k);
+  const uint32_t* reg = a.cache + (a.which ? hd.base_v : hd.base_k) + ((int64_t)b * a.capacity + a.pos0) * W;
+  const int nt = (int)((a.n_tokens - t0) < 16 ? (a.n_tokens - t0) : 16);
+  for (int e = threadIdx.x; e < 16 * r; e += 256) {
+    const int tt = e / r, j = e - tt * r;
+    float v = 0.0f;
+    if (tt < nt) {
+      const uint32_t* rec = reg + (t0 + tt) * W;
+      const uint32_t w0 = hdr ? rec[0] : sw;
+      const float mu = f16_bits_to_f32(w0 & 0xFFFFu), sg = f16_bits_to_f32(w0 >> 16);
+      v = fmaf(sg, (float)unpack_code(rec + hdr, j, bits), mu);  // one rounding to float32
+    }
+    ch[tt][j] = v;
+  }
+  __syncthreads();
+  float* o = a.out + (((int64_t)b * a.n_kv_heads + h) * a.n_tokens + t0) * kHeadDim;
+  for (int e = threadIdx.x; e < nt * kHeadDim; e += 256) {
+    const int tt = e / kHeadDim, i = e - tt * kHeadDim;
+    const float* pr = P + (int64_t)i * r;
+    float acc = 0.0f;
+    for (int j = 0; j < r; ++j) acc = fmaf(pr[j], ch[tt][j], acc);
+    o[e] = acc;
+  }
 }
 
 // ----------------------------------------------------------------- launchers
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  if (a.n_tokens == 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.n_tokens + 15) / 16), (unsigned)a.n_kv_heads, (unsigned)a.batch);
+  hipLaunchKernelGGL(decode_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_pack(const float* coords, int64_t n, int r, int b, uint32_t* records,
                                 hipStream_t s) {
   if (n == 0) return hipSuccess;

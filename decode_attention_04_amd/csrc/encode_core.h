@@ -31,14 +31,16 @@ struct EncodeScratch {
 };
 
 // Encode the token x[0..128) with basis P (128 x r, float32 row-major) and b-bit
-// codes into `rec` (record_words(r, b) words), using 128 threads whose index in
-// the group is t (0..127, two whole waves).  The caller synchronises the
+// codes into `rec` (record_words(r, b, hdr) words), using 128 threads whose index
+// in the group is t (0..127, two whole waves).  hdr = 1: the record starts with
+// the token's fp16 min and step; hdr = 0: header-free, the codes use the head's
+// fixed min and step `sw` (fp16 min | step << 16).  The caller synchronises the
 // workgroup around the call (`sync` is the workgroup barrier it uses between the
 // phases; all threads of the workgroup must reach it).
 template <typename T, typename Sync>
 __device__ __attribute__((always_inline)) inline void encode_token_128(const T* x, const float* P, int r, int bits,
-                                                                        uint32_t* rec, EncodeScratch& s, int t,
-                                                                        Sync&& sync) {
+                                                                        int hdr, uint32_t sw, uint32_t* rec,
+                                                                        EncodeScratch& s, int t, Sync&& sync) {
   // lane layout: four consecutive columns per lane, one row group per 32 lanes
   const int c4 = t % 32, rg = t / 32;
   const bool active = 4 * c4 < r;
@@ -87,15 +89,15 @@ __device__ __attribute__((always_inline)) inline void encode_token_128(const T* 
       mn = fmin(mn, __shfl_xor(mn, o));
       mx = fmax(mx, __shfl_xor(mx, o));
     }
-    qh = quant_header(mn, mx, bits);
+    qh = hdr ? quant_header(mn, mx, bits) : static_header(sw);
     if (lane < r) s.codes[lane] = quant_code(c0, qh.mu, qh.sigma, bits);
     if (lane + 64 < r) s.codes[lane + 64] = quant_code(c1, qh.mu, qh.sigma, bits);
   }
   sync();
   if (t < 64) {
-    const int W = record_words(r, bits);
-    if (t == 0) rec[0] = qh.word0;
-    if (t < W - 1) rec[1 + t] = pack_word(s.codes, r, bits, t);
+    const int nw = record_words(r, bits, 0);
+    if (t == 0 && hdr) rec[0] = qh.word0;
+    if (t < nw) rec[hdr + t] = pack_word(s.codes, r, bits, t);
   }
 }
 

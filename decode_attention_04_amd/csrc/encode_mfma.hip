@@ -199,7 +199,10 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
   const int b = blockIdx.z;
   const HeadDesc& hd = a.heads.h[h];
   const int bits = tensor ? hd.bv : hd.bk;
-  const int W = tensor ? hd.wv : hd.wk;
+  const int W = tensor ? hd.wv : hd.wk;             // words of a stored record
+  const int hdr = tensor ? hd.hv : hd.hk;           // 0: header-free, the head's fixed min and step
+  const uint32_t sw = tensor ? hd.sv : hd.sk;
+  const int WI = W + 1 - hdr;                       // words of a record assembled in LDS (header slot first)
   const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
   const T* xu = (const T*)(tensor ? a.v : a.k) + ((int64_t)b * a.n_kv_heads + h) * a.n_tokens * kHeadDim;
   uint32_t* cu = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + ((int64_t)b * a.capacity + a.pos0) * W;
@@ -353,8 +356,8 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
       const float muf0 = f16_bits_to_f32(m_lo);
       const uint32_t s_lo = h16_bits(fmaxf(mx - E - muf0, 0.f) * kinv);
       const uint32_t s_hi = h16_bits(fmaxf(mx + E - muf0, 0.f) * kinv);
-      w0[nt] = m_lo | (s_lo << 16);
-      hbad[nt] = valid && (m_lo != m_hi || s_lo != s_hi);
+      w0[nt] = hdr ? (m_lo | (s_lo << 16)) : sw;
+      hbad[nt] = hdr && valid && (m_lo != m_hi || s_lo != s_hi);
       cand[nt] = 0u;
       if (hbad[nt]) {
 #pragma unroll
@@ -414,7 +417,7 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
       const float inv = sgf > 0.f ? 1.0f / sgf : 0.f;
       const float tol = Ev[nt] * inv * 1.0001f + (top + 1.f) * 0x1p-22f;
       uint32_t fl = 0u;
-      uint32_t* rec = recw + n * W;
+      uint32_t* rec = recw + n * WI;
       if (G == 0) {
         if (pow2) rec[0] = w0[nt];
         else hdrw[n] = w0[nt];
@@ -465,14 +468,15 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
       wave_sync();
 
       // store the block's records (consecutive tokens are contiguous); f / W as a
-      // multiply-high by ceil(2^32 / W), exact for f < 2^16
+      // multiply-high by ceil(2^32 / W), exact for f < 2^16 (a one-word header-free
+      // record, whose magic would not fit 32 bits, is its own quotient)
       const int64_t btok0 = wtok0 + 16 * nt;
       for (int f = lane; f < 16 * W; f += 64) {
-        const int tn = (int)__umulhi((uint32_t)f, wmagic), w = f - tn * W;
+        const int tn = W == 1 ? f : (int)__umulhi((uint32_t)f, wmagic), wi = f - tn * W + 1 - hdr;
         if (btok0 + tn < a.n_tokens) {
           uint32_t word;
-          if (pow2) word = recw[f];
-          else word = w == 0 ? hdrw[tn] : pack_word(wb + tn * R, R, bits, w - 1);
+          if (pow2) word = recw[tn * WI + wi];
+          else word = wi == 0 ? hdrw[tn] : pack_word(wb + tn * R, R, bits, wi - 1);
           cu[btok0 * W + f] = word;
         }
       }

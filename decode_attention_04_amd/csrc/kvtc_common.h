@@ -21,19 +21,25 @@ constexpr int kSplitQuantum = 256;  // split-K sizes are multiples of this
 constexpr int kPartStride = 132;    // floats per split partial: o[128], m, l, tag, pad
 
 __host__ __device__ inline int record_words(int r, int b) { return 1 + (r * b + 31) / 32; }
+// Words of a record with (hdr = 1) or without (hdr = 0) its per-token header word.
+__host__ __device__ inline int record_words(int r, int b, int hdr) { return hdr + (r * b + 31) / 32; }
 
 inline bool supported_rank(int r) { return r == 16 || r == 32 || r == 64 || r == 128; }
 inline bool supported_bits(int b) { return b >= kMinBits && b <= kMaxBits; }
 
-// Per-KV-head allocation and addressing, passed by value in kernel arguments.
+// Per-KV-head allocation and addressing, passed by value in kernel arguments
+// (48 bytes: 64 heads of it fit the 4 KB argument segment with the rest).
 struct HeadDesc {
-  int32_t rk, bk, rv, bv;   // rank and bits of keys and values
-  int32_t wk, wv;           // record words
-  int32_t boff_k, boff_v;   // float offset of the head's basis
   int64_t base_k, base_v;   // word offset of the head's cache region
-  int32_t spec;             // index of the format in the specialised kernel's class (set at launch)
+  int32_t boff_k, boff_v;   // float offset of the head's basis
+  uint32_t sk, sv;          // header-free records: the head's fixed fp16 min | fp16 step << 16
   int32_t ns;               // splits of each of the head's (sequence, head) units (set at launch)
+  int16_t wk, wv;           // record words
+  int16_t spec;             // index of the format in the specialised kernel's class (set at launch)
+  uint8_t rk, bk, rv, bv;   // rank and bits of keys and values
+  uint8_t hk, hv;           // header words of a key / value record: 1 (per-token min and step) or 0
 };
+static_assert(sizeof(HeadDesc) == 48, "HeadDesc layout");
 
 struct HeadTable {
   HeadDesc h[kMaxKvHeads];
@@ -80,6 +86,15 @@ struct QuantHeader {
   uint32_t word0;  // fp16(min) | fp16(step) << 16
   double mu, sigma;
 };
+
+// The header of a head whose quantizer is fixed (header-free records).
+__device__ inline QuantHeader static_header(uint32_t word0) {
+  QuantHeader q;
+  q.word0 = word0;
+  q.mu = f16_bits_to_f64(word0 & 0xFFFFu);
+  q.sigma = f16_bits_to_f64(word0 >> 16);
+  return q;
+}
 
 __device__ inline QuantHeader quant_header(double cmin, double cmax, int b) {
   QuantHeader q;

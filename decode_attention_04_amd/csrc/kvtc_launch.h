@@ -57,14 +57,29 @@ struct AttendArgs {
   int32_t nbuf;        // tile buffers per wave: 2 (next tile streams in) or 1
 };
 
+struct DecodeArgs {
+  HeadTable heads;
+  const float* basis;     // the tensor's concatenated bases
+  const uint32_t* cache;  // the tensor's cache
+  float* out;             // [batch][n_kv_heads][n_tokens][head_dim]
+  int64_t n_tokens;
+  int64_t pos0;
+  int64_t capacity;
+  int32_t n_kv_heads;
+  int32_t batch;
+  int32_t which;          // 0 = K, 1 = V
+};
+
 // Kernel arguments travel in the kernarg segment, at most 4 KB.
 static_assert(sizeof(AttendArgs) <= 4096, "AttendArgs exceeds the kernel argument limit");
 static_assert(sizeof(EncodeArgs) <= 4096, "EncodeArgs exceeds the kernel argument limit");
+static_assert(sizeof(DecodeArgs) <= 4096, "DecodeArgs exceeds the kernel argument limit");
 
 hipError_t launch_quantize_pack(const float* coords, int64_t n, int r, int b, uint32_t* records,
                                 hipStream_t s);
 hipError_t launch_unpack(const uint32_t* records, int64_t n, int r, int b, uint16_t* min_step,
                          uint8_t* codes, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);       // records -> reconstructed vectors
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);       // one token: append kernel, else the below
 hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s);  // prefill: k, v 16-byte aligned
 // How a layout's decode attention runs: the specialised kernel class (-1: the
@@ -83,5 +98,7 @@ hipError_t launch_attend_spec2(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec3(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec4(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec5(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_spec6(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_spec7(const AttendArgs& a, hipStream_t s);
 
 }  // namespace kvtc

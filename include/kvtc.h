@@ -26,9 +26,16 @@
  *   Quantizer: min = fp16_rne(min_j c_j); step = fp16_rne(max(max_j c_j - min, 0)/(2^b - 1));
  *   code_j = clamp(round_half_even((c_j - min)/step), 0, 2^b - 1), all zero if step == 0.
  *   All rounding decisions are those of exact (float64) arithmetic.
+ * Header-free records (a layout with static scales for that tensor): the same
+ *   record without word 0, W - 1 = ceil(r*b/32) words; min and step are the
+ *   head's fixed values and code_j = clamp(round_half_even((c_j - min)/step),
+ *   0, 2^b - 1).  [KV-COBRA project page, "How KV-COBRA Works", Hadamard
+ *   rotation: one uniform quantizer per head suffices; abstract: no per-token
+ *   overhead]
  *
  * Cache layout (one flat uint32 array per tensor, K and V separately):
- *   head-major regions; region h holds batch x capacity records of W_h words;
+ *   head-major regions; region h holds batch x capacity records of W_h words
+ *   (one word fewer for header-free records);
  *   record (h, b, t) starts at word  sum_{h'<h} batch*capacity*W_h'  +  (b*capacity + t)*W_h.
  *
  * Basis layout: the heads' bases concatenated, head h is a row-major
@@ -69,12 +76,15 @@ typedef enum kv_status {
 
 typedef enum kv_dtype { KV_F32 = 0, KV_F16 = 1 } kv_dtype;
 
-/* Shape and per-head allocation of one layer's compressed cache.  The four
- * allocation arrays are HOST memory with n_kv_heads entries each; they are
- * read during the call only.  Query head h' reads KV head h'/g (g =
+/* Shape and per-head allocation of one layer's compressed cache.  The
+ * allocation and scale arrays are HOST memory with n_kv_heads entries each;
+ * they are read during the call only.  Query head h' reads KV head h'/g (g =
  * n_q_heads / n_kv_heads, contiguous groups).  Per-head (rank, bits) is the
  * allocation a calibration step (for example the C1 search of the KV-COBRA
- * page) chose; the library takes it as given. */
+ * page) chose; the library takes it as given.  scale_k / scale_v: NULL for
+ * records with per-token headers, else the head's fixed quantizer for
+ * header-free records of that tensor, fp16 bits of min | fp16 bits of step
+ * << 16 (finite, step > 0), also chosen at calibration. */
 typedef struct kv_layout {
   int32_t head_dim;       /* d; must be 128 */
   int32_t n_kv_heads;
@@ -85,9 +95,12 @@ typedef struct kv_layout {
   const int32_t *bits_k;  /* HOST [n_kv_heads] */
   const int32_t *rank_v;  /* HOST [n_kv_heads] */
   const int32_t *bits_v;  /* HOST [n_kv_heads] */
+  const uint32_t *scale_k; /* HOST [n_kv_heads] or NULL */
+  const uint32_t *scale_v; /* HOST [n_kv_heads] or NULL */
 } kv_layout;
 
-/* Words per record, 1 + ceil(rank*bits/32); 0 if (rank, bits) is unsupported. */
+/* Words per record with its header, 1 + ceil(rank*bits/32) (a header-free
+ * record has one word fewer); 0 if (rank, bits) is unsupported. */
 int32_t kv_record_words(int32_t rank, int32_t bits);
 
 /* Bytes of the K (which = 0) or V (which = 1) cache of `layout`, written to *bytes (HOST). */
@@ -230,6 +243,21 @@ kv_status kv_append_attend_decode_noalloc(const kv_layout *layout, const void *k
                                           int64_t n_tokens, int64_t split_tokens, const float *basis_k,
                                           const float *basis_v, uint32_t *cache_k, uint32_t *cache_v,
                                           float softmax_scale, float *out, void *stream);
+
+/* Reconstruct stored tokens: for records pos0 .. pos0+n_tokens-1 of every
+ * (sequence, KV head) of tensor `which` (0 = K, 1 = V), x^ = P (min + step *
+ * code) with P that head's basis (`basis`: the tensor's concatenated bases),
+ * each coordinate dequantized exactly and the d outputs summed in float32 over
+ * the coordinates in order.  out: DEVICE float32 [batch][n_kv_heads][n_tokens]
+ * [head_dim].  Not on the decode path (attention reads the codes directly):
+ * for measuring distortion and for consumers that need the vectors.
+ * Errors: KV_ERR_CAPACITY if pos0 < 0 or pos0 + n_tokens > capacity;
+ * KV_ERR_INVALID for NULL or misaligned pointers or which outside {0, 1};
+ * n_tokens == 0 launches nothing.
+ * [KV-COBRA project page, "How KV-COBRA Works", Inference: the inverse of the
+ *  rotation and truncation] */
+kv_status kv_decode(const kv_layout *layout, int32_t which, int64_t n_tokens, int64_t pos0,
+                    const float *basis, const uint32_t *cache, float *out, void *stream);
 
 /* Quantize and pack n tokens of r float32 coordinates each (coords [n][r])
  * into records [n][kv_record_words(r, b)].  Same device code as the encoder's

@@ -8,7 +8,7 @@ from __future__ import annotations
 import numpy as np
 
 import workloads as W
-from oracle import allocation, codec, packing, transform
+from oracle import allocation, codec, packing, quantizer, transform
 
 SCALE = 1.0 / np.sqrt(128.0)
 
@@ -47,26 +47,49 @@ def oracle_calibrate(wl: W.Workload):
     return alloc, bk, bv
 
 
-def oracle_cache(wl, alloc, bases_k, bases_v, batch, capacity, T, kv=None):
+def oracle_cache(wl, alloc, bases_k, bases_v, batch, capacity, T, kv=None, static_k=None, static_v=None):
     """Flat K and V caches (uint32) holding the oracle's records of tokens 0..T-1.
 
     kv: optional dict (tensor, b, h) -> token array [T, d] (defaults to the workload's tokens).
+    static_k / static_v: per-head (min, step) of header-free K / V records (None: per-token headers).
     """
     rk = [a[0] for a in alloc]
     bk = [a[1] for a in alloc]
     rv = [a[2] for a in alloc]
     bv = [a[3] for a in alloc]
-    ck = np.zeros(codec.region_offsets(rk, bk, batch, capacity)[-1], np.uint32)
-    cv = np.zeros(codec.region_offsets(rv, bv, batch, capacity)[-1], np.uint32)
+    fk = [static_k is not None] * len(alloc)
+    fv = [static_v is not None] * len(alloc)
+    ck = np.zeros(codec.region_offsets(rk, bk, batch, capacity, fk)[-1], np.uint32)
+    cv = np.zeros(codec.region_offsets(rv, bv, batch, capacity, fv)[-1], np.uint32)
+
+    def enc(x, P, b, st):
+        return codec.encode_tokens(x, P, b) if st is None else codec.encode_tokens_static(x, P, b, *st)
+
     for h in range(len(alloc)):
         for b in range(batch):
             xk = kv[("K", b, h)] if kv else W.tokens(wl, "K", b, h, 0, T)
             xv = kv[("V", b, h)] if kv else W.tokens(wl, "V", b, h, 0, T)
-            s0, s1, _ = codec.record_slice(rk, bk, batch, capacity, h, b, 0, T)
-            ck[s0:s1] = codec.encode_tokens(xk, bases_k[h], bk[h]).reshape(-1)
-            s0, s1, _ = codec.record_slice(rv, bv, batch, capacity, h, b, 0, T)
-            cv[s0:s1] = codec.encode_tokens(xv, bases_v[h], bv[h]).reshape(-1)
+            s0, s1, _ = codec.record_slice(rk, bk, batch, capacity, h, b, 0, T, fk)
+            ck[s0:s1] = enc(xk, bases_k[h], bk[h], None if static_k is None else static_k[h]).reshape(-1)
+            s0, s1, _ = codec.record_slice(rv, bv, batch, capacity, h, b, 0, T, fv)
+            cv[s0:s1] = enc(xv, bases_v[h], bv[h], None if static_v is None else static_v[h]).reshape(-1)
     return ck, cv
+
+
+def oracle_static_scales(covs, bases, bits):
+    """Each head's fixed (min, step) for header-free records: the oracle's static_scale of
+    the retained coordinates' common standard deviation sqrt(trace(P^T Sigma P) / r)."""
+    out = []
+    for cov, P, b in zip(covs, bases, bits):
+        P = np.asarray(P, np.float64)
+        s = float(np.sqrt(np.trace(P.T @ np.asarray(cov, np.float64) @ P) / P.shape[1]))
+        out.append(quantizer.static_scale(s, b))
+    return out
+
+
+def scale_words(static):
+    """(min, step) pairs -> the layout's 32-bit words (fp16 min | fp16 step << 16)."""
+    return [int(quantizer.fp16_bits(mu)) | (int(quantizer.fp16_bits(sg)) << 16) for mu, sg in static]
 
 
 # A code may differ from the oracle's only where the two float64 projections (the
@@ -114,6 +137,18 @@ def compare_records(got, ref, r, b, what, x=None, P=None):
     hdr_bad = int(((g_mu != r_mu) | (g_sg != r_sg)).sum())
     assert hdr_bad == 0, f"{what}: {hdr_bad} headers differ"
     n_diff = classify_ties(x, P, r_mu, r_sg, g_c, r_c, what)
+    frac = n_diff / g_c.size if g_c.size else 0.0
+    assert frac <= TIE_FRACTION, f"{what}: {frac:.2e} of codes differ"
+    return frac
+
+
+def compare_static_records(got, ref, r, b, mu, sg, what, x=None, P=None):
+    """Header-free records: every differing code a classified rounding tie (as in
+    compare_records, with the head's fixed min and step), at most TIE_FRACTION of them."""
+    g_c = packing.unpack_codes(got, r, b)
+    r_c = packing.unpack_codes(ref, r, b)
+    n = len(g_c)
+    n_diff = classify_ties(x, P, np.full(n, mu), np.full(n, sg), g_c, r_c, what)
     frac = n_diff / g_c.size if g_c.size else 0.0
     assert frac <= TIE_FRACTION, f"{what}: {frac:.2e} of codes differ"
     return frac

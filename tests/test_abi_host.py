@@ -202,3 +202,48 @@ def test_pack_validation():
     assert L.kv_quantize_pack(0, 0, 16, 4, 0, None) == lib_mod.KV_OK
     assert L.kv_unpack(16, 10, 16, 4, 0, 16, None) == lib_mod.KV_ERR_INVALID
     assert L.kv_unpack(16, 10, 20, 4, 16, 16, None) == lib_mod.KV_ERR_UNSUPPORTED
+
+
+def test_header_free_cache_bytes_match_the_oracle_layout():
+    """Static scales drop the header word of every record of that tensor."""
+    alloc = [(16, 4, 32, 4), (128, 2, 64, 4), (32, 8, 16, 6)]
+    word = 0x3C00 | (0x2E66 << 16)  # min 1.0, step 0.1 (fp16 bits)
+    lay = lib_mod.Layout(3, 12, 2, 1000, alloc, scale_k=[word] * 3)
+    rk, bk, rv, bv = zip(*alloc)
+    assert lib_mod.kv_cache_bytes(lay, 0) == 4 * codec.region_offsets(rk, bk, 2, 1000, [True] * 3)[-1]
+    assert lib_mod.kv_cache_bytes(lay, 1) == 4 * codec.region_offsets(rv, bv, 2, 1000)[-1]
+
+
+@pytest.mark.parametrize("bad", [0x7C00 | (0x2E66 << 16),   # infinite min
+                                 0x3C00 | (0x7C00 << 16),   # infinite step
+                                 0x3C00,                    # zero step
+                                 0x3C00 | (0xAE66 << 16)])  # negative step
+def test_invalid_static_scales_are_rejected(bad):
+    lay = lib_mod.Layout(3, 12, 2, 1000, [(16, 4, 32, 4)] * 3, scale_v=[0x3C00 | (0x2E66 << 16), bad, 0x3C00 | (0x2E66 << 16)])
+    with pytest.raises(lib_mod.KvError) as e:
+        lib_mod.kv_cache_bytes(lay, 0)
+    assert e.value.status == lib_mod.KV_ERR_INVALID
+    assert "static value scale" in str(e.value)
+
+
+def test_decode_validation_happens_before_launch():
+    lay = _layout()
+    ref = lay.ref()
+    assert L.kv_decode(ref, 2, 10, 0, 16, 16, 16, None) == lib_mod.KV_ERR_INVALID       # which
+    assert L.kv_decode(ref, 0, 10, 995, 16, 16, 16, None) == lib_mod.KV_ERR_CAPACITY    # past the capacity
+    assert L.kv_decode(ref, 0, 10, -1, 16, 16, 16, None) == lib_mod.KV_ERR_CAPACITY
+    assert L.kv_decode(ref, 1, 10, 0, 0, 16, 16, None) == lib_mod.KV_ERR_INVALID        # NULL basis
+    assert L.kv_decode(ref, 1, 10, 0, 16, 18, 16, None) == lib_mod.KV_ERR_INVALID       # misaligned cache
+    assert L.kv_decode(ref, 1, 0, 0, 0, 0, 0, None) == lib_mod.KV_OK                    # nothing to do
+
+
+def test_noalloc_refuses_oversize_requests_before_any_device_call():
+    """The allocation-free step checks its static scratch limits on the host first."""
+    lay = lib_mod.Layout(8, 128, 32, 9000, [(64, 4, 64, 4)] * 8)
+    f16 = lib_mod.KV_F16
+    st = L.kv_append_attend_decode_noalloc(lay.ref(), 16, 16, f16, 16, f16, 8192, 256, 16, 16, 16, 16, 0.1, 16, None)
+    assert st == lib_mod.KV_ERR_CAPACITY
+    assert "static scratch" in L.kv_last_error().decode()
+    big = lib_mod.Layout(64, 64, 65, 16, [(16, 4, 16, 4)] * 64)
+    st = L.kv_append_attend_decode_noalloc(big.ref(), 16, 16, f16, 16, f16, 16, 0, 16, 16, 16, 16, 0.1, 16, None)
+    assert st == lib_mod.KV_ERR_CAPACITY

@@ -121,3 +121,22 @@ def test_frozen_c2_kernel_class_matches_the_calibration():
         lambda h, r: W.hadamard_signs(wl, "K", h, r), lambda h, r: W.hadamard_signs(wl, "V", h, r),
         wl.allocation, [W.query_covariance(wl, h) for h in range(n)])
     assert sorted(set(alloc)) == sorted(set(listed))
+
+
+def test_static_scale_word_matches_the_oracle():
+    """The product's fixed quantizer of header-free records (golden-section clip) against
+    the oracle's (scanned clip, same reading), as fp16 bits, on generated heads."""
+    import workloads as W
+    from decode_attention_04_amd import calib
+    from oracle import quantizer, transform
+
+    wl = W.llama_t128k(0.5)
+    for h in range(4):
+        cov = W.covariance(wl, "K", h)
+        _, vecs = transform.eigenbasis(cov)
+        for r, b in ((16, 4), (32, 2), (64, 8)):
+            P = transform.folded_basis(vecs, r, W.hadamard_signs(wl, "K", h, r)).astype(np.float32)
+            s = float(np.sqrt(np.trace(P.astype(np.float64).T @ cov @ P.astype(np.float64)) / r))
+            mu, sg = quantizer.static_scale(s, b)
+            word = int(quantizer.fp16_bits(mu)) | (int(quantizer.fp16_bits(sg)) << 16)
+            assert calib.static_scale_word(cov, P, b) == word, (h, r, b)

@@ -94,12 +94,13 @@ def llama_t128k(bpd: float) -> Workload:
         note="C1 with attention-KL key weights from generated query variances")
 
 
-def llama_t128k_c2(bpd: float) -> Workload:
-    """The 128K LLaMA-shaped layer (same generated data) with the budget shared across heads."""
+def llama_t128k_c2(bpd: float, pool: str = "split") -> Workload:
+    """The 128K LLaMA-shaped layer (same generated data) with the budget shared across heads:
+    among the K heads and among the V heads ("split"), or among all of them ("joint")."""
     return dataclasses.replace(
-        llama_t128k(bpd), name=f"llama8b-layer-B4-T128K-{bpd:g}bpd-c2",
-        allocation=("c2", float(bpd), "kl", "split"),
-        note="C2 across the K heads and across the V heads, attention-KL key weights")
+        llama_t128k(bpd), name=f"llama8b-layer-B4-T128K-{bpd:g}bpd-c2" + ("" if pool == "split" else "-joint"),
+        allocation=("c2", float(bpd), "kl", pool),
+        note=f"C2 across the heads ({pool} K/V pools), attention-KL key weights")
 
 
 def llama_prefill(rank: int, bits: int) -> Workload:
