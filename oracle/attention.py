@@ -39,22 +39,28 @@ def attend_coords(q, basis_k, ck, basis_v, cv, scale: float) -> np.ndarray:
     return np.asarray(basis_v, np.float64) @ ot
 
 
-def attend_head_records(qs, basis_k, rec_k, rk, bk, basis_v, rec_v, rv, bv, scale, static_k=None, static_v=None):
+def attend_head_records(qs, basis_k, rec_k, rk, bk, basis_v, rec_v, rv, bv, scale, static_k=None, static_v=None,
+                        query_basis=None):
     """Query heads qs [g, d] of one KV head over its records [T, W] -> [g, d].
 
-    static_k / static_v: the head's fixed (min, step) when its records are header-free."""
+    static_k / static_v: the head's fixed (min, step) when its records are header-free.
+    query_basis: the d x r_K basis that projects the query when it is not the encode
+    basis itself (a non-orthogonal key transform: the keys are reconstructed as
+    query_basis @ c^, so q . k^ = (query_basis^T q) . c^)."""
     ck = decode_records(rec_k, rk, bk) if static_k is None else decode_records_static(rec_k, rk, bk, *static_k)
     cv = decode_records(rec_v, rv, bv) if static_v is None else decode_records_static(rec_v, rv, bv, *static_v)
-    return np.stack([attend_coords(q, basis_k, ck, basis_v, cv, scale) for q in np.atleast_2d(qs)])
+    qb = basis_k if query_basis is None else query_basis
+    return np.stack([attend_coords(q, qb, ck, basis_v, cv, scale) for q in np.atleast_2d(qs)])
 
 
 def attend_cache(q, bases_k, bases_v, cache_k, cache_v, alloc, batch, capacity, T, scale,
-                 static_k=None, static_v=None):
+                 static_k=None, static_v=None, query_bases=None):
     """Full decode attention: q [B, Hq, d] over records 0..T-1 of every head -> [B, Hq, d].
 
     ``alloc`` lists (r_K, b_K, r_V, b_V) per KV head; ``bases_k/v`` list the
     d x r bases; ``cache_k/v`` are the flat uint32 caches in the head-major layout.
     static_k / static_v: per-head fixed (min, step) of header-free K / V records (or None).
+    query_bases: per-head query-side key bases of a non-orthogonal key transform (or None).
     """
     from .codec import record_slice
 
@@ -78,6 +84,7 @@ def attend_cache(q, bases_k, bases_v, cache_k, cache_v, alloc, batch, capacity, 
             out[b, h * g:(h + 1) * g] = attend_head_records(
                 q[b, h * g:(h + 1) * g], bases_k[h], recs_k, rk[h], bk[h],
                 bases_v[h], recs_v, rv[h], bv[h], scale,
-                None if static_k is None else static_k[h], None if static_v is None else static_v[h])
+                None if static_k is None else static_k[h], None if static_v is None else static_v[h],
+                None if query_bases is None else query_bases[h])
     return out
 

@@ -80,3 +80,51 @@ def basis_for_head(cov, r, signs, query_cov=None) -> np.ndarray:
     """Full calibration of one head for a given rank: ordered eigenbasis, then the fold."""
     _, vecs = ordered_basis(cov, query_cov)
     return folded_basis(vecs, r, signs)
+
+
+# ---------------------------------------------------------------- attention-aware key transform (NOVA-KV)
+# NOVA-KV abstract and the pith.science verdict on it (key_machinery, core_discovery):
+# with M_q the second moment of the queries and S_k that of the keys, the key
+# transform R_K = M_q^(1/2) E, E the eigenbasis of M_q^(1/2) S_k M_q^(1/2), is not
+# orthogonal; R_K R_K^T = M_q, so coefficients r = R_K^T k turn the query-weighted
+# key error into plain squared error (generalized Parseval:
+# ||r - r^||^2 = (k - k^)^T M_q (k - k^)).  The inverse transform is folded into the
+# query: q . k^ = (R_K^-1 q) . r^.  Readings: E sorted by decreasing eigenvalue
+# (energy compaction); rank truncation keeps the first r coefficients, the key then
+# reconstructed as k^ = R_K^-T [r^; 0]; a random-sign Hadamard may be folded on the
+# right of both the encode basis P_K = (M_q^(1/2) E)_r and the query basis
+# Q_K = (M_q^(-1/2) E)_r (it leaves P_K^T Q_K = I_r).
+
+
+def psd_sqrt(m: np.ndarray, inverse: bool = False) -> np.ndarray:
+    """Symmetric square root (or its inverse) of a symmetric positive definite matrix."""
+    w, v = np.linalg.eigh(np.asarray(m, np.float64))
+    if w.min() <= 0:
+        raise ValueError("matrix is not positive definite")
+    s = np.sqrt(w)
+    return (v * (1.0 / s if inverse else s)[None, :]) @ v.T
+
+
+def nova_key_transform(query_moment: np.ndarray, key_moment: np.ndarray):
+    """(weights, R_K, E): E the eigenvectors of M_q^(1/2) S_k M_q^(1/2) by decreasing
+    eigenvalue (the weights: the coefficients' variances), R_K = M_q^(1/2) E."""
+    mh = psd_sqrt(query_moment)
+    w, e = eigenbasis(mh @ np.asarray(key_moment, np.float64) @ mh)
+    return w, mh @ e, e
+
+
+def nova_key_bases(query_moment, key_moment, r: int, signs=None):
+    """(P_K, Q_K), each d x r: encode basis (M_q^(1/2) E)_r and query basis (M_q^(-1/2) E)_r,
+    with the random-sign Hadamard D_s H_r / sqrt(r) folded on the right of both when
+    `signs` is given."""
+    _, _, e = nova_key_transform(query_moment, key_moment)
+    er = e[:, :r]
+    p = psd_sqrt(query_moment) @ er
+    q = psd_sqrt(query_moment, inverse=True) @ er
+    if signs is not None:
+        s = np.asarray(signs, np.float64)
+        if s.shape != (r,) or not np.all(np.abs(s) == 1.0):
+            raise ValueError("signs must be r values in {-1, +1}")
+        fold = s[:, None] * sylvester_hadamard(r) / np.sqrt(r)
+        p, q = p @ fold, q @ fold
+    return p, q

@@ -532,3 +532,142 @@ def test_header_free_region_offsets():
     assert off.tolist() == [0, 2 * 10 * 2, 2 * 10 * 2 + 2 * 10 * 9]
     s0, s1, w = codec.record_slice(ranks, bits, 2, 10, 0, 1, 3, 5, [True, False])
     assert (s0, s1, w) == (10 * 2 + 3 * 2, 10 * 2 + 5 * 2, 2)
+
+
+# ------------------------------------------------------------------ distortion against bits
+@pytest.mark.parametrize("b", [6, 7, 8])
+def test_quantization_noise_is_step_squared_over_12_at_high_resolution(b):
+    """The per-coordinate quantization noise of the deployed quantizer on a generated
+    head at full rank follows the high-resolution form behind q(b): for fine grids each
+    coordinate's error is uniform over one step, so sum_j (c_j - c^_j)^2 averages
+    r step_t^2 / 12 with each token's own step (within 2%)."""
+    wl = W.LLAMA_256_HEADS
+    x = W.tokens(wl, "K", 0, 17, 0, 4096).astype(np.float64)
+    _, vecs = transform.ordered_basis(W.covariance(wl, "K", 17))
+    P = transform.folded_basis(vecs, 128, W.hadamard_signs(wl, "K", 17, 128))
+    c = x @ P
+    mu, sg, codes = quantizer.quantize(c, b)
+    noise = ((c - quantizer.dequantize(mu, sg, codes)) ** 2).sum(axis=1).mean()
+    assert abs(noise / (128 * np.mean(sg ** 2) / 12) - 1.0) < 0.02
+
+
+def test_full_rank_distortion_falls_by_about_four_per_bit():
+    """Full rank removes the truncation term of D(r, b), and the quantization distortion
+    falls by 2^2 per added bit in the q(b) = 2^(-2b) / 12 model; the deployed endpoint grid
+    has step = range / (2^b - 1), so with the per-token range fixed the ratio
+    D(b) / D(b + 1) is ((2^(b+1) - 1) / (2^b - 1))^2 = 4 ((2^(b+1) - 1) / (2 (2^b - 1)))^2,
+    which tends to 4 from above (5.44 at b = 2): the measured ratios lie in [4, that]
+    up to 3%."""
+    wl = W.LLAMA_256_HEADS
+    x = W.tokens(wl, "V", 0, 40, 0, 4096).astype(np.float64)
+    _, vecs = transform.ordered_basis(W.covariance(wl, "V", 40))
+    P = transform.folded_basis(vecs, 128, W.hadamard_signs(wl, "V", 40, 128))
+    d = []
+    for b in range(2, 9):
+        rec = codec.encode_tokens(x, P, b)
+        d.append(((x - codec.decode_records(rec, 128, b) @ P.T) ** 2).sum() / (x ** 2).sum())
+    for b, (d0, d1) in enumerate(zip(d[:-1], d[1:]), start=2):
+        hi = 4.0 * (((1 << (b + 1)) - 1) / (2.0 * ((1 << b) - 1))) ** 2
+        assert 4.0 * 0.97 < d0 / d1 < hi * 1.03, (b, d0 / d1, hi)
+
+
+# ------------------------------------------------------------------ attention-aware key transform (NOVA-KV)
+def _nova_head(seed=3):
+    wl = W.llama_t128k(2.0)
+    return W.query_covariance(wl, seed % 8), W.covariance(wl, "K", seed % 8)
+
+
+def test_nova_transform_reproduces_the_query_moment():
+    """R_K R_K^T = M_q (the defining property of the attention-preserving transform)."""
+    mq, sk = _nova_head()
+    _, R, E = transform.nova_key_transform(mq, sk)
+    assert np.allclose(R @ R.T, mq, rtol=1e-10, atol=1e-12 * np.abs(mq).max())
+    assert np.allclose(E.T @ E, np.eye(128), atol=1e-12)
+
+
+def test_nova_generalized_parseval():
+    """||R_K^T (k - k^)||^2 = (k - k^)^T M_q (k - k^) for arbitrary key errors: squared
+    error of the coefficients is the query-weighted key error (the orientation R^T,
+    not R, is what makes it hold)."""
+    mq, sk = _nova_head(5)
+    _, R, _ = transform.nova_key_transform(mq, sk)
+    rng = np.random.default_rng(1)
+    for _ in range(5):
+        e = rng.standard_normal(128)
+        assert np.isclose(np.sum((R.T @ e) ** 2), e @ mq @ e, rtol=1e-10)
+    e = rng.standard_normal(128)
+    assert not np.isclose(np.sum((R @ e) ** 2), e @ mq @ e, rtol=1e-3)
+
+
+def test_nova_coefficients_are_decorrelated_and_ordered():
+    """The coefficients r = R_K^T k have covariance E^T M^(1/2) S_k M^(1/2) E: diagonal,
+    equal to the returned weights in decreasing order."""
+    mq, sk = _nova_head(2)
+    w, R, _ = transform.nova_key_transform(mq, sk)
+    c = R.T @ sk @ R
+    assert np.allclose(c, np.diag(w), atol=1e-10 * w.max())
+    assert np.all(np.diff(w) <= 0)
+
+
+@pytest.mark.parametrize("r", [16, 64, 128])
+def test_nova_bases_are_biorthogonal(r):
+    mq, sk = _nova_head(4)
+    P, Q = transform.nova_key_bases(mq, sk, r, W.random_basis_signs(9, r))
+    assert np.allclose(P.T @ Q, np.eye(r), atol=1e-10)
+    if r == 128:
+        assert np.allclose(Q @ P.T, np.eye(128), atol=1e-9)
+
+
+def test_nova_full_rank_unquantized_is_exact_attention():
+    """Full rank, keys and values carried without quantization: folding Q_K into the
+    query gives exactly softmax(q K^T / sqrt(d)) V."""
+    mq, sk = _nova_head(6)
+    P, Q = transform.nova_key_bases(mq, sk, 128, W.random_basis_signs(2, 128))
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((200, 128))
+    v = rng.standard_normal((200, 128))
+    qv = rng.standard_normal(128)
+    got = attention.attend_coords(qv, Q, k @ P, np.eye(128), v, 1 / np.sqrt(128))
+    s = k @ qv / np.sqrt(128)
+    p = np.exp(s - s.max())
+    assert np.allclose(got, (p / p.sum()) @ v, rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("r", [16, 32, 64])
+def test_nova_truncation_minimises_query_weighted_error(r):
+    """Low rank (no quantization): the query-weighted key error of the transform,
+    E (q . (k - k^))^2 = tr(M_q (I - Q P^T) S_k (I - Q P^T)^T), equals the sum of the
+    discarded weights, and no orthonormal truncation of the same rank (the key
+    covariance's own eigenbasis, or the one ordered by attention-KL weights) does better."""
+    mq, sk = _nova_head(7)
+    w, _, _ = transform.nova_key_transform(mq, sk)
+    P, Q = transform.nova_key_bases(mq, sk, r)
+    A = np.eye(128) - Q @ P.T
+    err = np.trace(mq @ A @ sk @ A.T)
+    assert np.isclose(err, w[r:].sum(), rtol=1e-9)
+    for qc in (None, mq):
+        _, vec = transform.ordered_basis(sk, qc)
+        B = np.eye(128) - vec[:, :r] @ vec[:, :r].T
+        assert err <= np.trace(mq @ B @ sk @ B.T) * (1 + 1e-12)
+
+
+def test_attention_with_a_query_basis_reconstructs_keys_through_it():
+    """attend_head_records with a separate query basis equals attention over the keys
+    reconstructed as Q c^ (and the values as P_V c^_V), written out directly."""
+    mq, sk = _nova_head(1)
+    r = 32
+    P, Q = transform.nova_key_bases(mq, sk, r, W.random_basis_signs(5, r))
+    Pv = transform.folded_basis(np.linalg.qr(np.random.default_rng(2).standard_normal((128, 128)))[0], 16,
+                                W.random_basis_signs(6, 16))
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((300, 128))
+    xv = rng.standard_normal((300, 128))
+    rk = codec.encode_tokens(x, P, 4)
+    rv = codec.encode_tokens(xv, Pv, 6)
+    qs = rng.standard_normal((3, 128))
+    got = attention.attend_head_records(qs, P, rk, r, 4, Pv, rv, 16, 6, 0.1, query_basis=Q)
+    kh = codec.decode_records(rk, r, 4) @ Q.T
+    vh = codec.decode_records(rv, 16, 6) @ Pv.T
+    s = qs @ kh.T * 0.1
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    assert np.allclose(got, (p / p.sum(axis=1, keepdims=True)) @ vh, rtol=1e-10, atol=1e-12)

@@ -118,6 +118,14 @@ QWEN_T128K = Workload(
     encode_tokens=4096,
     note="heads 0-1 full rank r=128 b=2, heads 2-3 r=16 b=6; Student-t outlier channels")
 
+# 256 KV heads shaped like those of the whole LLaMA-3.1-8B model (32 layers x 8 KV
+# heads), for the distortion-rate characterisation: each head its own seeded
+# spectrum exponent and outlier channels, as in the layer workloads.
+LLAMA_256_HEADS = Workload(
+    name="llama8b-256-kv-heads", wid=5, batch=1, n_q_heads=256, n_kv_heads=256, head_dim=128,
+    context=4096, dtype="f16", alpha=(1.0, 2.5), allocation=("c1", 2.0, "mse"),
+    note="32 layers x 8 KV heads; distortion against bits per coordinate")
+
 ALL_BUDGETS = (0.5, 1.0, 2.0, 4.0)
 C1_RANKS = (16, 32, 64, 128)
 
