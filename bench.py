@@ -53,7 +53,16 @@ def pick_workload(name: str) -> W.Workload:
 
 
 def calibrate(wl: W.Workload):
+    """(allocation, key bases, value bases) of every KV head; with the attention-aware key
+    transform each key entry is the head's flat [P_K; Q_K] block."""
     from decode_attention_04_amd import calib
+
+    if wl.allocation[0] == "nova":
+        out = [calib.calibrate_head_nova(W.covariance(wl, "K", h), W.covariance(wl, "V", h), W.query_covariance(wl, h),
+                                         lambda r, h=h: W.hadamard_signs(wl, "K", h, r),
+                                         lambda r, h=h: W.hadamard_signs(wl, "V", h, r), wl.allocation[1],
+                                         head_dim=wl.head_dim) for h in range(wl.n_kv_heads)]
+        return [o[0] for o in out], [o[1] for o in out], [o[2] for o in out]
 
     if wl.allocation[0] == "c2":
         n = wl.n_kv_heads
@@ -82,7 +91,8 @@ def step_bytes(wl, alloc, T, static=False):
     B, hq, d = wl.batch, wl.n_q_heads, wl.head_dim
     esz = 4 if wl.dtype == "f32" else 2
     rec = sum(4 * (kv_record_words(a[0], a[1]) + kv_record_words(a[2], a[3]) - (2 if static else 0)) for a in alloc)
-    basis = sum(4 * d * (a[0] + a[2]) for a in alloc)
+    nk = 2 if wl.allocation[0] == "nova" else 1  # the attention-aware transform reads P_K and Q_K
+    basis = sum(4 * d * (nk * a[0] + a[2]) for a in alloc)
     attend = B * T * rec + B * hq * d * esz + basis + B * hq * d * 4
     append = B * wl.n_kv_heads * 2 * d * esz + B * rec + basis
     return attend, append
@@ -150,7 +160,7 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
     if static:
         scales = {"scale_k": [calib.static_scale_word(W.covariance(wl, "K", h), bk[h], alloc[h][1]) for h in range(H)],
                   "scale_v": [calib.static_scale_word(W.covariance(wl, "V", h), bv[h], alloc[h][3]) for h in range(H)]}
-    lay = K.Layout(H, hq, B, T, alloc, **scales)
+    lay = K.Layout(H, hq, B, T, alloc, **scales, query_basis_k=wl.allocation[0] == "nova")
     dev = torch.device("cuda:0")
     pk = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bk])).to(dev)
     pv = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bv])).to(dev)
@@ -201,9 +211,101 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
     extra = {"lengths": lens, "step": "kv_attend_decode_ragged (no append)"} if ragged else {}
     if static:
         extra["records"] = "header-free (one fixed quantizer per head)"
+    kclass = K.kv_attend_plan(lay, T)[0]
     return {**extra, "batch": B, "n_q_heads": hq, "n_kv_heads": H, "context_tokens": T,
-            "allocation": [list(a) for a in alloc], "us_per_step": round(us, 2), "GB_per_s": round(gbs, 1),
+            "allocation": [list(a) for a in alloc],
+            "kernel": "generic" if kclass < 0 else (f"budget class {kclass}" if kclass < 6 else "frozen layout class"),
+            "us_per_step": round(us, 2), "GB_per_s": round(gbs, 1),
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "layer_caches_rotated": n_rep}
+
+
+def measure_distortion(K, wl, heads, n_tokens, formats, static=False):
+    """Relative reconstruction distortion sum_t ||x_t - x^_t||^2 / sum_t ||x_t||^2 of KV heads
+    `heads` of `wl` (keys and values, the first n_tokens of sequence 0), at each (rank,
+    bits) of `formats`, for records the library writes (kv_encode) and reconstructs
+    (kv_decode) on the GPU.  Bases: the MSE-ordered eigenvectors of each head's
+    covariance with the seeded Hadamard signs folded in; static: header-free records with
+    each head's fixed quantizer.  Returns {(head, tensor, (rank, bits)): D}."""
+    import torch
+
+    from decode_attention_04_amd import calib
+
+    dev = torch.device("cuda:0")
+    n = len(heads)
+    x = {t: torch.from_numpy(np.stack([W.tokens(wl, t, 0, h, 0, n_tokens, wl.dtype) for h in heads])[None]).to(dev)
+         for t in "KV"}
+    energy = {t: (x[t].double() ** 2).sum(dim=(0, 2, 3)) for t in "KV"}
+    dirs = {t: [calib.sorted_directions(W.covariance(wl, t, h))[1] for h in heads] for t in "KV"}
+    out = {}
+    for r, b in formats:
+        bases = {t: [calib.fold(dirs[t][i], r, W.hadamard_signs(wl, t, h, r)) for i, h in enumerate(heads)]
+                 for t in "KV"}
+        scales = {}
+        if static:
+            scales = {f"scale_{t.lower()}": [calib.static_scale_word(W.covariance(wl, t, h), bases[t][i], b)
+                                             for i, h in enumerate(heads)] for t in "KV"}
+        lay = K.Layout(n, n, 1, n_tokens, [(r, b, r, b)] * n, **scales)
+        pd = {t: torch.from_numpy(calib.concat(bases[t])).to(dev) for t in "KV"}
+        ck = torch.empty(K.kv_cache_bytes(lay, 0) // 4, dtype=torch.int32, device=dev)
+        cv = torch.empty(K.kv_cache_bytes(lay, 1) // 4, dtype=torch.int32, device=dev)
+        K.kv_encode(lay, x["K"], x["V"], n_tokens, 0, pd["K"], pd["V"], ck, cv)
+        for which, t, cache in ((0, "K", ck), (1, "V", cv)):
+            rec = torch.empty((1, n, n_tokens, wl.head_dim), dtype=torch.float32, device=dev)
+            K.kv_decode(lay, which, n_tokens, 0, pd[t], cache, rec)
+            err = ((x[t].double() - rec.double()) ** 2).sum(dim=(0, 2, 3)) / energy[t]
+            for i, h in enumerate(heads):
+                out[(h, t, (r, b))] = float(err[i])
+    return out
+
+
+def distortion_rate(K, wl=None, tokens=4096):
+    """Distortion against bits on 256 synthetic KV heads shaped like the whole LLaMA-3.1-8B
+    model's (32 layers x 8), measured on the library's own records: the relative
+    reconstruction distortion at full rank for b = 2..8 (quantization alone) with
+    per-token headers and header-free, the rate exponent alpha of D ~ 2^(-alpha b)
+    fitted per head (least squares of -log2 D over b = 2..8, and from b = 2 to 3), the
+    allocation model's D(r, b) = (sum_{i>r} lam_i + q(b) sum_{i<=r} lam_i) / sum lam
+    beside it, and the spread max/min of the per-head distortion at the uniform 2
+    bits/dim formats (128, 2), (64, 4), (32, 8)."""
+    wl = wl or W.LLAMA_256_HEADS
+    bits = list(range(2, 9))
+    full = [(128, b) for b in bits]
+    uni = [(128, 2), (64, 4), (32, 8)]
+    D, Ds = {}, {}
+    for l0 in range(0, wl.n_kv_heads, 8):
+        heads = list(range(l0, min(l0 + 8, wl.n_kv_heads)))
+        D.update(measure_distortion(K, wl, heads, tokens, full + uni[1:]))
+        Ds.update(measure_distortion(K, wl, heads, tokens, full, static=True))
+    H = wl.n_kv_heads
+
+    def exponents(src, t):
+        y = np.array([[-np.log2(src[(h, t, (128, b))]) for b in bits] for h in range(H)])
+        slope = np.polyfit(np.array(bits, np.float64), y.T, 1)[0]
+        local = y[:, 1] - y[:, 0]
+        return {"fit_b2_to_b8_mean": round(float(slope.mean()), 3), "fit_min": round(float(slope.min()), 3),
+                "fit_max": round(float(slope.max()), 3), "b2_to_b3_mean": round(float(local.mean()), 3)}
+
+    def model(t, r, b):
+        lam = np.array([np.sort(np.linalg.eigvalsh(W.covariance(wl, t, h)))[::-1] for h in range(H)])
+        return float(np.mean((lam[:, r:].sum(1) + 2.0 ** (-2 * b) / 12 * lam[:, :r].sum(1)) / lam.sum(1)))
+
+    rep = {"workload": wl.name, "heads": H, "tokens_per_head": tokens,
+           "bits": bits,
+           "full_rank_mean_D": {t: [float(np.mean([D[(h, t, (128, b))] for h in range(H)])) for b in bits]
+                                for t in "KV"},
+           "full_rank_mean_D_header_free": {t: [float(np.mean([Ds[(h, t, (128, b))] for h in range(H)]))
+                                                for b in bits] for t in "KV"},
+           "model_full_rank_D": {t: [model(t, 128, b) for b in bits] for t in "KV"},
+           "rate_exponent": {t: exponents(D, t) for t in "KV"},
+           "rate_exponent_header_free": {t: exponents(Ds, t) for t in "KV"},
+           "spread_uniform_2bpd": {}}
+    for r, b in uni:
+        rep["spread_uniform_2bpd"][f"r{r}b{b}"] = {
+            t: {"max_over_min": round(max(D[(h, t, (r, b))] for h in range(H)) /
+                                      min(D[(h, t, (r, b))] for h in range(H)), 2),
+                "mean_D": float(np.mean([D[(h, t, (r, b))] for h in range(H)])),
+                "model_mean_D": model(t, r, b)} for t in "KV"}
+    return rep
 
 
 def _cpu_workers() -> int:
@@ -302,6 +404,110 @@ def cpu_baseline(wl, alloc, bk, bv, T):
     }
 
 
+def phase_stamps(K, wl, reps=20, warmup=200, block=4096):
+    """Per-phase times of the fused decode step's workgroups, from the diagnostic build's
+    stamps (100 MHz real-time counter, 10 ns): the same launch configuration as the
+    benchmark on caches holding the workload's first `block` tokens repeated (same
+    per-token statistics), rotated over layer copies as in decode_rate.  Returns a
+    markdown summary: the launch timeline (when the last workgroup passes each phase)
+    and the per-workgroup phase durations (median, 90th percentile, maximum over the
+    workgroups, medians over `reps` launches)."""
+    import ctypes
+
+    import torch
+
+    lib = K.raw()
+    if not hasattr(lib, "kv_debug_stamps"):
+        raise SystemExit("the loaded library has no phase stamps: build it with "
+                         "`python -m decode_attention_04_amd.build --stamps` and set KVTC_LIBRARY")
+    alloc, bk, bv = calibrate(wl)
+    T = wl.context + 1
+    B, H, hq, d = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim
+    lay = K.Layout(H, hq, B, T, alloc)
+    kclass, ns, grid = K.kv_attend_plan(lay, T)
+    dev = torch.device("cuda:0")
+    pk = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bk])).to(dev)
+    pv = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bv])).to(dev)
+    reps_t = (T - 1 + block - 1) // block
+    kx = torch.from_numpy(W.kv_array(wl, "K", 0, block)).to(dev).repeat(1, 1, reps_t, 1)[:, :, :T - 1].contiguous()
+    vx = torch.from_numpy(W.kv_array(wl, "V", 0, block)).to(dev).repeat(1, 1, reps_t, 1)[:, :, :T - 1].contiguous()
+    ck = torch.zeros(K.kv_cache_bytes(lay, 0) // 4, dtype=torch.int32, device=dev)
+    cv = torch.zeros(K.kv_cache_bytes(lay, 1) // 4, dtype=torch.int32, device=dev)
+    K.kv_encode(lay, kx, vx, T - 1, 0, pk, pv, ck, cv)
+    k1, v1 = kx[:, :, -1].contiguous(), vx[:, :, -1].contiguous()
+    del kx, vx
+    n_rep = max(2, int(math.ceil(1.0e9 / ((ck.numel() + cv.numel()) * 4))))
+    caches = [(ck, cv)] + [(ck.clone(), cv.clone()) for _ in range(n_rep - 1)]
+    q = torch.from_numpy(W.query_array(wl, 0)).to(dev)
+    out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
+    ws = torch.zeros(K.kv_workspace_bytes(lay, T) // 4, dtype=torch.float32, device=dev)
+    st = torch.zeros((grid, 16), dtype=torch.int64, device=dev)
+    lib.kv_debug_stamps.restype = ctypes.c_int32
+    lib.kv_debug_stamps.argtypes = [ctypes.c_void_p]
+    scale = 1.0 / math.sqrt(d)
+    for i in range(warmup):
+        K.kv_append_attend_decode(lay, k1, v1, q, T, pk, pv, *caches[i % n_rep], scale, out, ws)
+    runs = []
+    lib.kv_debug_stamps(st.data_ptr())
+    for i in range(reps):
+        st.zero_()
+        K.kv_append_attend_decode(lay, k1, v1, q, T, pk, pv, *caches[i % n_rep], scale, out, ws)
+        torch.cuda.synchronize()
+        runs.append(st.cpu().numpy().astype(np.int64))
+    lib.kv_debug_stamps(None)
+    us = 0.01  # counter ticks (100 MHz) in microseconds
+    tl_names = ["first workgroup starts", "last workgroup starts", "last query projection done",
+                "median tile loop done (wave mean)", "last tile loop done", "last split partial stored",
+                "last arrival counted", "last split merge done"]
+    tl, ph = [], {}
+    for s_ in runs:
+        t0 = s_[:, 0].min()
+        rel = (s_ - t0) * us
+        loop_end = rel[:, 2:6]
+        tl.append([0.0, rel[:, 0].max(), rel[:, 1].max(), np.median(loop_end.mean(1)), loop_end.max(),
+                   rel[:, 6].max(), rel[:, 7].max(), rel[s_[:, 8] > 0, 8].max()])
+        durs = {
+            "start after the first workgroup": rel[:, 0],
+            "query projection (and first tile copies issued)": rel[:, 1] - rel[:, 0],
+            "tile loop, per wave": (loop_end - rel[:, 1:2]).reshape(-1),
+            "wave spread (last wave - first wave of a workgroup)": loop_end.max(1) - loop_end.min(1),
+            "wave merge, back-projection, partial stores (from the last wave)": rel[:, 6] - loop_end.max(1),
+            "arrival atomic": rel[:, 7] - rel[:, 6],
+            "split merge (merging workgroups)": (rel[:, 8] - rel[:, 7])[s_[:, 8] > 0],
+        }
+        for k, v in durs.items():
+            ph.setdefault(k, []).append((np.median(v), np.percentile(v, 90), v.max()))
+        app = s_[:, 11] > 0  # the workgroups that encode the appended token first
+        hw = s_[:, 9]
+        cu = (s_[:, 10] << 8) | ((hw >> 8) & 0xFF)  # XCC, then shader engine / array / CU bits of HW_ID
+        order = np.zeros(len(s_), np.int64)
+        for key in np.unique(cu):
+            idx = np.flatnonzero(cu == key)
+            order[idx[np.argsort(s_[idx, 0], kind="stable")]] = np.arange(len(idx))
+        extra = {
+            "appending workgroups: append encode": rel[app, 11] - rel[app, 0],
+            "appending workgroups: query projection after the append": rel[app, 1] - rel[app, 11],
+            "appending workgroups: tile loop end": loop_end[app].max(1),
+            "other workgroups: tile loop end": loop_end[~app].max(1),
+        }
+        for rank in range(int(order.max()) + 1):
+            extra[f"workgroups dispatched {rank + 1}. on their CU: tile loop, per wave"] = \
+                (loop_end[order == rank] - rel[order == rank, 1:2]).reshape(-1)
+        for k, v in extra.items():
+            if len(v):
+                ph.setdefault(k, []).append((np.median(v), np.percentile(v, 90), v.max()))
+    tl = np.median(np.array(tl), axis=0)
+    lines = [f"Workload {wl.name}: kernel class {kclass}, {grid} workgroups, {ns} splits per "
+             f"(sequence, KV head); {reps} stamped launches after {warmup} unstamped ones, medians.", "",
+             "| launch timeline (last workgroup to pass) | us after the first workgroup starts |", "|---|---:|"]
+    lines += [f"| {n} | {v:.2f} |" for n, v in zip(tl_names, tl)]
+    lines += ["", "| phase, per workgroup | median (us) | p90 (us) | max (us) |", "|---|---:|---:|---:|"]
+    for k, v in ph.items():
+        m = np.median(np.array(v), axis=0)
+        lines.append(f"| {k} | {m[0]:.2f} | {m[1]:.2f} | {m[2]:.2f} |")
+    return "\n".join(lines)
+
+
 def sources_digest() -> str:
     """sha256 over the HIP/C++ sources of the library (which code a counter profile belongs to)."""
     import hashlib
@@ -361,13 +567,23 @@ def main():
                     help="skip the decode measurements of the other layouts (128K budgets, Qwen, 32K batch 16)")
     ap.add_argument("--no-encode-rates", action="store_true",
                     help="skip the prefill encode measurements of the prefill workloads")
+    ap.add_argument("--no-distortion", action="store_true",
+                    help="skip the distortion-rate characterisation of the 256 synthetic KV heads")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a captured HIP graph per step instead of eager launches")
+    ap.add_argument("--phase-stamps", type=int, default=0, metavar="REPS",
+                    help="only run REPS launches of the decode step with the phase-stamp build "
+                         "(libkvtc_stamps.so) and print the per-phase timing summary")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 3 times (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.phase_stamps:
+        os.environ["KVTC_LIBRARY"] = os.path.join(ROOT, "decode_attention_04_amd", "libkvtc_stamps.so")
+        import decode_attention_04_amd._lib as K
+        print(phase_stamps(K, pick_workload(args.workload), reps=args.phase_stamps))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the decode step is measured on one GPU; --gpus must be 1 (a sharded layout splits the KV heads across GPUs, each running this same kernel on its share)"}))
@@ -496,6 +712,17 @@ def main():
         torch.cuda.synchronize()
         att_ms.append(e0.elapsed_time(e1) / (n_rep * 4))
     att_avg = float(np.median(att_ms))
+    # distribution of single launches: events around each of 100 launches (the events'
+    # own gaps are outside each interval)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
+    for i, (e0, e1) in enumerate(ev):
+        ck, cv = caches[i % n_rep]
+        e0.record(stream)
+        K.kv_append_attend_decode(lay, k_new, v_new, q, T + 1, pk, pv, ck, cv, scale, out, ws)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    one = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+    pct = {f"p{p}": round(float(np.percentile(one, p)), 2) for p in (10, 50, 90)}
     attend_bytes, append_bytes = step_bytes(wl, alloc, T + 1)
     gbs = (attend_bytes + append_bytes) / (ms_step * 1e-3) / 1e9
     att_gbs = (attend_bytes + append_bytes) / (att_avg * 1e-3) / 1e9
@@ -519,7 +746,7 @@ def main():
         dec_rates = {}
         for dwl in (W.llama_t128k(0.5), W.llama_t128k(1.0), W.llama_t128k(4.0), W.QWEN_T128K,
                     W.llama_prefill(32, 8), W.llama_prefill(64, 4), W.llama_t128k_c2(2.0),
-                    W.llama_t128k_c2(2.0, "joint"), W.LLAMA_T32K):
+                    W.llama_t128k_c2(2.0, "joint"), W.llama_t128k_c2(1.0), W.llama_t128k_nova(2.0), W.LLAMA_T32K):
             dec_rates[dwl.name] = decode_rate(K, dwl)
             log(f"decode {dwl.name}: {dec_rates[dwl.name]}")
         for bpd in (0.5, 1.0):
@@ -529,6 +756,11 @@ def main():
         name = W.llama_t128k(2.0).name + "-ragged"
         dec_rates[name] = decode_rate(K, W.llama_t128k(2.0), ragged=(1.0, 0.75, 0.5, 0.25))
         log(f"decode {name}: {dec_rates[name]}")
+
+    dist = None
+    if not args.no_distortion:
+        dist = distortion_rate(K)
+        log(f"distortion-rate: {json.dumps(dist)}")
 
     line = {
         "metric": METRIC,
@@ -551,11 +783,13 @@ def main():
             "timing": "HIP graph replay per step" if graphs else "one eager launch per step, back to back",
             "layer_caches_rotated": n_rep,
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "single_launch_us": pct,
             "context_tokens_per_s": round(B * (T + 1) / (ms_step * 1e-3), 1),
             "bytes_per_step": attend_bytes + append_bytes,
             "encode_prefill_ms": round(enc_ms, 4),
             "encode_rates": enc_rates,
             "other_decode_layouts": dec_rates,
+            "distortion_rate": dist,
         },
         "roofline": {
             "bound": "hbm",

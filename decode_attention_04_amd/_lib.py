@@ -12,13 +12,15 @@ import os
 from typing import Optional, Sequence, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvtc.so")
+# KVTC_LIBRARY may name another build of the same library (the phase-stamp diagnostic
+# variant libkvtc_stamps.so); by default the package's libkvtc.so.
+LIB_PATH = os.environ.get("KVTC_LIBRARY") or os.path.join(_PKG, "libkvtc.so")
 
 KV_OK, KV_ERR_INVALID, KV_ERR_UNSUPPORTED, KV_ERR_CAPACITY, KV_ERR_DEVICE = range(5)
 KV_F32, KV_F16 = 0, 1
 
 EXPORTED = (
-    "kv_record_words", "kv_cache_bytes", "kv_workspace_bytes", "kv_workspace_bytes_split",
+    "kv_record_words", "kv_cache_bytes", "kv_workspace_bytes", "kv_workspace_bytes_split", "kv_attend_plan",
     "kv_encode", "kv_append", "kv_attend_decode", "kv_attend_decode_split",
     "kv_append_attend_decode", "kv_attend_decode_ragged", "kv_append_attend_decode_noalloc",
     "kv_decode", "kv_quantize_pack", "kv_unpack", "kv_last_error",
@@ -44,6 +46,7 @@ class _Layout(ctypes.Structure):
         ("bits_v", ctypes.POINTER(ctypes.c_int32)),
         ("scale_k", ctypes.POINTER(ctypes.c_uint32)),
         ("scale_v", ctypes.POINTER(ctypes.c_uint32)),
+        ("query_basis_k", ctypes.c_int32),
     ]
 
 
@@ -65,6 +68,7 @@ def _load():
         "kv_cache_bytes": (i32, [L, i32, ctypes.POINTER(sz)]),
         "kv_workspace_bytes": (i32, [L, i64, ctypes.POINTER(sz)]),
         "kv_workspace_bytes_split": (i32, [L, i64, i64, ctypes.POINTER(sz)]),
+        "kv_attend_plan": (i32, [L, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "kv_encode": (i32, [L, P, P, i32, i64, i64, P, P, P, P, P]),
         "kv_append": (i32, [L, P, P, i32, i64, P, P, P, P, P]),
         "kv_attend_decode": (i32, [L, P, i32, i64, P, P, P, P, f32, P, P, sz, P]),
@@ -98,12 +102,15 @@ class Layout:
     ``alloc`` lists (rank_k, bits_k, rank_v, bits_v) per KV head.  ``scale_k`` /
     ``scale_v``: None (records with per-token headers) or one 32-bit word per KV
     head, the head's fixed quantizer for header-free records (fp16 bits of the min
-    in bits 0-15, of the step in bits 16-31).
+    in bits 0-15, of the step in bits 16-31).  ``query_basis_k``: each head's key basis
+    block holds the encode basis P_K then the query basis Q_K (a non-orthogonal key
+    transform; keys are reconstructed as Q_K c^).
     """
 
     def __init__(self, n_kv_heads: int, n_q_heads: int, batch: int, capacity: int,
                  alloc: Sequence[Tuple[int, int, int, int]], head_dim: int = 128,
-                 scale_k: Optional[Sequence[int]] = None, scale_v: Optional[Sequence[int]] = None):
+                 scale_k: Optional[Sequence[int]] = None, scale_v: Optional[Sequence[int]] = None,
+                 query_basis_k: bool = False):
         if len(alloc) != n_kv_heads:
             raise ValueError("alloc needs one (rank_k, bits_k, rank_v, bits_v) per KV head")
         self.head_dim, self.n_kv_heads, self.n_q_heads = head_dim, n_kv_heads, n_q_heads
@@ -122,10 +129,12 @@ class Layout:
         self.scale_v = None if scale_v is None else [int(x) for x in scale_v]
         self._sk = None if scale_k is None else u32(*self.scale_k)
         self._sv = None if scale_v is None else u32(*self.scale_v)
+        self.query_basis_k = bool(query_basis_k)
         self._c = _Layout(head_dim, n_kv_heads, n_q_heads, batch, capacity,
                           self._rk, self._bk, self._rv, self._bv,
                           ctypes.cast(self._sk, ctypes.POINTER(ctypes.c_uint32)) if self._sk else None,
-                          ctypes.cast(self._sv, ctypes.POINTER(ctypes.c_uint32)) if self._sv else None)
+                          ctypes.cast(self._sv, ctypes.POINTER(ctypes.c_uint32)) if self._sv else None,
+                          int(self.query_basis_k))
 
     @property
     def group(self) -> int:
@@ -175,6 +184,15 @@ def kv_workspace_bytes(layout: Layout, n_tokens: int, split_tokens: int = 0) -> 
     out = ctypes.c_size_t()
     _check(_lib.kv_workspace_bytes_split(layout.ref(), n_tokens, split_tokens, ctypes.byref(out)))
     return out.value
+
+
+def kv_attend_plan(layout: Layout, n_tokens: int, split_tokens: int = 0):
+    """(kernel class, largest split count, grid size) of decode attention over `layout`:
+    class -1 is the generic kernel, 0-5 the built-in budget classes, 6+ the frozen ones."""
+    c, n, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.kv_attend_plan(layout.ref(), n_tokens, split_tokens, ctypes.byref(c), ctypes.byref(n),
+                               ctypes.byref(w)))
+    return c.value, n.value, w.value
 
 
 def kv_encode(layout, k, v, n_tokens, pos0, basis_k, basis_v, cache_k, cache_v, stream=None):

@@ -20,6 +20,12 @@ KV-COBRA project page, "How KV-COBRA Works":
   programming over the bits spent).  The K heads and the V heads form one pool
   each, or one joint pool (the abstract's joint K+V allocation).
 
+* Attention-aware key transform (NOVA-KV abstract; pith.science verdict,
+  key_machinery) -- R_K = M_q^(1/2) E with E the eigenbasis of
+  M_q^(1/2) S_k M_q^(1/2): keys are encoded with P_K = (M_q^(1/2) E)_r and the
+  inverse is folded into the query through Q_K = (M_q^(-1/2) E)_r
+  (`nova_key_bases`); the coefficient variances (E's eigenvalues) are the C1
+  weights, so squared coefficient error is the query-weighted key error.
 * Header-free records -- with the Hadamard rotation one uniform quantizer per
   head suffices (KV-COBRA, Hadamard rotation) and no per-token header is stored
   (abstract).  Each retained coordinate of a head has the variance
@@ -246,3 +252,45 @@ def static_scale_word(cov: np.ndarray, basis: np.ndarray, bits: int) -> int:
     mu = np.float16(-k * s)
     step = np.float16((k * s - float(mu)) / ((1 << bits) - 1))
     return int(mu.view(np.uint16)) | (int(step.view(np.uint16)) << 16)
+
+
+def freeze_line(name: str, alloc: Sequence[Tuple[int, int, int, int]], header: int = 1) -> str:
+    """One line of frozen_layouts.txt for a layer's allocation: the decode kernel class
+    the build compiles for it (header = 0 for header-free records)."""
+    if any(c.isspace() for c in name):
+        raise ValueError("the layout name must not contain whitespace")
+    return f"{name} {int(header)} " + " ".join(f"{a[0]}:{a[1]}:{a[2]}:{a[3]}" for a in alloc)
+
+
+def nova_key_bases(query_cov: np.ndarray, key_cov: np.ndarray, r: int, signs: Optional[np.ndarray] = None):
+    """(P_K, Q_K, weights) of the attention-aware key transform: M = query second moment,
+    S = key covariance, E = eigenvectors of M^(1/2) S M^(1/2) by decreasing eigenvalue
+    (the weights); P_K = (M^(1/2) E)_r, Q_K = (M^(-1/2) E)_r, both times diag(s) H_r / sqrt(r)
+    when signs are given; float32, row-major d x r (the library's layout)."""
+    lq, vq = np.linalg.eigh(np.asarray(query_cov, np.float64))
+    if lq.min() <= 0:
+        raise ValueError("the query second moment must be positive definite")
+    root = (vq * np.sqrt(lq)[None, :]) @ vq.T
+    iroot = (vq / np.sqrt(lq)[None, :]) @ vq.T
+    lam, vec = np.linalg.eigh(root @ np.asarray(key_cov, np.float64) @ root)
+    lam, vec = lam[::-1], vec[:, ::-1]
+    p, q = root @ vec[:, :r], iroot @ vec[:, :r]
+    if signs is not None:
+        f = np.asarray(signs, np.float64).reshape(r)[:, None] * hadamard(r) / np.sqrt(r)
+        p, q = p @ f, q @ f
+    return np.ascontiguousarray(p, np.float32), np.ascontiguousarray(q, np.float32), lam
+
+
+def calibrate_head_nova(cov_k, cov_v, query_cov, signs_k_for, signs_v_for, bits_per_dim: float,
+                        ranks: Sequence[int] = (16, 32, 64, 128), head_dim: int = 128):
+    """Allocation and bases of one KV head with the attention-aware key transform: C1 on
+    the transform's coefficient variances for the keys, on the value covariance's
+    eigenvalues for the values.  Returns ((rk, bk, rv, bv), key basis block [P_K; Q_K]
+    as one flat float32 array, P_V)."""
+    budget = int(round(bits_per_dim * head_dim))
+    _, _, lam = nova_key_bases(query_cov, cov_k, 1)
+    rk, bk = c1_search(lam, budget, ranks)
+    wv, vv = sorted_directions(cov_v)
+    rv, bv = c1_search(wv, budget, ranks)
+    p, q, _ = nova_key_bases(query_cov, cov_k, rk, signs_k_for(rk))
+    return (rk, bk, rv, bv), np.concatenate([p.reshape(-1), q.reshape(-1)]), fold(vv, rv, signs_v_for(rv))

@@ -79,6 +79,8 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
   if (L->capacity < 1) return fail(KV_ERR_INVALID, "capacity %lld < 1", (long long)L->capacity);
   if (!L->rank_k || !L->bits_k || !L->rank_v || !L->bits_v)
     return fail(KV_ERR_INVALID, "allocation arrays must be non-NULL host pointers");
+  if (L->query_basis_k != 0 && L->query_basis_k != 1)
+    return fail(KV_ERR_INVALID, "query_basis_k must be 0 or 1");
   out.n_kv = L->n_kv_heads;
   out.n_q = L->n_q_heads;
   out.batch = L->batch;
@@ -111,12 +113,13 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
     d.wk = record_words(rk, bk, d.hk);
     d.wv = record_words(rv, bv, d.hv);
     d.boff_k = (int32_t)bk_total;
+    d.qoff_k = (int32_t)(bk_total + (L->query_basis_k ? (int64_t)kHeadDim * rk : 0));
     d.boff_v = (int32_t)bv_total;
     d.base_k = wk_total;
     d.base_v = wv_total;
     wk_total += (int64_t)L->batch * L->capacity * d.wk;
     wv_total += (int64_t)L->batch * L->capacity * d.wv;
-    bk_total += (int64_t)kHeadDim * rk;
+    bk_total += (int64_t)kHeadDim * rk * (L->query_basis_k ? 2 : 1);
     bv_total += (int64_t)kHeadDim * rv;
   }
   // kernels address one (sequence, head) region with 32-bit byte offsets
@@ -236,6 +239,11 @@ kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Works
   return KV_OK;
 }
 
+#ifdef KVTC_STAMPS
+// Diagnostic builds: the device buffer the next attention launches stamp their phases into.
+uint64_t* g_stamps = nullptr;
+#endif
+
 // ---------------------------------------------------------------- static split scratch
 // The split-merge scratch of kv_append_attend_decode_noalloc, one copy per GPU
 // (device globals are zero when the code object loads): arrival counters in the
@@ -340,6 +348,9 @@ kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_
   a.cnt = cnt;
   a.part = part;
   a.nonce = call_nonce();
+#ifdef KVTC_STAMPS
+  a.stamps = g_stamps;
+#endif
   a.n_tokens = n_tokens;
   a.lengths = lengths;
   a.capacity = L.capacity;
@@ -393,6 +404,20 @@ kv_status kv_workspace_bytes_split(const kv_layout* layout, int64_t n_tokens, in
   s = plan_workspace(L, n_tokens, split_tokens, w);
   if (s) return s;
   *bytes = (size_t)w.floats * 4u;
+  return ok();
+}
+
+kv_status kv_attend_plan(const kv_layout* layout, int64_t n_tokens, int64_t split_tokens, int32_t* kernel_class,
+                         int32_t* splits, int32_t* workgroups) {
+  Layout L;
+  kv_status s = build_layout(layout, L);
+  if (s) return s;
+  Workspace w;
+  s = plan_workspace(L, n_tokens, split_tokens, w);
+  if (s) return s;
+  if (kernel_class) *kernel_class = plan_attend(L.table, L.n_kv, L.group).spec_class;
+  if (splits) *splits = w.n_splits;
+  if (workgroups) *workgroups = (int32_t)((int64_t)w.wg_per_row * L.batch);
   return ok();
 }
 
@@ -566,5 +591,15 @@ kv_status kv_decode(const kv_layout* layout, int32_t which, int64_t n_tokens, in
 }
 
 const char* kv_last_error(void) { return g_error.c_str(); }
+
+#ifdef KVTC_STAMPS
+// Diagnostic builds only (not part of kvtc.h): every later attention launch writes 16
+// 64-bit phase stamps per workgroup into `stamps` (DEVICE, at least 128 bytes per
+// workgroup of the launch), or none when NULL.
+kv_status kv_debug_stamps(void* stamps) {
+  g_stamps = (uint64_t*)stamps;
+  return ok();
+}
+#endif
 
 }  // extern "C"

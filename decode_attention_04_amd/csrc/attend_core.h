@@ -623,6 +623,25 @@ __device__ inline void merge_splits(const AttendArgs& a, int h, int b, bool rese
     __hip_atomic_store(a.cnt + (int64_t)b * a.n_kv_heads + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ----------------------------------------------------------------- phase stamps (diagnostic builds)
+// Built with KVTC_STAMPS, the kernels record the 100 MHz real-time counter at the
+// phase boundaries of every workgroup into the caller's stamp buffer (kStampWords
+// 64-bit words per workgroup): 0 entry, 1 query projection done (wave 0), 2-5 tile
+// loop done per wave, 6 split partial stored, 7 arrival counted, 8 split merge done
+// (merging workgroup only), 9 hardware id, 10 XCC id, 11 fused append done.  Other
+// builds compile none of it.
+constexpr int kStampWords = 16;
+#ifdef KVTC_STAMPS
+#define KVTC_STAMP(ptr, i)                                            \
+  do {                                                                \
+    if (ptr) (ptr)[i] = (uint64_t)__builtin_amdgcn_s_memrealtime();   \
+  } while (0)
+#else
+#define KVTC_STAMP(ptr, i) \
+  do {                     \
+  } while (0)
+#endif
+
 // ----------------------------------------------------------------- wave state and context
 // Running state of one wave: reference maximum, per-lane partial sums of p and
 // p * min_V per head, and the value accumulators of up to 8 N-tiles (lane (n, G)
@@ -646,6 +665,7 @@ struct WaveCtx {
   int g;
   int h, b;                 // KV head and sequence of this workgroup
   int64_t unit;             // sequence * n_kv_heads + KV head
+  uint64_t* stamp;          // this workgroup's phase stamps (diagnostic builds), else null
 };
 
 // Key operand (A of the score MFMA) for one (K-step, lane): row = head (lane % 16),
@@ -682,8 +702,9 @@ __device__ inline void aq_slot(const float* qt, const float* E_h, int g, int rk,
 }
 
 // The g query heads of this KV head projected into its key basis by the whole
-// workgroup, q~ = scale * log2(e) * P_K^T q (the inverse key transform folded into
-// the query), while the first record tiles stream in: the queries and the basis
+// workgroup, q~ = scale * log2(e) * Q_K^T q (the inverse key transform folded into
+// the query; Q_K is the query-side key basis, P_K itself when orthonormal), while
+// the first record tiles stream in: the queries and the basis
 // columns are requested first, then `issue` starts the first tile copies, then the
 // arithmetic waits for its loads (the memory counter completes in order, so only
 // the last basis loads also wait for the copies, which were issued right behind
@@ -710,7 +731,7 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
   const int rpg = kHeadDim / rg;          // rows per group (r_K / 2)
   const int jj = lane % cw, rgi = lane / cw;
   const int j = wave * cw + jj;
-  const float* col = a.basis_k + hd.boff_k + (int64_t)(rgi * rpg) * rk + j;
+  const float* col = a.basis_k + hd.qoff_k + (int64_t)(rgi * rpg) * rk + j;
   // every load in flight before the first use: the queries (used first), then the
   // column segment, then the first tile copies
   constexpr int kQ = GM * kHeadDim / 256;
@@ -932,6 +953,14 @@ __device__ __attribute__((always_inline)) inline void p_operands(const float* S,
   }
 }
 
+// Quanta the last split of a (sequence, KV head) gives up to the others: half the
+// quanta of an average split, at least 2 and at most 8 (the encode of an appended
+// token costs about 8-9 quanta of streaming; a split of few quanta cannot absorb it).
+__host__ __device__ inline int split_slack(int nq, int ns) {
+  const int e = nq / (2 * ns);
+  return e < 2 ? 2 : (e > 8 ? 8 : e);
+}
+
 // ----------------------------------------------------------------- kernel body
 // One-dimensional grid of 256-thread workgroups; GM bounds the GQA group (g <= GM).
 // Sequence b takes workgroups [b W, (b + 1) W) with W = wg_per_row: head h the
@@ -944,6 +973,18 @@ __device__ __attribute__((always_inline)) inline void p_operands(const float* S,
 template <int GM, class Run>
 __device__ __attribute__((always_inline)) inline void attend_body(const AttendArgs& a, Run&& run) {
   extern __shared__ float lds[];
+#ifdef KVTC_STAMPS
+  uint64_t* stamp = a.stamps ? a.stamps + (int64_t)blockIdx.x * kStampWords : nullptr;
+  if (threadIdx.x == 0) {
+    KVTC_STAMP(stamp, 0);
+    if (stamp) {
+      stamp[9] = __builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (31 << 11));   // HW_REG_HW_ID, 32 bits
+      stamp[10] = __builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (31 << 11));  // HW_REG_XCC_ID
+    }
+  }
+#else
+  uint64_t* const stamp = nullptr;
+#endif
   const int WA = tile_lds_words(a.kbuf_words, a.vbuf_words, a.nbuf, GM);
   const int b = (int)blockIdx.x / a.wg_per_row;
   const int wr = (int)blockIdx.x - b * a.wg_per_row;
@@ -967,12 +1008,14 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
 
   WaveCtx c;
   // split x covers the 256-token quanta [q(x), q(x + 1)) of the nq in the context,
-  // q(x) = min(nq, x ne / ns) with ne = nq + 2: the splits differ by at most one
-  // quantum, so the XCDs (which take the splits round-robin) stream equal shares,
-  // and the last split (which holds the newest token, the one a fused append
-  // encodes first) is about two quanta lighter, roughly the time that encode
-  // takes.  Both entry points use the same splits, so appending in the same
-  // launch leaves the result bit for bit unchanged.
+  // q(x) = min(nq, x ne / ns) with ne = nq + split_slack(nq, ns): the splits differ
+  // by at most one quantum, so the XCDs (which take the splits round-robin) stream
+  // equal shares, and the last split (which holds the newest token, the one a fused
+  // append encodes first) is split_slack quanta lighter, about the time that encode
+  // and the later start of its query projection take (measured with phase stamps
+  // at 128K: 13 us of encode and a 4 us slower projection, against ~2 us per
+  // quantum of a 21-quantum split).  Both entry points use the same splits, so
+  // appending in the same launch leaves the result bit for bit unchanged.
   // this sequence's context: n_tokens, or its own length (clamped to [0, n_tokens])
   int n_tok = (int)a.n_tokens;
   if (a.lengths) {
@@ -980,7 +1023,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     n_tok = lb < 0 ? 0 : (lb < n_tok ? lb : n_tok);
   }
   const int nq = (n_tok + kSplitQuantum - 1) / kSplitQuantum;
-  const int ne = nq + 2;
+  const int ne = nq + split_slack(nq, ns);
   const int q0 = min(nq, (int)(((int64_t)split * ne) / ns));
   const int q1 = min(nq, (int)(((int64_t)split * ne + ne) / ns));
   const int s_begin = q0 * kSplitQuantum;
@@ -1006,6 +1049,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   c.h = h;
   c.b = b;
   c.unit = (int64_t)b * a.n_kv_heads + h;
+  c.stamp = stamp;
 
   // append fused with attention: the workgroup whose split holds the new token
   // encodes its key and value (waves 0-1 and 2-3) before any of its tiles stream in
@@ -1029,11 +1073,13 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     // tells the compiler that no store of the encoder is outstanding any more)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+    if (tid == 0) KVTC_STAMP(stamp, 11);
   }
 
   WaveState<GM> st;
   run(c, st);
   wait_tiles();
+  if (lane == 0) KVTC_STAMP(stamp, 2 + wave);
 
   // ---- wave partial: m, l, sum of p*min (per head), o~[head][j] in natural code order
   const int n = lane & 15, G = lane >> 4;
@@ -1143,6 +1189,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   // too; the partial tags keep any of those merges from folding a stale partial.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores have completed
   __syncthreads();
+  if (tid == 0) KVTC_STAMP(stamp, 6);
   uint32_t* flag = (uint32_t*)(ml + kWaves * 48);
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(a.cnt + c.unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1150,9 +1197,11 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     *flag = arrived == (uint64_t)ns ? 1u : (arrived > (uint64_t)ns ? 2u : 0u);
   }
   __syncthreads();
+  if (tid == 0) KVTC_STAMP(stamp, 7);
   const uint32_t fl = *flag;
   if (fl == 0u) return;
   merge_splits(a, h, b, fl == 1u);
+  if (tid == 0) KVTC_STAMP(stamp, 8);
 }
 
 }  // namespace kvtc

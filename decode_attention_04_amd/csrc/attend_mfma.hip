@@ -23,6 +23,7 @@
 // in one pass over packed codes); pith.science NOVA-KV verdict, forward
 // implications (the inverse key transform folded into the query).
 #include "attend_core.h"
+#include "attend_frozen.h"
 #include "attend_spec.h"
 
 namespace kvtc {
@@ -72,6 +73,7 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
       }
     }
   });
+  if (threadIdx.x == 0) KVTC_STAMP(c.stamp, 1);
   init_state(st);
   float* S = c.S;
   f32x4 (&acc2)[8] = st.acc2;
@@ -161,11 +163,11 @@ AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group) {
   }
   p.spec_class = -1;
   if (group <= 8) {
-    for (int cls = 0; cls < kSpecClasses && p.spec_class < 0; ++cls) {
+    for (int cls = 0; cls < kSpecClasses + kFrozenClasses && p.spec_class < 0; ++cls) {
       bool all = true;
       for (int h = 0; h < n_kv_heads && all; ++h) {
         const HeadDesc& d = heads.h[h];
-        all = spec_index(cls, d.rk, d.bk, d.rv, d.bv) >= 0 && d.hk == spec_header(cls) && d.hv == spec_header(cls);
+        all = class_index(cls, d.rk, d.bk, d.rv, d.bv) >= 0 && d.hk == class_header(cls) && d.hv == class_header(cls);
       }
       if (all) p.spec_class = cls;
     }
@@ -206,7 +208,7 @@ hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
   if (p.spec_class >= 0) {
     for (int h = 0; h < a.n_kv_heads; ++h) {
       HeadDesc& d = a.heads.h[h];
-      d.spec = spec_index(p.spec_class, d.rk, d.bk, d.rv, d.bv);
+      d.spec = class_index(p.spec_class, d.rk, d.bk, d.rv, d.bv);
     }
     switch (p.spec_class) {
       case 0: return launch_attend_spec0(a, s);
@@ -215,8 +217,7 @@ hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
       case 3: return launch_attend_spec3(a, s);
       case 4: return launch_attend_spec4(a, s);
       case 5: return launch_attend_spec5(a, s);
-      case 6: return launch_attend_spec6(a, s);
-      default: return launch_attend_spec7(a, s);
+      default: return launch_attend_frozen(p.spec_class - kSpecClasses, a, s);
     }
   }
   // the generic kernel; all power-of-two widths skip the general-width paths

@@ -6,11 +6,12 @@
 // a workgroup dispatches once, on its KV head's (r_K, b_K, r_V, b_V), to a tile
 // loop compiled for that format: record sizes, copy instruction counts and the
 // copy wait counts are constants, and each tile is one straight instruction
-// sequence.  The formats compiled are the ones the per-head bit allocation picks
-// under one budget of bits per vector (every rank of the allocation search with
-// b = min(8, floor(budget / r)) >= 2), all (K, V) pairs of a class, and the pairs
-// of frozen per-layer allocations (the mixed full-rank / low-rank layout, a
-// cross-head allocation); a layout outside one class runs the generic kernel.
+// sequence.  The built-in classes hold the formats the per-head bit allocation
+// picks under one budget of bits per vector (every rank of the allocation search
+// with b = min(8, floor(budget / r)) >= 2), all (K, V) pairs, with per-token
+// headers or header-free; the build adds one class per frozen per-layer
+// allocation (frozen_layouts.txt, generated into attend_frozen.h).  A layout
+// outside every class runs the generic kernel.
 #pragma once
 
 #include "attend_core.h"
@@ -29,23 +30,14 @@ namespace kvtc {
 // 512-bit budget per vector (C1 picks b = min(8, floor(budget / r)))
 #define KVTC_SPEC_CLASS3(X) X(0, 16, 8, 16, 8) X(1, 16, 8, 32, 8) X(2, 16, 8, 64, 8) X(3, 16, 8, 128, 4) X(4, 32, 8, 16, 8) X(5, 32, 8, 32, 8) X(6, 32, 8, 64, 8) X(7, 32, 8, 128, 4) X(8, 64, 8, 16, 8) X(9, 64, 8, 32, 8) X(10, 64, 8, 64, 8) X(11, 64, 8, 128, 4) X(12, 128, 4, 16, 8) X(13, 128, 4, 32, 8) X(14, 128, 4, 64, 8) X(15, 128, 4, 128, 4)
 
-// Mixed fixed-width layout: full-rank r = 128 at 2 bits beside r = 16 at 6 bits
-// (half of the heads each), every (K, V) pair of the two formats
-#define KVTC_SPEC_CLASS4(X) X(0, 128, 2, 128, 2) X(1, 128, 2, 16, 6) X(2, 16, 6, 128, 2) X(3, 16, 6, 16, 6)
-
-// A frozen cross-head (C2) allocation: the LLaMA-shaped layer of 8 KV heads at 2
-// bits per dimension on average, K heads and V heads each sharing their budget
-// (attention-KL key weights), as (r_K, b_K, r_V, b_V) per head
-#define KVTC_SPEC_CLASS5(X) X(0, 64, 4, 128, 3) X(1, 128, 4, 128, 3) X(2, 32, 5, 16, 5) X(3, 128, 3, 16, 5) X(4, 128, 4, 32, 4) X(5, 16, 4, 128, 3) X(6, 16, 5, 128, 4) X(7, 16, 5, 32, 3)
-
 // Header-free records (one fixed quantizer per head) of the 64- and 128-bit budget formats
-#define KVTC_SPEC_CLASS6(X) KVTC_SPEC_CLASS0(X)
-#define KVTC_SPEC_CLASS7(X) KVTC_SPEC_CLASS1(X)
+#define KVTC_SPEC_CLASS4(X) KVTC_SPEC_CLASS0(X)
+#define KVTC_SPEC_CLASS5(X) KVTC_SPEC_CLASS1(X)
 
-constexpr int kSpecClasses = 8;
+constexpr int kSpecClasses = 6;  // built-in classes; the frozen ones follow them
 
-// Header words of every record a class reads: 1 (per-token min and step) or 0.
-__host__ __device__ constexpr int spec_header(int cls) { return cls >= 6 ? 0 : 1; }
+// Header words of every record a built-in class reads: 1 (per-token min and step) or 0.
+__host__ __device__ constexpr int spec_header(int cls) { return cls >= 4 ? 0 : 1; }
 
 // Index of (rk, bk, rv, bv) in class `cls`, or -1.
 __host__ inline int spec_index(int cls, int rk, int bk, int rv, int bv) {
@@ -59,8 +51,6 @@ __host__ inline int spec_index(int cls, int rk, int bk, int rv, int bv) {
     case 3: KVTC_SPEC_CLASS3(KVTC_SPEC_FIND) break;
     case 4: KVTC_SPEC_CLASS4(KVTC_SPEC_FIND) break;
     case 5: KVTC_SPEC_CLASS5(KVTC_SPEC_FIND) break;
-    case 6: KVTC_SPEC_CLASS6(KVTC_SPEC_FIND) break;
-    case 7: KVTC_SPEC_CLASS7(KVTC_SPEC_FIND) break;
     default: break;
   }
 #undef KVTC_SPEC_FIND
@@ -103,6 +93,7 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
     for (int t = 0; t < (nbuf > 1 ? nbuf - 1 : 1); ++t)
       if (t_begin + t * kTileT < t_end) issue_tile<WK, WV>(c, t_begin + t * kTileT, t_end, t);
   });
+  if (threadIdx.x == 0) KVTC_STAMP(c.stamp, 1);
   init_state(st);
   if (lane < 4) ((uint32_t*)c.S)[score_floats(GM) + lane] = 0u;  // zero slot
   int slot = 0;
@@ -143,24 +134,28 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
 #define KVTC_SPEC_CASE(I, RK, BK, RV, BV) \
   case I: spec_tiles<GM, RK, BK, RV, BV, kHdr>(a, c, st); break;
 
-#define KVTC_DEFINE_SPEC_CLASS(CLS)                                                                  \
+// Kernel attend_NAME_kernel<GM> and launcher launch_attend_NAME of the class whose
+// formats LIST(X) enumerates, with HDR header words per record.
+#define KVTC_DEFINE_ATTEND_CLASS(NAME, LIST, HDR)                                                    \
   template <int GM>                                                                                  \
-  __global__ __launch_bounds__(256, 3) void attend_spec##CLS##_kernel(AttendArgs a) {               \
-    constexpr int kHdr = spec_header(CLS);                                                           \
+  __global__ __launch_bounds__(256, 3) void attend_##NAME##_kernel(AttendArgs a) {                  \
+    constexpr int kHdr = (HDR);                                                                      \
     attend_body<GM>(a, [&](const WaveCtx& c, WaveState<GM>& st) {                                    \
       switch (__builtin_amdgcn_readfirstlane(a.heads.h[c.h].spec)) {                                \
-        KVTC_SPEC_CLASS##CLS(KVTC_SPEC_CASE) default : break;                                        \
+        LIST(KVTC_SPEC_CASE) default : break;                                                        \
       }                                                                                              \
     });                                                                                              \
   }                                                                                                  \
-  hipError_t launch_attend_spec##CLS(const AttendArgs& a, hipStream_t s) {                          \
+  hipError_t launch_attend_##NAME(const AttendArgs& a, hipStream_t s) {                             \
     const size_t lds = attend_lds_bytes(a.kbuf_words, a.vbuf_words, a.nbuf, a.group);                \
     const dim3 grid((unsigned)(a.wg_per_row * a.batch));                                          \
     if (a.group <= 4)                                                                                \
-      hipLaunchKernelGGL(attend_spec##CLS##_kernel<4>, grid, dim3(256), lds, s, a);                 \
+      hipLaunchKernelGGL(attend_##NAME##_kernel<4>, grid, dim3(256), lds, s, a);                    \
     else                                                                                             \
-      hipLaunchKernelGGL(attend_spec##CLS##_kernel<8>, grid, dim3(256), lds, s, a);                 \
+      hipLaunchKernelGGL(attend_##NAME##_kernel<8>, grid, dim3(256), lds, s, a);                    \
     return hipGetLastError();                                                                        \
   }
+
+#define KVTC_DEFINE_SPEC_CLASS(CLS) KVTC_DEFINE_ATTEND_CLASS(spec##CLS, KVTC_SPEC_CLASS##CLS, spec_header(CLS))
 
 }  // namespace kvtc

@@ -1,5 +1,5 @@
-// Decode attention kernels for the mixed layout of full-rank 2-bit and rank-16
-// 6-bit heads.
+// Decode attention kernels for header-free records (one fixed quantizer per head)
+// of the formats of the 64-bit per-vector budget.
 #include "attend_spec.h"
 
 namespace kvtc {

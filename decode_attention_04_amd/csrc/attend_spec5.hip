@@ -1,5 +1,5 @@
-// Decode attention kernels for a frozen cross-head allocation of the LLaMA-shaped
-// layer (odd bit widths beside power-of-two ones).
+// Decode attention kernels for header-free records (one fixed quantizer per head)
+// of the formats of the 128-bit per-vector budget.
 #include "attend_spec.h"
 
 namespace kvtc {

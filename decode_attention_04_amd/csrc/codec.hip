@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int r = a.which ? hd.rv : hd.rk, bits = a.which ? hd.bv : hd.bk;
   const int W = a.which ? hd.wv : hd.wk, hdr = a.which ? hd.hv : hd.hk;
   const uint32_t sw = a.which ? hd.sv : hd.sk;
-  const float* P = a.basis + (a.which ? hd.boff_v : hd.boff_k);
+  const float* P = a.basis + (a.which ? hd.boff_v : hd.qoff_k);  // keys: reconstructed through Q_K
   const uint32_t* reg = a.cache + (a.which ? hd.base_v : hd.base_k) + ((int64_t)b * a.capacity + a.pos0) * W;
   const int nt = (int)((a.n_tokens - t0) < 16 ? (a.n_tokens - t0) : 16);
   for (int e = threadIdx.x; e < 16 * r; e += 256) {

@@ -503,9 +503,17 @@ hipError_t launch_rank(const EncodeArgs& a, uint64_t mask_k, uint64_t mask_v, hi
   if (units == 0) return hipSuccess;
   constexpr int kTileTok = kEncWaves * 16 * S::NT;
   const int64_t n_tiles = (a.n_tokens + kTileTok - 1) / kTileTok;
-  // about 2048 workgroups or more in flight, each staging the basis once for its tiles
+  // Tiles per workgroup: each workgroup stages the basis once for its tiles (for r =
+  // 128 that staging reads as many bytes as two tiles of fp16 inputs), so a chunk
+  // that fits the resident workgroups in one round gives each of them an equal share
+  // (one round of resident workgroups, each staging once); larger chunks run about
+  // 2048 workgroups or more, up to 8 tiles each.
   const int64_t per_tile_row = (int64_t)units * a.batch;
-  int64_t tpw = (n_tiles * per_tile_row) / 2048;
+  const int64_t total = n_tiles * per_tile_row;
+  const int64_t lds_per_cu = (160 * 1024) / enc_lds_bytes(R);
+  const int64_t resident = 256 * (lds_per_cu < S::OCC ? lds_per_cu : S::OCC);
+  int64_t tpw = total / 2048;
+  if (tpw < 1) tpw = (total + resident - 1) / resident;
   tpw = tpw < 1 ? 1 : (tpw > 8 ? 8 : tpw);
   const dim3 grid((unsigned)((n_tiles + tpw - 1) / tpw), (unsigned)units, (unsigned)a.batch);
   hipLaunchKernelGGL((encode_mfma_kernel<T, R, S::NT, S::PF, S::OCC>), grid, dim3(256), enc_lds_bytes(R), s, a,

@@ -28,10 +28,11 @@ inline bool supported_rank(int r) { return r == 16 || r == 32 || r == 64 || r ==
 inline bool supported_bits(int b) { return b >= kMinBits && b <= kMaxBits; }
 
 // Per-KV-head allocation and addressing, passed by value in kernel arguments
-// (48 bytes: 64 heads of it fit the 4 KB argument segment with the rest).
+// (56 bytes: 64 heads of it fit the 4 KB argument segment with the rest).
 struct HeadDesc {
   int64_t base_k, base_v;   // word offset of the head's cache region
-  int32_t boff_k, boff_v;   // float offset of the head's basis
+  int32_t boff_k, boff_v;   // float offset of the head's (encode) basis
+  int32_t qoff_k;           // float offset of the head's query-side key basis (== boff_k when orthonormal)
   uint32_t sk, sv;          // header-free records: the head's fixed fp16 min | fp16 step << 16
   int32_t ns;               // splits of each of the head's (sequence, head) units (set at launch)
   int16_t wk, wv;           // record words
@@ -39,7 +40,7 @@ struct HeadDesc {
   uint8_t rk, bk, rv, bv;   // rank and bits of keys and values
   uint8_t hk, hv;           // header words of a key / value record: 1 (per-token min and step) or 0
 };
-static_assert(sizeof(HeadDesc) == 48, "HeadDesc layout");
+static_assert(sizeof(HeadDesc) == 56, "HeadDesc layout");
 
 struct HeadTable {
   HeadDesc h[kMaxKvHeads];

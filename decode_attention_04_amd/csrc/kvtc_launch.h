@@ -55,6 +55,9 @@ struct AttendArgs {
   int32_t kbuf_words;  // LDS words per K / V record-tile buffer (set by launch_attend)
   int32_t vbuf_words;
   int32_t nbuf;        // tile buffers per wave: 2 (next tile streams in) or 1
+#ifdef KVTC_STAMPS
+  uint64_t* stamps;    // [grid][16] phase stamps of every workgroup, or null
+#endif
 };
 
 struct DecodeArgs {
@@ -83,7 +86,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);       // records -
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t s);       // one token: append kernel, else the below
 hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s);  // prefill: k, v 16-byte aligned
 // How a layout's decode attention runs: the specialised kernel class (-1: the
-// generic kernel), LDS tile buffers per wave and resident workgroups per CU.
+// generic kernel; built-in classes first, then the frozen ones the build generates),
+// LDS tile buffers per wave and resident workgroups per CU.
 struct AttendPlan {
   int spec_class = -1;
   bool gen = false;
@@ -98,7 +102,5 @@ hipError_t launch_attend_spec2(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec3(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec4(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec5(const AttendArgs& a, hipStream_t s);
-hipError_t launch_attend_spec6(const AttendArgs& a, hipStream_t s);
-hipError_t launch_attend_spec7(const AttendArgs& a, hipStream_t s);
 
 }  // namespace kvtc

@@ -41,6 +41,15 @@
  * Basis layout: the heads' bases concatenated, head h is a row-major
  *   head_dim x r_h float32 matrix (element (i, j) at offset_h + i*r_h + j),
  *   offset_h = sum_{h'<h} head_dim * r_h'.
+ *   With query_basis_k = 1 the key bases form pairs: head h's block is P_K
+ *   (head_dim x r) followed by Q_K (head_dim x r), offset_h = sum_{h'<h} 2 *
+ *   head_dim * r_h'.  Keys are encoded with P_K (c = P_K^T k) and reconstructed
+ *   through Q_K (k^ = Q_K c^), so attention projects the query with Q_K
+ *   (q . k^ = (Q_K^T q) . c^).  For an orthonormal basis Q_K = P_K.  This
+ *   carries a non-orthogonal key transform: P_K = (M_q^(1/2) E)_r and Q_K =
+ *   (M_q^(-1/2) E)_r with P_K^T Q_K = I.  [NOVA-KV abstract; pith.science
+ *   NOVA-KV verdict, key_machinery: R_K = M_q^(1/2) E, R_K R_K^T = M_q, the
+ *   inverse key transform folded into the query]
  *
  * Conventions for every call:
  *   - pointers are DEVICE memory unless the comment says HOST;
@@ -97,6 +106,8 @@ typedef struct kv_layout {
   const int32_t *bits_v;  /* HOST [n_kv_heads] */
   const uint32_t *scale_k; /* HOST [n_kv_heads] or NULL */
   const uint32_t *scale_v; /* HOST [n_kv_heads] or NULL */
+  int32_t query_basis_k;   /* 0: orthonormal key bases; 1: each head's key basis block holds
+                              the encode basis P_K then the query basis Q_K (see below) */
 } kv_layout;
 
 /* Words per record with its header, 1 + ceil(rank*bits/32) (a header-free
@@ -108,6 +119,17 @@ kv_status kv_cache_bytes(const kv_layout *layout, int32_t which, size_t *bytes);
 
 /* Bytes of device workspace kv_attend_decode needs for n_tokens context tokens. */
 kv_status kv_workspace_bytes(const kv_layout *layout, int64_t n_tokens, size_t *bytes);
+
+/* How decode attention over `layout` runs, written to HOST ints (any may be NULL):
+ * kernel_class: -1 for the generic kernel (widths read at run time), 0..5 for the
+ * built-in classes compiled for the formats of one per-vector budget (0-3: 64, 128,
+ * 256, 512 bits with per-token headers; 4-5: 64, 128 bits header-free), 6 and up
+ * for the classes the build compiled from frozen layer allocations, in the order
+ * they are listed; splits: the largest number of splits of one (sequence, KV head)
+ * for n_tokens and split_tokens (0: the default plan); workgroups: the launch's
+ * grid size.  No device work.  Errors as kv_workspace_bytes_split. */
+kv_status kv_attend_plan(const kv_layout *layout, int64_t n_tokens, int64_t split_tokens,
+                         int32_t *kernel_class, int32_t *splits, int32_t *workgroups);
 
 /* Prefill encode.  k, v: [batch][n_kv_heads][n_tokens][head_dim] of `dtype`
  * (KV_F32 or KV_F16), contiguous, 16-byte aligned when n_tokens > 1; every
@@ -168,9 +190,10 @@ kv_status kv_attend_decode(const kv_layout *layout, const void *q, kv_dtype dtyp
  * 256; 0 picks the default).  The context of every (sequence, KV head) is cut
  * into ns = ceil(n_tokens / split_tokens) splits of whole 256-token blocks:
  * with nq = ceil(n_tokens / 256) blocks, split x takes blocks [q(x), q(x+1))
- * where q(x) = min(nq, floor(x * (nq + 2) / ns)).  Consecutive splits differ
- * by at most one block, and the last splits are about two blocks lighter (the
- * newest token's split also encodes it in kv_append_attend_decode); with few
+ * where q(x) = min(nq, floor(x * (nq + e) / ns)) and e = min(8, max(2,
+ * floor(nq / (2 ns)))).  Consecutive splits differ by at most one block, and
+ * the last splits are about e blocks lighter (the newest token's split also
+ * encodes it in kv_append_attend_decode); with few
  * blocks per split a split may be larger than split_tokens and the last ones
  * may be empty (n_tokens = 512, split_tokens = 256: 512 and 0 tokens).  The
  * default gives each KV head a number of splits in proportion to the cost of
@@ -245,8 +268,9 @@ kv_status kv_append_attend_decode_noalloc(const kv_layout *layout, const void *k
                                           float softmax_scale, float *out, void *stream);
 
 /* Reconstruct stored tokens: for records pos0 .. pos0+n_tokens-1 of every
- * (sequence, KV head) of tensor `which` (0 = K, 1 = V), x^ = P (min + step *
- * code) with P that head's basis (`basis`: the tensor's concatenated bases),
+ * (sequence, KV head) of tensor `which` (0 = K, 1 = V), x^ = B (min + step *
+ * code) with B that head's reconstruction basis (`basis`: the tensor's
+ * concatenated bases; B = P, or Q_K for the keys of a query_basis_k layout),
  * each coordinate dequantized exactly and the d outputs summed in float32 over
  * the coordinates in order.  out: DEVICE float32 [batch][n_kv_heads][n_tokens]
  * [head_dim].  Not on the decode path (attention reads the codes directly):

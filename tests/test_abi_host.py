@@ -247,3 +247,22 @@ def test_noalloc_refuses_oversize_requests_before_any_device_call():
     big = lib_mod.Layout(64, 64, 65, 16, [(16, 4, 16, 4)] * 64)
     st = L.kv_append_attend_decode_noalloc(big.ref(), 16, 16, f16, 16, f16, 16, 0, 16, 16, 16, 16, 0.1, 16, None)
     assert st == lib_mod.KV_ERR_CAPACITY
+
+
+def test_attend_plan_reports_the_kernel_class():
+    """Budget formats run a built-in class, a frozen layer allocation its generated class,
+    anything else (or g > 8) the generic kernel; the split count and grid follow the plan."""
+    T = 131073
+    uni = lib_mod.Layout(8, 32, 4, T, [(64, 4, 64, 4)] * 8)
+    assert lib_mod.kv_attend_plan(uni, T) == (2, 24, 768)
+    half = lib_mod.Layout(8, 32, 4, T, [(16, 4, 32, 2)] * 8, scale_k=[0x3C00 | 0x2E66 << 16] * 8,
+                          scale_v=[0x3C00 | 0x2E66 << 16] * 8)
+    assert lib_mod.kv_attend_plan(half, T)[0] == 4
+    c2 = [(64, 4, 128, 3), (128, 4, 128, 3), (32, 5, 16, 5), (128, 3, 16, 5), (128, 4, 32, 4), (16, 4, 128, 3),
+          (16, 5, 128, 4), (16, 5, 32, 3)]
+    assert lib_mod.kv_attend_plan(lib_mod.Layout(8, 32, 4, T, c2), T)[0] >= 6
+    odd = lib_mod.Layout(2, 8, 1, 1000, [(32, 3, 64, 5), (16, 7, 128, 6)])
+    assert lib_mod.kv_attend_plan(odd, 1000)[0] == -1
+    big_group = lib_mod.Layout(1, 12, 1, 1000, [(64, 4, 64, 4)])
+    assert lib_mod.kv_attend_plan(big_group, 1000)[0] == -1
+    assert lib_mod.kv_attend_plan(uni, T, 4096)[1] == (T + 4095) // 4096

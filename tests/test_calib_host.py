@@ -1,4 +1,6 @@
 """Host-side calibration of the package (basis, Hadamard fold, C1, C2) against the oracle (no GPU)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -105,22 +107,53 @@ def test_calibrate_layer_c2(pool):
         assert np.abs(pk[h].astype(np.float64).T @ pk[h] - np.eye(alloc[h][0])).max() < 1e-5
 
 
-def test_frozen_c2_kernel_class_matches_the_calibration():
-    """The specialised kernel class compiled for the LLaMA-shaped C2 layout at 2 bits/dim
-    lists exactly the per-head formats its calibration picks (else the layout would
-    silently fall back to the generic kernel)."""
-    import os
-    import re
-    src = open(os.path.join(os.path.dirname(calib.__file__), "csrc", "attend_spec.h")).read()
-    body = re.search(r"#define KVTC_SPEC_CLASS5\(X\)(.*)", src).group(1)
-    listed = [tuple(int(v) for v in m[1:]) for m in re.findall(r"X\((\d+), (\d+), (\d+), (\d+), (\d+)\)", body)]
-    wl = W.llama_t128k_c2(2.0)
+def _layer_allocation(wl):
     n = wl.n_kv_heads
-    alloc, _, _ = calib.calibrate_layer(
-        [W.covariance(wl, "K", h) for h in range(n)], [W.covariance(wl, "V", h) for h in range(n)],
-        lambda h, r: W.hadamard_signs(wl, "K", h, r), lambda h, r: W.hadamard_signs(wl, "V", h, r),
-        wl.allocation, [W.query_covariance(wl, h) for h in range(n)])
-    assert sorted(set(alloc)) == sorted(set(listed))
+    if wl.allocation[0] == "c2":
+        alloc, _, _ = calib.calibrate_layer(
+            [W.covariance(wl, "K", h) for h in range(n)], [W.covariance(wl, "V", h) for h in range(n)],
+            lambda h, r: W.hadamard_signs(wl, "K", h, r), lambda h, r: W.hadamard_signs(wl, "V", h, r),
+            wl.allocation, [W.query_covariance(wl, h) for h in range(n)])
+        return alloc
+    return [tuple(a) for a in wl.allocation[1]]
+
+
+def test_frozen_layouts_are_the_calibration_output():
+    """Each frozen layer allocation compiled into a kernel class is, head by head, what
+    calibration picks for that layer (a stale line would leave the layout on the generic
+    kernel), and freeze_line writes exactly that line."""
+    from decode_attention_04_amd import build
+
+    frozen = {name: (h, heads) for name, h, heads in build.frozen_layouts()}
+    for wl in (W.QWEN_T128K, W.llama_t128k_c2(2.0), W.llama_t128k_c2(2.0, "joint")):
+        alloc = _layer_allocation(wl)
+        assert frozen[wl.name] == (1, alloc), wl.name
+        line = calib.freeze_line(wl.name, alloc)
+        assert line.split()[:2] == [wl.name, "1"]
+        assert [tuple(int(v) for v in t.split(":")) for t in line.split()[2:]] == alloc
+
+
+def test_frozen_class_generator(tmp_path):
+    """Generated sources: one class per layout listing its distinct formats in order, the
+    header flags, and an empty list that still yields the lookups and the dispatcher."""
+    from decode_attention_04_amd import build
+
+    srcs = build.generate([("a", 1, [(16, 4, 32, 2), (16, 4, 32, 2), (64, 3, 16, 8)]), ("b", 0, [(32, 2, 32, 2)])],
+                          str(tmp_path))
+    assert [os.path.basename(p) for p in srcs] == ["attend_frozen0.hip", "attend_frozen1.hip",
+                                                   "attend_frozen_dispatch.hip"]
+    h = (tmp_path / "attend_frozen.h").read_text()
+    assert "constexpr int kFrozenClasses = 2;" in h
+    assert "#define KVTC_FROZEN_CLASS0(X) X(0, 16, 4, 32, 2) X(1, 64, 3, 16, 8)" in h
+    assert "return i == 0 ? 1 : i == 1 ? 0 : 1;" in h
+    assert "KVTC_DEFINE_ATTEND_CLASS(frozen1, KVTC_FROZEN_CLASS1, 0)" in (tmp_path / "attend_frozen1.hip").read_text()
+    srcs = build.generate([], str(tmp_path))
+    assert [os.path.basename(p) for p in srcs] == ["attend_frozen_dispatch.hip"]
+    assert "constexpr int kFrozenClasses = 0;" in (tmp_path / "attend_frozen.h").read_text()
+    with pytest.raises(ValueError):
+        bad = tmp_path / "bad.txt"
+        bad.write_text("x 1 48:4:16:4\n")
+        build.frozen_layouts(str(bad))
 
 
 def test_static_scale_word_matches_the_oracle():
