@@ -61,6 +61,7 @@ class Workload:
     #   ("fixed", ((rk, bk, rv, bv), ...))  one tuple per KV head
     #   ("c1", budget_bits_per_dim, key_weights)  key_weights in {"mse", "kl"}; values use "mse"
     #   ("c2", budget_bits_per_dim, key_weights, "split"|"joint")  budget shared across heads
+    #   ("nova", budget_bits_per_dim)  attention-aware key transform, C1 on its coefficients
     allocation: tuple = ()
     decode_steps: int = 1        # decode steps the workload runs (append + attend each)
     encode_tokens: int = 0       # prefill chunk encoded per sequence (0: none)
@@ -101,6 +102,14 @@ def llama_t128k_c2(bpd: float, pool: str = "split") -> Workload:
         llama_t128k(bpd), name=f"llama8b-layer-B4-T128K-{bpd:g}bpd-c2" + ("" if pool == "split" else "-joint"),
         allocation=("c2", float(bpd), "kl", pool),
         note=f"C2 across the heads ({pool} K/V pools), attention-KL key weights")
+
+
+def llama_t128k_nova(bpd: float) -> Workload:
+    """The 128K LLaMA-shaped layer (same generated data) with the attention-aware key
+    transform: its query second moment is the generated query covariance."""
+    return dataclasses.replace(
+        llama_t128k(bpd), name=f"llama8b-layer-B4-T128K-{bpd:g}bpd-nova", allocation=("nova", float(bpd)),
+        note="keys through R_K = M_q^(1/2) E (C1 on its coefficient variances), values MSE")
 
 
 def llama_prefill(rank: int, bits: int) -> Workload:
