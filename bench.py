@@ -308,6 +308,55 @@ def distortion_rate(K, wl=None, tokens=4096):
     return rep
 
 
+def logit_error(K, wl=None, tokens=4096, n_queries=256):
+    """Relative attention-logit error sum (q . (k - k^))^2 / sum (q . k)^2 of the keys the
+    library encodes and reconstructs (kv_encode, kv_decode), for queries drawn from each
+    head's generated query distribution: the attention-aware transform (P_K encodes,
+    keys reconstructed through Q_K) against the orthonormal basis ordered by attention-KL
+    weights, both with the attention-aware allocation's (rank, bits) per head.  The
+    comparison the NOVA-KV review proposes as the test of the non-orthogonal transform."""
+    import torch
+
+    from decode_attention_04_amd import calib
+
+    wl = wl or W.llama_t128k_nova(2.0)
+    dev = torch.device("cuda:0")
+    alloc, kblocks, _ = calibrate(wl)
+    H = wl.n_kv_heads
+    x = torch.from_numpy(np.stack([W.tokens(wl, "K", 0, h, 0, tokens, wl.dtype) for h in range(H)])[None]).to(dev)
+    rng = np.random.default_rng(7)
+    out = {"workload": wl.name, "tokens_per_head": tokens, "queries_per_head": n_queries}
+    for name in ("attention-aware", "orthonormal-kl"):
+        if name == "attention-aware":
+            keys = [torch.from_numpy(b) for b in kblocks]
+            pair = True
+        else:
+            keys = [torch.from_numpy(calib.fold(calib.sorted_directions(W.covariance(wl, "K", h),
+                                                                         W.query_covariance(wl, h))[1], alloc[h][0],
+                                                W.hadamard_signs(wl, "K", h, alloc[h][0])).reshape(-1))
+                    for h in range(H)]
+            pair = False
+        lay = K.Layout(H, H, 1, tokens, [(a[0], a[1], a[0], a[1]) for a in alloc], query_basis_k=pair)
+        kb = torch.cat(keys).to(dev)
+        ck = torch.empty(K.kv_cache_bytes(lay, 0) // 4, dtype=torch.int32, device=dev)
+        cv = torch.empty(K.kv_cache_bytes(lay, 1) // 4, dtype=torch.int32, device=dev)
+        vb = torch.zeros(sum(128 * a[0] for a in alloc), dtype=torch.float32, device=dev)
+        K.kv_encode(lay, x, x, tokens, 0, kb, vb, ck, cv)
+        rec = torch.empty((1, H, tokens, wl.head_dim), dtype=torch.float32, device=dev)
+        K.kv_decode(lay, 0, tokens, 0, kb, ck, rec)
+        errs = []
+        for h in range(H):
+            qs = torch.from_numpy(rng.multivariate_normal(np.zeros(wl.head_dim), W.query_covariance(wl, h),
+                                                          n_queries)).to(dev)
+            kx = x[0, h].double()
+            num = ((qs @ (kx - rec[0, h].double()).T) ** 2).sum()
+            den = ((qs @ kx.T) ** 2).sum()
+            errs.append(float(num / den))
+        out[name] = {"per_head": [round(e, 6) for e in errs], "mean": float(np.mean(errs))}
+    out["allocation"] = [list(a[:2]) for a in alloc]
+    return out
+
+
 def _cpu_workers() -> int:
     """Host cores the oracle runs on: every core this process may use, at most 16."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
@@ -760,6 +809,7 @@ def main():
     dist = None
     if not args.no_distortion:
         dist = distortion_rate(K)
+        dist["attention_logit_error"] = logit_error(K)
         log(f"distortion-rate: {json.dumps(dist)}")
 
     line = {

@@ -182,3 +182,28 @@ def u32_host(t):
     import torch
     torch.cuda.synchronize()
     return t.cpu().numpy().view(np.uint32)
+
+
+def oracle_calibrate_nova(wl: W.Workload):
+    """(alloc, P_K list, Q_K list, P_V list) of a workload with the attention-aware key
+    transform, built with the oracle: C1 on the transform's coefficient variances for the
+    keys, on the value covariance's eigenvalues for the values; float32 bases."""
+    budget = int(round(wl.allocation[1] * wl.head_dim))
+    alloc, pk, qk, pv = [], [], [], []
+    for h in range(wl.n_kv_heads):
+        mq, sk = W.query_covariance(wl, h), W.covariance(wl, "K", h)
+        w, _, _ = transform.nova_key_transform(mq, sk)
+        rk, b_k, _ = allocation.c1(w, budget, W.C1_RANKS)
+        wv, vv = transform.ordered_basis(W.covariance(wl, "V", h))
+        rv, b_v, _ = allocation.c1(wv, budget, W.C1_RANKS)
+        P, Q = transform.nova_key_bases(mq, sk, rk, W.hadamard_signs(wl, "K", h, rk))
+        alloc.append((rk, b_k, rv, b_v))
+        pk.append(P.astype(np.float32))
+        qk.append(Q.astype(np.float32))
+        pv.append(transform.folded_basis(vv, rv, W.hadamard_signs(wl, "V", h, rv)).astype(np.float32))
+    return alloc, pk, qk, pv
+
+
+def key_pairs(pk, qk):
+    """The library's key basis array for a query_basis_k layout: per head P_K then Q_K."""
+    return codec.concat_bases([m for pair in zip(pk, qk) for m in pair])

@@ -173,3 +173,21 @@ def test_static_scale_word_matches_the_oracle():
             mu, sg = quantizer.static_scale(s, b)
             word = int(quantizer.fp16_bits(mu)) | (int(quantizer.fp16_bits(sg)) << 16)
             assert calib.static_scale_word(cov, P, b) == word, (h, r, b)
+
+
+def test_nova_key_bases_match_the_oracle():
+    """The product's attention-aware key bases against the oracle's: the oblique projector
+    P_K Q_K^T (invariant to eigenvector signs and to the Hadamard fold), biorthogonality,
+    and the coefficient variances that C1 uses."""
+    from oracle import transform as T
+
+    wl = W.llama_t128k_nova(2.0)
+    for h in range(3):
+        mq, sk = W.query_covariance(wl, h), W.covariance(wl, "K", h)
+        w_ref, _, _ = T.nova_key_transform(mq, sk)
+        for r in (16, 64):
+            P, Q, lam = calib.nova_key_bases(mq, sk, r, W.hadamard_signs(wl, "K", h, r))
+            Pr, Qr = T.nova_key_bases(mq, sk, r)
+            assert np.allclose(P.astype(np.float64) @ Q.astype(np.float64).T, Pr @ Qr.T, atol=1e-5)
+            assert np.allclose(P.astype(np.float64).T @ Q.astype(np.float64), np.eye(r), atol=1e-5)
+            assert np.allclose(lam, w_ref, rtol=1e-9, atol=1e-12 * w_ref.max())
