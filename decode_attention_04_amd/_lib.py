@@ -47,6 +47,9 @@ class _Layout(ctypes.Structure):
         ("scale_k", ctypes.POINTER(ctypes.c_uint32)),
         ("scale_v", ctypes.POINTER(ctypes.c_uint32)),
         ("query_basis_k", ctypes.c_int32),
+        ("page_tokens", ctypes.c_int32),
+        ("pool_pages", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p),
     ]
 
 
@@ -104,13 +107,16 @@ class Layout:
     head, the head's fixed quantizer for header-free records (fp16 bits of the min
     in bits 0-15, of the step in bits 16-31).  ``query_basis_k``: each head's key basis
     block holds the encode basis P_K then the query basis Q_K (a non-orthogonal key
-    transform; keys are reconstructed as Q_K c^).
+    transform; keys are reconstructed as Q_K c^).  ``page_tokens`` > 0 makes the caches
+    paged: each head's region is a pool of ``pool_pages`` pages and ``block_table`` (a
+    device int32 tensor [batch, capacity // page_tokens]) maps each sequence's logical
+    pages to pool pages.
     """
 
     def __init__(self, n_kv_heads: int, n_q_heads: int, batch: int, capacity: int,
                  alloc: Sequence[Tuple[int, int, int, int]], head_dim: int = 128,
                  scale_k: Optional[Sequence[int]] = None, scale_v: Optional[Sequence[int]] = None,
-                 query_basis_k: bool = False):
+                 query_basis_k: bool = False, page_tokens: int = 0, pool_pages: int = 0, block_table=None):
         if len(alloc) != n_kv_heads:
             raise ValueError("alloc needs one (rank_k, bits_k, rank_v, bits_v) per KV head")
         self.head_dim, self.n_kv_heads, self.n_q_heads = head_dim, n_kv_heads, n_q_heads
@@ -134,7 +140,9 @@ class Layout:
                           self._rk, self._bk, self._rv, self._bv,
                           ctypes.cast(self._sk, ctypes.POINTER(ctypes.c_uint32)) if self._sk else None,
                           ctypes.cast(self._sv, ctypes.POINTER(ctypes.c_uint32)) if self._sv else None,
-                          int(self.query_basis_k))
+                          int(self.query_basis_k), int(page_tokens), int(pool_pages), _ptr(block_table) or None)
+        self.page_tokens, self.pool_pages = int(page_tokens), int(pool_pages)
+        self._block_table = block_table  # keeps the tensor alive while the layout is used
 
     @property
     def group(self) -> int:

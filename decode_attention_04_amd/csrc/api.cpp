@@ -59,6 +59,7 @@ uint32_t call_nonce() {
 struct Layout {
   int n_kv = 0, n_q = 0, batch = 0, group = 0;
   int64_t capacity = 0;
+  Paging pg{};                                  // bt == null: contiguous records
   int64_t words_k = 0, words_v = 0;            // cache sizes in 32-bit words
   int64_t basis_k_floats = 0, basis_v_floats = 0;
   HeadTable table{};
@@ -81,6 +82,23 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
     return fail(KV_ERR_INVALID, "allocation arrays must be non-NULL host pointers");
   if (L->query_basis_k != 0 && L->query_basis_k != 1)
     return fail(KV_ERR_INVALID, "query_basis_k must be 0 or 1");
+  if (L->page_tokens < 0) return fail(KV_ERR_INVALID, "page_tokens %d < 0", L->page_tokens);
+  if (L->page_tokens > 0) {
+    if (L->page_tokens % 64 != 0)
+      return fail(KV_ERR_INVALID, "page_tokens %d is not a multiple of 64", L->page_tokens);
+    if (L->capacity % L->page_tokens != 0)
+      return fail(KV_ERR_INVALID, "capacity %lld is not a multiple of page_tokens %d", (long long)L->capacity,
+                  L->page_tokens);
+    if (L->pool_pages < 1) return fail(KV_ERR_INVALID, "pool_pages %lld < 1", (long long)L->pool_pages);
+    if (!L->block_table || !aligned(L->block_table, 4))
+      return fail(KV_ERR_INVALID, "a paged layout needs a 4-byte aligned device block table");
+    out.pg.bt = L->block_table;
+    out.pg.page = L->page_tokens;
+    out.pg.pages_per_seq = (int32_t)(L->capacity / L->page_tokens);
+    out.pg.pool_pages = L->pool_pages;
+  }
+  // records of one head's region: the sequences' own, or the pool's
+  const int64_t region_recs = L->page_tokens > 0 ? L->pool_pages * L->page_tokens : (int64_t)L->batch * L->capacity;
   out.n_kv = L->n_kv_heads;
   out.n_q = L->n_q_heads;
   out.batch = L->batch;
@@ -117,18 +135,19 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
     d.boff_v = (int32_t)bv_total;
     d.base_k = wk_total;
     d.base_v = wv_total;
-    wk_total += (int64_t)L->batch * L->capacity * d.wk;
-    wv_total += (int64_t)L->batch * L->capacity * d.wv;
+    wk_total += region_recs * d.wk;
+    wv_total += region_recs * d.wv;
     bk_total += (int64_t)kHeadDim * rk * (L->query_basis_k ? 2 : 1);
     bv_total += (int64_t)kHeadDim * rv;
   }
-  // kernels address one (sequence, head) region with 32-bit byte offsets
+  // kernels address one (sequence, head) region, or one head's pool, with 32-bit byte offsets
+  const int64_t span = L->page_tokens > 0 ? region_recs : L->capacity;
   for (int h = 0; h < L->n_kv_heads; ++h) {
-    const int64_t region = L->capacity * 4 * (int64_t)(out.table.h[h].wk > out.table.h[h].wv ? out.table.h[h].wk
-                                                                                            : out.table.h[h].wv);
+    const int64_t region = span * 4 * (int64_t)(out.table.h[h].wk > out.table.h[h].wv ? out.table.h[h].wk
+                                                                                      : out.table.h[h].wv);
     if (region >= ((int64_t)1 << 31))
-      return fail(KV_ERR_UNSUPPORTED, "capacity %lld too large: one sequence's records of a head must stay below 2 GiB",
-                  (long long)L->capacity);
+      return fail(KV_ERR_UNSUPPORTED, "%s too large: the records a kernel addresses in one region must stay below 2 GiB",
+                  L->page_tokens > 0 ? "pool" : "capacity");
   }
   out.words_k = wk_total;
   out.words_v = wv_total;
@@ -354,6 +373,7 @@ kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_
   a.n_tokens = n_tokens;
   a.lengths = lengths;
   a.capacity = L.capacity;
+  a.pg = L.pg;
   a.split_tokens = w.split_tokens;
   a.n_splits = w.n_splits;
   a.wg_per_row = w.wg_per_row;
@@ -458,6 +478,7 @@ kv_status kv_encode(const kv_layout* layout, const void* k, const void* v, kv_dt
   a.n_tokens = n_tokens;
   a.pos0 = pos0;
   a.capacity = L.capacity;
+  a.pg = L.pg;
   a.n_kv_heads = L.n_kv;
   a.batch = L.batch;
   a.dtype = dtype == KV_F32 ? 0 : 1;
@@ -584,6 +605,7 @@ kv_status kv_decode(const kv_layout* layout, int32_t which, int64_t n_tokens, in
   a.n_tokens = n_tokens;
   a.pos0 = pos0;
   a.capacity = L.capacity;
+  a.pg = L.pg;
   a.n_kv_heads = L.n_kv;
   a.batch = L.batch;
   a.which = which;

@@ -666,7 +666,22 @@ struct WaveCtx {
   int h, b;                 // KV head and sequence of this workgroup
   int64_t unit;             // sequence * n_kv_heads + KV head
   uint64_t* stamp;          // this workgroup's phase stamps (diagnostic builds), else null
+  const int32_t* bt_row;    // paged: this sequence's block-table row, else null
+  int page;                 // paged: tokens per page
+  uint32_t pool_recs;       // paged: records in a head's pool (an offset past them reads zeros)
+  int64_t pool_pages;
 };
+
+// Record index, within the buffer resource of the wave's cache regions, of the tile
+// that starts at token t0 (a multiple of 64: a tile never crosses a page): t0 for
+// contiguous records, its pool slot for paged ones (past the pool, so that the copy
+// reads zeros, for a block-table entry outside it).
+__device__ inline uint32_t tile_rec(const WaveCtx& c, int t0) {
+  if (!c.bt_row) return (uint32_t)t0;
+  const int p = __builtin_amdgcn_readfirstlane(c.bt_row[t0 / c.page]);
+  if (p < 0 || (int64_t)p >= c.pool_pages) return c.pool_recs;
+  return (uint32_t)p * (uint32_t)c.page + (uint32_t)(t0 % c.page);
+}
 
 // Key operand (A of the score MFMA) for one (K-step, lane): row = head (lane % 16),
 // element of pair slot = q~_j * 2^(E_head - s), split into fp16 hi + lo.  PACK =
@@ -1033,10 +1048,18 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   c.t_end = c.t_begin + wq;
   if (c.t_end > n_tok) c.t_end = n_tok;
   const int wk = hd.wk, wv = hd.wv;
-  const uint32_t* kreg = a.cache_k + hd.base_k + (int64_t)b * a.capacity * wk;
-  const uint32_t* vreg = a.cache_v + hd.base_v + (int64_t)b * a.capacity * wv;
-  c.rk_ = make_rsrc(kreg, (uint32_t)a.capacity * 4u * wk);
-  c.rv_ = make_rsrc(vreg, (uint32_t)a.capacity * 4u * wv);
+  // buffer resources over the sequence's records (contiguous) or the head's pool (paged)
+  const bool paged = a.pg.bt != nullptr;
+  const int64_t rbase = paged ? 0 : (int64_t)b * a.capacity;
+  const uint32_t nrec = paged ? (uint32_t)(a.pg.pool_pages * a.pg.page) : (uint32_t)a.capacity;
+  const uint32_t* kreg = a.cache_k + hd.base_k + rbase * wk;
+  const uint32_t* vreg = a.cache_v + hd.base_v + rbase * wv;
+  c.rk_ = make_rsrc(kreg, nrec * 4u * wk);
+  c.rv_ = make_rsrc(vreg, nrec * 4u * wv);
+  c.bt_row = paged ? a.pg.bt + (int64_t)b * a.pg.pages_per_seq : nullptr;
+  c.page = a.pg.page;
+  c.pool_recs = nrec;
+  c.pool_pages = a.pg.pool_pages;
   c.kbuf = a.kbuf_words;
   c.vbuf = a.vbuf_words;
   c.nbuf = a.nbuf;
@@ -1053,7 +1076,9 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
 
   // append fused with attention: the workgroup whose split holds the new token
   // encodes its key and value (waves 0-1 and 2-3) before any of its tiles stream in
-  if (a.append_pos >= s_begin && a.append_pos < s_end) {
+  const int64_t append_rec = a.append_pos >= s_begin && a.append_pos < s_end
+                                 ? record_index(a.pg, a.capacity, b, a.append_pos) : -1;
+  if (append_rec >= 0) {
     EncodeScratch* scr = (EncodeScratch*)scores;  // score and tile areas are not in use yet
     const int tensor = tid >> 7, t = tid & 127;
     const int r = tensor ? hd.rv : hd.rk, bits = tensor ? hd.bv : hd.bk, W = tensor ? hd.wv : hd.wk;
@@ -1062,8 +1087,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
     const int64_t xo = ((int64_t)b * a.n_kv_heads + h) * kHeadDim;
     // the fused entry point hands writable caches (kv_append_attend_decode)
-    uint32_t* rec = const_cast<uint32_t*>(tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) +
-                    ((int64_t)b * a.capacity + a.append_pos) * W;
+    uint32_t* rec = const_cast<uint32_t*>(tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + append_rec * W;
     auto sync = [] { __syncthreads(); };
     if (a.append_dtype == 0)
       encode_token_128((const float*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, hdr, sw, rec, scr[tensor], t, sync);

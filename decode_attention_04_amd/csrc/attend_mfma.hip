@@ -68,8 +68,9 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
       const int t0 = t_begin + t * kTileT;
       if (t0 < t_end) {
         const int nn = (t_end - t0) < kTileT ? (t_end - t0) : kTileT;
-        tile_copy(c.rk_, (uint32_t)t0 * 4u * wk, (uint32_t)nn * 4u * wk, kl + 4u * (uint32_t)(t * c.kbuf));
-        tile_copy(c.rv_, (uint32_t)t0 * 4u * wv, (uint32_t)nn * 4u * wv, vl + 4u * (uint32_t)(t * c.vbuf));
+        const uint32_t r0 = tile_rec(c, t0);
+        tile_copy(c.rk_, r0 * 4u * wk, (uint32_t)nn * 4u * wk, kl + 4u * (uint32_t)(t * c.kbuf));
+        tile_copy(c.rv_, r0 * 4u * wv, (uint32_t)nn * 4u * wv, vl + 4u * (uint32_t)(t * c.vbuf));
       }
     }
   });
@@ -93,8 +94,9 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
       const int nn = (t_end - tn) < kTileT ? (t_end - tn) : kTileT;
       int sn = slot + nbuf - 1;
       sn = sn >= nbuf ? sn - nbuf : sn;
-      tile_copy(c.rk_, (uint32_t)tn * 4u * wk, (uint32_t)nn * 4u * wk, c.ktile + sn * c.kbuf);
-      tile_copy(c.rv_, (uint32_t)tn * 4u * wv, (uint32_t)nn * 4u * wv, c.vtile + sn * c.vbuf);
+      const uint32_t rn = tile_rec(c, tn);
+      tile_copy(c.rk_, rn * 4u * wk, (uint32_t)nn * 4u * wk, c.ktile + sn * c.kbuf);
+      tile_copy(c.rv_, rn * 4u * wv, (uint32_t)nn * 4u * wv, c.vtile + sn * c.vbuf);
     }
     progress_priority(t0, t_begin, t_end);
     if constexpr (GEN) {
@@ -121,8 +123,9 @@ __device__ __attribute__((always_inline)) inline void generic_tiles(const Attend
     if (nbuf == 1) {
       if (t1 < t_end) {  // single buffer: refill after the tile is consumed
         const int n1 = (t_end - t1) < kTileT ? (t_end - t1) : kTileT;
-        tile_copy(c.rk_, (uint32_t)t1 * 4u * wk, (uint32_t)n1 * 4u * wk, c.ktile);
-        tile_copy(c.rv_, (uint32_t)t1 * 4u * wv, (uint32_t)n1 * 4u * wv, c.vtile);
+        const uint32_t r1 = tile_rec(c, t1);
+        tile_copy(c.rk_, r1 * 4u * wk, (uint32_t)n1 * 4u * wk, c.ktile);
+        tile_copy(c.rv_, r1 * 4u * wv, (uint32_t)n1 * 4u * wv, c.vtile);
       }
     } else {
       slot = slot + 1 == nbuf ? 0 : slot + 1;

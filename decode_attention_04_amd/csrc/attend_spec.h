@@ -62,13 +62,14 @@ template <int WK, int WV>
 __device__ __attribute__((always_inline)) inline void issue_tile(const WaveCtx& c, int t0, int t_end, int slot) {
   uint32_t* kd = c.ktile + slot * c.kbuf;
   uint32_t* vd = c.vtile + slot * c.vbuf;
+  const uint32_t r0 = tile_rec(c, t0);
   if (t0 + kTileT <= t_end) {
-    tile_copy_n<64u * 4u * WK>(c.rk_, (uint32_t)t0 * 4u * WK, kd);
-    tile_copy_n<64u * 4u * WV>(c.rv_, (uint32_t)t0 * 4u * WV, vd);
+    tile_copy_n<64u * 4u * WK>(c.rk_, r0 * 4u * WK, kd);
+    tile_copy_n<64u * 4u * WV>(c.rv_, r0 * 4u * WV, vd);
   } else {
     const uint32_t nn = (uint32_t)(t_end - t0);
-    tile_copy(c.rk_, (uint32_t)t0 * 4u * WK, nn * 4u * WK, kd);
-    tile_copy(c.rv_, (uint32_t)t0 * 4u * WV, nn * 4u * WV, vd);
+    tile_copy(c.rk_, r0 * 4u * WK, nn * 4u * WK, kd);
+    tile_copy(c.rv_, r0 * 4u * WV, nn * 4u * WV, vd);
   }
 }
 

@@ -71,7 +71,9 @@ __global__ __launch_bounds__(256) void append_kernel(EncodeArgs a) {
   const uint32_t sw = tensor ? hd.sv : hd.sk;
   const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
   const T* x = (const T*)(tensor ? a.v : a.k) + ((int64_t)b * a.n_kv_heads + h) * kHeadDim;
-  uint32_t* rec = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + ((int64_t)b * a.capacity + a.pos0) * W;
+  const int64_t ri = record_index(a.pg, a.capacity, b, a.pos0);
+  if (ri < 0) return;  // the whole block: both tensors share the block table
+  uint32_t* rec = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + ri * W;
   encode_token_128(x, P, r, bits, hdr, sw, rec, scr[tensor], t, [] { __syncthreads(); });
 }
 
@@ -89,13 +91,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int W = a.which ? hd.wv : hd.wk, hdr = a.which ? hd.hv : hd.hk;
   const uint32_t sw = a.which ? hd.sv : hd.sk;
   const float* P = a.basis + (a.which ? hd.boff_v : hd.qoff_k);  // keys: reconstructed through Q_K
-  const uint32_t* reg = a.cache + (a.which ? hd.base_v : hd.base_k) + ((int64_t)b * a.capacity + a.pos0) * W;
+  const uint32_t* reg = a.cache + (a.which ? hd.base_v : hd.base_k);
   const int nt = (int)((a.n_tokens - t0) < 16 ? (a.n_tokens - t0) : 16);
   for (int e = threadIdx.x; e < 16 * r; e += 256) {
     const int tt = e / r, j = e - tt * r;
     float v = 0.0f;
-    if (tt < nt) {
-      const uint32_t* rec = reg + (t0 + tt) * W;
+    const int64_t ri = tt < nt ? record_index(a.pg, a.capacity, b, a.pos0 + t0 + tt) : -1;
+    if (ri >= 0) {  // a page outside the pool reconstructs as zeros
+      const uint32_t* rec = reg + ri * W;
       const uint32_t w0 = hdr ? rec[0] : sw;
       const float mu = f16_bits_to_f32(w0 & 0xFFFFu), sg = f16_bits_to_f32(w0 >> 16);
       v = fmaf(sg, (float)unpack_code(rec + hdr, j, bits), mu);  // one rounding to float32

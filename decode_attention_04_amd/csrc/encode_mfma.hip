@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
   const int WI = W + 1 - hdr;                       // words of a record assembled in LDS (header slot first)
   const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
   const T* xu = (const T*)(tensor ? a.v : a.k) + ((int64_t)b * a.n_kv_heads + h) * a.n_tokens * kHeadDim;
-  uint32_t* cu = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + ((int64_t)b * a.capacity + a.pos0) * W;
+  uint32_t* region = tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k;  // the head's records
 
   // stage the basis as A operands: for (mb, ks, lane) the eight rows 32ks + 8G ..
   // of column 16mb + m, hi parts then (64 lanes later) lo parts; the basis is scaled
@@ -467,17 +467,19 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
       }
       wave_sync();
 
-      // store the block's records (consecutive tokens are contiguous); f / W as a
+      // store the block's records, each at its record index (consecutive for
+      // contiguous caches, through the block table for paged ones); f / W as a
       // multiply-high by ceil(2^32 / W), exact for f < 2^16 (a one-word header-free
       // record, whose magic would not fit 32 bits, is its own quotient)
       const int64_t btok0 = wtok0 + 16 * nt;
       for (int f = lane; f < 16 * W; f += 64) {
         const int tn = W == 1 ? f : (int)__umulhi((uint32_t)f, wmagic), wi = f - tn * W + 1 - hdr;
-        if (btok0 + tn < a.n_tokens) {
+        const int64_t ri = btok0 + tn < a.n_tokens ? record_index(a.pg, a.capacity, b, a.pos0 + btok0 + tn) : -1;
+        if (ri >= 0) {
           uint32_t word;
           if (pow2) word = recw[tn * WI + wi];
           else word = wi == 0 ? hdrw[tn] : pack_word(wb + tn * R, R, bits, wi - 1);
-          cu[btok0 * W + f] = word;
+          region[ri * W + (f - tn * W)] = word;
         }
       }
       wave_sync();

@@ -46,6 +46,26 @@ struct HeadTable {
   HeadDesc h[kMaxKvHeads];
 };
 
+// Where the records of a sequence live within its head's cache region: contiguous
+// (bt == null: token t of sequence b is record b * capacity + t) or paged (token t
+// in pool page bt[b * pages_per_seq + t / page], slot t % page; the region is the
+// head's pool of pool_pages pages).
+struct Paging {
+  const int32_t* bt;      // DEVICE [batch][pages_per_seq] block table, or null
+  int32_t page;           // tokens per page (a multiple of 64)
+  int32_t pages_per_seq;  // capacity / page
+  int64_t pool_pages;     // pages in each head's pool
+};
+
+// Record index of token t of sequence b in its head's region, or -1 when the block
+// table names a page outside the pool (nothing is written there; reads see zeros).
+__device__ inline int64_t record_index(const Paging& pg, int64_t capacity, int b, int64_t t) {
+  if (!pg.bt) return (int64_t)b * capacity + t;
+  const int64_t p = pg.bt[(int64_t)b * pg.pages_per_seq + t / pg.page];
+  if (p < 0 || p >= pg.pool_pages) return -1;
+  return p * pg.page + t % pg.page;
+}
+
 // ------------------------------------------------------------------ fp16 helpers
 // Round a double to the nearest binary16 (ties to even) in one step, returning
 // the bit pattern.  Handles subnormal results, overflow to infinity and NaN.

@@ -19,6 +19,7 @@ struct EncodeArgs {
   int64_t n_tokens;
   int64_t pos0;
   int64_t capacity;
+  Paging pg;
   int32_t n_kv_heads;
   int32_t batch;
   int32_t dtype;  // 0 = f32, 1 = f16
@@ -38,6 +39,7 @@ struct AttendArgs {
   int64_t n_tokens;
   const int32_t* lengths;  // [batch] per-sequence context lengths (device), or null: n_tokens for all
   int64_t capacity;
+  Paging pg;
   int64_t split_tokens;
   int32_t n_splits;    // the largest per-head split count: the stride of `part`
   int32_t wg_per_row;  // workgroups per sequence: the sum of the heads' split counts
@@ -68,6 +70,7 @@ struct DecodeArgs {
   int64_t n_tokens;
   int64_t pos0;
   int64_t capacity;
+  Paging pg;
   int32_t n_kv_heads;
   int32_t batch;
   int32_t which;          // 0 = K, 1 = V

@@ -37,6 +37,17 @@
  *   head-major regions; region h holds batch x capacity records of W_h words
  *   (one word fewer for header-free records);
  *   record (h, b, t) starts at word  sum_{h'<h} batch*capacity*W_h'  +  (b*capacity + t)*W_h.
+ * Paged cache layout (page_tokens > 0): region h is a pool of pool_pages pages of
+ *   page_tokens records; logical page p of sequence b is pool page
+ *   P = block_table[b][p], and record (h, b, t) starts at word
+ *   sum_{h'<h} pool_pages*page_tokens*W_h'  +  (P*page_tokens + t % page_tokens)*W_h
+ *   with P = block_table[b][t / page_tokens].  capacity (a multiple of
+ *   page_tokens) is the longest sequence; sequences may share no page (the
+ *   library does not check).  A block-table entry outside [0, pool_pages) is
+ *   never written through and its records read as zeros.  The block table is
+ *   read by the kernels on `stream`, so earlier work on the stream may update it.
+ *   [PagedAttention, cited among the pages' serving systems; the records keep
+ *   their fixed width, so a page is a plain array of them]
  *
  * Basis layout: the heads' bases concatenated, head h is a row-major
  *   head_dim x r_h float32 matrix (element (i, j) at offset_h + i*r_h + j),
@@ -108,6 +119,11 @@ typedef struct kv_layout {
   const uint32_t *scale_v; /* HOST [n_kv_heads] or NULL */
   int32_t query_basis_k;   /* 0: orthonormal key bases; 1: each head's key basis block holds
                               the encode basis P_K then the query basis Q_K (see below) */
+  int32_t page_tokens;     /* 0: each sequence's records contiguous (see the cache layout);
+                              > 0: paged records, pages of this many tokens (a multiple of 64) */
+  int64_t pool_pages;      /* paged: pages in each head's pool */
+  const int32_t *block_table; /* paged: DEVICE int32 [batch][capacity / page_tokens], the pool
+                              page holding each logical page of each sequence */
 } kv_layout;
 
 /* Words per record with its header, 1 + ceil(rank*bits/32) (a header-free

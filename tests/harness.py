@@ -207,3 +207,51 @@ def oracle_calibrate_nova(wl: W.Workload):
 def key_pairs(pk, qk):
     """The library's key basis array for a query_basis_k layout: per head P_K then Q_K."""
     return codec.concat_bases([m for pair in zip(pk, qk) for m in pair])
+
+
+def to_pool(cache, ranks, bits, batch, capacity, page, pool_pages, table, fill=0xA5A5A5A5, static=None):
+    """The paged form of a contiguous cache: head h's pool holds, at pool page table[b][p],
+    the records of logical page p of sequence b; pool pages no entry names hold `fill`.
+    Entries outside [0, pool_pages) are skipped."""
+    cache = np.asarray(cache, np.uint32)
+    flags = static if static is not None else [False] * len(ranks)
+    src = codec.region_offsets(ranks, bits, batch, capacity, flags)
+    widths = [codec.width(r, b, f) for r, b, f in zip(ranks, bits, flags)]
+    dst = np.concatenate([[0], np.cumsum([pool_pages * page * w for w in widths])]).astype(np.int64)
+    pool = np.full(dst[-1], fill, np.uint32)
+    for h, w in enumerate(widths):
+        for b in range(batch):
+            for p in range(capacity // page):
+                P = int(table[b][p])
+                if not 0 <= P < pool_pages:
+                    continue
+                s0 = src[h] + (b * capacity + p * page) * w
+                d0 = dst[h] + P * page * w
+                pool[d0:d0 + page * w] = cache[s0:s0 + page * w]
+    return pool
+
+
+def from_pool(pool, ranks, bits, batch, capacity, page, pool_pages, table, fill=0, static=None):
+    """The contiguous form of a paged cache (pages an entry does not name: `fill`)."""
+    pool = np.asarray(pool, np.uint32)
+    flags = static if static is not None else [False] * len(ranks)
+    widths = [codec.width(r, b, f) for r, b, f in zip(ranks, bits, flags)]
+    src = np.concatenate([[0], np.cumsum([pool_pages * page * w for w in widths])]).astype(np.int64)
+    dst = codec.region_offsets(ranks, bits, batch, capacity, flags)
+    out = np.full(dst[-1], fill, np.uint32)
+    for h, w in enumerate(widths):
+        for b in range(batch):
+            for p in range(capacity // page):
+                P = int(table[b][p])
+                if not 0 <= P < pool_pages:
+                    continue
+                d0 = dst[h] + (b * capacity + p * page) * w
+                s0 = src[h] + P * page * w
+                out[d0:d0 + page * w] = pool[s0:s0 + page * w]
+    return out
+
+
+def block_table(seed, batch, pages_per_seq, pool_pages):
+    """A seeded block table: distinct pool pages for every (sequence, logical page)."""
+    rng = np.random.default_rng(seed)
+    return rng.permutation(pool_pages)[: batch * pages_per_seq].reshape(batch, pages_per_seq).astype(np.int32)

@@ -266,3 +266,19 @@ def test_attend_plan_reports_the_kernel_class():
     big_group = lib_mod.Layout(1, 12, 1, 1000, [(64, 4, 64, 4)])
     assert lib_mod.kv_attend_plan(big_group, 1000)[0] == -1
     assert lib_mod.kv_attend_plan(uni, T, 4096)[1] == (T + 4095) // 4096
+
+
+def test_paged_layout_sizes_and_validation():
+    """A paged cache holds pool_pages x page_tokens records per head; the page size, the
+    capacity and the block table are checked before any launch."""
+    alloc = [(16, 4, 32, 4), (128, 2, 64, 4)]
+    lay = lib_mod.Layout(2, 8, 3, 1024, alloc)
+    lay._c.page_tokens, lay._c.pool_pages, lay._c.block_table = 256, 20, 256  # a dummy device address
+    rk, bk, rv, bv = zip(*alloc)
+    out = ctypes.c_size_t()
+    assert L.kv_cache_bytes(lay.ref(), 0, ctypes.byref(out)) == lib_mod.KV_OK
+    assert out.value == 4 * sum(20 * 256 * codec.width(r, b) for r, b in zip(rk, bk))
+    for page, pool, table, cap in ((100, 20, 256, 1024), (256, 0, 256, 1024), (256, 20, 0, 1024),
+                                   (256, 20, 258, 1024), (256, 20, 256, 1000), (-64, 20, 256, 1024)):
+        lay._c.page_tokens, lay._c.pool_pages, lay._c.block_table, lay._c.capacity = page, pool, table, cap
+        assert L.kv_cache_bytes(lay.ref(), 0, ctypes.byref(out)) == lib_mod.KV_ERR_INVALID, (page, pool, table, cap)
