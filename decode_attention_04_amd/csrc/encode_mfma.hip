@@ -62,27 +62,6 @@ __device__ inline void load8(const float* p, float (&f)[8]) {
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// Exact (float64) coordinate j of the token whose 128 inputs start at `row`,
-// summed in the fixed order of the encoder (rows 32q .. 32q+31 in order, q = 0..3,
-// then ((g0 + g1) + g2) + g3), with the basis P (128 x R, fp32) from memory.
-template <typename T>
-__device__ inline double exact_coord(const T* row, const float* P, int R, int j) {
-  double g[kRowGroups];
-#pragma unroll 1
-  for (int q = 0; q < kRowGroups; ++q) {
-    double acc = 0.0;
-#pragma unroll 1
-    for (int c8 = 0; c8 < 4; ++c8) {
-      float xv[8];
-      load8(row + 32 * q + 8 * c8, xv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc = fma((double)xv[i], (double)P[(32 * q + 8 * c8 + i) * R + j], acc);
-    }
-    g[q] = acc;
-  }
-  return ((g[0] + g[1]) + g[2]) + g[3];
-}
-
 __device__ inline uint32_t h16_bits(float x) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x); }
 
 // Four codes (bytes of v, codes < 16) as one 16-bit field, and (codes < 4) as one byte.
@@ -119,11 +98,14 @@ __device__ inline uint32_t item_code(int nt, int n, int G, int s) {
   return ((uint32_t)(16 * nt + n) << 8) | (uint32_t)(16 * (s >> 2) + 4 * G + (s & 3));
 }
 
-constexpr int kRepairList = 64;  // items one wave recomputes together (more: lane by lane)
+constexpr int kRepairList = 64;  // items one wave recomputes per round
 
 // Exact values of the `cnt` listed coordinates (cnt <= kRepairList), four lanes per
 // item, lane 4i + q summing rows 32q .. 32q+31 of item i in order; the group sums
-// are added in the fixed order, so each value equals exact_coord's.
+// are added in the fixed order, so each value is the float64 encoder's.  A lane
+// issues all 64 loads of its row group (32 inputs, 32 basis elements) before the
+// first product, so a round costs one memory latency.  P is the basis in memory or
+// its float32 copy in LDS.
 template <typename T>
 __device__ inline void coop_exact(const uint32_t* items, double* res, int cnt, const T* xu, int64_t wtok0,
                                   const float* P, int R, int lane) {
@@ -137,13 +119,16 @@ __device__ inline void coop_exact(const uint32_t* items, double* res, int cnt, c
       const uint32_t e = items[it];
       const T* row = xu + (wtok0 + (int64_t)(e >> 8)) * kHeadDim + 32 * q;
       const float* pc = P + 32 * q * R + (int)(e & 255u);
-#pragma unroll 1
-      for (int c8 = 0; c8 < 4; ++c8) {
-        float xv[8];
-        load8(row + 8 * c8, xv);
+      constexpr int kVec = 16 / sizeof(T);  // inputs per 16-byte load, kept packed
+      typedef T xvec __attribute__((ext_vector_type(kVec)));
+      xvec xv[32 / kVec];
+      float pv[32];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) g = fma((double)xv[i], (double)pc[(8 * c8 + i) * R], g);
-      }
+      for (int c = 0; c < 32 / kVec; ++c) xv[c] = *(const xvec*)(row + kVec * c);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) pv[i] = pc[i * R];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) g = fma((double)xv[i / kVec][i % kVec], (double)pv[i], g);
     }
     const double g0 = __shfl(g, l0), g1 = __shfl(g, l0 + 1), g2 = __shfl(g, l0 + 2), g3 = __shfl(g, l0 + 3);
     if (q == 0 && it < cnt) res[it] = ((g0 + g1) + g2) + g3;
@@ -151,12 +136,16 @@ __device__ inline void coop_exact(const uint32_t* items, double* res, int cnt, c
   wave_sync();
 }
 
-// Dynamic LDS: the basis as fp16 hi/lo A operands (R x 128 x 4 bytes), then per
-// wave one 16-token block: the records being assembled ([16][W] words, header
+// Dynamic LDS: the basis as fp16 hi/lo A operands (R x 128 x 4 bytes); for R <= 32
+// also the basis in float32 (the exact recomputations read it there; for larger R
+// it would cost a resident workgroup per CU, and they read it from memory); then
+// per wave one 16-token block: the records being assembled ([16][W] words, header
 // first) for b = 2, 4, 8, or the codes ([16][R] bytes) and headers for other b;
-// and the list of coordinates to recompute with their exact values.
+// and one round of coordinates to recompute with their exact values.
+__host__ __device__ constexpr bool enc_p32(int R) { return R <= 32; }
+__host__ __device__ constexpr int enc_base_bytes(int R) { return R * kHeadDim * (enc_p32(R) ? 8 : 4); }
 __host__ __device__ constexpr int enc_wave_bytes(int R) { return 16 * R + 128 + kRepairList * 12; }
-__host__ __device__ constexpr int enc_lds_bytes(int R) { return R * kHeadDim * 4 + kEncWaves * enc_wave_bytes(R); }
+__host__ __device__ constexpr int enc_lds_bytes(int R) { return enc_base_bytes(R) + kEncWaves * enc_wave_bytes(R); }
 
 // Grid: x = groups of `tiles_per_wg` token tiles, y = the (head, tensor) units of
 // rank R (keys of the heads in mask_k, then values of the heads in mask_v), z =
@@ -176,7 +165,7 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
   uint8_t* ab = (uint8_t*)enc_lds;
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, G = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint8_t* wb = ab + R * kHeadDim * 4 + wave * enc_wave_bytes(R);
+  uint8_t* wb = ab + enc_base_bytes(R) + wave * enc_wave_bytes(R);
   uint32_t* recw = (uint32_t*)wb;                  // b = 2, 4, 8: [16][W] words
   uint32_t* hdrw = (uint32_t*)(wb + 16 * R + 64);  // other b: header words
   double* res = (double*)(wb + 16 * R + 128);       // exact values of the listed coordinates
@@ -225,6 +214,10 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
     *(enc_half8*)dst = hi;
     *(enc_half8*)(dst + 1024) = lo;
   }
+  float* p32 = (float*)(ab + R * kHeadDim * 4);
+  if constexpr (enc_p32(R))
+    for (int q = tid; q < R * kHeadDim; q += 256) p32[q] = P[q];
+  const float* Px = enc_p32(R) ? (const float*)p32 : P;  // the basis the recomputations read
   __syncthreads();
 
   const float top = (float)((1 << bits) - 1);
@@ -374,31 +367,38 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
       if (__ballot(mine != 0)) {
         int total;
         const int off = wave_prefix(mine, lane, total);
-        const bool coop = total <= kRepairList;
-        if (coop) {
+        double emin[NT], emax[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          emin[nt] = __builtin_inf();
+          emax[nt] = -__builtin_inf();
+        }
+#pragma unroll 1
+        for (int base = 0; base < total; base += kRepairList) {  // rounds of kRepairList items
+          const int cnt = total - base < kRepairList ? total - base : kRepairList;
           int k = off;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
-            for (uint32_t m = cand[nt]; m; m &= m - 1u) items[k++] = item_code(nt, n, G, __builtin_ctz(m));
-          coop_exact(items, res, total, xu, wtok0, P, R, lane);
+            for (uint32_t m = cand[nt]; m; m &= m - 1u, ++k)
+              if (k >= base && k < base + cnt) items[k - base] = item_code(nt, n, G, __builtin_ctz(m));
+          coop_exact(items, res, cnt, xu, wtok0, Px, R, lane);
+          k = off;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            for (uint32_t m = cand[nt]; m; m &= m - 1u, ++k)
+              if (k >= base && k < base + cnt) {
+                emin[nt] = fmin(emin[nt], res[k - base]);
+                emax[nt] = fmax(emax[nt], res[k - base]);
+              }
         }
-        int k = off;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          double emin = __builtin_inf(), emax = -__builtin_inf();
-          const T* row = xu + (wtok0 + 16 * nt + n) * kHeadDim;
-          for (uint32_t m = cand[nt]; m; m &= m - 1u) {
-            const int s = __builtin_ctz(m);
-            const double v = coop ? res[k] : exact_coord(row, P, R, 16 * (s >> 2) + 4 * G + (s & 3));
-            ++k;
-            emin = fmin(emin, v);
-            emax = fmax(emax, v);
-          }
-          emin = fmin(emin, __shfl_xor(emin, 16));
-          emin = fmin(emin, __shfl_xor(emin, 32));
-          emax = fmax(emax, __shfl_xor(emax, 16));
-          emax = fmax(emax, __shfl_xor(emax, 32));
-          if (hbad[nt]) w0[nt] = quant_header(emin, emax, bits).word0;
+          double lo = emin[nt], hi = emax[nt];
+          lo = fmin(lo, __shfl_xor(lo, 16));
+          lo = fmin(lo, __shfl_xor(lo, 32));
+          hi = fmax(hi, __shfl_xor(hi, 16));
+          hi = fmax(hi, __shfl_xor(hi, 32));
+          if (hbad[nt]) w0[nt] = quant_header(lo, hi, bits).word0;
         }
         wave_sync();
       }
@@ -409,7 +409,6 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
     for (int nt = 0; nt < NT; ++nt) {
       const int64_t tok = wtok0 + 16 * nt + n;
       const bool valid = tok < a.n_tokens;
-      const T* row = xu + tok * kHeadDim;
       // q = (c - min) / step + 1/2, code = floor(q) clamped, unless q is within tol
       // of an integer (tol: the coordinate bound E, and 4u (2^b) for the fp32 steps)
       const float muf = f16_bits_to_f32(w0[nt] & 0xFFFFu), sgf = f16_bits_to_f32(w0[nt] >> 16);
@@ -439,29 +438,31 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
         else *(uint32_t*)(wb + n * R + j0) = v;
       }
       if (!sig_pos) fl = 0u;
-      if (__ballot(fl != 0u)) {  // exact codes of the flagged coordinates
+      if (__ballot(fl != 0u)) {  // exact codes of the flagged coordinates, in rounds
         int total;
         const int off = wave_prefix(__popc(fl), lane, total);
-        const bool coop = total <= kRepairList;
-        if (coop) {
-          int k = off;
-          for (uint32_t m = fl; m; m &= m - 1u) items[k++] = item_code(nt, n, G, __builtin_ctz(m));
-          coop_exact(items, res, total, xu, wtok0, P, R, lane);
-        }
         const double mu = (double)muf, sg = (double)sgf;
-        int k = off;
-        for (uint32_t m = fl; m; m &= m - 1u) {
-          const int s = __builtin_ctz(m);
-          const int j = 16 * (s >> 2) + 4 * G + (s & 3);
-          const uint32_t code = quant_code(coop ? res[k] : exact_coord(row, P, R, j), mu, sg, bits);
-          ++k;
-          if (pow2) {  // codes of other lanes share the word: atomic field update
-            const int bit = j * bits;
-            const uint32_t sh = bit & 31, fm = ((1u << bits) - 1u) << sh;
-            atomicAnd(rec + 1 + (bit >> 5), ~fm);
-            atomicOr(rec + 1 + (bit >> 5), code << sh);
-          } else {
-            wb[n * R + j] = (uint8_t)code;
+#pragma unroll 1
+        for (int base = 0; base < total; base += kRepairList) {
+          const int cnt = total - base < kRepairList ? total - base : kRepairList;
+          int k = off;
+          for (uint32_t m = fl; m; m &= m - 1u, ++k)
+            if (k >= base && k < base + cnt) items[k - base] = item_code(nt, n, G, __builtin_ctz(m));
+          coop_exact(items, res, cnt, xu, wtok0, Px, R, lane);
+          k = off;
+          for (uint32_t m = fl; m; m &= m - 1u, ++k) {
+            if (k < base || k >= base + cnt) continue;
+            const int s = __builtin_ctz(m);
+            const int j = 16 * (s >> 2) + 4 * G + (s & 3);
+            const uint32_t code = quant_code(res[k - base], mu, sg, bits);
+            if (pow2) {  // codes of other lanes share the word: atomic field update
+              const int bit = j * bits;
+              const uint32_t sh = bit & 31, fm = ((1u << bits) - 1u) << sh;
+              atomicAnd(rec + 1 + (bit >> 5), ~fm);
+              atomicOr(rec + 1 + (bit >> 5), code << sh);
+            } else {
+              wb[n * R + j] = (uint8_t)code;
+            }
           }
         }
       }
