@@ -20,4 +20,4 @@ Pinned by the ``-m "not gpu"`` tests against closed forms, hand-worked
 examples (``tests/golden``), brute force and textbook special cases.  No
 function here is "parity unpinned".
 """
-from . import allocation, attention, codec, packing, quantizer, transform  # noqa: F401
+from . import allocation, attention, codec, packing, quantizer, transform, vq  # noqa: F401
