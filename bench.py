@@ -214,7 +214,8 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
     kclass = K.kv_attend_plan(lay, T)[0]
     return {**extra, "batch": B, "n_q_heads": hq, "n_kv_heads": H, "context_tokens": T,
             "allocation": [list(a) for a in alloc],
-            "kernel": "generic" if kclass < 0 else (f"budget class {kclass}" if kclass < 6 else "frozen layout class"),
+            "kernel": "generic" if kclass < 0 else (f"budget class {kclass}" if kclass < 6 else
+                                                  "vector-quantized class" if kclass == 6 else "frozen layout class"),
             "us_per_step": round(us, 2), "GB_per_s": round(gbs, 1),
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "layer_caches_rotated": n_rep}
 

@@ -50,6 +50,10 @@ class _Layout(ctypes.Structure):
         ("page_tokens", ctypes.c_int32),
         ("pool_pages", ctypes.c_int64),
         ("block_table", ctypes.c_void_p),
+        ("vq_k", ctypes.c_int32),
+        ("vq_v", ctypes.c_int32),
+        ("codebook_k", ctypes.c_void_p),
+        ("codebook_v", ctypes.c_void_p),
     ]
 
 
@@ -110,13 +114,16 @@ class Layout:
     transform; keys are reconstructed as Q_K c^).  ``page_tokens`` > 0 makes the caches
     paged: each head's region is a pool of ``pool_pages`` pages and ``block_table`` (a
     device int32 tensor [batch, capacity // page_tokens]) maps each sequence's logical
-    pages to pool pages.
+    pages to pool pages.  ``codebook_k`` / ``codebook_v``: device uint32 (int32) tensors of
+    per-pair codebooks make that tensor's records vector-quantized over coordinate pairs
+    (the allocation's bits are then index bits per pair).
     """
 
     def __init__(self, n_kv_heads: int, n_q_heads: int, batch: int, capacity: int,
                  alloc: Sequence[Tuple[int, int, int, int]], head_dim: int = 128,
                  scale_k: Optional[Sequence[int]] = None, scale_v: Optional[Sequence[int]] = None,
-                 query_basis_k: bool = False, page_tokens: int = 0, pool_pages: int = 0, block_table=None):
+                 query_basis_k: bool = False, page_tokens: int = 0, pool_pages: int = 0, block_table=None,
+                 codebook_k=None, codebook_v=None):
         if len(alloc) != n_kv_heads:
             raise ValueError("alloc needs one (rank_k, bits_k, rank_v, bits_v) per KV head")
         self.head_dim, self.n_kv_heads, self.n_q_heads = head_dim, n_kv_heads, n_q_heads
@@ -140,9 +147,13 @@ class Layout:
                           self._rk, self._bk, self._rv, self._bv,
                           ctypes.cast(self._sk, ctypes.POINTER(ctypes.c_uint32)) if self._sk else None,
                           ctypes.cast(self._sv, ctypes.POINTER(ctypes.c_uint32)) if self._sv else None,
-                          int(self.query_basis_k), int(page_tokens), int(pool_pages), _ptr(block_table) or None)
+                          int(self.query_basis_k), int(page_tokens), int(pool_pages), _ptr(block_table) or None,
+                          2 if codebook_k is not None else 0, 2 if codebook_v is not None else 0,
+                          _ptr(codebook_k) or None, _ptr(codebook_v) or None)
         self.page_tokens, self.pool_pages = int(page_tokens), int(pool_pages)
-        self._block_table = block_table  # keeps the tensor alive while the layout is used
+        self.vq_k, self.vq_v = codebook_k is not None, codebook_v is not None
+        # keep the device tensors alive while the layout is used
+        self._block_table, self._codebooks = block_table, (codebook_k, codebook_v)
 
     @property
     def group(self) -> int:

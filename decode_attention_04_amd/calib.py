@@ -294,3 +294,100 @@ def calibrate_head_nova(cov_k, cov_v, query_cov, signs_k_for, signs_v_for, bits_
     rv, bv = c1_search(wv, budget, ranks)
     p, q, _ = nova_key_bases(query_cov, cov_k, rk, signs_k_for(rk))
     return (rk, bk, rv, bv), np.concatenate([p.reshape(-1), q.reshape(-1)]), fold(vv, rv, signs_v_for(rv))
+
+
+# ----------------------------------------------------------------- vector-quantized pairs
+# NOVA-KV abstract and pith.science verdict (key_machinery, referee_report): the
+# transform coefficients are grouped so that every group has about the same
+# volume (product of variances) -- sorted by log-variance and dealt out across
+# the groups -- and each group is vector-quantized with its own codebook of the
+# same size, trained by k-means on per-token RMS-normalised coefficients; the
+# record keeps a per-token scale.  Groups here are pairs; the deal goes back and
+# forth over the pairs (first to last, then last to first, ...), which makes the
+# volumes equal for a geometric spectrum.  The basis columns are reordered so
+# that pair j holds coordinates 2j and 2j + 1.
+
+
+def pair_order(variances: np.ndarray) -> np.ndarray:
+    """Column order of the pair grouping: entry 2j + s is the coefficient in slot s of pair j."""
+    v = np.asarray(variances, np.float64)
+    n = len(v)
+    pairs = n // 2
+    ranked = sorted(range(n), key=lambda i: (-math.log(v[i]), i))
+    order = np.empty(n, np.int64)
+    for k, i in enumerate(ranked):
+        sweep, pos = k // pairs, k % pairs
+        j = pos if sweep % 2 == 0 else pairs - 1 - pos
+        order[2 * j + sweep] = i
+    return order
+
+
+def rms_scales(coeffs: np.ndarray) -> np.ndarray:
+    """Per-token scale rho = fp16(root mean square of the coefficients), as float64."""
+    c = np.asarray(coeffs, np.float64)
+    return np.sqrt(np.mean(c * c, axis=1)).astype(np.float16).astype(np.float64)
+
+
+def lloyd_pairs(points: np.ndarray, start: np.ndarray, iters: int) -> np.ndarray:
+    """k-means (Lloyd) of every pair at once: points [n, pairs, 2], start [pairs, K, 2].
+    Each round assigns every point to the nearest codeword of its pair (first on
+    ties) and moves each codeword with points to their mean, for `iters` rounds; a
+    pair whose cells no longer change keeps its codewords, so the extra rounds of the
+    pairs that settled early change nothing."""
+    x = np.asarray(points, np.float64)
+    w = np.array(start, np.float64)
+    n, pairs, _ = x.shape
+    K = w.shape[1]
+    base = (np.arange(pairs) * K)[None, :]
+    for _ in range(iters):
+        d0 = x[:, :, 0:1] - w[None, :, :, 0]
+        d1 = x[:, :, 1:2] - w[None, :, :, 1]
+        cell = np.argmin(d0 * d0 + d1 * d1, axis=2)  # [n, pairs]
+        flat = (cell + base).reshape(-1)
+        cnt = np.bincount(flat, minlength=pairs * K).reshape(pairs, K)
+        for dim in range(2):
+            tot = np.bincount(flat, weights=x[:, :, dim].reshape(-1), minlength=pairs * K).reshape(pairs, K)
+            w[:, :, dim] = np.where(cnt > 0, tot / np.maximum(cnt, 1), w[:, :, dim])
+    return w
+
+
+def pair_codebooks(coeffs: np.ndarray, bits: int, starts: np.ndarray, iters: int) -> np.ndarray:
+    """fp16 codebooks [pairs, 2^bits, 2] (as float64) from training coefficients [n, r]
+    in pair order; starts[j] = 2^bits distinct training tokens that seed pair j."""
+    c = np.asarray(coeffs, np.float64)
+    rho = rms_scales(c)
+    u = np.where(rho[:, None] > 0, c / np.where(rho > 0, rho, 1.0)[:, None], 0.0)
+    pts = u.reshape(len(u), -1, 2)
+    st = np.asarray(starts)
+    start = np.stack([pts[st[j], j] for j in range(pts.shape[1])])
+    return lloyd_pairs(pts, start, iters).astype(np.float16).astype(np.float64)
+
+
+def codebook_words(codebooks: np.ndarray) -> np.ndarray:
+    """The library's codebook layout: one uint32 per codeword, fp16 of the even
+    coordinate in bits 0-15 and of the odd one in bits 16-31."""
+    h = np.asarray(codebooks, np.float64).astype(np.float16).view(np.uint16).astype(np.uint32)
+    return np.ascontiguousarray((h[..., 0] | (h[..., 1] << 16)).reshape(-1))
+
+
+def calibrate_head_nova_vq(cov_k, cov_v, query_cov, train_k, train_v, bits: int, starts_k, starts_v,
+                           iters: int):
+    """One KV head at full rank with vector-quantized pairs: keys through the
+    attention-aware transform, values through their covariance's eigenbasis, the
+    columns of both in pair order of their coefficient variances.  train_k / train_v:
+    training keys / values [n, d] (tokens the codebooks are fitted on).  Returns
+    ((128, bits, 128, bits), key basis block [P_K; Q_K] flat float32, P_V float32,
+    K codebook words, V codebook words)."""
+    d = np.asarray(cov_k).shape[0]
+    p, q, lam = nova_key_bases(query_cov, cov_k, d)
+    ok = pair_order(lam)
+    p, q = p[:, ok], q[:, ok]
+    wv, vv = sorted_directions(cov_v)
+    ov = pair_order(wv)
+    pv = np.ascontiguousarray(vv[:, ov], np.float32)
+    ck = np.asarray(train_k, np.float64) @ p.astype(np.float64)
+    cv = np.asarray(train_v, np.float64) @ pv.astype(np.float64)
+    cbk = pair_codebooks(ck, bits, starts_k, iters)
+    cbv = pair_codebooks(cv, bits, starts_v, iters)
+    block = np.concatenate([np.ascontiguousarray(p).reshape(-1), np.ascontiguousarray(q).reshape(-1)])
+    return (d, bits, d, bits), block, pv, codebook_words(cbk), codebook_words(cbv)

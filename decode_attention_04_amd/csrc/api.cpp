@@ -62,6 +62,9 @@ struct Layout {
   Paging pg{};                                  // bt == null: contiguous records
   int64_t words_k = 0, words_v = 0;            // cache sizes in 32-bit words
   int64_t basis_k_floats = 0, basis_v_floats = 0;
+  const uint32_t* cb_k = nullptr;  // codebooks of vector-quantized records, else null
+  const uint32_t* cb_v = nullptr;
+  bool vq = false;
   HeadTable table{};
 };
 
@@ -82,6 +85,20 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
     return fail(KV_ERR_INVALID, "allocation arrays must be non-NULL host pointers");
   if (L->query_basis_k != 0 && L->query_basis_k != 1)
     return fail(KV_ERR_INVALID, "query_basis_k must be 0 or 1");
+  for (int t = 0; t < 2; ++t) {
+    const int vq = t ? L->vq_v : L->vq_k;
+    const uint32_t* cb = t ? L->codebook_v : L->codebook_k;
+    const char* name = t ? "value" : "key";
+    if (vq != 0 && vq != 2)
+      return fail(KV_ERR_UNSUPPORTED, "vq_%c = %d: 0 (scalar codes) or 2 (coordinate pairs)", t ? 'v' : 'k', vq);
+    if (vq && (t ? L->scale_v : L->scale_k))
+      return fail(KV_ERR_INVALID, "vector-quantized %s records keep their per-token scale: no static scale", name);
+    if (vq && (!cb || !aligned(cb, 4)))
+      return fail(KV_ERR_INVALID, "vector-quantized %s records need a 4-byte aligned device codebook", name);
+  }
+  out.cb_k = L->vq_k ? L->codebook_k : nullptr;
+  out.cb_v = L->vq_v ? L->codebook_v : nullptr;
+  out.vq = L->vq_k || L->vq_v;
   if (L->page_tokens < 0) return fail(KV_ERR_INVALID, "page_tokens %d < 0", L->page_tokens);
   if (L->page_tokens > 0) {
     if (L->page_tokens % 64 != 0)
@@ -104,13 +121,15 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
   out.batch = L->batch;
   out.group = g;
   out.capacity = L->capacity;
-  int64_t wk_total = 0, wv_total = 0, bk_total = 0, bv_total = 0;
+  int64_t wk_total = 0, wv_total = 0, bk_total = 0, bv_total = 0, ck_total = 0, cv_total = 0;
   for (int h = 0; h < L->n_kv_heads; ++h) {
     const int rk = L->rank_k[h], bk = L->bits_k[h], rv = L->rank_v[h], bv = L->bits_v[h];
     if (!supported_rank(rk) || !supported_rank(rv))
       return fail(KV_ERR_UNSUPPORTED, "head %d: rank (%d, %d) not in {16, 32, 64, 128}", h, rk, rv);
     if (!supported_bits(bk) || !supported_bits(bv))
       return fail(KV_ERR_UNSUPPORTED, "head %d: bits (%d, %d) not in [2, 8]", h, bk, bv);
+    if ((L->vq_k && rk < 32) || (L->vq_v && rv < 32))
+      return fail(KV_ERR_UNSUPPORTED, "head %d: vector-quantized records need rank >= 32", h);
     for (int t = 0; t < 2; ++t) {
       const uint32_t* sc = t ? L->scale_v : L->scale_k;
       if (!sc) continue;
@@ -121,15 +140,18 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
     }
     HeadDesc& d = out.table.h[h];
     d.rk = rk;
-    d.bk = bk;
+    d.bk = bk + (L->vq_k ? kVq : 0);
     d.rv = rv;
-    d.bv = bv;
+    d.bv = bv + (L->vq_v ? kVq : 0);
     d.hk = L->scale_k ? 0 : 1;
     d.hv = L->scale_v ? 0 : 1;
-    d.sk = L->scale_k ? L->scale_k[h] : 0u;
-    d.sv = L->scale_v ? L->scale_v[h] : 0u;
-    d.wk = record_words(rk, bk, d.hk);
-    d.wv = record_words(rv, bv, d.hv);
+    // the static scale word, or the word offset of the head's codebook
+    d.sk = L->scale_k ? L->scale_k[h] : (uint32_t)ck_total;
+    d.sv = L->scale_v ? L->scale_v[h] : (uint32_t)cv_total;
+    ck_total += codebook_words(rk, d.bk);
+    cv_total += codebook_words(rv, d.bv);
+    d.wk = format_words(rk, d.bk, d.hk);
+    d.wv = format_words(rv, d.bv, d.hv);
     d.boff_k = (int32_t)bk_total;
     d.qoff_k = (int32_t)(bk_total + (L->query_basis_k ? (int64_t)kHeadDim * rk : 0));
     d.boff_v = (int32_t)bv_total;
@@ -356,6 +378,9 @@ kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_
     cnt = (uint32_t*)(ws + w.cnt);
     part = ws + w.part;
   }
+  if (L.vq && plan_attend(L.table, L.n_kv, L.group).spec_class < 0)
+    return fail(KV_ERR_UNSUPPORTED, "no decode kernel class holds this layout's vector-quantized formats "
+                "(or its group of %d query heads exceeds 8)", L.group);
   AttendArgs a{};
   a.heads = L.table;
   a.q = q;
@@ -363,6 +388,8 @@ kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_
   a.basis_v = basis_v;
   a.cache_k = cache_k;
   a.cache_v = cache_v;
+  a.cb_k = L.cb_k;
+  a.cb_v = L.cb_v;
   a.out = out;
   a.cnt = cnt;
   a.part = part;
@@ -435,7 +462,10 @@ kv_status kv_attend_plan(const kv_layout* layout, int64_t n_tokens, int64_t spli
   Workspace w;
   s = plan_workspace(L, n_tokens, split_tokens, w);
   if (s) return s;
-  if (kernel_class) *kernel_class = plan_attend(L.table, L.n_kv, L.group).spec_class;
+  const int cls = plan_attend(L.table, L.n_kv, L.group).spec_class;
+  if (L.vq && cls < 0)
+    return fail(KV_ERR_UNSUPPORTED, "no decode kernel class holds this layout's vector-quantized formats");
+  if (kernel_class) *kernel_class = cls;
   if (splits) *splits = w.n_splits;
   if (workgroups) *workgroups = (int32_t)((int64_t)w.wg_per_row * L.batch);
   return ok();
@@ -475,6 +505,8 @@ kv_status kv_encode(const kv_layout* layout, const void* k, const void* v, kv_dt
   a.basis_v = basis_v;
   a.cache_k = cache_k;
   a.cache_v = cache_v;
+  a.cb_k = L.cb_k;
+  a.cb_v = L.cb_v;
   a.n_tokens = n_tokens;
   a.pos0 = pos0;
   a.capacity = L.capacity;
@@ -601,6 +633,7 @@ kv_status kv_decode(const kv_layout* layout, int32_t which, int64_t n_tokens, in
   a.heads = L.table;
   a.basis = basis;
   a.cache = cache;
+  a.cb = which ? L.cb_v : L.cb_k;
   a.out = out;
   a.n_tokens = n_tokens;
   a.pos0 = pos0;

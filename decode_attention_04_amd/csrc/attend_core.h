@@ -300,7 +300,7 @@ __device__ inline void k_slot_rt(int B, int G, int nks, int ks, int p, int rk, b
 template <int B, int NKS, int GM>
 __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt, int wk,
                                                               const u32x4 (&aq_hi)[4], const u32x4 (&aq_lo)[4],
-                                                              float* S) {
+                                                              float* S, const uint32_t* cb = nullptr) {
   // tokens past the tile's last record read stale LDS: their codes are finite and
   // their scores are replaced by -inf before the softmax.  The four 16-token
   // sub-tiles are interleaved so that consecutive MFMAs never depend on each other.
@@ -329,6 +329,34 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
           const int pl = ks * 4 + p;
           bop[tt][p] = Pow2<B>::pair(w[tt][pl / PPW], (pl % PPW) * B);
         }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_hi[ks], bop[tt], acc[tt]);
+      if constexpr (!k_packed(GM)) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_lo[ks], bop[tt], acc[tt]);
+      }
+    }
+  } else if constexpr (is_vq(B)) {
+    // vector-quantized pairs: lane group G holds pairs [4 NKS G, 4 NKS (G + 1)) of each
+    // token (pair slot p of K-step ks is pair pi = 4 NKS G + 4 ks + p, coordinates 2 pi
+    // and 2 pi + 1), one b-bit index each; the operand dword is the pair's codeword
+    // from the LDS codebook cb ([pair][2^b], fp16 even | odd << 16): normal fp16
+    // values, so the key scale carries no 2^24 (see project_query)
+    constexpr int BI = code_bits(B);
+    constexpr int SPAN = 4 * NKS * BI;
+    constexpr int NA = (SPAN + 31) / 32;
+    uint32_t a[4][NA];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) span_words<NA, SPAN % 32 == 0>(rec0 + tt * 16 * wk + 1, G * SPAN, a[tt]);
+    const uint32_t* cbg = cb + ((G * 4 * NKS) << BI);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 bop[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) bop[tt][p] = cbg[((4 * ks + p) << BI) + span_code<BI>(a[tt], 4 * ks + p)];
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_hi[ks], bop[tt], acc[tt]);
@@ -390,7 +418,8 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
 // blocks of the accumulator are added at the end; otherwise two MFMAs (hi, lo).
 template <int B, int NT, bool PACK>
 __device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt, int wv, int kk,
-                                                              u32x4 ahi, u32x4 alo, f32x4 (&acc2)[8]) {
+                                                              u32x4 ahi, u32x4 alo, f32x4 (&acc2)[8],
+                                                              const uint32_t* cb = nullptr) {
   // tokens past the tile's last record carry p = 0 in A, so their (finite) codes add nothing
   const int lane = threadIdx.x & 63, n = lane & 15, G = lane >> 4;
   const uint32_t* rec0 = vt + (32 * kk + 8 * G) * wv + 1;
@@ -435,6 +464,37 @@ __device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt
       if constexpr (!PACK) {
         acc2[n2] = mfma(alo, bop[0], acc2[n2]);
         if (n2 + 1 < NT) acc2[n2 + 1] = mfma(alo, bop[1], acc2[n2 + 1]);
+      }
+    }
+  } else if constexpr (is_vq(B)) {
+    // vector-quantized pairs: lane column block n holds pairs [n NT/2, (n + 1) NT/2) of
+    // each of its 8 tokens; N-tiles 2u and 2u + 1 take the even and odd coordinate of
+    // pair n NT/2 + u, so that column n of N-tile nt is coordinate n NT + nt as with
+    // scalar codes.  One LDS codebook read per (token, pair) serves both N-tiles.
+    static_assert(NT % 2 == 0, "vector-quantized values need r_V >= 32");
+    constexpr int BI = code_bits(B);
+    constexpr int FS = (NT / 2) * BI;
+    constexpr int NA = (FS + 31) / 32;
+    uint32_t a[8][NA];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) span_words<NA, FS % 32 == 0>(rec0 + e * wv, n * FS, a[e]);
+    const uint32_t* cbn = cb + ((n * (NT / 2)) << BI);
+#pragma unroll
+    for (int u = 0; u < NT / 2; ++u) {
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = cbn[(u << BI) + span_code<BI>(a[e], u)];
+      u32x4 b0, b1;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        b0[p] = (w[2 * p] & 0xFFFFu) | (w[2 * p + 1] << 16);
+        b1[p] = (w[2 * p] >> 16) | (w[2 * p + 1] & 0xFFFF0000u);
+      }
+      acc2[2 * u] = mfma(ahi, b0, acc2[2 * u]);
+      acc2[2 * u + 1] = mfma(ahi, b1, acc2[2 * u + 1]);
+      if constexpr (!PACK) {
+        acc2[2 * u] = mfma(alo, b0, acc2[2 * u]);
+        acc2[2 * u + 1] = mfma(alo, b1, acc2[2 * u + 1]);
       }
     }
   } else {
@@ -670,6 +730,8 @@ struct WaveCtx {
   int page;                 // paged: tokens per page
   uint32_t pool_recs;       // paged: records in a head's pool (an offset past them reads zeros)
   int64_t pool_pages;
+  const uint32_t* cbk;      // vector-quantized records: the head's K / V codebooks in LDS, else null
+  const uint32_t* cbv;
 };
 
 // Record index, within the buffer resource of the wave's cache regions, of the tile
@@ -808,7 +870,7 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
     if (lane == 0) {
       Eh[hh] = (float)e;
       Eh[kMaxGroup + hh] = sum;
-      Eh[2 * kMaxGroup + hh] = ldexpf(1.0f, 24 - e);
+      Eh[2 * kMaxGroup + hh] = ldexpf(1.0f, (is_vq(hd.bk) ? 0 : 24) - e);  // codes: subnormal fp16 operands
     }
   }
   __syncthreads();
@@ -1073,6 +1135,15 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   c.b = b;
   c.unit = (int64_t)b * a.n_kv_heads + h;
   c.stamp = stamp;
+  c.cbk = c.cbv = nullptr;
+  if (a.cb_words > 0) {  // vector-quantized records: the head's codebooks after the tile areas
+    uint32_t* cbl = (uint32_t*)(areas + kWaves * WA);
+    const int nk = codebook_words(hd.rk, hd.bk), nv = codebook_words(hd.rv, hd.bv);
+    for (int i = tid; i < nk; i += 256) cbl[i] = a.cb_k[hd.sk + i];
+    for (int i = tid; i < nv; i += 256) cbl[nk + i] = a.cb_v[hd.sv + i];
+    c.cbk = cbl;
+    c.cbv = cbl + nk;  // read after the barriers of the query projection
+  }
 
   // append fused with attention: the workgroup whose split holds the new token
   // encodes its key and value (waves 0-1 and 2-3) before any of its tiles stream in
@@ -1085,14 +1156,16 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     const int hdr = tensor ? hd.hv : hd.hk;
     const uint32_t sw = tensor ? hd.sv : hd.sk;
     const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
+    const uint32_t* cbt = is_vq(bits) ? (tensor ? a.cb_v : a.cb_k) + sw : nullptr;
     const int64_t xo = ((int64_t)b * a.n_kv_heads + h) * kHeadDim;
     // the fused entry point hands writable caches (kv_append_attend_decode)
     uint32_t* rec = const_cast<uint32_t*>(tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + append_rec * W;
     auto sync = [] { __syncthreads(); };
     if (a.append_dtype == 0)
-      encode_token_128((const float*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, hdr, sw, rec, scr[tensor], t, sync);
+      encode_token_128((const float*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, hdr, sw, cbt, rec, scr[tensor], t, sync);
     else
-      encode_token_128((const _Float16*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, hdr, sw, rec, scr[tensor], t, sync);
+      encode_token_128((const _Float16*)(tensor ? a.v1 : a.k1) + xo, P, r, bits, hdr, sw, cbt, rec, scr[tensor], t,
+                       sync);
     // the records are in L2 before any tile copy (the builtin, unlike an asm wait, also
     // tells the compiler that no store of the encoder is outstanding any more)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -1126,7 +1199,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       if (nt < NT) {
-        const float f = ldexpf(1.0f, 24 - kPScale - v_shift(bv, nt));
+        const float f = ldexpf(1.0f, (is_vq(bv) ? 0 : 24) - kPScale - v_shift(bv, nt));  // VQ: normal operands
         const int j = n * NT + nt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

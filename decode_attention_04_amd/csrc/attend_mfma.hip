@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void attend_mfma_kernel(AttendArgs a) {
 
 template <int GM, bool GEN>
 static hipError_t launch_gm(const AttendArgs& a, hipStream_t s) {
-  const size_t lds = attend_lds_bytes(a.kbuf_words, a.vbuf_words, a.nbuf, a.group);
+  const size_t lds = attend_lds_bytes(a.kbuf_words, a.vbuf_words, a.nbuf, a.group) + 4u * a.cb_words;
   const dim3 grid((unsigned)(a.wg_per_row * a.batch));
   hipLaunchKernelGGL((attend_mfma_kernel<GM, GEN>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
@@ -158,11 +158,16 @@ static hipError_t launch_widths(const AttendArgs& a, hipStream_t s) {
 AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group) {
   AttendPlan p;
   int wkm = 1, wvm = 1;
+  p.cb_words = 0;
+  p.vq = false;
   for (int h = 0; h < n_kv_heads; ++h) {
     const HeadDesc& d = heads.h[h];
     wkm = d.wk > wkm ? d.wk : wkm;
     wvm = d.wv > wvm ? d.wv : wvm;
     p.gen |= !(pow2_bits(d.bk) && pow2_bits(d.bv));
+    p.vq |= is_vq(d.bk) || is_vq(d.bv);
+    const int cw = codebook_words(d.rk, d.bk) + codebook_words(d.rv, d.bv);
+    p.cb_words = cw > p.cb_words ? cw : p.cb_words;
   }
   p.spec_class = -1;
   if (group <= 8) {
@@ -182,7 +187,8 @@ AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group) {
   // up to it; 1280 bytes bounds the gfx950 granule from above)
   const size_t kLds = 160 * 1024, kGranule = 1280;
   auto fits = [&](int wpc, int nb) {
-    const size_t per_wg = (attend_lds_bytes(p.kbuf_words, p.vbuf_words, nb, group) + kGranule - 1) / kGranule * kGranule;
+    const size_t per_wg =
+        (attend_lds_bytes(p.kbuf_words, p.vbuf_words, nb, group) + 4u * p.cb_words + kGranule - 1) / kGranule * kGranule;
     return (size_t)wpc * per_wg <= kLds;
   };
   const int max_wpc = p.spec_class >= 0 ? 3 : 2;
@@ -208,6 +214,8 @@ hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
   a.kbuf_words = p.kbuf_words;
   a.vbuf_words = p.vbuf_words;
   a.nbuf = p.nbuf;
+  a.cb_words = p.cb_words;
+  if (p.vq && p.spec_class < 0) return hipErrorNotSupported;  // the host rejects such layouts first
   if (p.spec_class >= 0) {
     for (int h = 0; h < a.n_kv_heads; ++h) {
       HeadDesc& d = a.heads.h[h];
@@ -220,6 +228,7 @@ hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
       case 3: return launch_attend_spec3(a, s);
       case 4: return launch_attend_spec4(a, s);
       case 5: return launch_attend_spec5(a, s);
+      case 6: return launch_attend_spec6(a, s);
       default: return launch_attend_frozen(p.spec_class - kSpecClasses, a, s);
     }
   }

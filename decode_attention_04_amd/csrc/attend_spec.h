@@ -34,10 +34,17 @@ namespace kvtc {
 #define KVTC_SPEC_CLASS4(X) KVTC_SPEC_CLASS0(X)
 #define KVTC_SPEC_CLASS5(X) KVTC_SPEC_CLASS1(X)
 
-constexpr int kSpecClasses = 6;  // built-in classes; the frozen ones follow them
+// Vector-quantized pairs (format code kVq + index bits) of the attention-aware key
+// transform and the value eigenbasis: full rank at 1, 2 and 3 bits per coordinate,
+// rank 64 and 32 at 2 bits per coordinate; and vector-quantized keys (2 bits per
+// coordinate) with scalar-quantized values of the same rank
+#define KVTC_SPEC_CLASS6(X) X(0, 128, 20, 128, 20) X(1, 128, 18, 128, 18) X(2, 128, 22, 128, 22) \
+  X(3, 64, 20, 64, 20) X(4, 32, 20, 32, 20) X(5, 128, 20, 64, 20) X(6, 128, 20, 128, 2) X(7, 64, 20, 64, 4)
 
-// Header words of every record a built-in class reads: 1 (per-token min and step) or 0.
-__host__ __device__ constexpr int spec_header(int cls) { return cls >= 4 ? 0 : 1; }
+constexpr int kSpecClasses = 7;  // built-in classes; the frozen ones follow them
+
+// Header words of every record a built-in class reads: 1 (per-token header word) or 0.
+__host__ __device__ constexpr int spec_header(int cls) { return cls == 4 || cls == 5 ? 0 : 1; }
 
 // Index of (rk, bk, rv, bv) in class `cls`, or -1.
 __host__ inline int spec_index(int cls, int rk, int bk, int rv, int bv) {
@@ -51,6 +58,7 @@ __host__ inline int spec_index(int cls, int rk, int bk, int rv, int bv) {
     case 3: KVTC_SPEC_CLASS3(KVTC_SPEC_FIND) break;
     case 4: KVTC_SPEC_CLASS4(KVTC_SPEC_FIND) break;
     case 5: KVTC_SPEC_CLASS5(KVTC_SPEC_FIND) break;
+    case 6: KVTC_SPEC_CLASS6(KVTC_SPEC_FIND) break;
     default: break;
   }
 #undef KVTC_SPEC_FIND
@@ -78,8 +86,11 @@ __device__ __attribute__((always_inline)) inline void issue_tile(const WaveCtx& 
 template <int GM, int RK, int BK, int RV, int BV, int HDR>
 __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArgs& a, const WaveCtx& c,
                                                                  WaveState<GM>& st) {
-  constexpr int WK = HDR + (RK * BK + 31) / 32, WV = HDR + (RV * BV + 31) / 32;
+  constexpr int WK = HDR + (code_count(RK, BK) * code_bits(BK) + 31) / 32;
+  constexpr int WV = HDR + (code_count(RV, BV) * code_bits(BV) + 31) / 32;
   constexpr int NKS = RK >= 32 ? RK / 32 : 1, NT = RV / 16;
+  static_assert(!(is_vq(BK) || is_vq(BV)) || (RK >= 32 && RV >= 32 && HDR == 1),
+                "vector-quantized formats: ranks >= 32, records with their scale word");
   constexpr int KI = (16 * WK + 63) / 64, VI = (16 * WV + 63) / 64;  // copy instructions of a full tile
   static_assert(KI + VI <= 63, "vmcnt range");
   const int t_begin = c.t_begin, t_end = c.t_end, nbuf = c.nbuf;
@@ -115,13 +126,13 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
     }
     progress_priority(t0, t_begin, t_end);
     // codes of record n start at word n * W + HDR: the phases take the tile shifted to n * W + 1
-    k_phase<BK, NKS, GM>(kt + HDR - 1, WK, aq_hi, aq_lo, c.S);
+    k_phase<BK, NKS, GM>(kt + HDR - 1, WK, aq_hi, aq_lo, c.S, c.cbk);
     softmax_tile<GM>(kt, vt, WK, WV, HDR, HDR, sk, sv, nvalid, c.g, c.S, sq, kf, st);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       u32x4 ahi, alo;
       p_operands<GM>(c.S, kk, ahi, alo);
-      v_phase<BV, NT, (GM <= 8)>(vt + HDR - 1, WV, kk, ahi, alo, st.acc2);
+      v_phase<BV, NT, (GM <= 8)>(vt + HDR - 1, WV, kk, ahi, alo, st.acc2, c.cbv);
     }
     lds_fence();
     if (nbuf == 1) {
@@ -148,7 +159,7 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
     });                                                                                              \
   }                                                                                                  \
   hipError_t launch_attend_##NAME(const AttendArgs& a, hipStream_t s) {                             \
-    const size_t lds = attend_lds_bytes(a.kbuf_words, a.vbuf_words, a.nbuf, a.group);                \
+    const size_t lds = attend_lds_bytes(a.kbuf_words, a.vbuf_words, a.nbuf, a.group) + 4u * a.cb_words; \
     const dim3 grid((unsigned)(a.wg_per_row * a.batch));                                          \
     if (a.group <= 4)                                                                                \
       hipLaunchKernelGGL(attend_##NAME##_kernel<4>, grid, dim3(256), lds, s, a);                    \

@@ -58,6 +58,11 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict_
 }
 
 // ----------------------------------------------------------------- append
+// The head's codebook of one tensor (vector-quantized records), else null.
+__device__ inline const uint32_t* head_codebook(const uint32_t* cb, int B, uint32_t off) {
+  return is_vq(B) ? cb + off : nullptr;
+}
+
 // Grid (n_kv_heads, batch), 256 threads: waves 0-1 encode the sequence's new key,
 // waves 2-3 its new value, each with half of its basis loads in flight at once.
 template <typename T>
@@ -66,15 +71,38 @@ __global__ __launch_bounds__(256) void append_kernel(EncodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int tensor = threadIdx.x >> 7, t = threadIdx.x & 127;
   const HeadDesc& hd = a.heads.h[h];
-  const int r = tensor ? hd.rv : hd.rk, bits = tensor ? hd.bv : hd.bk, W = tensor ? hd.wv : hd.wk;
+  const int r = tensor ? hd.rv : hd.rk, B = tensor ? hd.bv : hd.bk, W = tensor ? hd.wv : hd.wk;
   const int hdr = tensor ? hd.hv : hd.hk;
   const uint32_t sw = tensor ? hd.sv : hd.sk;
   const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
+  const uint32_t* cb = head_codebook(tensor ? a.cb_v : a.cb_k, B, sw);
   const T* x = (const T*)(tensor ? a.v : a.k) + ((int64_t)b * a.n_kv_heads + h) * kHeadDim;
   const int64_t ri = record_index(a.pg, a.capacity, b, a.pos0);
   if (ri < 0) return;  // the whole block: both tensors share the block table
   uint32_t* rec = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + ri * W;
-  encode_token_128(x, P, r, bits, hdr, sw, rec, scr[tensor], t, [] { __syncthreads(); });
+  encode_token_128(x, P, r, B, hdr, sw, cb, rec, scr[tensor], t, [] { __syncthreads(); });
+}
+
+// Prefill of vector-quantized tensors, one token per 128-thread block with the
+// float64 encoder of the append: grid (n_tokens, 2 n_kv_heads, batch), y = 2h + tensor;
+// blocks of scalar-quantized tensors (which the matrix-core encoder writes) exit.
+template <typename T>
+__global__ __launch_bounds__(128) void vq_prefill_kernel(EncodeArgs a) {
+  __shared__ EncodeScratch scr;
+  const int64_t tok = blockIdx.x;
+  const int h = blockIdx.y >> 1, tensor = blockIdx.y & 1, b = blockIdx.z;
+  const HeadDesc& hd = a.heads.h[h];
+  const int B = tensor ? hd.bv : hd.bk;
+  if (!is_vq(B)) return;
+  const int64_t ri = record_index(a.pg, a.capacity, b, a.pos0 + tok);
+  if (ri < 0) return;
+  const int r = tensor ? hd.rv : hd.rk, W = tensor ? hd.wv : hd.wk;
+  const uint32_t off = tensor ? hd.sv : hd.sk;
+  const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
+  const T* x = (const T*)(tensor ? a.v : a.k) + (((int64_t)b * a.n_kv_heads + h) * a.n_tokens + tok) * kHeadDim;
+  uint32_t* rec = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + ri * W;
+  encode_token_128(x, P, r, B, 1, 0u, (tensor ? a.cb_v : a.cb_k) + off, rec, scr, (int)threadIdx.x,
+                   [] { __syncthreads(); });
 }
 
 // ----------------------------------------------------------------- reconstruction
@@ -87,7 +115,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t t0 = (int64_t)blockIdx.x * 16;
   const HeadDesc& hd = a.heads.h[h];
-  const int r = a.which ? hd.rv : hd.rk, bits = a.which ? hd.bv : hd.bk;
+  const int r = a.which ? hd.rv : hd.rk, B = a.which ? hd.bv : hd.bk, bits = code_bits(B);
   const int W = a.which ? hd.wv : hd.wk, hdr = a.which ? hd.hv : hd.hk;
   const uint32_t sw = a.which ? hd.sv : hd.sk;
   const float* P = a.basis + (a.which ? hd.boff_v : hd.qoff_k);  // keys: reconstructed through Q_K
@@ -101,7 +129,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const uint32_t* rec = reg + ri * W;
       const uint32_t w0 = hdr ? rec[0] : sw;
       const float mu = f16_bits_to_f32(w0 & 0xFFFFu), sg = f16_bits_to_f32(w0 >> 16);
-      v = fmaf(sg, (float)unpack_code(rec + hdr, j, bits), mu);  // one rounding to float32
+      if (is_vq(B)) {  // rho * the pair's codeword element
+        const uint32_t we = a.cb[sw + ((uint32_t)(j >> 1) << bits) + unpack_code(rec + 1, j >> 1, bits)];
+        v = sg * f16_bits_to_f32((j & 1) ? we >> 16 : we & 0xFFFFu);
+      } else {
+        v = fmaf(sg, (float)unpack_code(rec + hdr, j, bits), mu);  // one rounding to float32
+      }
     }
     ch[tt][j] = v;
   }
@@ -151,7 +184,18 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(append_kernel<_Float16>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  return launch_encode_mfma(a, s);
+  bool vq = false;
+  for (int h = 0; h < a.n_kv_heads; ++h) vq |= is_vq(a.heads.h[h].bk) || is_vq(a.heads.h[h].bv);
+  if (vq) {  // vector-quantized tensors: the float64 encoder, one token per block
+    const dim3 grid((unsigned)a.n_tokens, (unsigned)(2 * a.n_kv_heads), (unsigned)a.batch);
+    if (a.dtype == 0)
+      hipLaunchKernelGGL(vq_prefill_kernel<float>, grid, dim3(128), 0, s, a);
+    else
+      hipLaunchKernelGGL(vq_prefill_kernel<_Float16>, grid, dim3(128), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_encode_mfma(a, s);  // the scalar-quantized tensors
 }
 
 }  // namespace kvtc

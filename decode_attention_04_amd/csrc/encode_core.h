@@ -30,17 +30,60 @@ struct EncodeScratch {
   uint32_t codes[kMaxRank];
 };
 
-// Encode the token x[0..128) with basis P (128 x r, float32 row-major) and b-bit
-// codes into `rec` (record_words(r, b, hdr) words), using 128 threads whose index
-// in the group is t (0..127, two whole waves).  hdr = 1: the record starts with
-// the token's fp16 min and step; hdr = 0: header-free, the codes use the head's
-// fixed min and step `sw` (fp16 min | step << 16).  The caller synchronises the
-// workgroup around the call (`sync` is the workgroup barrier it uses between the
-// phases; all threads of the workgroup must reach it).
+// Vector quantization of one token's coordinates by one wave (lane holds c0 =
+// coordinate lane and c1 = coordinate lane + 64): rho = fp16(sqrt(mean c^2)), u =
+// c / rho (0 when rho = 0), and for each pair (2j, 2j + 1) the index of the nearest
+// of its 2^bits codewords cb[j 2^bits + e] (fp16 even | odd << 16), by the float64
+// distance (u_2j - w0)^2 + (u_2j+1 - w1)^2 (each square and the sum rounded once),
+// the first one on ties.  Indices go to codes[j]; returns the header word
+// (fp16 +0 | fp16 rho << 16).
+__device__ inline uint32_t vq_encode_wave(double c0, double c1, int lane, int r, int bits, const uint32_t* cb,
+                                          uint32_t* codes) {
+  double sq = (lane < r ? c0 * c0 : 0.0) + (lane + 64 < r ? c1 * c1 : 0.0);
+  for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o);
+  const uint32_t rb = f64_to_f16_rne(__builtin_sqrt(sq / (double)r));
+  const double rho = (double)f16_bits_to_f32(rb);
+  const int K = 1 << bits, el = lane & 1;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int j = lane + 64 * half;        // this lane's coordinate
+    if (64 * half >= r) break;             // uniform: no coordinates in the second half
+    const double c = half ? c1 : c0;
+    const double u = rho > 0.0 ? c / rho : 0.0;
+    const uint32_t* w = cb + (int64_t)(j >> 1) * K;
+    double best = __builtin_inf();
+    int bi = 0;
+    for (int e = 0; e < K; ++e) {
+      const uint32_t we = j < r ? w[e] : 0u;
+      const double d = u - (double)f16_bits_to_f32(el ? we >> 16 : we & 0xFFFFu);
+      const double sq1 = __dmul_rn(d, d);
+      const double oth = __shfl_xor(sq1, 1);
+      const double dist = el ? __dadd_rn(oth, sq1) : __dadd_rn(sq1, oth);  // even term first
+      if (dist < best) {
+        best = dist;
+        bi = e;
+      }
+    }
+    if (el == 0 && j < r) codes[j >> 1] = (uint32_t)bi;
+  }
+  return rb << 16;
+}
+
+// Encode the token x[0..128) with basis P (128 x r, float32 row-major) into `rec`
+// (format_words(r, B, hdr) words), using 128 threads whose index in the group is t
+// (0..127, two whole waves).  B: b-bit scalar codes (2..8), or kVq + b for
+// vector-quantized pairs with the tensor's codebook of this head at `cb`.  hdr = 1:
+// the record starts with the token's header word (fp16 min and step, or +0 and rho);
+// hdr = 0: header-free scalar codes with the head's fixed min and step `sw` (fp16
+// min | step << 16).  The caller synchronises the workgroup around the call (`sync`
+// is the workgroup barrier it uses between the phases; all threads of the workgroup
+// must reach it).
 template <typename T, typename Sync>
-__device__ __attribute__((always_inline)) inline void encode_token_128(const T* x, const float* P, int r, int bits,
-                                                                        int hdr, uint32_t sw, uint32_t* rec,
-                                                                        EncodeScratch& s, int t, Sync&& sync) {
+__device__ __attribute__((always_inline)) inline void encode_token_128(const T* x, const float* P, int r, int B,
+                                                                        int hdr, uint32_t sw, const uint32_t* cb,
+                                                                        uint32_t* rec, EncodeScratch& s, int t,
+                                                                        Sync&& sync) {
+  const int bits = code_bits(B);
   // lane layout: four consecutive columns per lane, one row group per 32 lanes
   const int c4 = t % 32, rg = t / 32;
   const bool active = 4 * c4 < r;
@@ -74,30 +117,35 @@ __device__ __attribute__((always_inline)) inline void encode_token_128(const T* 
     s.gs[rg][4 * c4 + 3] = a3;
   }
   sync();
-  QuantHeader qh;
+  uint32_t w0 = 0u;
   if (t < 64) {  // one wave: coordinates j = t, t + 64
     const int lane = t;
     double c0 = 0.0, c1 = 0.0;
     if (lane < r) c0 = ((s.gs[0][lane] + s.gs[1][lane]) + s.gs[2][lane]) + s.gs[3][lane];
     if (lane + 64 < r) c1 = ((s.gs[0][lane + 64] + s.gs[1][lane + 64]) + s.gs[2][lane + 64]) + s.gs[3][lane + 64];
-    double mn = lane < r ? c0 : __builtin_inf(), mx = lane < r ? c0 : -__builtin_inf();
-    if (lane + 64 < r) {
-      mn = fmin(mn, c1);
-      mx = fmax(mx, c1);
+    if (is_vq(B)) {
+      w0 = vq_encode_wave(c0, c1, lane, r, bits, cb, s.codes);
+    } else {
+      double mn = lane < r ? c0 : __builtin_inf(), mx = lane < r ? c0 : -__builtin_inf();
+      if (lane + 64 < r) {
+        mn = fmin(mn, c1);
+        mx = fmax(mx, c1);
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        mn = fmin(mn, __shfl_xor(mn, o));
+        mx = fmax(mx, __shfl_xor(mx, o));
+      }
+      const QuantHeader qh = hdr ? quant_header(mn, mx, bits) : static_header(sw);
+      w0 = qh.word0;
+      if (lane < r) s.codes[lane] = quant_code(c0, qh.mu, qh.sigma, bits);
+      if (lane + 64 < r) s.codes[lane + 64] = quant_code(c1, qh.mu, qh.sigma, bits);
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      mn = fmin(mn, __shfl_xor(mn, o));
-      mx = fmax(mx, __shfl_xor(mx, o));
-    }
-    qh = hdr ? quant_header(mn, mx, bits) : static_header(sw);
-    if (lane < r) s.codes[lane] = quant_code(c0, qh.mu, qh.sigma, bits);
-    if (lane + 64 < r) s.codes[lane + 64] = quant_code(c1, qh.mu, qh.sigma, bits);
   }
   sync();
   if (t < 64) {
-    const int nw = record_words(r, bits, 0);
-    if (t == 0 && hdr) rec[0] = qh.word0;
-    if (t < nw) rec[hdr + t] = pack_word(s.codes, r, bits, t);
+    const int nw = format_words(r, B, 0);
+    if (t == 0 && hdr) rec[0] = w0;
+    if (t < nw) rec[hdr + t] = pack_word(s.codes, code_count(r, B), bits, t);
   }
 }
 

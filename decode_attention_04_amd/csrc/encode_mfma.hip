@@ -527,10 +527,10 @@ hipError_t launch_rank(const EncodeArgs& a, uint64_t mask_k, uint64_t mask_v, hi
 template <typename T>
 hipError_t launch_all_ranks(const EncodeArgs& a, int n_heads, hipStream_t s) {
   uint64_t mk[4] = {0, 0, 0, 0}, mv[4] = {0, 0, 0, 0};
-  for (int h = 0; h < n_heads; ++h) {
+  for (int h = 0; h < n_heads; ++h) {  // vector-quantized tensors are encoded elsewhere
     const int ik = __builtin_ctz((unsigned)a.heads.h[h].rk) - 4, iv = __builtin_ctz((unsigned)a.heads.h[h].rv) - 4;
-    mk[ik] |= 1ull << h;
-    mv[iv] |= 1ull << h;
+    if (!is_vq(a.heads.h[h].bk)) mk[ik] |= 1ull << h;
+    if (!is_vq(a.heads.h[h].bv)) mv[iv] |= 1ull << h;
   }
   hipError_t e;
   if ((e = launch_rank<T, 16>(a, mk[0], mv[0], s)) != hipSuccess) return e;

@@ -24,6 +24,20 @@ __host__ __device__ inline int record_words(int r, int b) { return 1 + (r * b + 
 // Words of a record with (hdr = 1) or without (hdr = 0) its per-token header word.
 __host__ __device__ inline int record_words(int r, int b, int hdr) { return hdr + (r * b + 31) / 32; }
 
+// Record formats are named by a width code B: 2..8 for b-bit scalar codes, kVq + b
+// for vector-quantized records of coordinate pairs with b-bit indices (one index per
+// pair; the codebook entry of pair j holds fp16 coordinates 2j and 2j + 1).
+constexpr int kVq = 16;
+__host__ __device__ constexpr bool is_vq(int B) { return B >= kVq; }
+__host__ __device__ constexpr int code_bits(int B) { return B >= kVq ? B - kVq : B; }
+__host__ __device__ constexpr int code_count(int r, int B) { return B >= kVq ? r / 2 : r; }
+// Words of a record of rank r in format B, with or without the header word.
+__host__ __device__ inline int format_words(int r, int B, int hdr) {
+  return hdr + (code_count(r, B) * code_bits(B) + 31) / 32;
+}
+// 32-bit codebook entries of a vector-quantized tensor of rank r (r/2 pairs x 2^b).
+__host__ __device__ inline int codebook_words(int r, int B) { return is_vq(B) ? (r / 2) << code_bits(B) : 0; }
+
 inline bool supported_rank(int r) { return r == 16 || r == 32 || r == 64 || r == 128; }
 inline bool supported_bits(int b) { return b >= kMinBits && b <= kMaxBits; }
 
@@ -33,11 +47,12 @@ struct HeadDesc {
   int64_t base_k, base_v;   // word offset of the head's cache region
   int32_t boff_k, boff_v;   // float offset of the head's (encode) basis
   int32_t qoff_k;           // float offset of the head's query-side key basis (== boff_k when orthonormal)
-  uint32_t sk, sv;          // header-free records: the head's fixed fp16 min | fp16 step << 16
+  uint32_t sk, sv;          // header-free records: the head's fixed fp16 min | fp16 step << 16;
+                            // vector-quantized records: the word offset of the head's codebook
   int32_t ns;               // splits of each of the head's (sequence, head) units (set at launch)
   int16_t wk, wv;           // record words
   int16_t spec;             // index of the format in the specialised kernel's class (set at launch)
-  uint8_t rk, bk, rv, bv;   // rank and bits of keys and values
+  uint8_t rk, bk, rv, bv;   // rank and format code B (bits, or kVq + index bits) of keys and values
   uint8_t hk, hv;           // header words of a key / value record: 1 (per-token min and step) or 0
 };
 static_assert(sizeof(HeadDesc) == 56, "HeadDesc layout");

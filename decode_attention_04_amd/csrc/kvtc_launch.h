@@ -16,6 +16,8 @@ struct EncodeArgs {
   const float* basis_v;
   uint32_t* cache_k;
   uint32_t* cache_v;
+  const uint32_t* cb_k;  // codebooks of vector-quantized K / V records (else null)
+  const uint32_t* cb_v;
   int64_t n_tokens;
   int64_t pos0;
   int64_t capacity;
@@ -32,6 +34,8 @@ struct AttendArgs {
   const float* basis_v;
   const uint32_t* cache_k;
   const uint32_t* cache_v;
+  const uint32_t* cb_k;  // codebooks of vector-quantized K / V records (else null)
+  const uint32_t* cb_v;
   float* out;
   uint32_t* cnt; // [batch][n_kv_heads] split arrival counters: zero on entry, left zero
   float* part;   // [batch][n_q_heads][n_splits][kPartStride] (head h fills its first heads.h[h].ns)
@@ -57,6 +61,7 @@ struct AttendArgs {
   int32_t kbuf_words;  // LDS words per K / V record-tile buffer (set by launch_attend)
   int32_t vbuf_words;
   int32_t nbuf;        // tile buffers per wave: 2 (next tile streams in) or 1
+  int32_t cb_words;    // LDS words for the codebooks of one KV head (K then V), 0 without any
 #ifdef KVTC_STAMPS
   uint64_t* stamps;    // [grid][16] phase stamps of every workgroup, or null
 #endif
@@ -66,6 +71,7 @@ struct DecodeArgs {
   HeadTable heads;
   const float* basis;     // the tensor's concatenated bases
   const uint32_t* cache;  // the tensor's cache
+  const uint32_t* cb;     // the tensor's codebooks (vector-quantized records), else null
   float* out;             // [batch][n_kv_heads][n_tokens][head_dim]
   int64_t n_tokens;
   int64_t pos0;
@@ -94,6 +100,8 @@ hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s);  // prefill: 
 struct AttendPlan {
   int spec_class = -1;
   bool gen = false;
+  bool vq = false;        // some head has vector-quantized records (only the specialised classes read them)
+  int cb_words = 0;       // LDS words of the largest head's codebooks
   int kbuf_words = 0, vbuf_words = 0, nbuf = 1, wg_per_cu = 1;
 };
 AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group);
@@ -105,5 +113,6 @@ hipError_t launch_attend_spec2(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec3(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec4(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec5(const AttendArgs& a, hipStream_t s);
+hipError_t launch_attend_spec6(const AttendArgs& a, hipStream_t s);
 
 }  // namespace kvtc

@@ -33,6 +33,30 @@
  *   rotation: one uniform quantizer per head suffices; abstract: no per-token
  *   overhead]
  *
+ * Vector-quantized records (a layout with vq_k / vq_v = 2 for that tensor): the
+ *   coordinates are taken in pairs (2j, 2j+1), each pair with its own codebook
+ *   of 2^b two-dimensional fp16 codewords (b index bits per pair, b/2 bits per
+ *   coordinate); W = 1 + ceil((r/2)*b/32) words:
+ *   word 0      : fp16 bits of +0 (bits 0-15) | fp16 bits of rho (bits 16-31),
+ *                 rho = fp16_rne(sqrt(mean_j c_j^2)), the token's RMS scale;
+ *   words 1..W-1: the r/2 pair indices as the bitstream above (b bits each).
+ *   Reconstructed coordinates (2j, 2j+1) = rho * codebook_j[index_j]; a decoder
+ *   of the scalar records therefore reads (min, step) = (0, rho).  Encode: u =
+ *   c / rho (u = 0 when rho = 0), index_j = the codeword w nearest (u_2j, u_2j+1)
+ *   in float64 (u_2j - w0)^2 + (u_2j+1 - w1)^2, the first one on ties.
+ *   Codebook layout: per head, (r_h / 2) pairs x 2^b_h codewords of one uint32
+ *   each (fp16 of the even coordinate in bits 0-15, of the odd one in bits
+ *   16-31), heads concatenated.  The calibration that makes codebooks (k-means
+ *   on RMS-normalised coefficient pairs, the coefficients grouped so that each
+ *   pair's variance product is about equal) and orders the basis columns
+ *   accordingly is the caller's.  [NOVA-KV abstract: MSE-optimal vector
+ *   quantizers on the transformed coefficients, equal-volume grouping with
+ *   equal-size codebooks for a fixed-width layout; pith.science NOVA-KV verdict,
+ *   key_machinery and referee_report: groups dealt by log-variance, k-means
+ *   codebooks on per-token RMS-normalised coefficients with a per-token scale;
+ *   forward_implications: a fixed-width codebook lookup plus a per-token scale
+ *   on the read path]
+ *
  * Cache layout (one flat uint32 array per tensor, K and V separately):
  *   head-major regions; region h holds batch x capacity records of W_h words
  *   (one word fewer for header-free records);
@@ -104,7 +128,11 @@ typedef enum kv_dtype { KV_F32 = 0, KV_F16 = 1 } kv_dtype;
  * page) chose; the library takes it as given.  scale_k / scale_v: NULL for
  * records with per-token headers, else the head's fixed quantizer for
  * header-free records of that tensor, fp16 bits of min | fp16 bits of step
- * << 16 (finite, step > 0), also chosen at calibration. */
+ * << 16 (finite, step > 0), also chosen at calibration.  Vector-quantized
+ * records (vq_k / vq_v) keep their per-token scale word, so they take no static
+ * scale; decode attention runs them in the kernel classes compiled for their
+ * formats (rank 32, 64 or 128 with 2-8 index bits, listed in the class table of
+ * the library) and returns KV_ERR_UNSUPPORTED for others. */
 typedef struct kv_layout {
   int32_t head_dim;       /* d; must be 128 */
   int32_t n_kv_heads;
@@ -124,6 +152,11 @@ typedef struct kv_layout {
   int64_t pool_pages;      /* paged: pages in each head's pool */
   const int32_t *block_table; /* paged: DEVICE int32 [batch][capacity / page_tokens], the pool
                               page holding each logical page of each sequence */
+  int32_t vq_k;            /* 0: scalar-quantized K records; 2: vector-quantized K records over
+                              coordinate pairs (bits_k = index bits per pair, see above) */
+  int32_t vq_v;            /* the same for V */
+  const uint32_t *codebook_k; /* vq_k = 2: DEVICE K codebooks (layout above), else NULL */
+  const uint32_t *codebook_v; /* vq_v = 2: DEVICE V codebooks, else NULL */
 } kv_layout;
 
 /* Words per record with its header, 1 + ceil(rank*bits/32) (a header-free
@@ -137,13 +170,15 @@ kv_status kv_cache_bytes(const kv_layout *layout, int32_t which, size_t *bytes);
 kv_status kv_workspace_bytes(const kv_layout *layout, int64_t n_tokens, size_t *bytes);
 
 /* How decode attention over `layout` runs, written to HOST ints (any may be NULL):
- * kernel_class: -1 for the generic kernel (widths read at run time), 0..5 for the
- * built-in classes compiled for the formats of one per-vector budget (0-3: 64, 128,
- * 256, 512 bits with per-token headers; 4-5: 64, 128 bits header-free), 6 and up
- * for the classes the build compiled from frozen layer allocations, in the order
- * they are listed; splits: the largest number of splits of one (sequence, KV head)
- * for n_tokens and split_tokens (0: the default plan); workgroups: the launch's
- * grid size.  No device work.  Errors as kv_workspace_bytes_split. */
+ * kernel_class: -1 for the generic kernel (widths read at run time), 0..6 for the
+ * built-in classes (0-3: the formats of one per-vector budget of 64, 128, 256, 512
+ * bits with per-token headers; 4-5: 64, 128 bits header-free; 6: vector-quantized
+ * pairs), 7 and up for the classes the build compiled from frozen layer
+ * allocations, in the order they are listed; splits: the largest number of splits
+ * of one (sequence, KV head) for n_tokens and split_tokens (0: the default plan);
+ * workgroups: the launch's grid size.  No device work.  Errors as
+ * kv_workspace_bytes_split, and KV_ERR_UNSUPPORTED for vector-quantized formats
+ * no class holds. */
 kv_status kv_attend_plan(const kv_layout *layout, int64_t n_tokens, int64_t split_tokens,
                          int32_t *kernel_class, int32_t *splits, int32_t *workgroups);
 

@@ -255,3 +255,105 @@ def block_table(seed, batch, pages_per_seq, pool_pages):
     """A seeded block table: distinct pool pages for every (sequence, logical page)."""
     rng = np.random.default_rng(seed)
     return rng.permutation(pool_pages)[: batch * pages_per_seq].reshape(batch, pages_per_seq).astype(np.int32)
+
+
+# ---------------------------------------------------------------- vector-quantized pairs
+def oracle_calibrate_nova_vq(wl: W.Workload, heads=None):
+    """(alloc, P_K list, Q_K list, P_V list, K codebooks, V codebooks) of a workload with
+    the attention-aware key transform at full rank and vector-quantized pairs, built
+    with the oracle: columns in pair order of the coefficient variances, per-pair
+    codebooks from k-means on the training sequence's tokens (float32 bases, codebooks
+    [r/2, 2^b, 2] of fp16 values)."""
+    from oracle import transform as T
+    from oracle import vq
+
+    bits = wl.allocation[1]
+    hs = range(wl.n_kv_heads) if heads is None else heads
+    alloc, pk, qk, pv, cbk, cbv = [], [], [], [], [], []
+    for h in hs:
+        mq, sk, sv = W.query_covariance(wl, h), W.covariance(wl, "K", h), W.covariance(wl, "V", h)
+        lam_k, _, _ = T.nova_key_transform(mq, sk)
+        p, q = T.nova_key_bases(mq, sk, wl.head_dim)
+        ok = vq.snake_partition(lam_k)
+        p, q = p[:, ok].astype(np.float32), q[:, ok].astype(np.float32)
+        lam_v, ev = T.eigenbasis(sv)
+        ov = vq.snake_partition(lam_v)
+        v = ev[:, ov].astype(np.float32)
+        xk = W.tokens(wl, "K", W.VQ_TRAIN_SEQ, h, 0, W.VQ_TRAIN_TOKENS).astype(np.float64)
+        xv = W.tokens(wl, "V", W.VQ_TRAIN_SEQ, h, 0, W.VQ_TRAIN_TOKENS).astype(np.float64)
+        m = wl.head_dim // 2
+        cbk.append(vq.train_codebooks(xk @ p.astype(np.float64), bits, W.vq_starts(wl, "K", h, m, 1 << bits),
+                                      W.VQ_ITERS))
+        cbv.append(vq.train_codebooks(xv @ v.astype(np.float64), bits, W.vq_starts(wl, "V", h, m, 1 << bits),
+                                      W.VQ_ITERS))
+        alloc.append((wl.head_dim, bits, wl.head_dim, bits))
+        pk.append(p)
+        qk.append(q)
+        pv.append(v)
+    return alloc, pk, qk, pv, cbk, cbv
+
+
+def codebook_u32(codebooks):
+    """Per-head codebooks [r/2, 2^b, 2] (fp16 values) -> the library's uint32 words, heads
+    concatenated (fp16 of the even coordinate low, of the odd one high)."""
+    out = []
+    for cb in codebooks:
+        h16 = np.asarray(cb, np.float64).astype(np.float16).view(np.uint16).astype(np.uint32)
+        out.append((h16[..., 0] | (h16[..., 1] << 16)).reshape(-1))
+    return np.concatenate(out).astype(np.uint32)
+
+
+def random_codebooks(seed, ranks, bits, scale=1.0):
+    """Seeded random fp16 codebooks [r/2, 2^b, 2] per head (for format-level tests)."""
+    from oracle.quantizer import fp16_round
+    rng = np.random.default_rng(seed)
+    return [fp16_round(rng.standard_normal((r // 2, 1 << b, 2)) * scale) for r, b in zip(ranks, bits)]
+
+
+VQ_DIST_TIE = 1e-9    # distances of two codewords this close (relative) are a tie of summation order
+VQ_RHO_TIE = 1e-12    # relative distance of the exact RMS from an fp16 rounding midpoint
+
+
+def _fp16_midpoint_near(v, rel):
+    """True where v (float64) lies within rel * |v| of a midpoint between two fp16 values."""
+    v = np.asarray(v, np.float64)
+    lo = np.asarray(v, np.float16).astype(np.float64)
+    nxt = np.nextafter(np.asarray(lo, np.float16), np.float16(np.inf)).astype(np.float64)
+    prv = np.nextafter(np.asarray(lo, np.float16), np.float16(-np.inf)).astype(np.float64)
+    mids = np.stack([(lo + nxt) / 2, (lo + prv) / 2])
+    return (np.abs(mids - v[None]) <= rel * np.abs(v)[None]).any(axis=0)
+
+
+def compare_vq_records(got, ref, x, P, r, bits, cb, what):
+    """Vector-quantized records against the oracle's: every scale word equal unless the
+    oracle's exact RMS sits at an fp16 rounding midpoint (then the token is a tie), and
+    every index equal unless the oracle's float64 distances to both codewords agree to
+    VQ_DIST_TIE (a summation-order tie).  Returns the number of classified ties; at most
+    1e-5 of the indices may be ties."""
+    from oracle import vq
+    got = np.asarray(got, np.uint32)
+    ref = np.asarray(ref, np.uint32)
+    assert got.shape == ref.shape, what
+    bad = np.flatnonzero((got != ref).any(axis=1))
+    if len(bad) == 0:
+        return 0
+    c = np.asarray(x, np.float64)[bad] @ np.asarray(P, np.float64)
+    rho_exact = np.sqrt((c * c).mean(axis=1))
+    rg, ig = vq.unpack_records(got[bad], r, bits)
+    rr, ir = vq.unpack_records(ref[bad], r, bits)
+    ties = 0
+    for k, t in enumerate(bad):
+        if rg[k] != rr[k]:
+            assert _fp16_midpoint_near(rho_exact[k], VQ_RHO_TIE), f"{what}: token {t} scale {rg[k]} against {rr[k]}"
+            ties += 1
+            continue
+        u = c[k] / rr[k] if rr[k] > 0 else np.zeros(r)
+        for j in np.flatnonzero(ig[k] != ir[k]):
+            pair = u[2 * j:2 * j + 2]
+            dg = float(((pair - cb[j][ig[k, j]]) ** 2).sum())
+            dr = float(((pair - cb[j][ir[k, j]]) ** 2).sum())
+            assert abs(dg - dr) <= VQ_DIST_TIE * max(dr, 1e-300), \
+                f"{what}: token {t} pair {j}: index {ig[k, j]} (distance {dg}) against {ir[k, j]} ({dr})"
+            ties += 1
+    assert ties <= max(1, 1e-5 * ref.shape[0] * (r // 2)), f"{what}: {ties} ties"
+    return ties

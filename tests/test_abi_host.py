@@ -260,7 +260,7 @@ def test_attend_plan_reports_the_kernel_class():
     assert lib_mod.kv_attend_plan(half, T)[0] == 4
     c2 = [(64, 4, 128, 3), (128, 4, 128, 3), (32, 5, 16, 5), (128, 3, 16, 5), (128, 4, 32, 4), (16, 4, 128, 3),
           (16, 5, 128, 4), (16, 5, 32, 3)]
-    assert lib_mod.kv_attend_plan(lib_mod.Layout(8, 32, 4, T, c2), T)[0] >= 6
+    assert lib_mod.kv_attend_plan(lib_mod.Layout(8, 32, 4, T, c2), T)[0] >= 7
     odd = lib_mod.Layout(2, 8, 1, 1000, [(32, 3, 64, 5), (16, 7, 128, 6)])
     assert lib_mod.kv_attend_plan(odd, 1000)[0] == -1
     big_group = lib_mod.Layout(1, 12, 1, 1000, [(64, 4, 64, 4)])
@@ -282,3 +282,49 @@ def test_paged_layout_sizes_and_validation():
                                    (256, 20, 258, 1024), (256, 20, 256, 1000), (-64, 20, 256, 1024)):
         lay._c.page_tokens, lay._c.pool_pages, lay._c.block_table, lay._c.capacity = page, pool, table, cap
         assert L.kv_cache_bytes(lay.ref(), 0, ctypes.byref(out)) == lib_mod.KV_ERR_INVALID, (page, pool, table, cap)
+
+
+def _vq_layout(alloc, vq_k=True, vq_v=True, g=4, cap=1000):
+    lay = lib_mod.Layout(len(alloc), g * len(alloc), 2, cap, alloc)
+    lay._c.vq_k, lay._c.vq_v = int(vq_k) * 2, int(vq_v) * 2
+    lay._c.codebook_k = 4096 if vq_k else None  # dummy device addresses: nothing is launched
+    lay._c.codebook_v = 8192 if vq_v else None
+    return lay
+
+
+def test_vq_cache_bytes_and_plan():
+    """Vector-quantized records are the scale word plus r/2 indices of b bits; the
+    compiled formats run in class 6 and others are refused before any launch."""
+    from oracle import vq
+    alloc = [(128, 4, 64, 4), (128, 4, 64, 4)]
+    lay = _vq_layout(alloc)
+    out = ctypes.c_size_t()
+    assert L.kv_cache_bytes(lay.ref(), 0, ctypes.byref(out)) == lib_mod.KV_OK
+    assert out.value == 4 * 2 * 1000 * 2 * vq.record_words(128, 4)
+    assert L.kv_cache_bytes(lay.ref(), 1, ctypes.byref(out)) == lib_mod.KV_OK
+    assert out.value == 4 * 2 * 1000 * 2 * vq.record_words(64, 4)
+    assert lib_mod.kv_attend_plan(lay, 1000)[0] == 6
+    # vector-quantized keys, scalar values of a compiled pair
+    mixed = _vq_layout([(128, 4, 128, 2)], vq_v=False)
+    assert lib_mod.kv_attend_plan(mixed, 1000)[0] == 6
+    # a format no class holds, and a group above 8
+    for lay in (_vq_layout([(128, 8, 128, 8)]), _vq_layout([(128, 4, 128, 4)], g=12)):
+        with pytest.raises(lib_mod.KvError) as e:
+            lib_mod.kv_attend_plan(lay, 1000)
+        assert e.value.status == lib_mod.KV_ERR_UNSUPPORTED
+
+
+def test_vq_layouts_are_validated():
+    out = ctypes.c_size_t()
+    bad_mode = _vq_layout([(128, 4, 128, 4)])
+    bad_mode._c.vq_k = 3
+    assert L.kv_cache_bytes(bad_mode.ref(), 0, ctypes.byref(out)) == lib_mod.KV_ERR_UNSUPPORTED
+    no_cb = _vq_layout([(128, 4, 128, 4)])
+    no_cb._c.codebook_v = None
+    assert L.kv_cache_bytes(no_cb.ref(), 0, ctypes.byref(out)) == lib_mod.KV_ERR_INVALID
+    small = _vq_layout([(16, 4, 128, 4)])
+    assert L.kv_cache_bytes(small.ref(), 0, ctypes.byref(out)) == lib_mod.KV_ERR_UNSUPPORTED
+    static = _vq_layout([(128, 4, 128, 4)])
+    sc = (ctypes.c_uint32 * 1)(0x3C000000)
+    static._c.scale_k = ctypes.cast(sc, ctypes.POINTER(ctypes.c_uint32))
+    assert L.kv_cache_bytes(static.ref(), 0, ctypes.byref(out)) == lib_mod.KV_ERR_INVALID

@@ -191,3 +191,48 @@ def test_nova_key_bases_match_the_oracle():
             assert np.allclose(P.astype(np.float64) @ Q.astype(np.float64).T, Pr @ Qr.T, atol=1e-5)
             assert np.allclose(P.astype(np.float64).T @ Q.astype(np.float64), np.eye(r), atol=1e-5)
             assert np.allclose(lam, w_ref, rtol=1e-9, atol=1e-12 * w_ref.max())
+
+
+def test_pair_grouping_matches_the_oracle():
+    from oracle import vq
+    rng = np.random.default_rng(3)
+    for n in (8, 32, 128):
+        v = np.exp(rng.standard_normal(n) * 2)
+        assert np.array_equal(calib.pair_order(v), vq.snake_partition(v))
+
+
+def test_vq_calibration_matches_the_oracle():
+    """The product's pair codebooks (all pairs at once) against the oracle's per-pair
+    k-means from the same starting points: the same fp16 codewords, and calibrated heads
+    whose bases reproduce the oracle's projectors."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    import harness as H
+    from oracle import vq
+    wl = W.llama_t128k_nova_vq(2.0)
+    h = 1
+    alloc, pk, qk, pv, cbk, cbv = H.oracle_calibrate_nova_vq(wl, heads=[h])
+    xk = W.tokens(wl, "K", W.VQ_TRAIN_SEQ, h, 0, W.VQ_TRAIN_TOKENS).astype(np.float64)
+    xv = W.tokens(wl, "V", W.VQ_TRAIN_SEQ, h, 0, W.VQ_TRAIN_TOKENS).astype(np.float64)
+    # codebooks from the oracle's own bases: identical up to k-means summation order
+    cb = calib.pair_codebooks(xv @ pv[0].astype(np.float64), 4, W.vq_starts(wl, "V", h, 64, 16), W.VQ_ITERS)
+    assert np.abs(cb - cbv[0]).max() <= 2e-3
+    assert np.mean(cb == cbv[0]) > 0.99
+    # the full product calibration (eigenvector signs may differ: compare projectors and distortion)
+    a, block, pv2, wk, wv = calib.calibrate_head_nova_vq(
+        W.covariance(wl, "K", h), W.covariance(wl, "V", h), W.query_covariance(wl, h), xk, xv, 4,
+        W.vq_starts(wl, "K", h, 64, 16), W.vq_starts(wl, "V", h, 64, 16), W.VQ_ITERS)
+    assert a == alloc[0]
+    p2 = block[:128 * 128].reshape(128, 128).astype(np.float64)
+    q2 = block[128 * 128:].reshape(128, 128).astype(np.float64)
+    assert np.allclose(p2 @ q2.T, pk[0].astype(np.float64) @ qk[0].astype(np.float64).T, atol=1e-4)
+    assert np.allclose(np.abs(pv2), np.abs(pv[0]), atol=1e-5)
+    assert wk.dtype == np.uint32 and wk.shape == (64 * 16,) and wv.shape == (64 * 16,)
+    # the codebook words decode to codebooks whose distortion on the training values
+    # is the oracle's to within a percent
+    cbv2 = wv.view(np.uint16).reshape(64, 16, 2).view(np.float16).astype(np.float64)
+    cv = xv @ pv2.astype(np.float64)
+    cv_o = xv @ pv[0].astype(np.float64)
+    d2 = np.mean((vq.decode_records(vq.encode_coords(cv, cbv2, 4), 128, 4, cbv2) - cv) ** 2)
+    d1 = np.mean((vq.decode_records(vq.encode_coords(cv_o, cbv[0], 4), 128, 4, cbv[0]) - cv_o) ** 2)
+    assert d2 == pytest.approx(d1, rel=0.01)

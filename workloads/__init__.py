@@ -36,7 +36,7 @@ import numpy as np
 CHUNK = 4096  # tokens per independently seeded block of keys/values
 
 # purposes (part of the seed key)
-_U, _OUTLIER, _ALPHA, _TOKENS, _QUERY, _SIGNS, _TCHAN, _QCOV, _QBETA = range(1, 10)
+_U, _OUTLIER, _ALPHA, _TOKENS, _QUERY, _SIGNS, _TCHAN, _QCOV, _QBETA, _VQSTART = range(1, 11)
 _TENSOR = {"K": 0, "V": 1}
 
 
@@ -62,6 +62,8 @@ class Workload:
     #   ("c1", budget_bits_per_dim, key_weights)  key_weights in {"mse", "kl"}; values use "mse"
     #   ("c2", budget_bits_per_dim, key_weights, "split"|"joint")  budget shared across heads
     #   ("nova", budget_bits_per_dim)  attention-aware key transform, C1 on its coefficients
+    #   ("nova-vq", index_bits)  attention-aware key transform and value eigenbasis at full
+    #       rank, vector-quantized coordinate pairs with index_bits bits per pair
     allocation: tuple = ()
     decode_steps: int = 1        # decode steps the workload runs (append + attend each)
     encode_tokens: int = 0       # prefill chunk encoded per sequence (0: none)
@@ -110,6 +112,31 @@ def llama_t128k_nova(bpd: float) -> Workload:
     return dataclasses.replace(
         llama_t128k(bpd), name=f"llama8b-layer-B4-T128K-{bpd:g}bpd-nova", allocation=("nova", float(bpd)),
         note="keys through R_K = M_q^(1/2) E (C1 on its coefficient variances), values MSE")
+
+
+def llama_t128k_nova_vq(bpd: float) -> Workload:
+    """The 128K LLaMA-shaped layer (same generated data) with the attention-aware key
+    transform and fixed-width vector quantization of coordinate pairs at full rank:
+    2 * bpd index bits per pair of coordinates, for keys and values."""
+    return dataclasses.replace(
+        llama_t128k(bpd), name=f"llama8b-layer-B4-T128K-{bpd:g}bpd-nova-vq", allocation=("nova-vq", int(2 * bpd)),
+        note="keys through R_K = M_q^(1/2) E, values through their eigenbasis; pairs of coefficients "
+             "vector-quantized with per-pair codebooks")
+
+
+# Codebook training: tokens of a sequence no workload attends over, so that the
+# codebooks are fitted on data disjoint from what is encoded and measured.
+VQ_TRAIN_SEQ = 1000
+VQ_TRAIN_TOKENS = 4096
+VQ_ITERS = 20
+
+
+def vq_starts(wl: Workload, tensor: str, h: int, n_pairs: int, n_codewords: int,
+              n_train: int = VQ_TRAIN_TOKENS) -> np.ndarray:
+    """Starting training points of k-means: for each pair, n_codewords distinct token
+    indices into the n_train training tokens (random numbers the codec draws)."""
+    rng = _rng(wl.wid, _VQSTART, _TENSOR[tensor], h)
+    return np.stack([rng.choice(n_train, size=n_codewords, replace=False) for _ in range(n_pairs)])
 
 
 def llama_prefill(rank: int, bits: int) -> Workload:
