@@ -83,16 +83,42 @@ def calibrate(wl: W.Workload):
     return alloc, bk, bv
 
 
+def calibrate_vq(wl: W.Workload):
+    """(allocation, key blocks [P_K; Q_K], value bases, K codebook words, V codebook words) of
+    a workload with vector-quantized pairs, from the product's calibration: codebooks
+    fitted on the training sequence's tokens (disjoint from the measured ones)."""
+    from decode_attention_04_amd import calib
+
+    bits = wl.allocation[1]
+    m, kcw = wl.head_dim // 2, 1 << bits
+    out = []
+    for h in range(wl.n_kv_heads):
+        xk = W.tokens(wl, "K", W.VQ_TRAIN_SEQ, h, 0, W.VQ_TRAIN_TOKENS).astype(np.float64)
+        xv = W.tokens(wl, "V", W.VQ_TRAIN_SEQ, h, 0, W.VQ_TRAIN_TOKENS).astype(np.float64)
+        out.append(calib.calibrate_head_nova_vq(
+            W.covariance(wl, "K", h), W.covariance(wl, "V", h), W.query_covariance(wl, h), xk, xv, bits,
+            W.vq_starts(wl, "K", h, m, kcw), W.vq_starts(wl, "V", h, m, kcw), W.VQ_ITERS))
+    return tuple([o[i] for o in out] for i in range(5))
+
+
 def step_bytes(wl, alloc, T, static=False):
     """Algorithmic HBM bytes of one decode step: attention part and append part
-    (static: header-free records, one word fewer each)."""
+    (static: header-free records, one word fewer each; vector-quantized pairs: the
+    scale word and r/2 indices per record, plus the codebooks once)."""
     from decode_attention_04_amd import kv_record_words
 
     B, hq, d = wl.batch, wl.n_q_heads, wl.head_dim
     esz = 4 if wl.dtype == "f32" else 2
-    rec = sum(4 * (kv_record_words(a[0], a[1]) + kv_record_words(a[2], a[3]) - (2 if static else 0)) for a in alloc)
-    nk = 2 if wl.allocation[0] == "nova" else 1  # the attention-aware transform reads P_K and Q_K
-    basis = sum(4 * d * (nk * a[0] + a[2]) for a in alloc)
+    vq = wl.allocation[0] == "nova-vq"
+    if vq:
+        rec = sum(4 * (2 + (a[0] // 2 * a[1] + 31) // 32 + (a[2] // 2 * a[3] + 31) // 32) for a in alloc)
+        tables = sum(4 * ((a[0] // 2 << a[1]) + (a[2] // 2 << a[3])) for a in alloc)
+    else:
+        rec = sum(4 * (kv_record_words(a[0], a[1]) + kv_record_words(a[2], a[3]) - (2 if static else 0))
+                  for a in alloc)
+        tables = 0
+    nk = 2 if wl.allocation[0] in ("nova", "nova-vq") else 1  # the attention-aware transform reads P_K and Q_K
+    basis = sum(4 * d * (nk * a[0] + a[2]) for a in alloc) + tables
     attend = B * T * rec + B * hq * d * esz + basis + B * hq * d * 4
     append = B * wl.n_kv_heads * 2 * d * esz + B * rec + basis
     return attend, append
@@ -140,7 +166,8 @@ def encode_rate(K, wl, block=2048, reps=5):
             "pct_of_hbm_peak": round(100 * (in_bytes + out_bytes) / ms / 1e6 / HBM_PEAK_GBS, 2)}
 
 
-def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragged=None, static=False):
+def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragged=None, static=False,
+                page=0):
     """Sustained kv_append_attend_decode throughput of another decode layout at its full size.
 
     The caches hold the workload's generated keys and values of the first `block` tokens
@@ -148,20 +175,37 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
     layer caches rotate to exceed the Infinity Cache.  Not checked against anything here:
     the GPU parity tests cover these layouts.  ragged: fractions of the context, one per
     sequence, timed as kv_attend_decode_ragged (attention only) over those lengths.
-    static: header-free records with each head's fixed quantizer from calibration."""
+    static: header-free records with each head's fixed quantizer from calibration.
+    page: paged caches with pages of this many tokens, the pool holding exactly the
+    sequences' pages, assigned by a seeded permutation."""
     import torch
 
     from decode_attention_04_amd import calib
 
-    alloc, bk, bv = calibrate(wl)
+    vq = wl.allocation[0] == "nova-vq"
+    dev = torch.device("cuda:0")
+    if vq:
+        alloc, bk, bv, cwk, cwv = calibrate_vq(wl)
+    else:
+        alloc, bk, bv = calibrate(wl)
     T = wl.context + 1
     B, H, hq, d = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim
-    scales = {}
+    extra_lay = {}
     if static:
-        scales = {"scale_k": [calib.static_scale_word(W.covariance(wl, "K", h), bk[h], alloc[h][1]) for h in range(H)],
-                  "scale_v": [calib.static_scale_word(W.covariance(wl, "V", h), bv[h], alloc[h][3]) for h in range(H)]}
-    lay = K.Layout(H, hq, B, T, alloc, **scales, query_basis_k=wl.allocation[0] == "nova")
-    dev = torch.device("cuda:0")
+        extra_lay = {"scale_k": [calib.static_scale_word(W.covariance(wl, "K", h), bk[h], alloc[h][1])
+                                 for h in range(H)],
+                     "scale_v": [calib.static_scale_word(W.covariance(wl, "V", h), bv[h], alloc[h][3])
+                                 for h in range(H)]}
+    if vq:
+        extra_lay = {"codebook_k": torch.from_numpy(np.concatenate(cwk).view(np.int32)).to(dev),
+                     "codebook_v": torch.from_numpy(np.concatenate(cwv).view(np.int32)).to(dev)}
+    cap = T
+    if page:
+        cap = (T + page - 1) // page * page
+        pps = cap // page
+        perm = np.random.default_rng(77).permutation(B * pps).reshape(B, pps).astype(np.int32)
+        extra_lay.update(page_tokens=page, pool_pages=B * pps, block_table=torch.from_numpy(perm).to(dev))
+    lay = K.Layout(H, hq, B, cap, alloc, **extra_lay, query_basis_k=wl.allocation[0] in ("nova", "nova-vq"))
     pk = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bk])).to(dev)
     pv = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bv])).to(dev)
     reps_t = (T - 1 + block - 1) // block
@@ -211,6 +255,10 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
     extra = {"lengths": lens, "step": "kv_attend_decode_ragged (no append)"} if ragged else {}
     if static:
         extra["records"] = "header-free (one fixed quantizer per head)"
+    if vq:
+        extra["records"] = "vector-quantized coordinate pairs (scale word, one index per pair)"
+    if page:
+        extra["paged"] = f"pages of {page} tokens, block table a seeded permutation"
     kclass = K.kv_attend_plan(lay, T)[0]
     return {**extra, "batch": B, "n_q_heads": hq, "n_kv_heads": H, "context_tokens": T,
             "allocation": [list(a) for a in alloc],
@@ -796,9 +844,13 @@ def main():
         dec_rates = {}
         for dwl in (W.llama_t128k(0.5), W.llama_t128k(1.0), W.llama_t128k(4.0), W.QWEN_T128K,
                     W.llama_prefill(32, 8), W.llama_prefill(64, 4), W.llama_t128k_c2(2.0),
-                    W.llama_t128k_c2(2.0, "joint"), W.llama_t128k_c2(1.0), W.llama_t128k_nova(2.0), W.LLAMA_T32K):
+                    W.llama_t128k_c2(2.0, "joint"), W.llama_t128k_c2(1.0), W.llama_t128k_nova(2.0), W.LLAMA_T32K,
+                    W.llama_t128k_nova_vq(2.0), W.llama_t128k_nova_vq(1.0)):
             dec_rates[dwl.name] = decode_rate(K, dwl)
             log(f"decode {dwl.name}: {dec_rates[dwl.name]}")
+        name = W.llama_t128k(2.0).name + "-paged"
+        dec_rates[name] = decode_rate(K, W.llama_t128k(2.0), page=256)
+        log(f"decode {name}: {dec_rates[name]}")
         for bpd in (0.5, 1.0):
             name = W.llama_t128k(bpd).name + "-header-free"
             dec_rates[name] = decode_rate(K, W.llama_t128k(bpd), static=True)

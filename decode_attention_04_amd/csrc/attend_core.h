@@ -349,14 +349,15 @@ __device__ __attribute__((always_inline)) inline void k_phase(const uint32_t* kt
     uint32_t a[4][NA];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) span_words<NA, SPAN % 32 == 0>(rec0 + tt * 16 * wk + 1, G * SPAN, a[tt]);
-    const uint32_t* cbg = cb + ((G * 4 * NKS) << BI);
+    constexpr int SK = vq_kstride(B, 32 * NKS);  // padded row stride: the lane groups read different banks
+    const uint32_t* cbg = cb + G * 4 * NKS * SK;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       u32x4 bop[4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) bop[tt][p] = cbg[((4 * ks + p) << BI) + span_code<BI>(a[tt], 4 * ks + p)];
+        for (int p = 0; p < 4; ++p) bop[tt][p] = cbg[(4 * ks + p) * SK + span_code<BI>(a[tt], 4 * ks + p)];
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[tt] = mfma(aq_hi[ks], bop[tt], acc[tt]);
@@ -478,17 +479,18 @@ __device__ __attribute__((always_inline)) inline void v_phase(const uint32_t* vt
     uint32_t a[8][NA];
 #pragma unroll
     for (int e = 0; e < 8; ++e) span_words<NA, FS % 32 == 0>(rec0 + e * wv, n * FS, a[e]);
-    const uint32_t* cbn = cb + ((n * (NT / 2)) << BI);
+    constexpr int SV = vq_vstride(B);
+    const uint32_t* cbn = cb + n * (NT / 2) * SV;
 #pragma unroll
     for (int u = 0; u < NT / 2; ++u) {
       uint32_t w[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = cbn[(u << BI) + span_code<BI>(a[e], u)];
+      for (int e = 0; e < 8; ++e) w[e] = cbn[u * SV + span_code<BI>(a[e], u)];
       u32x4 b0, b1;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        b0[p] = (w[2 * p] & 0xFFFFu) | (w[2 * p + 1] << 16);
-        b1[p] = (w[2 * p] >> 16) | (w[2 * p + 1] & 0xFFFF0000u);
+      for (int p = 0; p < 4; ++p) {  // byte permutes: the low halves, then the high halves, of tokens 2p, 2p + 1
+        b0[p] = __builtin_amdgcn_perm(w[2 * p + 1], w[2 * p], 0x05040100u);
+        b1[p] = __builtin_amdgcn_perm(w[2 * p + 1], w[2 * p], 0x07060302u);
       }
       acc2[2 * u] = mfma(ahi, b0, acc2[2 * u]);
       acc2[2 * u + 1] = mfma(ahi, b1, acc2[2 * u + 1]);
@@ -1136,13 +1138,17 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   c.unit = (int64_t)b * a.n_kv_heads + h;
   c.stamp = stamp;
   c.cbk = c.cbv = nullptr;
-  if (a.cb_words > 0) {  // vector-quantized records: the head's codebooks after the tile areas
+  if (a.cb_words > 0) {  // vector-quantized records: the head's codebooks after the tile areas,
+                         // one row of 2^b entries per pair at the padded strides of the phases
     uint32_t* cbl = (uint32_t*)(areas + kWaves * WA);
+    const int ek = code_bits(hd.bk), ev = code_bits(hd.bv);
     const int nk = codebook_words(hd.rk, hd.bk), nv = codebook_words(hd.rv, hd.bv);
-    for (int i = tid; i < nk; i += 256) cbl[i] = a.cb_k[hd.sk + i];
-    for (int i = tid; i < nv; i += 256) cbl[nk + i] = a.cb_v[hd.sv + i];
+    const int sk = vq_kstride(hd.bk, hd.rk), sv = vq_vstride(hd.bv);
+    const int lk = is_vq(hd.bk) ? (hd.rk / 2) * sk : 0;
+    for (int i = tid; i < nk; i += 256) cbl[(i >> ek) * sk + (i & ((1 << ek) - 1))] = a.cb_k[hd.sk + i];
+    for (int i = tid; i < nv; i += 256) cbl[lk + (i >> ev) * sv + (i & ((1 << ev) - 1))] = a.cb_v[hd.sv + i];
     c.cbk = cbl;
-    c.cbv = cbl + nk;  // read after the barriers of the query projection
+    c.cbv = cbl + lk;  // read after the barriers of the query projection
   }
 
   // append fused with attention: the workgroup whose split holds the new token

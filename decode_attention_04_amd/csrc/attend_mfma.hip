@@ -166,7 +166,7 @@ AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group) {
     wvm = d.wv > wvm ? d.wv : wvm;
     p.gen |= !(pow2_bits(d.bk) && pow2_bits(d.bv));
     p.vq |= is_vq(d.bk) || is_vq(d.bv);
-    const int cw = codebook_words(d.rk, d.bk) + codebook_words(d.rv, d.bv);
+    const int cw = vq_lds_words(d.rk, d.bk, d.rv, d.bv);
     p.cb_words = cw > p.cb_words ? cw : p.cb_words;
   }
   p.spec_class = -1;

@@ -38,6 +38,24 @@ __host__ __device__ inline int format_words(int r, int B, int hdr) {
 // 32-bit codebook entries of a vector-quantized tensor of rank r (r/2 pairs x 2^b).
 __host__ __device__ inline int codebook_words(int r, int B) { return is_vq(B) ? (r / 2) << code_bits(B) : 0; }
 
+// LDS row stride (words) of the per-pair codebooks in the decode kernel.  Keys: the
+// four lane groups of a score operand read pairs 4 * nks apart (nks = r/32 K-steps),
+// so with at most 16 entries per pair the stride is padded until those reads fall in
+// four different quarters of the 64 LDS banks; values: an odd stride spreads the
+// sixteen pairs one operand reads over the banks.
+__host__ __device__ constexpr int vq_kstride(int B, int r) {
+  const int e = 1 << code_bits(B), nks = r >= 32 ? r / 32 : 1;
+  if (e <= 16)
+    for (int pad = 0; pad < 16; ++pad)
+      if ((4 * nks * (e + pad)) % 64 == 16) return e + pad;
+  return e + 1;
+}
+__host__ __device__ constexpr int vq_vstride(int B) { return (1 << code_bits(B)) + 1; }
+// LDS words of a head's codebooks in the decode kernel (keys then values).
+__host__ __device__ inline int vq_lds_words(int rk, int bk, int rv, int bv) {
+  return (is_vq(bk) ? (rk / 2) * vq_kstride(bk, rk) : 0) + (is_vq(bv) ? (rv / 2) * vq_vstride(bv) : 0);
+}
+
 inline bool supported_rank(int r) { return r == 16 || r == 32 || r == 64 || r == 128; }
 inline bool supported_bits(int b) { return b >= kMinBits && b <= kMaxBits; }
 
