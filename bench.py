@@ -620,10 +620,10 @@ def sources_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per append + attend launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size)
-    from the committed counter profile of this workload, if it was taken on these sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_append_attend_{workload}.md")
+def profile_fields(name: str):
+    """The machine-readable fields ("- key: `value`" lines) of a committed profile summary,
+    or None when it is missing or was taken on other library sources."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -634,7 +634,24 @@ def measured_traffic(workload: str):
                 fields[k.strip()] = v.strip().strip("`")
     if fields.get("sources_sha256") != sources_digest():
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return fields
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per append + attend launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size)
+    from the committed counter profile of this workload, if it was taken on these sources."""
+    f = profile_fields(f"traffic_append_attend_{workload}.md")
+    return int(f["traffic_bytes_per_launch"]) if f else None
+
+
+def measured_busy(workload: str):
+    """Share of the SIMD cycles of a decode launch spent issuing VALU, matrix-core and LDS
+    instructions, from the committed SQ counter profile of this workload (same source check)."""
+    f = profile_fields(f"sq_append_attend_{workload}.md")
+    if not f:
+        return None
+    return {k: float(f[k]) for k in ("valu_issue_pct", "mfma_busy_pct", "lds_issue_pct")} | \
+        {"source": f"profiles/sq_append_attend_{workload}.md"}
 
 
 def copy_probe(mib: int):
@@ -655,8 +672,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # a few hundred back-to-back launches bring the GPU to its sustained clocks (the
-    # first ~100 decode launches run up to 10% slower); 200 steps take about 16 ms
+    # the timed steps start from the steady state of back-to-back launches (clocks
+    # and caches settled); isolated launches vary more (single_launch_us reports
+    # their p10 / p50 / p90); 200 steps take about 16 ms
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="llama-128k-2bpd")
     ap.add_argument("--replica-bytes", type=float, default=1.2e9, help="total bytes of rotated layer caches")
@@ -893,6 +911,7 @@ def main():
             "encode_rates": enc_rates,
             "other_decode_layouts": dec_rates,
             "distortion_rate": dist,
+            "unit_busy_pct": measured_busy(wl.name),
         },
         "roofline": {
             "bound": "hbm",
