@@ -15,13 +15,15 @@
 // products survive the sum, cancellations are exact, an accumulator bit 25 places
 // below the largest product is dropped).  Per instruction the error is then at
 // most u |D| + u max|p| (u = 2^-24); over the 8 chained instructions of a
-// coordinate, with S_j = sum_i |x_i P_ij| <= ||x||_2 (the columns of P are
-// orthonormal), at most 9u S_j, and the split remainders add 4u S_j (the absolute
-// part, 2^-33 ||x||_1, is negligible).  The encoder uses
-//     E = 20u ||x||_2
+// coordinate, with S_j = sum_i |x_i P_ij| <= ||x||_2 ||P_j||_2 <= ||x||_2 n_P
+// (n_P: the largest column norm of the basis, formed while it is staged, slightly
+// rounded up; 1 for an orthonormal basis, more or less for a non-orthogonal key
+// transform), at most 9u S_j, and the split remainders add 4u S_j (the absolute
+// part, 2^-33 ||x||_1 n_P, is negligible).  The encoder uses
+//     E = 20u ||x||_2 n_P
 // for fp16 inputs (fp32 inputs: three products per term, 24 instructions, and the
-// absolute split error of inputs below the fp16 normal range: E = 96u ||x||_2 +
-// 2^-21; they must lie inside the fp16 range, |x| < 65504).  The header (fp16 min
+// absolute split error of inputs below the fp16 normal range: E = (96u ||x||_2 +
+// 2^-21) n_P; they must lie inside the fp16 range, |x| < 65504).  The header (fp16 min
 // and step) and the codes are monotone functions of the coordinates, so a
 // decision that takes the same value at c~ - E and c~ + E is the exact decision.
 // The others are recomputed from the float64 projection in the fixed summation
@@ -200,16 +202,22 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
   // of column 16mb + m, hi parts then (64 lanes later) lo parts; the basis is scaled
   // by 2^8 (undone exactly on the sums) so that the lo parts of its elements stay in
   // the fp16 normal range down to |P| = 2^-11
+  __shared__ float colsq[kMaxRank];  // squared column norms of the basis (times 2^16)
+  if (tid < R) colsq[tid] = 0.0f;
+  __syncthreads();
   for (int q = tid; q < R * 16; q += 256) {
     const int ln = q & 63, ks = (q >> 6) & 3, mb = q >> 8;
     const int k0 = 32 * ks + 8 * (ln >> 4), j = 16 * mb + (ln & 15);
     enc_half8 hi, lo;
+    float sq = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float p = P[(k0 + i) * R + j] * 0x1p8f;
+      sq = fmaf(p, p, sq);
       hi[i] = (_Float16)p;
       lo[i] = (_Float16)(p - (float)hi[i]);
     }
+    atomicAdd(&colsq[j], sq);
     uint8_t* dst = ab + (((mb * 4 + ks) * 2 * 64 + ln) << 4);
     *(enc_half8*)dst = hi;
     *(enc_half8*)(dst + 1024) = lo;
@@ -220,6 +228,12 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
   const float* Px = enc_p32(R) ? (const float*)p32 : P;  // the basis the recomputations read
   __syncthreads();
 
+  // n_P, the largest column norm: the float32 sums of squares, rounded up by far more than
+  // their rounding error
+  float pn2 = 0.0f;
+  for (int j = lane; j < R; j += 64) pn2 = fmaxf(pn2, colsq[j]);
+  for (int o = 32; o > 0; o >>= 1) pn2 = fmaxf(pn2, __shfl_xor(pn2, o));
+  const float pnorm = __builtin_sqrtf(pn2) * 0x1p-8f * 1.0001f;
   const float top = (float)((1 << bits) - 1);
   const float kinv = 1.0f / top;
   const bool pow2 = (bits & (bits - 1)) == 0;
@@ -342,8 +356,8 @@ __global__ __launch_bounds__(256, OCC) void encode_mfma_kernel(EncodeArgs a, uin
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // error bound of the coordinates (see the top of the file); an fp32 input below
       // the fp16 normal range keeps an absolute split error of up to 2^-25 per
-      // element, at most 2^-25 * ||P_j||_1 <= 2^-21.5 per coordinate
-      const float E = kF32 ? 0x1.8p-18f * __builtin_sqrtf(s2) + 0x1p-21f : 0x1.4p-20f * __builtin_sqrtf(s2);
+      // element, at most 2^-25 * ||P_j||_1 <= 2^-21.5 ||P_j||_2 per coordinate
+      const float E = (kF32 ? 0x1.8p-18f * __builtin_sqrtf(s2) + 0x1p-21f : 0x1.4p-20f * __builtin_sqrtf(s2)) * pnorm;
       Ev[nt] = E;
       const uint32_t m_lo = h16_bits(mn - E), m_hi = h16_bits(mn + E);
       const float muf0 = f16_bits_to_f32(m_lo);

@@ -184,9 +184,10 @@ kv_status kv_attend_plan(const kv_layout *layout, int64_t n_tokens, int64_t spli
 
 /* Prefill encode.  k, v: [batch][n_kv_heads][n_tokens][head_dim] of `dtype`
  * (KV_F32 or KV_F16), contiguous, 16-byte aligned when n_tokens > 1; every
- * token must have ||x||_2 <= 65504 (its coordinates, bounded by the norm since
- * the basis columns are orthonormal, then keep the fp16 min and step finite;
- * outside that range the records are unspecified but the call stays defined).
+ * token must have ||x||_2 * max_j ||P_j||_2 <= 65504 (its coordinates, bounded by
+ * that product, then keep the fp16 min and step finite; an orthonormal basis has
+ * unit columns; outside that range the records are unspecified but the call stays
+ * defined).
  * Writes records
  * pos0 .. pos0+n_tokens-1 of every (sequence, head) into cache_k / cache_v
  * (other records untouched).  basis_k / basis_v: concatenated float32 bases

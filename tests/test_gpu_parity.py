@@ -167,13 +167,15 @@ def _near_basis_nullspace(P, n, seed, dtype):
     return x.astype(np.float16 if dtype == "f16" else np.float32)
 
 
-@pytest.mark.parametrize("dtype", ["f16", "f32"])
-def test_prefill_records_equal_append_records(K, dtype):
+@pytest.mark.parametrize("dtype,scale", [("f16", 1.0), ("f32", 1.0), ("f16", 8.0), ("f32", 0.125)])
+def test_prefill_records_equal_append_records(K, dtype, scale):
     """kv_encode (matrix-core projection, exact recomputation near rounding boundaries)
     writes the same records, bit for bit, as kv_append (float64 projection) token by
     token, for every rank and bit width, on ordinary tokens and on tokens whose
-    coordinates sit within the float32 error bound of each other."""
-    say(f"prefill records == append records {dtype}")
+    coordinates sit within the float32 error bound of each other.  scale != 1: the
+    bases are scaled (columns of norm 8 or 1/8, as a non-orthogonal key transform
+    has), so the encoder's error bound must follow the basis' column norms."""
+    say(f"prefill records == append records {dtype}, basis scale {scale}")
     wl = W.LLAMA_T32K
     alloc = MIXED_ALLOC
     hkv, B, n, pos0 = len(alloc), 2, 320, 5
@@ -185,6 +187,8 @@ def test_prefill_records_equal_append_records(K, dtype):
         x[t] = np.stack([np.stack([np.concatenate([W.tokens(wl, t, b, h, 0, n - 96, dtype),
                                                    _near_basis_nullspace(bases[h], 96, 100 * b + h, dtype)])
                                    for h in range(hkv)]) for b in range(B)])
+    bk = [(p.astype(np.float64) * scale).astype(np.float32) for p in bk]
+    bv = [(p.astype(np.float64) * scale).astype(np.float32) for p in bv]
     pk, pv = H.dev(codec.concat_bases(bk)), H.dev(codec.concat_bases(bv))
     kd, vd = H.dev(x["K"], tdt), H.dev(x["V"], tdt)
     nk, nv = K.kv_cache_bytes(lay, 0) // 4, K.kv_cache_bytes(lay, 1) // 4
