@@ -273,3 +273,50 @@ def test_vq_calibrated_layer_end_to_end(K):
     err = H.rel_err_per_head(out.cpu().numpy(), ref)
     say(f"calibrated 2 bits/dim layer: {ties} ties, max rel err {err:.3e}")
     assert err <= REL_TOL
+
+
+def test_vq_full_size_128k_sampled_units(K):
+    """The vector-quantized 128K layer at full size (4 sequences x 8 KV heads x 131073
+    tokens, 2 bits per coordinate; calibrated by the oracle: attention-aware key transform,
+    pair grouping, k-means codebooks), encoded on the GPU and attended with the default
+    split plan, the configuration the benchmark times.  Sampled (sequence, KV head) units
+    are re-encoded by the oracle from the same inputs: their records must match (classified
+    ties only) and their query heads' outputs match oracle attention."""
+    from oracle import codec
+    wl = W.llama_t128k_nova_vq(2.0)
+    T = wl.context + 1
+    B, hkv, hq, d, g = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.group
+    alloc, pk, qk, pv, cbk, cbv = H.oracle_calibrate_nova_vq(wl)
+    say(f"full size {wl.name}")
+    lay = _layout(K, alloc, g, B, T, cbk, cbv, query_basis=True)
+    kb = H.dev(np.concatenate([np.concatenate([p.reshape(-1), q.reshape(-1)]) for p, q in zip(pk, qk)]))
+    vb = H.dev(codec.concat_bases(pv))
+    ck = torch.zeros(K.kv_cache_bytes(lay, 0) // 4, dtype=torch.int32, device="cuda")
+    cv = torch.zeros(K.kv_cache_bytes(lay, 1) // 4, dtype=torch.int32, device="cuda")
+    for t0 in range(0, T, 1 << 15):
+        n = min(1 << 15, T - t0)
+        K.kv_encode(lay, H.dev(W.kv_array(wl, "K", t0, n)), H.dev(W.kv_array(wl, "V", t0, n)), n, t0, kb, vb, ck, cv)
+    q = W.query_array(wl, 0)
+    out = torch.empty((B, hq, d), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(K.kv_workspace_bytes(lay, T) // 4, dtype=torch.float32, device="cuda")
+    K.kv_attend_decode(lay, H.dev(q), T, kb, vb, ck, cv, H.SCALE, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    gk, gv = H.u32_host(ck), H.u32_host(cv)
+    w = vq.record_words(d, alloc[0][1])
+    for b, h in [(0, 0), (B - 1, hkv - 1)]:
+        xk = W.tokens(wl, "K", b, h, 0, T).astype(np.float64)
+        xv = W.tokens(wl, "V", b, h, 0, T).astype(np.float64)
+        rk = np.concatenate([vq.encode_tokens(xk[i:i + 16384], pk[h], cbk[h], alloc[h][1]) for i in range(0, T, 16384)])
+        rv = np.concatenate([vq.encode_tokens(xv[i:i + 16384], pv[h], cbv[h], alloc[h][3]) for i in range(0, T, 16384)])
+        s0 = (h * B + b) * T * w
+        tk = H.compare_vq_records(gk[s0:s0 + T * w].reshape(T, w), rk, xk, pk[h], d, alloc[h][1], cbk[h], f"K b{b} h{h}")
+        tv = H.compare_vq_records(gv[s0:s0 + T * w].reshape(T, w), rv, xv, pv[h], d, alloc[h][3], cbv[h], f"V b{b} h{h}")
+        ck_ = vq.decode_records(rk, d, alloc[h][1], cbk[h])
+        cv_ = vq.decode_records(rv, d, alloc[h][3], cbv[h])
+        from oracle import attention
+        ref = np.stack([attention.attend_coords(qq, qk[h], ck_, pv[h], cv_, H.SCALE)
+                        for qq in q[b, h * g:(h + 1) * g].astype(np.float64)])
+        err = H.rel_err_per_head(got[b, h * g:(h + 1) * g], ref)
+        say(f"  unit (b={b}, h={h}): ties K {tk} V {tv}, max rel err {err:.3e}")
+        assert err <= REL_TOL
