@@ -15,6 +15,7 @@ Prints one JSON line (metric, value, roofline, cpu_baseline, ...); details go to
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -132,11 +133,18 @@ def encode_rate(K, wl, block=2048, reps=5):
     statistics, so the same share of coordinates near a rounding boundary)."""
     import torch
 
-    alloc, bk, bv = calibrate(wl)
+    dev = torch.device("cuda:0")
+    vq = wl.allocation[0] == "nova-vq"
+    extra = {}
+    if vq:
+        alloc, bk, bv, cwk, cwv = calibrate_vq(wl)
+        extra = {"codebook_k": torch.from_numpy(np.concatenate(cwk).view(np.int32)).to(dev),
+                 "codebook_v": torch.from_numpy(np.concatenate(cwv).view(np.int32)).to(dev), "query_basis_k": True}
+    else:
+        alloc, bk, bv = calibrate(wl)
     T = wl.encode_tokens or wl.context
     B, H, d = wl.batch, wl.n_kv_heads, wl.head_dim
-    lay = K.Layout(H, wl.n_q_heads, B, T, alloc)
-    dev = torch.device("cuda:0")
+    lay = K.Layout(H, wl.n_q_heads, B, T, alloc, **extra)
     pk = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bk])).to(dev)
     pv = torch.from_numpy(np.concatenate([p.reshape(-1) for p in bv])).to(dev)
     nb = min(block, T)
@@ -853,7 +861,8 @@ def main():
     enc_rates = None
     if not args.no_encode_rates:
         enc_rates = {}
-        for ewl in (W.llama_prefill(32, 8), W.llama_prefill(64, 4), W.QWEN_T128K):
+        for ewl in (W.llama_prefill(32, 8), W.llama_prefill(64, 4), W.QWEN_T128K,
+                    dataclasses.replace(W.llama_t128k_nova_vq(2.0), encode_tokens=4096)):
             enc_rates[ewl.name] = encode_rate(K, ewl)
             log(f"encode {ewl.name}: {enc_rates[ewl.name]}")
 

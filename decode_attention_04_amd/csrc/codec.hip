@@ -83,26 +83,85 @@ __global__ __launch_bounds__(256) void append_kernel(EncodeArgs a) {
   encode_token_128(x, P, r, B, hdr, sw, cb, rec, scr[tensor], t, [] { __syncthreads(); });
 }
 
-// Prefill of vector-quantized tensors, one token per 128-thread block with the
-// float64 encoder of the append: grid (n_tokens, 2 n_kv_heads, batch), y = 2h + tensor;
-// blocks of scalar-quantized tensors (which the matrix-core encoder writes) exit.
+// Prefill of vector-quantized tensors.  Grid (token tiles of kVqTile, 2 n_kv_heads,
+// batch), y = 2h + tensor, 256 threads; blocks of scalar-quantized tensors (which the
+// matrix-core encoder writes) exit.  The block stages the head's basis in LDS once,
+// then takes its tokens eight at a time: every thread forms one coordinate of four of
+// them in float64 in the encoders' fixed order (rows 32q .. 32q+31 in order, then
+// ((g0 + g1) + g2) + g3), and one wave per token runs the append's vector quantizer
+// on them, so the records are the append's bit for bit.
+constexpr int kVqTile = 64;
+constexpr int kVqChunk = 8;
+
+inline size_t vq_prefill_lds_bytes(int rmax) {
+  return (size_t)kVqChunk * kHeadDim * (sizeof(double) + sizeof(float)) + kVqChunk * 64 * sizeof(uint32_t) +
+         (size_t)kHeadDim * rmax * sizeof(float);
+}
+
 template <typename T>
-__global__ __launch_bounds__(128) void vq_prefill_kernel(EncodeArgs a) {
-  __shared__ EncodeScratch scr;
-  const int64_t tok = blockIdx.x;
+__global__ __launch_bounds__(256) void vq_prefill_kernel(EncodeArgs a) {
+  extern __shared__ double vq_lds[];
   const int h = blockIdx.y >> 1, tensor = blockIdx.y & 1, b = blockIdx.z;
   const HeadDesc& hd = a.heads.h[h];
   const int B = tensor ? hd.bv : hd.bk;
-  if (!is_vq(B)) return;
-  const int64_t ri = record_index(a.pg, a.capacity, b, a.pos0 + tok);
-  if (ri < 0) return;
-  const int r = tensor ? hd.rv : hd.rk, W = tensor ? hd.wv : hd.wk;
-  const uint32_t off = tensor ? hd.sv : hd.sk;
+  if (!is_vq(B)) return;  // uniform: the whole block
+  const int r = tensor ? hd.rv : hd.rk, W = tensor ? hd.wv : hd.wk, bits = code_bits(B);
   const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
-  const T* x = (const T*)(tensor ? a.v : a.k) + (((int64_t)b * a.n_kv_heads + h) * a.n_tokens + tok) * kHeadDim;
-  uint32_t* rec = (tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k) + ri * W;
-  encode_token_128(x, P, r, B, 1, 0u, (tensor ? a.cb_v : a.cb_k) + off, rec, scr, (int)threadIdx.x,
-                   [] { __syncthreads(); });
+  const uint32_t* cb = (tensor ? a.cb_v : a.cb_k) + (tensor ? hd.sv : hd.sk);
+  const T* xu = (const T*)(tensor ? a.v : a.k) + ((int64_t)b * a.n_kv_heads + h) * a.n_tokens * kHeadDim;
+  uint32_t* region = tensor ? a.cache_v + hd.base_v : a.cache_k + hd.base_k;
+  double* cs = vq_lds;                                      // [kVqChunk][128] the coordinates
+  float* xs = (float*)(cs + kVqChunk * kHeadDim);           // [kVqChunk][128] the inputs (exact in fp32)
+  uint32_t* codes = (uint32_t*)(xs + kVqChunk * kHeadDim);  // [kVqChunk][64] pair indices
+  float* Ps = (float*)(codes + kVqChunk * 64);              // [128][r] the basis
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < kHeadDim * r; i += 256) Ps[i] = P[i];
+  const int64_t t_begin = (int64_t)blockIdx.x * kVqTile;
+  const int64_t t_end = t_begin + kVqTile < a.n_tokens ? t_begin + kVqTile : a.n_tokens;
+  // this thread's coordinate j of tokens 4 k0 .. 4 k0 + 3 of a chunk: one basis load serves four
+  const int j = tid & 127, k0 = tid >> 7;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kVqChunk) {
+    const int nt = t_end - t0 < kVqChunk ? (int)(t_end - t0) : kVqChunk;
+    for (int i = tid; i < kVqChunk * kHeadDim; i += 256) {
+      const int k = i / kHeadDim;
+      xs[i] = k < nt ? (float)load_f64(xu + (t0 + k) * kHeadDim + (i - k * kHeadDim)) : 0.0f;
+    }
+    __syncthreads();  // inputs (and, on the first chunk, the basis) in LDS
+    if (j < r) {
+      const float* x = xs + 4 * k0 * kHeadDim;
+      double g[4][kRowGroups];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int q = 0; q < kRowGroups; ++q) g[kk][q] = 0.0;
+#pragma unroll 4
+      for (int i = 0; i < kGroupRows; ++i) {
+#pragma unroll
+        for (int q = 0; q < kRowGroups; ++q) {
+          const double p = (double)Ps[(q * kGroupRows + i) * r + j];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) g[kk][q] = fma((double)x[kk * kHeadDim + q * kGroupRows + i], p, g[kk][q]);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) cs[(4 * k0 + kk) * kHeadDim + j] = ((g[kk][0] + g[kk][1]) + g[kk][2]) + g[kk][3];
+    }
+    __syncthreads();  // coordinates complete
+    for (int k = wave; k < nt; k += 4) {  // wave-uniform: one token per wave at a time
+      uint32_t* cw = codes + k * 64;
+      const uint32_t w0 = vq_encode_wave(cs + k * kHeadDim, lane, r, bits, cb, cw);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int64_t ri = record_index(a.pg, a.capacity, b, a.pos0 + t0 + k);
+      if (ri >= 0) {
+        uint32_t* rec = region + ri * W;
+        if (lane == 0) rec[0] = w0;
+        if (lane < W - 1) rec[1 + lane] = pack_word(cw, r / 2, bits, lane);
+      }
+    }
+    __syncthreads();  // before the next chunk overwrites the inputs, coordinates and codes
+  }
 }
 
 // ----------------------------------------------------------------- reconstruction
@@ -186,12 +245,18 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t s) {
   }
   bool vq = false;
   for (int h = 0; h < a.n_kv_heads; ++h) vq |= is_vq(a.heads.h[h].bk) || is_vq(a.heads.h[h].bv);
-  if (vq) {  // vector-quantized tensors: the float64 encoder, one token per block
-    const dim3 grid((unsigned)a.n_tokens, (unsigned)(2 * a.n_kv_heads), (unsigned)a.batch);
+  if (vq) {  // vector-quantized tensors: float64 coordinates and the append's quantizer
+    int rmax = 0;
+    for (int h = 0; h < a.n_kv_heads; ++h) {
+      if (is_vq(a.heads.h[h].bk) && a.heads.h[h].rk > rmax) rmax = a.heads.h[h].rk;
+      if (is_vq(a.heads.h[h].bv) && a.heads.h[h].rv > rmax) rmax = a.heads.h[h].rv;
+    }
+    const dim3 grid((unsigned)((a.n_tokens + kVqTile - 1) / kVqTile), (unsigned)(2 * a.n_kv_heads), (unsigned)a.batch);
+    const size_t lds = vq_prefill_lds_bytes(rmax);
     if (a.dtype == 0)
-      hipLaunchKernelGGL(vq_prefill_kernel<float>, grid, dim3(128), 0, s, a);
+      hipLaunchKernelGGL(vq_prefill_kernel<float>, grid, dim3(256), lds, s, a);
     else
-      hipLaunchKernelGGL(vq_prefill_kernel<_Float16>, grid, dim3(128), 0, s, a);
+      hipLaunchKernelGGL(vq_prefill_kernel<_Float16>, grid, dim3(256), lds, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -30,41 +30,45 @@ struct EncodeScratch {
   uint32_t codes[kMaxRank];
 };
 
-// Vector quantization of one token's coordinates by one wave (lane holds c0 =
-// coordinate lane and c1 = coordinate lane + 64): rho = fp16(sqrt(mean c^2)), u =
-// c / rho (0 when rho = 0), and for each pair (2j, 2j + 1) the index of the nearest
-// of its 2^bits codewords cb[j 2^bits + e] (fp16 even | odd << 16), by the float64
-// distance (u_2j - w0)^2 + (u_2j+1 - w1)^2 (each square and the sum rounded once),
-// the first one on ties.  Indices go to codes[j]; returns the header word
-// (fp16 +0 | fp16 rho << 16).
-__device__ inline uint32_t vq_encode_wave(double c0, double c1, int lane, int r, int bits, const uint32_t* cb,
+// Vector quantization of one token's coordinates c[0..r) (float64, in LDS) by one
+// wave: rho = fp16(sqrt(mean c^2)) (lane sums c_lane^2 + c_(lane+64)^2, then a
+// butterfly over the wave), u = c / rho (0 when rho = 0), and lane j < r/2 picks for
+// pair (2j, 2j + 1) the nearest of its 2^bits codewords cb[j 2^bits + e] (fp16 even |
+// odd << 16) by the float64 distance (u_2j - w0)^2 + (u_2j+1 - w1)^2 (each square and
+// the sum rounded once), the first one on ties, eight codewords' loads at a time.
+// Indices go to codes[j]; returns the header word (fp16 +0 | fp16 rho << 16).  Every
+// encode path calls this, so their records agree bit for bit.
+__device__ inline uint32_t vq_encode_wave(const double* c, int lane, int r, int bits, const uint32_t* cb,
                                           uint32_t* codes) {
-  double sq = (lane < r ? c0 * c0 : 0.0) + (lane + 64 < r ? c1 * c1 : 0.0);
-  for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o);
+  const double c0 = lane < r ? c[lane] : 0.0, c1 = lane + 64 < r ? c[lane + 64] : 0.0;
+  double sq = __dadd_rn(__dmul_rn(c0, c0), __dmul_rn(c1, c1));
+  for (int o = 32; o > 0; o >>= 1) sq = __dadd_rn(sq, __shfl_xor(sq, o));
   const uint32_t rb = f64_to_f16_rne(__builtin_sqrt(sq / (double)r));
   const double rho = (double)f16_bits_to_f32(rb);
-  const int K = 1 << bits, el = lane & 1;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int j = lane + 64 * half;        // this lane's coordinate
-    if (64 * half >= r) break;             // uniform: no coordinates in the second half
-    const double c = half ? c1 : c0;
-    const double u = rho > 0.0 ? c / rho : 0.0;
-    const uint32_t* w = cb + (int64_t)(j >> 1) * K;
+  const int K = 1 << bits;
+  if (2 * lane < r) {
+    const double u0 = rho > 0.0 ? c[2 * lane] / rho : 0.0;
+    const double u1 = rho > 0.0 ? c[2 * lane + 1] / rho : 0.0;
+    const uint32_t* w = cb + (int64_t)lane * K;
     double best = __builtin_inf();
     int bi = 0;
-    for (int e = 0; e < K; ++e) {
-      const uint32_t we = j < r ? w[e] : 0u;
-      const double d = u - (double)f16_bits_to_f32(el ? we >> 16 : we & 0xFFFFu);
-      const double sq1 = __dmul_rn(d, d);
-      const double oth = __shfl_xor(sq1, 1);
-      const double dist = el ? __dadd_rn(oth, sq1) : __dadd_rn(sq1, oth);  // even term first
-      if (dist < best) {
-        best = dist;
-        bi = e;
+    for (int e0 = 0; e0 < K; e0 += 8) {
+      uint32_t we[8];
+#pragma unroll
+      for (int u8 = 0; u8 < 8; ++u8) we[u8] = e0 + u8 < K ? w[e0 + u8] : 0u;
+#pragma unroll
+      for (int u8 = 0; u8 < 8; ++u8) {
+        if (e0 + u8 >= K) break;  // K >= 4
+        const double d0 = u0 - (double)f16_bits_to_f32(we[u8] & 0xFFFFu);
+        const double d1 = u1 - (double)f16_bits_to_f32(we[u8] >> 16);
+        const double dist = __dadd_rn(__dmul_rn(d0, d0), __dmul_rn(d1, d1));
+        if (dist < best) {
+          best = dist;
+          bi = e0 + u8;
+        }
       }
     }
-    if (el == 0 && j < r) codes[j >> 1] = (uint32_t)bi;
+    codes[lane] = (uint32_t)bi;
   }
   return rb << 16;
 }
@@ -124,7 +128,13 @@ __device__ __attribute__((always_inline)) inline void encode_token_128(const T* 
     if (lane < r) c0 = ((s.gs[0][lane] + s.gs[1][lane]) + s.gs[2][lane]) + s.gs[3][lane];
     if (lane + 64 < r) c1 = ((s.gs[0][lane + 64] + s.gs[1][lane + 64]) + s.gs[2][lane + 64]) + s.gs[3][lane + 64];
     if (is_vq(B)) {
-      w0 = vq_encode_wave(c0, c1, lane, r, bits, cb, s.codes);
+      double* cs = s.xs;  // the token's inputs are no longer needed: its coordinates
+      if (lane < r) cs[lane] = c0;
+      if (lane + 64 < r) cs[lane + 64] = c1;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      w0 = vq_encode_wave(cs, lane, r, bits, cb, s.codes);
     } else {
       double mn = lane < r ? c0 : __builtin_inf(), mx = lane < r ? c0 : -__builtin_inf();
       if (lane + 64 < r) {
