@@ -14,10 +14,11 @@ pages (cited per function) so that it can be checked by eye:
 * ``packing``    -- fixed-width little-endian bit packing of records
 * ``codec``      -- project -> quantize -> pack, cache layout
 * ``attention``  -- decode attention over the dequantized cache, textbook attention
+* ``rope``       -- rotary position embedding; attention over keys compressed before it
 * ``allocation`` -- rate-distortion model D(r, b) and the per-head C1 rank/bit search
 
 Pinned by the ``-m "not gpu"`` tests against closed forms, hand-worked
 examples (``tests/golden``), brute force and textbook special cases.  No
 function here is "parity unpinned".
 """
-from . import allocation, attention, codec, packing, quantizer, transform, vq  # noqa: F401
+from . import allocation, attention, codec, packing, quantizer, rope, transform, vq  # noqa: F401
