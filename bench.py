@@ -175,7 +175,7 @@ def encode_rate(K, wl, block=2048, reps=5):
 
 
 def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragged=None, static=False,
-                page=0):
+                page=0, rope=False):
     """Sustained kv_append_attend_decode throughput of another decode layout at its full size.
 
     The caches hold the workload's generated keys and values of the first `block` tokens
@@ -185,7 +185,10 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
     sequence, timed as kv_attend_decode_ragged (attention only) over those lengths.
     static: header-free records with each head's fixed quantizer from calibration.
     page: paged caches with pages of this many tokens, the pool holding exactly the
-    sequences' pages, assigned by a seeded permutation."""
+    sequences' pages, assigned by a seeded permutation.  rope: the keys are compressed
+    before RoPE (kv_append_attend_decode_rope, LLaMA-3's inverse frequencies, base 500000);
+    the line adds the key reconstruction's useful matrix-core rate (2 * 128 * r_K flops
+    per token and KV head)."""
     import torch
 
     from decode_attention_04_amd import calib
@@ -230,8 +233,10 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
     caches = [(ck, cv)] + [(ck.clone(), cv.clone()) for _ in range(n_rep - 1)]
     q = torch.from_numpy(W.query_array(wl, 0)).to(dev)
     out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
-    ws = torch.zeros(K.kv_workspace_bytes(lay, T) // 4, dtype=torch.float32, device=dev)
+    ws_bytes = K.kv_workspace_bytes_rope(lay, T) if rope else K.kv_workspace_bytes(lay, T)
+    ws = torch.zeros(ws_bytes // 4, dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(d)
+    inv_freq = torch.from_numpy(500000.0 ** (-np.arange(0, d, 2, dtype=np.float64) / d)).to(dev) if rope else None
     lens = [int(T * f) for f in ragged] if ragged else None
     lens_d = torch.tensor(lens, dtype=torch.int32, device=dev) if ragged else None
 
@@ -239,6 +244,8 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
         ck_, cv_ = caches[i % n_rep]
         if ragged:
             K.kv_attend_decode_ragged(lay, q, lens_d, T, pk, pv, ck_, cv_, scale, out, ws)
+        elif rope:
+            K.kv_append_attend_decode_rope(lay, k1, v1, q, T, pk, pv, ck_, cv_, scale, inv_freq, out, ws)
         else:
             K.kv_append_attend_decode(lay, k1, v1, q, T, pk, pv, ck_, cv_, scale, out, ws)
 
@@ -265,13 +272,18 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
         extra["records"] = "header-free (one fixed quantizer per head)"
     if vq:
         extra["records"] = "vector-quantized coordinate pairs (scale word, one index per pair)"
+    if rope:
+        extra["keys"] = "compressed before RoPE, turned by position at decode (inverse frequencies base 500000)"
+        flops = 2.0 * 128 * B * T * sum(a[0] for a in alloc)
+        extra["key_reconstruction_TFLOP_per_s"] = round(flops / (us * 1e-6) / 1e12, 1)
     if page:
         extra["paged"] = f"pages of {page} tokens, block table a seeded permutation"
     kclass = K.kv_attend_plan(lay, T)[0]
+    kname = "generic" if kclass < 0 else (f"budget class {kclass}" if kclass < 6 else
+                                          "vector-quantized class" if kclass == 6 else "frozen layout class")
     return {**extra, "batch": B, "n_q_heads": hq, "n_kv_heads": H, "context_tokens": T,
             "allocation": [list(a) for a in alloc],
-            "kernel": "generic" if kclass < 0 else (f"budget class {kclass}" if kclass < 6 else
-                                                  "vector-quantized class" if kclass == 6 else "frozen layout class"),
+            "kernel": "pre-RoPE key kernel" if rope else kname,
             "us_per_step": round(us, 2), "GB_per_s": round(gbs, 1),
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "layer_caches_rotated": n_rep}
 
@@ -885,6 +897,10 @@ def main():
         name = W.llama_t128k(2.0).name + "-ragged"
         dec_rates[name] = decode_rate(K, W.llama_t128k(2.0), ragged=(1.0, 0.75, 0.5, 0.25))
         log(f"decode {name}: {dec_rates[name]}")
+        for bpd in (2.0, 0.5):
+            name = W.llama_t128k(bpd).name + "-pre-rope-keys"
+            dec_rates[name] = decode_rate(K, W.llama_t128k(bpd), rope=True)
+            log(f"decode {name}: {dec_rates[name]}")
 
     dist = None
     if not args.no_distortion:

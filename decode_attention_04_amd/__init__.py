@@ -13,6 +13,7 @@ _BINDING = (
     "KV_ERR_CAPACITY", "KV_ERR_DEVICE", "KV_ERR_INVALID", "KV_ERR_UNSUPPORTED", "KV_OK", "KvError",
     "Layout", "kv_append", "kv_append_attend_decode", "kv_append_attend_decode_noalloc", "kv_attend_decode", "kv_attend_plan", "kv_attend_decode_ragged", "kv_cache_bytes", "kv_decode", "kv_encode", "kv_quantize_pack",
     "kv_record_words", "kv_unpack", "kv_workspace_bytes",
+    "kv_attend_decode_rope", "kv_append_attend_decode_rope", "kv_workspace_bytes_rope",
 )
 
 

@@ -24,6 +24,7 @@ EXPORTED = (
     "kv_encode", "kv_append", "kv_attend_decode", "kv_attend_decode_split",
     "kv_append_attend_decode", "kv_attend_decode_ragged", "kv_append_attend_decode_noalloc",
     "kv_decode", "kv_quantize_pack", "kv_unpack", "kv_last_error",
+    "kv_workspace_bytes_rope", "kv_attend_decode_rope", "kv_append_attend_decode_rope",
 )
 
 
@@ -84,6 +85,9 @@ def _load():
         "kv_attend_decode_ragged": (i32, [L, P, i32, P, i64, P, P, P, P, f32, P, P, sz, P]),
         "kv_append_attend_decode_noalloc": (i32, [L, P, P, i32, P, i32, i64, i64, P, P, P, P, f32, P, P]),
         "kv_decode": (i32, [L, i32, i64, i64, P, P, P, P]),
+        "kv_workspace_bytes_rope": (i32, [L, i64, i64, ctypes.POINTER(sz)]),
+        "kv_attend_decode_rope": (i32, [L, P, i32, i64, i64, P, P, P, P, f32, P, P, P, sz, P]),
+        "kv_append_attend_decode_rope": (i32, [L, P, P, i32, P, i32, i64, i64, P, P, P, P, f32, P, P, P, sz, P]),
         "kv_quantize_pack": (i32, [P, i64, i32, i32, P, P]),
         "kv_unpack": (i32, [P, i64, i32, i32, P, P, P]),
         "kv_last_error": (ctypes.c_char_p, []),
@@ -271,6 +275,37 @@ def kv_append_attend_decode_noalloc(layout, k1, v1, q, n_tokens, basis_k, basis_
                                                 _dtype_code(q), n_tokens, split_tokens, _ptr(basis_k),
                                                 _ptr(basis_v), _ptr(cache_k), _ptr(cache_v), float(softmax_scale),
                                                 _ptr(out), _stream(stream)))
+
+
+def kv_workspace_bytes_rope(layout: Layout, n_tokens: int, split_tokens: int = 0) -> int:
+    """Workspace bytes of kv_attend_decode_rope (its own split plan)."""
+    out = ctypes.c_size_t()
+    _check(_lib.kv_workspace_bytes_rope(layout.ref(), n_tokens, split_tokens, ctypes.byref(out)))
+    return out.value
+
+
+def kv_attend_decode_rope(layout, q, n_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale, inv_freq, out,
+                          workspace, split_tokens: int = 0, stream=None):
+    """Decode attention over keys compressed before RoPE: q [batch, n_q_heads, head_dim]
+    (already rotated to its position), inv_freq a device float64 tensor [head_dim / 2];
+    token t's key is turned by t * inv_freq.  Workspace: kv_workspace_bytes_rope bytes,
+    zero-filled on first use."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.kv_attend_decode_rope(layout.ref(), _ptr(q), _dtype_code(q), n_tokens, split_tokens,
+                                      _ptr(basis_k), _ptr(basis_v), _ptr(cache_k), _ptr(cache_v),
+                                      float(softmax_scale), _ptr(inv_freq), _ptr(out), _ptr(workspace), nbytes,
+                                      _stream(stream)))
+
+
+def kv_append_attend_decode_rope(layout, k1, v1, q, n_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale,
+                                 inv_freq, out, workspace, split_tokens: int = 0, stream=None):
+    """Append the unrotated k1, v1 at position n_tokens - 1, then attend as
+    kv_attend_decode_rope, in one launch."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.kv_append_attend_decode_rope(layout.ref(), _ptr(k1), _ptr(v1), _dtype_code(k1), _ptr(q),
+                                             _dtype_code(q), n_tokens, split_tokens, _ptr(basis_k), _ptr(basis_v),
+                                             _ptr(cache_k), _ptr(cache_v), float(softmax_scale), _ptr(inv_freq),
+                                             _ptr(out), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def kv_decode(layout, which, n_tokens, pos0, basis, cache, out, stream=None):

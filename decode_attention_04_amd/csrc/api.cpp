@@ -188,9 +188,9 @@ constexpr int64_t kMinSplitTokens = 4 * kSplitQuantum;
 // Default split-K size: one workgroup for every resident slot of the 256 CUs
 // (as many per CU as the layout's kernel and LDS use allow), each split a
 // multiple of 256 tokens (64 per wave) and at least kMinSplitTokens.
-int64_t default_split_tokens(const Layout& L, int64_t T) {
+int64_t default_split_tokens(const Layout& L, int64_t T, bool rope) {
   const int64_t units = (int64_t)L.batch * L.n_kv;
-  const int64_t target = 256 * (int64_t)plan_attend(L.table, L.n_kv, L.group).wg_per_cu;
+  const int64_t target = 256 * (int64_t)plan_attend(L.table, L.n_kv, L.group, rope).wg_per_cu;
   int64_t ns = (target + units - 1) / units;
   if (ns < 1) ns = 1;
   int64_t st = (T + ns - 1) / ns;
@@ -216,7 +216,8 @@ static int64_t quantum_split(int64_t T, int64_t ns) {
   return st < kSplitQuantum ? kSplitQuantum : st;
 }
 
-kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Workspace& w) {
+// rope: the plan of the kernel for keys compressed before RoPE (its own resident slots).
+kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Workspace& w, bool rope = false) {
   if (T < 0) return fail(KV_ERR_INVALID, "n_tokens %lld < 0", (long long)T);
   if (T > L.capacity)
     return fail(KV_ERR_CAPACITY, "n_tokens %lld exceeds capacity %lld", (long long)T, (long long)L.capacity);
@@ -237,7 +238,7 @@ kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Works
     const int64_t ns = splits_for(T, split_tokens);
     for (int h = 0; h < L.n_kv; ++h) w.ns[h] = (int32_t)(ns > 65535 ? 65536 : ns);
   } else {
-    const int64_t st_uniform = default_split_tokens(L, T);
+    const int64_t st_uniform = default_split_tokens(L, T, rope);
     const int64_t ns_uniform = splits_for(T, st_uniform);
     // largest-remainder apportionment of ns_uniform * n_kv splits, at least one per
     // head, so that the layout never launches more workgroups than with equal counts
@@ -346,10 +347,16 @@ kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_
                       const float* basis_k, const float* basis_v, const uint32_t* cache_k, const uint32_t* cache_v,
                       float softmax_scale, float* out, void* workspace, size_t workspace_bytes, void* stream,
                       const void* k1, const void* v1, kv_dtype kv_dt, const int32_t* lengths = nullptr,
-                      bool static_ws = false) {
+                      bool static_ws = false, const double* rope = nullptr) {
   if (dtype != KV_F32 && dtype != KV_F16) return fail(KV_ERR_INVALID, "dtype %d unknown", (int)dtype);
+  if (rope) {
+    if (L.vq) return fail(KV_ERR_UNSUPPORTED, "keys compressed before RoPE need scalar records (no vector-quantized formats)");
+    if (L.group > 8)
+      return fail(KV_ERR_UNSUPPORTED, "keys compressed before RoPE: a group of %d query heads exceeds 8", L.group);
+    if (!aligned(rope, 8)) return fail(KV_ERR_INVALID, "misaligned inv_freq");
+  }
   Workspace w;
-  kv_status s = plan_workspace(L, n_tokens, split_tokens, w);
+  kv_status s = plan_workspace(L, n_tokens, split_tokens, w, rope != nullptr);
   if (s) return s;
   if (!q || !basis_k || !basis_v || !cache_k || !cache_v || !out || (!static_ws && !workspace))
     return fail(KV_ERR_INVALID, "NULL query, basis, cache, output or workspace pointer");
@@ -426,6 +433,7 @@ kv_status attend_impl(const Layout& L, const void* q, kv_dtype dtype, int64_t n_
   a.v1 = v1;
   a.append_pos = k1 ? n_tokens - 1 : -1;
   a.append_dtype = kv_dt == KV_F32 ? 0 : 1;
+  a.rope = rope;
   return device_status(launch_attend(a, (hipStream_t)stream), "attend launch");
 }
 
@@ -480,6 +488,49 @@ kv_status kv_attend_plan(const kv_layout* layout, int64_t n_tokens, int64_t spli
 
 kv_status kv_workspace_bytes(const kv_layout* layout, int64_t n_tokens, size_t* bytes) {
   return kv_workspace_bytes_split(layout, n_tokens, 0, bytes);
+}
+
+kv_status kv_workspace_bytes_rope(const kv_layout* layout, int64_t n_tokens, int64_t split_tokens, size_t* bytes) {
+  Layout L;
+  kv_status s = build_layout(layout, L);
+  if (s) return s;
+  if (!bytes) return fail(KV_ERR_INVALID, "bytes is NULL");
+  Workspace w;
+  s = plan_workspace(L, n_tokens, split_tokens, w, true);
+  if (s) return s;
+  *bytes = (size_t)w.floats * 4u;
+  return ok();
+}
+
+kv_status kv_attend_decode_rope(const kv_layout* layout, const void* q, kv_dtype dtype, int64_t n_tokens,
+                                int64_t split_tokens, const float* basis_k, const float* basis_v,
+                                const uint32_t* cache_k, const uint32_t* cache_v, float softmax_scale,
+                                const double* inv_freq, float* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  Layout L;
+  kv_status s = build_layout(layout, L);
+  if (s) return s;
+  if (!inv_freq) return fail(KV_ERR_INVALID, "NULL inv_freq");
+  return attend_impl(L, q, dtype, n_tokens, split_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale, out,
+                     workspace, workspace_bytes, stream, nullptr, nullptr, KV_F32, nullptr, false, inv_freq);
+}
+
+kv_status kv_append_attend_decode_rope(const kv_layout* layout, const void* k1, const void* v1, kv_dtype kv_dt,
+                                       const void* q, kv_dtype q_dt, int64_t n_tokens, int64_t split_tokens,
+                                       const float* basis_k, const float* basis_v, uint32_t* cache_k,
+                                       uint32_t* cache_v, float softmax_scale, const double* inv_freq, float* out,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  Layout L;
+  kv_status s = build_layout(layout, L);
+  if (s) return s;
+  if (!inv_freq) return fail(KV_ERR_INVALID, "NULL inv_freq");
+  if (kv_dt != KV_F32 && kv_dt != KV_F16) return fail(KV_ERR_INVALID, "dtype %d unknown", (int)kv_dt);
+  if (n_tokens < 1) return fail(KV_ERR_INVALID, "n_tokens %lld < 1: nothing to append", (long long)n_tokens);
+  if (!k1 || !v1) return fail(KV_ERR_INVALID, "NULL key or value to append");
+  const size_t esz = kv_dt == KV_F32 ? 4 : 2;
+  if (!aligned(k1, esz) || !aligned(v1, esz)) return fail(KV_ERR_INVALID, "misaligned pointer");
+  return attend_impl(L, q, q_dt, n_tokens, split_tokens, basis_k, basis_v, cache_k, cache_v, softmax_scale, out,
+                     workspace, workspace_bytes, stream, k1, v1, kv_dt, nullptr, false, inv_freq);
 }
 
 kv_status kv_encode(const kv_layout* layout, const void* k, const void* v, kv_dtype dtype, int64_t n_tokens,

@@ -541,6 +541,14 @@ __host__ __device__ inline int tile_lds_words(int kbuf_words, int vbuf_words, in
   const int part = (gm <= 8 ? 2 : 1) * gm * kMaxRank;  // the wave's value partial (hi and lo rows when packed)
   return w > part ? w : part;
 }
+// LDS words of the RoPE kernel's exchange (after the tile areas): the partial scores
+// [source wave][tile of wave][64 tokens][GM] of one step; the 128 row sums of the key
+// basis; (cos, sin) of 16 theta_i per pair; the 64 inverse frequencies (float64); and
+// each wave's query operands [wave][lane][8].
+__host__ __device__ constexpr int rope_lds_words(int gm) {
+  return kWaves * kWaves * kTileT * gm + kHeadDim + kHeadDim + kHeadDim + kWaves * 64 * 8;
+}
+
 constexpr int kHeadStats = 3 * kMaxGroup;
 constexpr int kCommonWords = kWaves * 48 + 4 + kHeadStats;
 
@@ -734,6 +742,11 @@ struct WaveCtx {
   int64_t pool_pages;
   const uint32_t* cbk;      // vector-quantized records: the head's K / V codebooks in LDS, else null
   const uint32_t* cbv;
+  int split_begin;          // the split's first token; wave w streams [split_begin + w wave_tokens, + wave_tokens)
+  int wave_tokens;          //   clipped to n_tok
+  int n_tok;                // this sequence's context length
+  int wave_area;            // LDS words of one wave's record tiles (wave w's tiles at ktile + (w - wave) wave_area)
+  float* extra;             // LDS after the tile areas (codebooks, or the exchange of the RoPE kernel)
 };
 
 // Record index, within the buffer resource of the wave's cache regions, of the tile
@@ -1111,6 +1124,11 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   c.t_begin = s_begin + wave * wq;
   c.t_end = c.t_begin + wq;
   if (c.t_end > n_tok) c.t_end = n_tok;
+  c.split_begin = s_begin;
+  c.wave_tokens = wq;
+  c.n_tok = n_tok;
+  c.wave_area = WA;
+  c.extra = areas + kWaves * WA;
   const int wk = hd.wk, wv = hd.wv;
   // buffer resources over the sequence's records (contiguous) or the head's pool (paged)
   const bool paged = a.pg.bt != nullptr;
@@ -1138,7 +1156,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   c.unit = (int64_t)b * a.n_kv_heads + h;
   c.stamp = stamp;
   c.cbk = c.cbv = nullptr;
-  if (a.cb_words > 0) {  // vector-quantized records: the head's codebooks after the tile areas,
+  if (a.cb_words > 0 && !a.rope) {  // vector-quantized records: the head's codebooks after the tile areas,
                          // one row of 2^b entries per pair at the padded strides of the phases
     uint32_t* cbl = (uint32_t*)(areas + kWaves * WA);
     const int ek = code_bits(hd.bk), ev = code_bits(hd.bv);

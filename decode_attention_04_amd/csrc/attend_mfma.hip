@@ -155,7 +155,7 @@ static hipError_t launch_widths(const AttendArgs& a, hipStream_t s) {
 // specialised kernels fit three waves per SIMD (at most 168 VGPRs), the generic
 // ones two; resident workgroups count for more than a third tile buffer (more
 // waves hide the LDS and matrix-core latencies of the tile loop).
-AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group) {
+AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group, bool rope) {
   AttendPlan p;
   int wkm = 1, wvm = 1;
   p.cb_words = 0;
@@ -170,7 +170,8 @@ AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group) {
     p.cb_words = cw > p.cb_words ? cw : p.cb_words;
   }
   p.spec_class = -1;
-  if (group <= 8) {
+  if (rope) p.cb_words = rope_lds_words(group <= 4 ? 4 : 8);  // the RoPE kernel: generic tiles and its exchange
+  if (group <= 8 && !rope) {
     for (int cls = 0; cls < kSpecClasses + kFrozenClasses && p.spec_class < 0; ++cls) {
       bool all = true;
       for (int h = 0; h < n_kv_heads && all; ++h) {
@@ -209,6 +210,7 @@ AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group) {
 }
 
 hipError_t launch_attend(const AttendArgs& a_in, hipStream_t s) {
+  if (a_in.rope) return launch_attend_rope(a_in, s);
   AttendArgs a = a_in;
   const AttendPlan p = plan_attend(a.heads, a.n_kv_heads, a.group);
   a.kbuf_words = p.kbuf_words;

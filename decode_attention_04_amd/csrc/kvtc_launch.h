@@ -62,6 +62,7 @@ struct AttendArgs {
   int32_t vbuf_words;
   int32_t nbuf;        // tile buffers per wave: 2 (next tile streams in) or 1
   int32_t cb_words;    // LDS words for the codebooks of one KV head (K then V), 0 without any
+  const double* rope;  // keys compressed before RoPE: DEVICE inverse frequencies [64] (else null)
 #ifdef KVTC_STAMPS
   uint64_t* stamps;    // [grid][16] phase stamps of every workgroup, or null
 #endif
@@ -104,8 +105,10 @@ struct AttendPlan {
   int cb_words = 0;       // LDS words of the largest head's codebooks
   int kbuf_words = 0, vbuf_words = 0, nbuf = 1, wg_per_cu = 1;
 };
-AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group);
+AttendPlan plan_attend(const HeadTable& heads, int n_kv_heads, int group, bool rope = false);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+// Decode attention over keys compressed before RoPE (a.rope set; group <= 8, scalar records).
+hipError_t launch_attend_rope(const AttendArgs& a, hipStream_t s);
 // Decode attention specialised for the record formats of one class (group <= 8).
 hipError_t launch_attend_spec0(const AttendArgs& a, hipStream_t s);
 hipError_t launch_attend_spec1(const AttendArgs& a, hipStream_t s);

@@ -321,6 +321,48 @@ kv_status kv_append_attend_decode_noalloc(const kv_layout *layout, const void *k
                                           const float *basis_v, uint32_t *cache_k, uint32_t *cache_v,
                                           float softmax_scale, float *out, void *stream);
 
+/* Decode attention over keys compressed before the rotary position embedding
+ * (RoPE): the cache holds the codes of each token's unrotated key (as kv_encode
+ * and kv_append write them from pre-RoPE keys), and the score of token t is
+ *     s_t = softmax_scale * q . RoPE(k^_t, t),   k^_t = Q_K (min_t + step_t code_t),
+ * with Q_K the head's key reconstruction basis (P_K, or the query-side basis of a
+ * query_basis_k layout).  RoPE turns each dimension pair (2i, 2i+1) of a vector at
+ * position t by the angle t * inv_freq[i]; token t of a sequence sits at position
+ * t.  q: [batch][n_q_heads][128] of `dtype`, already rotated to its own position.
+ * inv_freq: DEVICE float64 [64] (RoFormer's base^(-2i/128), or any other
+ * frequencies; a model that pairs dimensions (i, i + 64) is this rotation after a
+ * fixed permutation of the head dimensions, applied to its keys, queries and
+ * bases).  Values, softmax, splits, merges and the workspace contract are those
+ * of kv_attend_decode_split, but the split plan is this kernel's own: the
+ * workspace must hold kv_workspace_bytes_rope(layout, n_tokens, split_tokens)
+ * bytes.  Each key is reconstructed in the head dimension on the matrix cores
+ * (2 * 128 * r_K products per token): wide keys make this path bound by
+ * arithmetic rather than by the cache bytes.
+ * Errors: KV_ERR_UNSUPPORTED for vector-quantized records or a group of more
+ * than 8 query heads; KV_ERR_INVALID for a NULL or misaligned inv_freq; otherwise
+ * as kv_attend_decode_split.
+ * [KV-COBRA project page, Results (the note under the results table: keys
+ *  compressed before RoPE); rotary embedding as defined by RoFormer] */
+kv_status kv_workspace_bytes_rope(const kv_layout *layout, int64_t n_tokens, int64_t split_tokens,
+                                  size_t *bytes);
+kv_status kv_attend_decode_rope(const kv_layout *layout, const void *q, kv_dtype dtype, int64_t n_tokens,
+                                int64_t split_tokens, const float *basis_k, const float *basis_v,
+                                const uint32_t *cache_k, const uint32_t *cache_v, float softmax_scale,
+                                const double *inv_freq, float *out, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* kv_append_attend_decode for keys compressed before RoPE: appends the new
+ * (unrotated) key and value at position n_tokens - 1, then attends as
+ * kv_attend_decode_rope.  The records are those of kv_append; `out` equals that of
+ * kv_append followed by kv_attend_decode_rope with the same split size.  Errors
+ * as kv_append_attend_decode and kv_attend_decode_rope. */
+kv_status kv_append_attend_decode_rope(const kv_layout *layout, const void *k1, const void *v1,
+                                       kv_dtype kv_dt, const void *q, kv_dtype q_dt, int64_t n_tokens,
+                                       int64_t split_tokens, const float *basis_k, const float *basis_v,
+                                       uint32_t *cache_k, uint32_t *cache_v, float softmax_scale,
+                                       const double *inv_freq, float *out, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
 /* Reconstruct stored tokens: for records pos0 .. pos0+n_tokens-1 of every
  * (sequence, KV head) of tensor `which` (0 = K, 1 = V), x^ = B (min + step *
  * code) with B that head's reconstruction basis (`basis`: the tensor's

@@ -328,3 +328,34 @@ def test_vq_layouts_are_validated():
     sc = (ctypes.c_uint32 * 1)(0x3C000000)
     static._c.scale_k = ctypes.cast(sc, ctypes.POINTER(ctypes.c_uint32))
     assert L.kv_cache_bytes(static.ref(), 0, ctypes.byref(out)) == lib_mod.KV_ERR_INVALID
+
+
+def test_rope_attend_validation_and_workspace():
+    """The RoPE entry points validate before any launch: no inverse frequencies,
+    misaligned ones, vector-quantized records and groups above 8 are refused; their
+    workspace follows the RoPE kernel's own split plan (two resident workgroups per
+    CU: 16 splits per unit at the 128K batch-4 shape, against 24 for the other
+    kernels)."""
+    lay = _layout()
+    ref = lay.ref()
+    need = lib_mod.kv_workspace_bytes_rope(lay, 500)
+    args = lambda T, ws_bytes, inv=16, split=0: (ref, 16, 1, T, split, 16, 16, 16, 16, 0.1, inv, 16, 16,
+                                                   ws_bytes, None)
+    assert L.kv_attend_decode_rope(*args(500, need, inv=None)) == lib_mod.KV_ERR_INVALID
+    assert "inv_freq" in L.kv_last_error().decode()
+    assert L.kv_attend_decode_rope(*args(500, need, inv=20)) == lib_mod.KV_ERR_INVALID
+    assert L.kv_attend_decode_rope(*args(1001, need)) == lib_mod.KV_ERR_CAPACITY
+    assert L.kv_attend_decode_rope(*args(500, need - 4)) == lib_mod.KV_ERR_INVALID
+    fused = (ref, 16, 16, 1, 16, 1, 500, 0, 16, 16, 16, 16, 0.1, None, 16, 16, need, None)
+    assert L.kv_append_attend_decode_rope(*fused) == lib_mod.KV_ERR_INVALID
+    g12 = _layout(n_kv_heads=1, n_q_heads=12, alloc=[(64, 4, 64, 4)])
+    assert L.kv_attend_decode_rope(g12.ref(), 16, 1, 500, 0, 16, 16, 16, 16, 0.1, 16, 16, 16, 1 << 30,
+                                   None) == lib_mod.KV_ERR_UNSUPPORTED
+    vq_lay = _vq_layout([(128, 4, 128, 4)])
+    assert L.kv_attend_decode_rope(vq_lay.ref(), 16, 1, 500, 0, 16, 16, 16, 16, 0.1, 16, 16, 16, 1 << 30,
+                                   None) == lib_mod.KV_ERR_UNSUPPORTED
+    T = 131073
+    uni = lib_mod.Layout(8, 32, 4, T, [(64, 4, 64, 4)] * 8)
+    words = lib_mod.kv_workspace_bytes_rope(uni, T) // 4
+    assert (words - 32) // (4 * 32 * 132) == 16
+    assert lib_mod.kv_workspace_bytes_rope(uni, T) <= lib_mod.kv_workspace_bytes(uni, T)
