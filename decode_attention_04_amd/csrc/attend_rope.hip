@@ -127,7 +127,8 @@ __device__ __attribute__((always_inline)) inline void rope_k_tile(const uint32_t
       }
     const uint32_t kh = hk ? kt[tok * wk] : skw;
     const float mu = f16_bits_to_f32(kh & 0xFFFFu), sg = f16_bits_to_f32(kh >> 16) * rw.escale;
-    u32x4 bh, bl;  // the turned key at the lane's 8 dimensions, fp16 hi and lo, times 1/4
+    u32x4 bh, bl;  // the turned key at the lane's 8 dimensions, fp16 hi and lo (times 1/4: the step and
+                   // the row sums carry it)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -136,15 +137,17 @@ __device__ __attribute__((always_inline)) inline void rope_k_tile(const uint32_t
         const float x = fmaf(sg, d[mb][2 * pp], mu * rt.p1[mb][2 * pp]);
         const float y = fmaf(sg, d[mb][2 * pp + 1], mu * rt.p1[mb][2 * pp + 1]);
         const float c = cr[mb][pp], s = sr[mb][pp];
-        const float xr = (c * x - s * y) * 0.25f, yr = (s * x + c * y) * 0.25f;
+        const float xr = c * x - s * y, yr = s * x + c * y;
         if (tt < 3) {  // on to the token 16 positions later
           cr[mb][pp] = c * rt.c16[mb][pp] - s * rt.s16[mb][pp];
           sr[mb][pp] = s * rt.c16[mb][pp] + c * rt.s16[mb][pp];
         }
-        const _Float16 xh = (_Float16)xr, yh = (_Float16)yr;
-        const _Float16 xl = (_Float16)(xr - (float)xh), yl = (_Float16)(yr - (float)yh);
-        bh[2 * mb + pp] = h2u(xh) | (h2u(yh) << 16);
-        bl[2 * mb + pp] = h2u(xl) | (h2u(yl) << 16);
+        // hi = the pair truncated to fp16 (packed conversion), lo = the exact remainder
+        // truncated again: ~21 significant bits
+        const auto hp = __builtin_amdgcn_cvt_pkrtz(xr, yr);
+        const auto lp = __builtin_amdgcn_cvt_pkrtz(xr - (float)hp[0], yr - (float)hp[1]);
+        bh[2 * mb + pp] = __builtin_bit_cast(uint32_t, hp);
+        bl[2 * mb + pp] = __builtin_bit_cast(uint32_t, lp);
       }
     }
     // rows [0, GM): hi(q) . (hi(k) + lo(k)); rows [GM, 2 GM): lo(q) . hi(k)
@@ -229,7 +232,7 @@ __device__ __attribute__((always_inline)) inline void rope_tiles(const AttendArg
       frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
       e = 14 - e;      // max |P| 2^E < 2^14
     }
-    rw.escale = ldexpf(1.0f, 24 - e);  // codes are fp16 subnormals: code 2^-24
+    rw.escale = ldexpf(1.0f, 22 - e);  // codes are fp16 subnormals (code 2^-24); the key carries 1/4
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -275,7 +278,7 @@ __device__ __attribute__((always_inline)) inline void rope_tiles(const AttendArg
     float sum = 0.0f;
     for (int j = 0; j < hr; ++j) sum += pr[j];
     sum += __shfl_xor(sum, 1);
-    if (half == 0) p1s[row] = sum;
+    if (half == 0) p1s[row] = sum * 0.25f;  // the key carries 1/4
   }
   // the first tiles, behind the loads above
   for (int t = 0; t < (nbuf > 1 ? nbuf - 1 : 1); ++t) {
