@@ -674,6 +674,47 @@ def measured_busy(workload: str):
         {"source": f"profiles/sq_append_attend_{workload}.md"}
 
 
+def read_ceiling(nbytes: int, reps: int = 100):
+    """The GPU's own streaming-read rate: libkvtc_probe.so's plain read of nbytes (the
+    decode step's bytes), four buffers rotated (beyond the Infinity Cache), back to back,
+    at a few grid sizes; the best rate in GB/s and its grid.  A reference for the decode
+    kernels beside the datasheet peak."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "decode_attention_04_amd", "libkvtc_probe.so"))
+    fn = lib.kvtc_read_probe
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    n = (nbytes // 16) * 16
+    bufs = [torch.ones(n // 4, dtype=torch.int32, device="cuda") for _ in range(4)]
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = (0.0, 0)
+    for wgs in (768, 2048, 8192):
+        def launch(i):
+            rc = fn(bufs[i % 4].data_ptr(), n, wgs, sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"read probe launch failed ({rc})")
+        for i in range(20):
+            launch(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            launch(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbs = n / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
+        best = max(best, (gbs, wgs))
+    del bufs
+    torch.cuda.empty_cache()
+    return {"GB_per_s": round(best[0], 1), "pct_of_hbm_peak": round(100 * best[0] / HBM_PEAK_GBS, 2),
+            "workgroups": best[1], "bytes": n,
+            "probe": "plain 16-byte non-temporal reads, four buffers rotated, back-to-back launches"}
+
+
 def copy_probe(mib: int):
     """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counter readings."""
     import torch
@@ -902,6 +943,9 @@ def main():
             dec_rates[name] = decode_rate(K, W.llama_t128k(bpd), rope=True)
             log(f"decode {name}: {dec_rates[name]}")
 
+    ceiling = read_ceiling(attend_bytes + append_bytes)
+    log(f"streaming-read ceiling of this GPU: {ceiling}")
+
     dist = None
     if not args.no_distortion:
         dist = distortion_rate(K)
@@ -929,6 +973,8 @@ def main():
             "timing": "HIP graph replay per step" if graphs else "one eager launch per step, back to back",
             "layer_caches_rotated": n_rep,
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "hbm_read_ceiling": ceiling,
+            "pct_of_read_ceiling": round(100 * gbs / ceiling["GB_per_s"], 2),
             "single_launch_us": pct,
             "context_tokens_per_s": round(B * (T + 1) / (ms_step * 1e-3), 1),
             "bytes_per_step": attend_bytes + append_bytes,
