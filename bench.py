@@ -559,7 +559,7 @@ def phase_stamps(K, wl, reps=20, warmup=200, block=4096):
     q = torch.from_numpy(W.query_array(wl, 0)).to(dev)
     out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
     ws = torch.zeros(K.kv_workspace_bytes(lay, T) // 4, dtype=torch.float32, device=dev)
-    st = torch.zeros((grid, 16), dtype=torch.int64, device=dev)
+    st = torch.zeros((grid, 24), dtype=torch.int64, device=dev)
     lib.kv_debug_stamps.restype = ctypes.c_int32
     lib.kv_debug_stamps.argtypes = [ctypes.c_void_p]
     scale = 1.0 / math.sqrt(d)
@@ -590,6 +590,13 @@ def phase_stamps(K, wl, reps=20, warmup=200, block=4096):
             "tile loop, per wave": (loop_end - rel[:, 1:2]).reshape(-1),
             "wave spread (last wave - first wave of a workgroup)": loop_end.max(1) - loop_end.min(1),
             "wave merge, back-projection, partial stores (from the last wave)": rel[:, 6] - loop_end.max(1),
+            "  wave partials staged in LDS (from the last wave)": rel[:, 12] - loop_end.max(1),
+            "    per wave: tile loop end to partial in LDS": (rel[:, 16:20] - loop_end).reshape(-1),
+            "    per wave: P_V row loads issued": (rel[:, 20:24] - rel[:, 16:20]).reshape(-1),
+            "    last wave's loads issued to the barrier passed": rel[:, 12] - rel[:, 20:24].max(1),
+            "  wave merge": rel[:, 13] - rel[:, 12],
+            "  back-projection, partial stores issued": rel[:, 14] - rel[:, 13],
+            "  partial stores completed": rel[:, 6] - rel[:, 14],
             "arrival atomic": rel[:, 7] - rel[:, 6],
             "split merge (merging workgroups)": (rel[:, 8] - rel[:, 7])[s_[:, 8] > 0],
         }

@@ -698,9 +698,11 @@ __device__ inline void merge_splits(const AttendArgs& a, int h, int b, bool rese
 // phase boundaries of every workgroup into the caller's stamp buffer (kStampWords
 // 64-bit words per workgroup): 0 entry, 1 query projection done (wave 0), 2-5 tile
 // loop done per wave, 6 split partial stored, 7 arrival counted, 8 split merge done
-// (merging workgroup only), 9 hardware id, 10 XCC id, 11 fused append done.  Other
-// builds compile none of it.
-constexpr int kStampWords = 16;
+// (merging workgroup only), 9 hardware id, 10 XCC id, 11 fused append done, 12 wave
+// partials staged in LDS, 13 wave merge done, 14 back-projection stored (issued),
+// 16-19 per wave: its partial written to LDS, 20-23 per wave: its P_V row loads issued.
+// Other builds compile none of it.
+constexpr int kStampWords = 24;
 #ifdef KVTC_STAMPS
 #define KVTC_STAMP(ptr, i)                                            \
   do {                                                                \
@@ -1201,6 +1203,10 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   run(c, st);
   wait_tiles();
   if (lane == 0) KVTC_STAMP(stamp, 2 + wave);
+  // The tile loop ends at issue priority 0 (progress_priority); the epilogue and the
+  // split merge are short and gate the unit's output (and, for the last workgroups, the
+  // launch), so they take the highest priority over the streaming waves of the CU.
+  __builtin_amdgcn_s_setprio(3);
 
   // ---- wave partial: m, l, sum of p*min (per head), o~[head][j] in natural code order
   const int n = lane & 15, G = lane >> 4;
@@ -1234,6 +1240,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     }
   }
 
+  if (lane == 0) KVTC_STAMP(stamp, 16 + wave);
   // this thread's half row of P_V for the back-projection of the workgroup's partial,
   // in flight during the wave merge (issued once the value accumulators are free):
   // segment [bhalf jh, bhalf jh + jh) of row bi, jh = r_V / 2, in float4 steps;
@@ -1245,7 +1252,9 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   float4 pv[kMaxRank / 8];
 #pragma unroll
   for (int k = 0; k < kMaxRank / 8; ++k) pv[k] = *(const float4*)(prow + (4 * k < jh ? 4 * k : 0));
+  if (lane == 0) KVTC_STAMP(stamp, 20 + wave);
   __syncthreads();
+  if (tid == 0) KVTC_STAMP(stamp, 12);
 
   // ---- merge the four wave partials into one partial o~ per query head, staged
   // in the score area (free after the token loop) as ot[head][half][64]: half h of
@@ -1280,6 +1289,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     }
   }
   __syncthreads();
+  if (tid == 0) KVTC_STAMP(stamp, 13);
   {
     float accb[GM];
 #pragma unroll
@@ -1304,6 +1314,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
       if (hh < g && bhalf == 0) part_store(part0 + (int64_t)hh * a.n_splits * kPartStride + bi, v);
     }
   }
+  if (tid == 0) KVTC_STAMP(stamp, 14);
 
   // ---- arrival: the last workgroup of this (sequence, KV head) merges all splits.
   // A counter that was not zero on entry makes later arrivals (count past ns) merge
