@@ -559,7 +559,7 @@ def phase_stamps(K, wl, reps=20, warmup=200, block=4096):
     q = torch.from_numpy(W.query_array(wl, 0)).to(dev)
     out = torch.empty((B, hq, d), dtype=torch.float32, device=dev)
     ws = torch.zeros(K.kv_workspace_bytes(lay, T) // 4, dtype=torch.float32, device=dev)
-    st = torch.zeros((grid, 24), dtype=torch.int64, device=dev)
+    st = torch.zeros((grid, 32), dtype=torch.int64, device=dev)
     lib.kv_debug_stamps.restype = ctypes.c_int32
     lib.kv_debug_stamps.argtypes = [ctypes.c_void_p]
     scale = 1.0 / math.sqrt(d)
@@ -587,6 +587,11 @@ def phase_stamps(K, wl, reps=20, warmup=200, block=4096):
         durs = {
             "start after the first workgroup": rel[:, 0],
             "query projection (and first tile copies issued)": rel[:, 1] - rel[:, 0],
+            "  basis and query loads, first tile copies issued": (rel[:, 24] - rel[:, 0])[s_[:, 24] > 0],
+            "  queries staged (their loads complete)": (rel[:, 25] - rel[:, 24])[s_[:, 24] > 0],
+            "  projection (basis loads complete)": (rel[:, 26] - rel[:, 25])[s_[:, 24] > 0],
+            "  exponents and sums": (rel[:, 27] - rel[:, 26])[s_[:, 24] > 0],
+            "  operands built": (rel[:, 1] - rel[:, 27])[s_[:, 24] > 0],
             "tile loop, per wave": (loop_end - rel[:, 1:2]).reshape(-1),
             "wave spread (last wave - first wave of a workgroup)": loop_end.max(1) - loop_end.min(1),
             "wave merge, back-projection, partial stores (from the last wave)": rel[:, 6] - loop_end.max(1),

@@ -700,9 +700,11 @@ __device__ inline void merge_splits(const AttendArgs& a, int h, int b, bool rese
 // loop done per wave, 6 split partial stored, 7 arrival counted, 8 split merge done
 // (merging workgroup only), 9 hardware id, 10 XCC id, 11 fused append done, 12 wave
 // partials staged in LDS, 13 wave merge done, 14 back-projection stored (issued),
-// 16-19 per wave: its partial written to LDS, 20-23 per wave: its P_V row loads issued.
+// 16-19 per wave: its partial written to LDS, 20-23 per wave: its P_V row loads issued;
+// query projection (wave 0): 24 loads and first copies issued, 25 queries staged,
+// 26 projected, 27 exponents and sums done.
 // Other builds compile none of it.
-constexpr int kStampWords = 24;
+constexpr int kStampWords = 32;
 #ifdef KVTC_STAMPS
 #define KVTC_STAMP(ptr, i)                                            \
   do {                                                                \
@@ -844,12 +846,14 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
   for (int k = 0; k < kMaxRank / 2; ++k)
     if (k < rpg) pk[k] = col[(int64_t)k * rk];
   issue();
+  if (tid == 0) KVTC_STAMP(c.stamp, 24);
 #pragma unroll
   for (int k = 0; k < kQ; ++k) {
     const int idx = tid + 256 * k;  // head idx / 128, dimension idx % 128
     qs[(idx % kHeadDim) * GM + idx / kHeadDim] = qv[k];
   }
   __syncthreads();
+  if (tid == 0) KVTC_STAMP(c.stamp, 25);
   for (int h4 = 0; h4 < g; h4 += 4) {  // four heads at a time; the column segment stays in registers
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -873,12 +877,13 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
     }
   }
   __syncthreads();
+  if (tid == 0) KVTC_STAMP(c.stamp, 26);
   float* Eh = c.stats;
   for (int hh = wave; hh < g; hh += kWaves) {  // one wave per head: sum and max |q~| over the rank
     const float v0 = lane < rk ? qt[hh * kMaxRank + lane] : 0.0f;
     const float v1 = lane + 64 < rk ? qt[hh * kMaxRank + lane + 64] : 0.0f;
-    const float sum = wave_sum(v0 + v1);
-    const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    const float sum = wave_sum_uniform(v0 + v1);  // DPP row reductions: no LDS round trips
+    const float mx = wave_max_uniform(fmaxf(fabsf(v0), fabsf(v1)));
     int e = 0;
     if (mx > 0.0f) {
       frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
@@ -891,6 +896,7 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
     }
   }
   __syncthreads();
+  if (tid == 0) KVTC_STAMP(c.stamp, 27);
   const int nks = rk >= 32 ? rk / 32 : 1;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
