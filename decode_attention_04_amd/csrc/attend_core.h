@@ -1232,6 +1232,9 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   // operand for rows >= GM (GM <= 8); the sum p*min joins the hi row
   constexpr int kRows = GM <= 8 ? 2 * GM : GM;
   if (4 * G < kRows) {
+    // the sums p * min of this lane group's heads (4G + e) mod GM, read once: read inside
+    // the store loop, each store would wait for a read behind the previous store
+    const f32x4 cs4 = *(const f32x4*)(mlw + 32 + ((4 * G) & (GM - 1)));
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       if (nt < NT) {
@@ -1240,7 +1243,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = 4 * G + e, hh = row & (GM - 1);
-          if (hh < g) wl[row * rv + j] = fmaf(st.acc2[nt][e], f, row < GM ? mlw[32 + hh] : 0.0f);
+          if (hh < g) wl[row * rv + j] = fmaf(st.acc2[nt][e], f, row < GM ? cs4[e] : 0.0f);
         }
       }
     }
