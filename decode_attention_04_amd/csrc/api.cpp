@@ -178,25 +178,26 @@ kv_status build_layout(const kv_layout* L, Layout& out) {
   return KV_OK;
 }
 
-// A split streams at least this many tokens by default: a workgroup's fixed costs (the
-// query projection before its first tile, the merge, back-projection and partial
-// stores after its last) take ~15 us, so shorter splits make a launch slower although
-// they fill more slots (measured at 32K tokens, batch 1, 8 KV heads: 37.9 us per step
-// with the 520 workgroups of 512-token splits, 28.0 us with 264 of 1024 tokens).
+// A split streams at least this many tokens on average by default: a workgroup's fixed
+// costs (the query projection before its first tile, the merge, back-projection and
+// partial stores after its last) take ~15 us, so shorter splits make a launch slower
+// although they fill more slots (measured at 32K tokens, batch 1, 8 KV heads: 37.9 us
+// per step with the 520 workgroups of 512-token splits, 28.0 us with 264 of 1024 tokens).
 constexpr int64_t kMinSplitTokens = 4 * kSplitQuantum;
 
-// Default split-K size: one workgroup for every resident slot of the 256 CUs
-// (as many per CU as the layout's kernel and LDS use allow), each split a
-// multiple of 256 tokens (64 per wave) and at least kMinSplitTokens.
-int64_t default_split_tokens(const Layout& L, int64_t T, bool rope) {
+// Default split count of a (sequence, KV head) unit: one workgroup for every resident
+// slot of the 256 CUs (as many per CU as the layout's kernel and LDS use allow), but no
+// more than T / kMinSplitTokens (rounded down, so that a context one token past a
+// multiple of 1024 does not take an extra split: the merge folds up to 32 splits in one
+// round of loads, 33 take two).  The kernel spreads the 256-token blocks of a unit
+// evenly over its splits, so any count up to the number of blocks works.
+int64_t default_splits(const Layout& L, int64_t T, bool rope) {
   const int64_t units = (int64_t)L.batch * L.n_kv;
   const int64_t target = 256 * (int64_t)plan_attend(L.table, L.n_kv, L.group, rope).wg_per_cu;
   int64_t ns = (target + units - 1) / units;
-  if (ns < 1) ns = 1;
-  int64_t st = (T + ns - 1) / ns;
-  st = ((st + kSplitQuantum - 1) / kSplitQuantum) * kSplitQuantum;
-  if (st < kMinSplitTokens) st = kMinSplitTokens;
-  return st;
+  const int64_t cap = T / kMinSplitTokens;
+  if (ns > cap) ns = cap;
+  return ns < 1 ? 1 : ns;
 }
 
 struct Workspace {
@@ -210,11 +211,6 @@ struct Workspace {
 // Splits of a unit of T tokens when each split takes about st tokens (a multiple of
 // the quantum), as the kernel cuts them.
 static int64_t splits_for(int64_t T, int64_t st) { return T > 0 ? (T + st - 1) / st : 1; }
-static int64_t quantum_split(int64_t T, int64_t ns) {
-  int64_t st = (T + ns - 1) / ns;
-  st = ((st + kSplitQuantum - 1) / kSplitQuantum) * kSplitQuantum;
-  return st < kSplitQuantum ? kSplitQuantum : st;
-}
 
 // rope: the plan of the kernel for keys compressed before RoPE (its own resident slots).
 kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Workspace& w, bool rope = false) {
@@ -238,8 +234,7 @@ kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Works
     const int64_t ns = splits_for(T, split_tokens);
     for (int h = 0; h < L.n_kv; ++h) w.ns[h] = (int32_t)(ns > 65535 ? 65536 : ns);
   } else {
-    const int64_t st_uniform = default_split_tokens(L, T, rope);
-    const int64_t ns_uniform = splits_for(T, st_uniform);
+    const int64_t ns_uniform = default_splits(L, T, rope);
     // largest-remainder apportionment of ns_uniform * n_kv splits, at least one per
     // head, so that the layout never launches more workgroups than with equal counts
     const int64_t total = ns_uniform * L.n_kv;
@@ -264,8 +259,9 @@ kv_status plan_workspace(const Layout& L, int64_t T, int64_t split_tokens, Works
       ++nh[best];
       rem[best] = -1;
     }
+    const int64_t nq = T > 0 ? (T + kSplitQuantum - 1) / kSplitQuantum : 1;  // 256-token blocks
     for (int h = 0; h < L.n_kv; ++h) {
-      const int64_t ns = splits_for(T, quantum_split(T, nh[h]));
+      const int64_t ns = nh[h] < nq ? nh[h] : nq;
       w.ns[h] = (int32_t)(ns > 65535 ? 65536 : ns);
     }
   }

@@ -248,9 +248,10 @@ kv_status kv_attend_decode(const kv_layout *layout, const void *q, kv_dtype dtyp
  * encodes it in kv_append_attend_decode); with few
  * blocks per split a split may be larger than split_tokens and the last ones
  * may be empty (n_tokens = 512, split_tokens = 256: 512 and 0 tokens).  The
- * default fills every resident workgroup slot of the GPU with splits of at least
- * 1024 tokens (shorter splits cost more in per-split fixed work than they gain in
- * parallelism), giving each KV head a number of splits in proportion to the cost
+ * default fills every resident workgroup slot of the GPU, with at most
+ * floor(n_tokens / 1024) splits per unit (shorter splits cost more in per-split
+ * fixed work than they gain in parallelism; 32769 tokens take 32 splits, not 33),
+ * giving each KV head a number of splits in proportion to the cost
  * of its tokens (record words per token, key plus value, plus a fixed per-token
  * share for the softmax), so that heads of different widths finish together.
  * The result is the same up to float rounding for every split size.  The

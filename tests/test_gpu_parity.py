@@ -475,7 +475,8 @@ def test_full_size_llama_b1_t32k_fused_step(K):
     """The LLaMA-shaped single-sequence layer at its own size: 32 query heads over 8 KV
     heads, C1 at 2 bits per dimension with MSE weights, a 32768-token prefill encoded
     on the GPU, then one decode step (the append of token 32768 fused with attention
-    over all 32769 tokens) with the default split plan (more than 32 splits per unit).
+    over all 32769 tokens) with the default split plan (32 splits per unit, at most
+    T / 1024: the merge folds them in one round).
     The fused step equals kv_append + kv_attend_decode bit for bit; every unit's
     records match the oracle's (exact headers, codes only at classified ties) and all
     32 query heads' outputs match oracle attention."""
@@ -486,7 +487,7 @@ def test_full_size_llama_b1_t32k_fused_step(K):
     lay = K.Layout(hkv, hq, B, T, alloc)
     ns = _n_splits(K, lay, T)
     say(f"full size {wl.name}: {alloc}, {ns} splits per unit")
-    assert ns > 32
+    assert ns == 32
     kx = W.kv_array(wl, "K", 0, T)
     vx = W.kv_array(wl, "V", 0, T)
     pk, pv = H.dev(codec.concat_bases(bk)), H.dev(codec.concat_bases(bv))
