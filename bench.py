@@ -763,11 +763,27 @@ def main():
     ap.add_argument("--phase-stamps", type=int, default=0, metavar="REPS",
                     help="only run REPS launches of the decode step with the phase-stamp build "
                          "(libkvtc_stamps.so) and print the per-phase timing summary")
+    ap.add_argument("--decode-layout", default="", metavar="NAME",
+                    help="only time one other decode layout (pre-rope-2bpd, pre-rope-0.5bpd, vq-2bpd, paged-2bpd) "
+                         "with --steps / --warmup launches and print its line (for counter profiles)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 3 times (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.decode_layout:
+        import decode_attention_04_amd as K
+        layouts = {
+            "pre-rope-2bpd": lambda: decode_rate(K, W.llama_t128k(2.0), steps=args.steps, warmup=args.warmup, rope=True),
+            "pre-rope-0.5bpd": lambda: decode_rate(K, W.llama_t128k(0.5), steps=args.steps, warmup=args.warmup,
+                                                   rope=True),
+            "vq-2bpd": lambda: decode_rate(K, W.llama_t128k_nova_vq(2.0), steps=args.steps, warmup=args.warmup),
+            "paged-2bpd": lambda: decode_rate(K, W.llama_t128k(2.0), steps=args.steps, warmup=args.warmup, page=256),
+        }
+        if args.decode_layout not in layouts:
+            raise SystemExit(f"unknown decode layout {args.decode_layout}; choose from {sorted(layouts)}")
+        print(json.dumps(layouts[args.decode_layout]()), flush=True)
         return
     if args.phase_stamps:
         os.environ["KVTC_LIBRARY"] = os.path.join(ROOT, "decode_attention_04_amd", "libkvtc_stamps.so")
