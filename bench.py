@@ -249,8 +249,14 @@ def decode_rate(K, wl, block=4096, steps=200, warmup=200, min_bytes=1.0e9, ragge
         else:
             K.kv_append_attend_decode(lay, k1, v1, q, T, pk, pv, ck_, cv_, scale, out, ws)
 
-    for i in range(warmup):
+    # at least `warmup` steps and 30 ms of them: after the set-up's idle the first
+    # milliseconds of sustained load run slower while the clocks settle
+    i, t_w = 0, time.perf_counter()
+    while i < warmup or time.perf_counter() - t_w < 0.03:
         step(i)
+        i += 1
+        if i % 50 == 0:
+            torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -709,8 +715,12 @@ def read_ceiling(nbytes: int, reps: int = 100):
             rc = fn(bufs[i % 4].data_ptr(), n, wgs, sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
             if rc != 0:
                 raise RuntimeError(f"read probe launch failed ({rc})")
-        for i in range(20):
+        i, t_w = 0, time.perf_counter()  # 30 ms of load first, as for the decode rates
+        while i < 20 or time.perf_counter() - t_w < 0.03:
             launch(i)
+            i += 1
+            if i % 50 == 0:
+                torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
@@ -764,7 +774,7 @@ def main():
                     help="only run REPS launches of the decode step with the phase-stamp build "
                          "(libkvtc_stamps.so) and print the per-phase timing summary")
     ap.add_argument("--decode-layout", default="", metavar="NAME",
-                    help="only time one other decode layout (pre-rope-2bpd, pre-rope-0.5bpd, vq-2bpd, paged-2bpd) "
+                    help="only time one other decode layout (pre-rope-2bpd, pre-rope-0.5bpd, vq-2bpd, paged-2bpd, b1-t32k) "
                          "with --steps / --warmup launches and print its line (for counter profiles)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 3 times (calibrates the HBM byte counters)")
@@ -780,6 +790,7 @@ def main():
                                                    rope=True),
             "vq-2bpd": lambda: decode_rate(K, W.llama_t128k_nova_vq(2.0), steps=args.steps, warmup=args.warmup),
             "paged-2bpd": lambda: decode_rate(K, W.llama_t128k(2.0), steps=args.steps, warmup=args.warmup, page=256),
+            "b1-t32k": lambda: decode_rate(K, W.LLAMA_T32K, steps=args.steps, warmup=args.warmup),
         }
         if args.decode_layout not in layouts:
             raise SystemExit(f"unknown decode layout {args.decode_layout}; choose from {sorted(layouts)}")
@@ -860,7 +871,7 @@ def main():
     torch.cuda.synchronize()
     two_call_out = out.clone()
     out.zero_()
-    for i in range(max(args.warmup, n_rep)):
+    for i in range(n_rep):
         step(i)
     torch.cuda.synchronize()
     ref_out = out.clone()
@@ -890,15 +901,23 @@ def main():
                 assert torch.equal(out, ref_out), "graph replay differs from the eager step"
             step(r)
             torch.cuda.synchronize()
+    def timed_step(i):
+        if graphs:
+            graphs[i % n_rep].replay()
+        else:
+            step(i)
+
+    # the warm-up steps run right before the timed ones: the checks above leave the GPU
+    # idle for ~0.1 s (first use of torch's comparison kernels), and after such an idle
+    # the first milliseconds of sustained load run up to 20% slower while the clocks settle
+    for i in range(args.warmup):
+        timed_step(i)
     steps = args.steps
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(steps):
-        if graphs:
-            graphs[i % n_rep].replay()
-        else:
-            step(i)
+        timed_step(i)
     stop.record(stream)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_out), "timed steps changed the output"
