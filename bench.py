@@ -774,7 +774,8 @@ def main():
                     help="only run REPS launches of the decode step with the phase-stamp build "
                          "(libkvtc_stamps.so) and print the per-phase timing summary")
     ap.add_argument("--decode-layout", default="", metavar="NAME",
-                    help="only time one other decode layout (pre-rope-2bpd, pre-rope-0.5bpd, vq-2bpd, paged-2bpd, b1-t32k) "
+                    help="only time one other decode layout (pre-rope-2bpd, pre-rope-0.5bpd, vq-2bpd, paged-2bpd, b1-t32k, "
+                         "0.5bpd, 4bpd) "
                          "with --steps / --warmup launches and print its line (for counter profiles)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 3 times (calibrates the HBM byte counters)")
@@ -791,6 +792,8 @@ def main():
             "vq-2bpd": lambda: decode_rate(K, W.llama_t128k_nova_vq(2.0), steps=args.steps, warmup=args.warmup),
             "paged-2bpd": lambda: decode_rate(K, W.llama_t128k(2.0), steps=args.steps, warmup=args.warmup, page=256),
             "b1-t32k": lambda: decode_rate(K, W.LLAMA_T32K, steps=args.steps, warmup=args.warmup),
+            "0.5bpd": lambda: decode_rate(K, W.llama_t128k(0.5), steps=args.steps, warmup=args.warmup),
+            "4bpd": lambda: decode_rate(K, W.llama_t128k(4.0), steps=args.steps, warmup=args.warmup),
         }
         if args.decode_layout not in layouts:
             raise SystemExit(f"unknown decode layout {args.decode_layout}; choose from {sorted(layouts)}")
