@@ -297,6 +297,40 @@ def test_attention_group_sizes(K, g):
     _attention_case(K, alloc, bk, bv, 2, g, 900, 873, [0, 256])
 
 
+# The largest layouts the boundary accepts: 64 KV heads (the kernel-argument head
+# table), and GQA groups of 16 query heads per KV head.
+ALLOC_64_CLASS = [[(64, 4, 128, 2), (32, 8, 64, 4), (128, 2, 16, 8), (16, 8, 32, 8)][h % 4] for h in range(64)]
+ALLOC_64_MIXED = [[(64, 4, 128, 2), (32, 3, 64, 5), (16, 6, 32, 7), (128, 4, 16, 2)][h % 4] for h in range(64)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_encode_64_kv_heads(K, dtype):
+    """Prefill encode of a 64-head layout (every head's own format) against the oracle."""
+    say(f"encode 64 KV heads {dtype}")
+    wl = W.LLAMA_T32K
+    bk, bv = _mixed_bases(ALLOC_64_MIXED, seed=71)
+    _encode_case(K, lambda t, b, h, n: W.tokens(wl, t, b, h % wl.n_kv_heads, 0, n, dtype), ALLOC_64_MIXED, bk, bv,
+                 1, 200, 3, 150, dtype)
+
+
+@pytest.mark.parametrize("alloc", [ALLOC_64_CLASS, ALLOC_64_MIXED], ids=["class-kernel", "generic-kernel"])
+def test_attention_64_kv_heads(K, alloc):
+    """Decode attention over 64 KV heads (GQA group 2), on the class kernel and on the
+    generic one."""
+    say(f"attention 64 KV heads, class {K.kv_attend_plan(K.Layout(64, 128, 1, 300, alloc), 300)[0]}")
+    bk, bv = _mixed_bases(alloc, seed=73)
+    _attention_case(K, alloc, bk, bv, 1, 2, 300, 300, [0, 256])
+
+
+def test_attention_group_16(K):
+    """The largest GQA group: 16 query heads per KV head (two value operands per row
+    block, the generic kernel), with several splits."""
+    say("attention g=16")
+    alloc = [(64, 4, 128, 2), (32, 5, 16, 8)]
+    bk, bv = _mixed_bases(alloc, seed=79)
+    _attention_case(K, alloc, bk, bv, 2, 16, 900, 873, [0, 256])
+
+
 def _budget_formats(budget_bits):
     """(rank, bits) the per-head search can pick under one budget of bits per vector:
     b = min(8, floor(budget / r)) for every rank with b >= 2."""
@@ -536,6 +570,7 @@ FUSED_CASES = [
     pytest.param(MIXED_ALLOC, 4, 2, 1600, 1500, 0, "f32", id="mixed-ragged"),
     pytest.param([(32, 3, 64, 5), (16, 7, 128, 6)], 7, 1, 800, 777, 256, "f16", id="odd-widths-g7"),
     pytest.param([(64, 4, 64, 4), (16, 8, 128, 4)], 8, 1, 600, 513, 512, "f16", id="g8"),
+    pytest.param([(64, 4, 128, 2), (32, 5, 16, 8)], 16, 1, 700, 650, 256, "f16", id="g16-largest-group"),
 ]
 
 
