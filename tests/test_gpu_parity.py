@@ -156,6 +156,73 @@ def test_encode_ragged_token_counts(K, n):
     _encode_case(K, lambda t, b, h, n_: W.tokens(wl, t, b, h, 11, n_), alloc, bk, bv, 2, n + 9, 9, n, "f16")
 
 
+def _degenerate_tokens(n, seed, dtype):
+    """Tokens at the edges of the encoder's input domain, in a repeating pattern: zero
+    vectors (all coordinates 0: step 0, every code 0), constant vectors, one non-zero
+    dimension, repeated identical tokens, and tokens of norm 60000 (the documented
+    limit is ||x||_2 max_j ||P_j||_2 <= 65504; here the bases are orthonormal)."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i in range(n):
+        kind = i % 6
+        if kind == 0:
+            x = np.zeros(128)
+        elif kind == 1:
+            x = np.full(128, 0.75 * (1 + i % 5))
+        elif kind == 2:
+            x = np.zeros(128)
+            x[(7 * i) % 128] = 1000.0 * (-1) ** i
+        elif kind == 3:
+            x = np.linspace(-1.0, 1.0, 128) * 3.0  # the same token each time
+        else:
+            z = rng.standard_normal(128)
+            x = z * (60000.0 / np.linalg.norm(z)) if kind == 4 else z * 1e-3
+        rows.append(x)
+    return np.array(rows).astype(np.float32 if dtype == "f32" else np.float16)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_encode_degenerate_tokens(K, dtype):
+    """Zero, constant, one-hot, repeated, tiny and near-limit tokens: prefill records
+    against the oracle (headers exact, codes up to classified ties)."""
+    say(f"encode degenerate tokens {dtype}")
+    alloc = [(16, 2, 128, 8), (64, 4, 32, 5), (128, 3, 64, 7)]
+    bk, bv = _mixed_bases(alloc, seed=83)
+    _encode_case(K, lambda t, b, h, n: _degenerate_tokens(n, 1000 * b + 10 * h + (t == "V"), dtype), alloc, bk, bv,
+                 2, 140, 6, 130, dtype)
+
+
+def test_attention_identical_keys_is_the_value_mean(K):
+    """Every key zero: all scores equal, so each query head's output is the plain mean
+    of its KV head's reconstructed values (a closed form), for GPU and oracle alike."""
+    say("attention over identical keys")
+    alloc = [(64, 4, 128, 2), (32, 8, 64, 4)]
+    bk, bv = _mixed_bases(alloc, seed=89)
+    wl, B, g, T = W.LLAMA_T32K, 2, 4, 700
+    kv = {}
+    for b in range(B):
+        for h in range(len(alloc)):
+            kv[("K", b, h)] = np.zeros((T, 128), np.float16)
+            kv[("V", b, h)] = W.tokens(wl, "V", b, h, 0, T)
+    ck_h, cv_h = H.oracle_cache(wl, alloc, bk, bv, B, T, T, kv=kv)
+    q = W.random_vectors(91, (B, len(alloc) * g, 128)).astype(np.float16)
+    ref = attention.attend_cache(q.astype(np.float64), bk, bv, ck_h, cv_h, alloc, B, T, T, H.SCALE)
+    rk, bits_k, rv, bits_v = zip(*alloc)
+    for b in range(B):
+        for h in range(len(alloc)):
+            s0, s1, w = codec.record_slice(rv, bits_v, B, T, h, b, 0, T)
+            vhat = codec.decode_records(cv_h[s0:s1].reshape(T, w), rv[h], bits_v[h]) @ bv[h].astype(np.float64).T
+            mean = vhat.mean(axis=0)
+            for i in range(g):
+                assert np.abs(ref[b, h * g + i] - mean).max() <= 1e-9 * np.abs(mean).max()
+    lay = K.Layout(len(alloc), len(alloc) * g, B, T, alloc)
+    for split in (0, 256):
+        got = _attend(K, lay, q, T, bk, bv, H.u32_dev(ck_h), H.u32_dev(cv_h), split)
+        err = H.rel_err_per_head(got, ref)
+        say(f"  split={split} max rel err {err:.3e}")
+        assert err <= REL_TOL
+
+
 def _near_basis_nullspace(P, n, seed, dtype):
     """Tokens almost orthogonal to the span of P: coordinates of the order of the
     float32 error bound, so that most header and code decisions are near a boundary
