@@ -109,6 +109,62 @@ def test_vq_encode_matches_oracle(K, alloc, dtype):
     say(f"  records match ({ties} classified ties)")
 
 
+def _edge_tokens(B, hkv, n, seed, dtype):
+    """Zero tokens (scale 0: every coefficient normalises to 0), constant tokens,
+    one non-zero dimension, repeated tokens and tokens of norm 60000, in turn."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((B, hkv, n, 128))
+    for i in range(n):
+        kind = i % 5
+        if kind == 1:
+            x[:, :, i] = 0.5 * (1 + i % 4)
+        elif kind == 2:
+            x[:, :, i, (5 * i) % 128] = 700.0 * (-1) ** i
+        elif kind == 3:
+            x[:, :, i] = np.linspace(-2.0, 2.0, 128)
+        elif kind == 4:
+            z = rng.standard_normal((B, hkv, 128))
+            x[:, :, i] = z * (60000.0 / np.linalg.norm(z, axis=-1, keepdims=True))
+    return x.astype(dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_vq_encode_edge_tokens(K, dtype):
+    """Vector-quantized records of zero, constant, one-hot, repeated and near-limit
+    tokens against the oracle (prefill, then one append)."""
+    say(f"vq encode edge tokens {dtype}")
+    alloc = [(128, 4, 128, 4), (64, 4, 32, 6)]
+    B, hkv, n = 2, len(alloc), 150
+    cap = n + 1
+    rk, bk, rv, bv = zip(*alloc)
+    pk = [_orth(30 + h, r) for h, r in enumerate(rk)]
+    pv = [_orth(40 + h, r) for h, r in enumerate(rv)]
+    cbk = H.random_codebooks(5, rk, bk)
+    cbv = H.random_codebooks(6, rv, bv)
+    lay = _layout(K, alloc, 1, B, cap, cbk, cbv)
+    npdt = np.float32 if dtype == "f32" else np.float16
+    xk, xv = _edge_tokens(B, hkv, n + 1, 7, npdt), _edge_tokens(B, hkv, n + 1, 8, npdt)
+    ck = torch.zeros(K.kv_cache_bytes(lay, 0) // 4, dtype=torch.int32, device="cuda")
+    cv = torch.zeros(K.kv_cache_bytes(lay, 1) // 4, dtype=torch.int32, device="cuda")
+    from oracle import codec
+    basis_k, basis_v = H.dev(codec.concat_bases(pk)), H.dev(codec.concat_bases(pv))
+    K.kv_encode(lay, H.dev(xk[:, :, :n]), H.dev(xv[:, :, :n]), n, 0, basis_k, basis_v, ck, cv)
+    K.kv_append(lay, H.dev(xk[:, :, n]), H.dev(xv[:, :, n]), n, basis_k, basis_v, ck, cv)
+    gk, gv = H.u32_host(ck), H.u32_host(cv)
+    ties = 0
+    for got, ranks, bits, bases, cbs, x in ((gk, rk, bk, pk, cbk, xk), (gv, rv, bv, pv, cbv, xv)):
+        widths = [vq.record_words(r, b) for r, b in zip(ranks, bits)]
+        off = np.concatenate([[0], np.cumsum([B * cap * w for w in widths])]).astype(np.int64)
+        for h, w in enumerate(widths):
+            for b in range(B):
+                s0 = off[h] + b * cap * w
+                recs = got[s0:s0 + cap * w].reshape(cap, w)
+                xs = x[b, h].astype(np.float64)
+                ref = vq.encode_tokens(xs, bases[h], cbs[h], bits[h])
+                ties += H.compare_vq_records(recs, ref, xs, bases[h], ranks[h], bits[h], cbs[h], f"h{h} b{b}")
+    say(f"  records match ({ties} classified ties)")
+
+
 # ------------------------------------------------------------------ attention
 VQ_CASES = [
     # allocation, g, batch, tokens, split
