@@ -590,10 +590,16 @@ def phase_stamps(K, wl, reps=20, warmup=200, block=4096):
         loop_end = rel[:, 2:6]
         tl.append([0.0, rel[:, 0].max(), rel[:, 1].max(), np.median(loop_end.mean(1)), loop_end.max(),
                    rel[:, 6].max(), rel[:, 7].max(), rel[s_[:, 8] > 0, 8].max()])
+        app0 = s_[:, 11] > 0  # appending workgroups: their projection starts after the encode
         durs = {
             "start after the first workgroup": rel[:, 0],
             "query projection (and first tile copies issued)": rel[:, 1] - rel[:, 0],
-            "  basis and query loads, first tile copies issued": (rel[:, 24] - rel[:, 0])[s_[:, 24] > 0],
+            "  to the start of the projection (head, split and buffer set-up)": (rel[:, 28] - rel[:, 0])[~app0],
+            "    head and its descriptor": (rel[:, 29] - rel[:, 0])[~app0],
+            "    split bounds": (rel[:, 30] - rel[:, 29])[~app0],
+            "    buffers and tile areas": (rel[:, 31] - rel[:, 30])[~app0],
+            "    format dispatch to the projection start": (rel[:, 28] - rel[:, 31])[~app0],
+            "  basis and query loads, first tile copies issued": (rel[:, 24] - rel[:, 28])[~app0],
             "  queries staged (their loads complete)": (rel[:, 25] - rel[:, 24])[s_[:, 24] > 0],
             "  projection (basis loads complete)": (rel[:, 26] - rel[:, 25])[s_[:, 24] > 0],
             "  exponents and sums": (rel[:, 27] - rel[:, 26])[s_[:, 24] > 0],

@@ -611,7 +611,7 @@ constexpr int kMergeChunk = 16;  // splits whose loads one merging thread has in
 // for the next call.
 __device__ inline void merge_splits(const AttendArgs& a, int h, int b, bool reset) {
   const int tid = threadIdx.x;
-  const int g = a.group, ns = a.heads.h[h].ns;
+  const int g = a.group, ns = head_desc(a.heads, h).ns;
   const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
   // item = (query head, four output dimensions); two threads per item when they fit
   const int items = g * (kHeadDim / 4);
@@ -701,8 +701,9 @@ __device__ inline void merge_splits(const AttendArgs& a, int h, int b, bool rese
 // (merging workgroup only), 9 hardware id, 10 XCC id, 11 fused append done, 12 wave
 // partials staged in LDS, 13 wave merge done, 14 back-projection stored (issued),
 // 16-19 per wave: its partial written to LDS, 20-23 per wave: its P_V row loads issued;
-// query projection (wave 0): 24 loads and first copies issued, 25 queries staged,
-// 26 projected, 27 exponents and sums done.
+// query projection (wave 0): 28 start, 24 loads and first copies issued, 25 queries
+// staged, 26 projected, 27 exponents and sums done; set-up: 29 head found, 30 split
+// bounds, 31 buffers set (before the fused append).
 // Other builds compile none of it.
 constexpr int kStampWords = 32;
 #ifdef KVTC_STAMPS
@@ -818,7 +819,7 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = c.h, b = c.b, g = c.g;
-  const HeadDesc& hd = a.heads.h[h];
+  const HeadDesc hd = head_desc(a.heads, h);
   const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
   float* qs = c.stage;                    // [128][GM] raw queries, row-major over the head dimension
   float* qt = c.stage + GM * kHeadDim;    // [g][kMaxRank] projected
@@ -827,6 +828,7 @@ __device__ __attribute__((always_inline)) inline void project_query(const Attend
   const int rpg = kHeadDim / rg;          // rows per group (r_K / 2)
   const int jj = lane % cw, rgi = lane / cw;
   const int j = wave * cw + jj;
+  if (tid == 0) KVTC_STAMP(c.stamp, 28);
   const float* col = a.basis_k + hd.qoff_k + (int64_t)(rgi * rpg) * rk + j;
   // every load in flight before the first use: the queries (used first), then the
   // column segment, then the first tile copies
@@ -1061,6 +1063,39 @@ __host__ __device__ inline int split_slack(int nq, int ns) {
   return e < 2 ? 2 : (e > 8 ? 8 : e);
 }
 
+// Entry h of the first-workgroup table (16-bit entries, read through the 32-bit word
+// that holds them: a scalar load).
+__device__ inline int wg0_entry(const AttendArgs& a, int h) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(a.wg0)[h >> 1];
+  return (int)((h & 1) ? w >> 16 : w & 0xFFFFu);
+}
+
+// The KV head of workgroup wr of a sequence's run: the last head whose first
+// workgroup wg0[h] <= wr, i.e. the number of heads h >= 1 with wg0[h] <= wr (the
+// table is non-decreasing).  The table's 32-bit words are scalar loads issued
+// together and counted with scalar compares; a search through the 16-bit entries
+// would take one dependent vector load per head.
+__device__ inline int head_of_workgroup(const AttendArgs& a, int wr) {
+  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(a.wg0);
+  const int nkv = a.n_kv_heads;
+  int h = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxKvHeads / 4; ++i) {
+    const uint32_t w = w2[i];
+    h += (2 * i >= 1 && 2 * i < nkv && (int)(w & 0xFFFFu) <= wr) ? 1 : 0;
+    h += (2 * i + 1 < nkv && (int)(w >> 16) <= wr) ? 1 : 0;
+  }
+  if (nkv > kMaxKvHeads / 2) {
+#pragma unroll
+    for (int i = kMaxKvHeads / 4; i < kMaxKvHeads / 2; ++i) {
+      const uint32_t w = w2[i];
+      h += (2 * i < nkv && (int)(w & 0xFFFFu) <= wr) ? 1 : 0;
+      h += (2 * i + 1 < nkv && (int)(w >> 16) <= wr) ? 1 : 0;
+    }
+  }
+  return h;
+}
+
 // ----------------------------------------------------------------- kernel body
 // One-dimensional grid of 256-thread workgroups; GM bounds the GQA group (g <= GM).
 // Sequence b takes workgroups [b W, (b + 1) W) with W = wg_per_row: head h the
@@ -1088,18 +1123,18 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   const int WA = tile_lds_words(a.kbuf_words, a.vbuf_words, a.nbuf, GM);
   const int b = (int)blockIdx.x / a.wg_per_row;
   const int wr = (int)blockIdx.x - b * a.wg_per_row;
-  int h = 0;
-  while (h + 1 < a.n_kv_heads && (int)a.wg0[h + 1] <= wr) ++h;
-  const int split = wr - (int)a.wg0[h];
+  const int h = head_of_workgroup(a, wr);
+  const int split = wr - wg0_entry(a, h);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the token loop scalar
-  const HeadDesc& hd = a.heads.h[h];
+  const HeadDesc hd = head_desc(a.heads, h);
   const int ns = hd.ns;
   const int g = __builtin_amdgcn_readfirstlane(a.group);
   const int rv = __builtin_amdgcn_readfirstlane(hd.rv);
   const int bv = __builtin_amdgcn_readfirstlane(hd.bv);
   const int NT = rv / 16;
   const int64_t bq0 = (int64_t)b * a.n_q_heads + (int64_t)h * g;
+  if (tid == 0) KVTC_STAMP(stamp, 29);
 
   float* ml = lds;                                    // per wave: m[16] l[16] c[16]; then the flag word
   float* scores = lds + kCommonWords;                 // per wave: score_words(GM)
@@ -1132,6 +1167,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   c.t_begin = s_begin + wave * wq;
   c.t_end = c.t_begin + wq;
   if (c.t_end > n_tok) c.t_end = n_tok;
+  if (tid == 0) KVTC_STAMP(stamp, 30);
   c.split_begin = s_begin;
   c.wave_tokens = wq;
   c.n_tok = n_tok;
@@ -1205,6 +1241,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
     if (tid == 0) KVTC_STAMP(stamp, 11);
   }
 
+  if (tid == 0) KVTC_STAMP(stamp, 31);
   WaveState<GM> st;
   run(c, st);
   wait_tiles();

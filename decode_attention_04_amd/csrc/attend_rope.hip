@@ -182,7 +182,7 @@ __device__ __attribute__((always_inline)) inline void rope_k_tile(const uint32_t
 template <int GM>
 __device__ __attribute__((always_inline)) inline void rope_tiles(const AttendArgs& a, const WaveCtx& c,
                                                                  WaveState<GM>& st) {
-  const HeadDesc& hd = a.heads.h[c.h];
+  const HeadDesc hd = head_desc(a.heads, c.h);
   const int rk = __builtin_amdgcn_readfirstlane(hd.rk), rv = __builtin_amdgcn_readfirstlane(hd.rv);
   const int bk = __builtin_amdgcn_readfirstlane(hd.bk), bv = __builtin_amdgcn_readfirstlane(hd.bv);
   const int wk = hd.wk, wv = hd.wv;

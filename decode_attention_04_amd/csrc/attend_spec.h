@@ -153,7 +153,7 @@ __device__ __attribute__((always_inline)) inline void spec_tiles(const AttendArg
   __global__ __launch_bounds__(256, 3) void attend_##NAME##_kernel(AttendArgs a) {                  \
     constexpr int kHdr = (HDR);                                                                      \
     attend_body<GM>(a, [&](const WaveCtx& c, WaveState<GM>& st) {                                    \
-      switch (__builtin_amdgcn_readfirstlane(a.heads.h[c.h].spec)) {                                \
+      switch (__builtin_amdgcn_readfirstlane(head_desc(a.heads, c.h).spec)) {                                \
         LIST(KVTC_SPEC_CASE) default : break;                                                        \
       }                                                                                              \
     });                                                                                              \

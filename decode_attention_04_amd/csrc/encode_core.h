@@ -91,11 +91,14 @@ __device__ __attribute__((always_inline)) inline void encode_token_128(const T* 
   // lane layout: four consecutive columns per lane, one row group per 32 lanes
   const int c4 = t % 32, rg = t / 32;
   const bool active = 4 * c4 < r;
+  // lanes past the rank re-read columns 0..3 and drop them: with no load conditional,
+  // a batch's loads are all in flight before the first use (a load under a lane mask
+  // is followed by its own wait)
+  const int col = active ? 4 * c4 : 0;
   constexpr int kHalf = kGroupRows / 2;  // rows loaded per batch (keeps 64 VGPRs of the basis live)
   float4 p[kHalf];
 #pragma unroll
-  for (int k = 0; k < kHalf; ++k)
-    if (active) p[k] = *(const float4*)(P + (int64_t)(rg * kGroupRows + k) * r + 4 * c4);
+  for (int k = 0; k < kHalf; ++k) p[k] = *(const float4*)(P + (int64_t)(rg * kGroupRows + k) * r + col);
   s.xs[t] = load_f64(x + t);
   sync();
   if (active) {
@@ -104,7 +107,7 @@ __device__ __attribute__((always_inline)) inline void encode_token_128(const T* 
     for (int half = 0; half < 2; ++half) {
       if (half == 1) {
 #pragma unroll
-        for (int k = 0; k < kHalf; ++k) p[k] = *(const float4*)(P + (int64_t)(rg * kGroupRows + kHalf + k) * r + 4 * c4);
+        for (int k = 0; k < kHalf; ++k) p[k] = *(const float4*)(P + (int64_t)(rg * kGroupRows + kHalf + k) * r + col);
       }
 #pragma unroll
       for (int k = 0; k < kHalf; ++k) {

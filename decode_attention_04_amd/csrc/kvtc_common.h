@@ -79,6 +79,19 @@ struct HeadTable {
   HeadDesc h[kMaxKvHeads];
 };
 
+// Head h's descriptor from a kernel-argument table, read as 32-bit words: a
+// uniform h makes them scalar loads, issued together (one round trip), where the
+// 8- and 16-bit fields read in place would each be a vector load of its own.
+__device__ inline HeadDesc head_desc(const HeadTable& t, int h) {
+  struct Words {
+    uint32_t w[sizeof(HeadDesc) / 4];
+  } x;
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(&t.h[h]);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(HeadDesc) / 4); ++i) x.w[i] = p[i];
+  return __builtin_bit_cast(HeadDesc, x);
+}
+
 // Where the records of a sequence live within its head's cache region: contiguous
 // (bt == null: token t of sequence b is record b * capacity + t) or paged (token t
 // in pool page bt[b * pages_per_seq + t / page], slot t % page; the region is the

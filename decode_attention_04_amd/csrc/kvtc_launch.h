@@ -47,7 +47,7 @@ struct AttendArgs {
   int64_t split_tokens;
   int32_t n_splits;    // the largest per-head split count: the stride of `part`
   int32_t wg_per_row;  // workgroups per sequence: the sum of the heads' split counts
-  uint16_t wg0[kMaxKvHeads];  // first workgroup of head h within a sequence's run
+  alignas(4) uint16_t wg0[kMaxKvHeads];  // first workgroup of head h within a sequence's run (read as 32-bit pairs)
   int32_t n_kv_heads;
   int32_t n_q_heads;
   int32_t group;
