@@ -1057,7 +1057,9 @@ __device__ __attribute__((always_inline)) inline void p_operands(const float* S,
 
 // Quanta the last split of a (sequence, KV head) gives up to the others: half the
 // quanta of an average split, at least 2 and at most 8 (the encode of an appended
-// token costs about 8-9 quanta of streaming; a split of few quanta cannot absorb it).
+// token and the later start of the split's query projection cost about 5-6 quanta of
+// streaming, yet at 128K a cap of 8 measured ~0.6 us per step faster than 6; a split
+// of few quanta cannot absorb it).
 __host__ __device__ inline int split_slack(int nq, int ns) {
   const int e = nq / (2 * ns);
   return e < 2 ? 2 : (e > 8 ? 8 : e);
@@ -1148,7 +1150,7 @@ __device__ __attribute__((always_inline)) inline void attend_body(const AttendAr
   // equal shares, and the last split (which holds the newest token, the one a fused
   // append encodes first) is split_slack quanta lighter, about the time that encode
   // and the later start of its query projection take (measured with phase stamps
-  // at 128K: 13 us of encode and a 4 us slower projection, against ~2 us per
+  // at 128K: 9.5 us of encode and a 2 us slower projection, against ~2 us per
   // quantum of a 21-quantum split).  Both entry points use the same splits, so
   // appending in the same launch leaves the result bit for bit unchanged.
   // this sequence's context: n_tokens, or its own length (clamped to [0, n_tokens])

@@ -145,6 +145,53 @@ def test_encode_mixed_allocation_matches_oracle(K, dtype):
                  2, 1100, 37, 1001, dtype)
 
 
+def test_encode_mixed_ranks_stream_ordered(K):
+    """A layout with four ranks encodes them in four launches on the caller's stream.
+    What that stream runs next must see every record: a clone enqueued right behind
+    each encode on a non-default stream (no device-wide synchronisation in between)
+    equals the records encoded on the default stream, and so does a captured graph of
+    the encode, replayed three times with eager work between the replays."""
+    say("encode mixed ranks: stream order, graph replays")
+    wl = W.LLAMA_T32K
+    bk, bv = _mixed_bases(MIXED_ALLOC)
+    hkv, batch, cap, n = len(MIXED_ALLOC), 2, 1100, 1001
+    lay = K.Layout(hkv, hkv, batch, cap, MIXED_ALLOC)
+    kx = np.stack([np.stack([W.tokens(wl, "K", b, h, 0, n, "f16") for h in range(hkv)]) for b in range(batch)])
+    vx = np.stack([np.stack([W.tokens(wl, "V", b, h, 0, n, "f16") for h in range(hkv)]) for b in range(batch)])
+    kd, vd = H.dev(kx, torch.float16), H.dev(vx, torch.float16)
+    pk, pv = H.dev(codec.concat_bases(bk)), H.dev(codec.concat_bases(bv))
+    nk, nv = K.kv_cache_bytes(lay, 0) // 4, K.kv_cache_bytes(lay, 1) // 4
+    dev = torch.device("cuda")
+    ref_k = torch.zeros(nk, dtype=torch.int32, device=dev)
+    ref_v = torch.zeros(nv, dtype=torch.int32, device=dev)
+    K.kv_encode(lay, kd, vd, n, 0, pk, pv, ref_k, ref_v)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    copies = []
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            ck = torch.zeros(nk, dtype=torch.int32, device=dev)
+            cv = torch.zeros(nv, dtype=torch.int32, device=dev)
+            K.kv_encode(lay, kd, vd, n, 0, pk, pv, ck, cv)
+            copies.append((ck.clone(), cv.clone()))
+    side.synchronize()
+    for i, (ck, cv) in enumerate(copies):
+        assert torch.equal(ck, ref_k) and torch.equal(cv, ref_v), f"stream-ordered copy {i} differs"
+    gk = torch.zeros(nk, dtype=torch.int32, device=dev)
+    gv = torch.zeros(nv, dtype=torch.int32, device=dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        K.kv_encode(lay, kd, vd, n, 0, pk, pv, gk, gv)
+    for rep in range(3):
+        gk.zero_()
+        gv.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gk, ref_k) and torch.equal(gv, ref_v), f"graph replay {rep} differs"
+
+
 @pytest.mark.parametrize("n", [2, 15, 16, 17, 63, 65, 129, 257, 513])
 def test_encode_ragged_token_counts(K, n):
     """Token counts around the encoder's 16-token blocks and 64/128-token tiles; nothing
