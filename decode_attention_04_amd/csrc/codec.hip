@@ -89,7 +89,8 @@ __global__ __launch_bounds__(256) void append_kernel(EncodeArgs a) {
 // then takes its tokens eight at a time: every thread forms one coordinate of four of
 // them in float64 in the encoders' fixed order (rows 32q .. 32q+31 in order, then
 // ((g0 + g1) + g2) + g3), and one wave per token runs the append's vector quantizer
-// on them, so the records are the append's bit for bit.
+// on them (the same scale, inputs and search, with each lane's codewords in
+// registers), so the records are the append's bit for bit.
 constexpr int kVqTile = 64;
 constexpr int kVqChunk = 8;
 
@@ -98,13 +99,15 @@ inline size_t vq_prefill_lds_bytes(int rmax) {
          (size_t)kHeadDim * rmax * sizeof(float);
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void vq_prefill_kernel(EncodeArgs a) {
+// The tokens of one block.  KC > 0: the pair's 2^bits = KC codewords are read once
+// into registers (lane j holds those of pair j) and every search runs from them;
+// KC = 0: from memory.  The inputs of the next chunk load while the current one is
+// projected and searched.
+template <typename T, int KC>
+__device__ __attribute__((always_inline)) inline void vq_prefill_tokens(const EncodeArgs& a, int h, int tensor, int b,
+                                                                        const HeadDesc& hd) {
   extern __shared__ double vq_lds[];
-  const int h = blockIdx.y >> 1, tensor = blockIdx.y & 1, b = blockIdx.z;
-  const HeadDesc& hd = a.heads.h[h];
   const int B = tensor ? hd.bv : hd.bk;
-  if (!is_vq(B)) return;  // uniform: the whole block
   const int r = tensor ? hd.rv : hd.rk, W = tensor ? hd.wv : hd.wk, bits = code_bits(B);
   const float* P = tensor ? a.basis_v + hd.boff_v : a.basis_k + hd.boff_k;
   const uint32_t* cb = (tensor ? a.cb_v : a.cb_k) + (tensor ? hd.sv : hd.sk);
@@ -115,18 +118,36 @@ __global__ __launch_bounds__(256) void vq_prefill_kernel(EncodeArgs a) {
   uint32_t* codes = (uint32_t*)(xs + kVqChunk * kHeadDim);  // [kVqChunk][64] pair indices
   float* Ps = (float*)(codes + kVqChunk * 64);              // [128][r] the basis
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int K = 1 << bits;
+  uint32_t wreg[KC > 0 ? KC : 1];
+  if constexpr (KC > 0) {
+    const uint32_t* w = cb + (int64_t)(2 * lane < r ? lane : 0) * KC;  // lanes past the pairs re-read pair 0
+#pragma unroll
+    for (int e = 0; e < KC; ++e) wreg[e] = w[e];
+  }
   for (int i = tid; i < kHeadDim * r; i += 256) Ps[i] = P[i];
   const int64_t t_begin = (int64_t)blockIdx.x * kVqTile;
   const int64_t t_end = t_begin + kVqTile < a.n_tokens ? t_begin + kVqTile : a.n_tokens;
+  // inputs of one chunk: element tid + 256 m of [kVqChunk][128], zero past the tokens
+  constexpr int kPer = kVqChunk * kHeadDim / 256;
+  float xv[kPer];
+  auto fetch = [&](int64_t t0) {
+    const int nt = t_end - t0 < kVqChunk ? (int)(t_end - t0) : kVqChunk;
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int i = tid + 256 * m, k = i / kHeadDim;
+      xv[m] = k < nt ? (float)load_f64(xu + (t0 + k) * kHeadDim + (i - k * kHeadDim)) : 0.0f;
+    }
+  };
+  fetch(t_begin);
   // this thread's coordinate j of tokens 4 k0 .. 4 k0 + 3 of a chunk: one basis load serves four
   const int j = tid & 127, k0 = tid >> 7;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += kVqChunk) {
     const int nt = t_end - t0 < kVqChunk ? (int)(t_end - t0) : kVqChunk;
-    for (int i = tid; i < kVqChunk * kHeadDim; i += 256) {
-      const int k = i / kHeadDim;
-      xs[i] = k < nt ? (float)load_f64(xu + (t0 + k) * kHeadDim + (i - k * kHeadDim)) : 0.0f;
-    }
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) xs[tid + 256 * m] = xv[m];
     __syncthreads();  // inputs (and, on the first chunk, the basis) in LDS
+    if (t0 + kVqChunk < t_end) fetch(t0 + kVqChunk);
     if (j < r) {
       const float* x = xs + 4 * k0 * kHeadDim;
       double g[4][kRowGroups];
@@ -149,18 +170,40 @@ __global__ __launch_bounds__(256) void vq_prefill_kernel(EncodeArgs a) {
     __syncthreads();  // coordinates complete
     for (int k = wave; k < nt; k += 4) {  // wave-uniform: one token per wave at a time
       uint32_t* cw = codes + k * 64;
-      const uint32_t w0 = vq_encode_wave(cs + k * kHeadDim, lane, r, bits, cb, cw);
+      const double* c = cs + k * kHeadDim;
+      const uint32_t rb = vq_scale_bits(c, lane, r);
+      if (2 * lane < r) {
+        double u0, u1;
+        vq_pair_inputs(c, lane, rb, u0, u1);
+        if constexpr (KC > 0) cw[lane] = (uint32_t)vq_nearest_regs<KC>(u0, u1, wreg);
+        else cw[lane] = (uint32_t)vq_nearest(u0, u1, cb + (int64_t)lane * K, K);
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int64_t ri = record_index(a.pg, a.capacity, b, a.pos0 + t0 + k);
       if (ri >= 0) {
         uint32_t* rec = region + ri * W;
-        if (lane == 0) rec[0] = w0;
+        if (lane == 0) rec[0] = rb << 16;
         if (lane < W - 1) rec[1 + lane] = pack_word(cw, r / 2, bits, lane);
       }
     }
     __syncthreads();  // before the next chunk overwrites the inputs, coordinates and codes
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void vq_prefill_kernel(EncodeArgs a) {
+  const int h = blockIdx.y >> 1, tensor = blockIdx.y & 1, b = blockIdx.z;
+  const HeadDesc hd = head_desc(a.heads, h);
+  const int B = tensor ? hd.bv : hd.bk;
+  if (!is_vq(B)) return;  // uniform: the whole block
+  // codewords per pair held in registers for up to 16 (the compiler keeps each one's
+  // float64 halves live across the token loop: 64 codewords would take 256 registers)
+  switch (code_bits(B)) {
+    case 2: vq_prefill_tokens<T, 4>(a, h, tensor, b, hd); break;
+    case 4: vq_prefill_tokens<T, 16>(a, h, tensor, b, hd); break;
+    default: vq_prefill_tokens<T, 0>(a, h, tensor, b, hd); break;
   }
 }
 

@@ -35,40 +35,79 @@ struct EncodeScratch {
 // butterfly over the wave), u = c / rho (0 when rho = 0), and lane j < r/2 picks for
 // pair (2j, 2j + 1) the nearest of its 2^bits codewords cb[j 2^bits + e] (fp16 even |
 // odd << 16) by the float64 distance (u_2j - w0)^2 + (u_2j+1 - w1)^2 (each square and
-// the sum rounded once), the first one on ties, eight codewords' loads at a time.
-// Indices go to codes[j]; returns the header word (fp16 +0 | fp16 rho << 16).  Every
-// encode path calls this, so their records agree bit for bit.
-__device__ inline uint32_t vq_encode_wave(const double* c, int lane, int r, int bits, const uint32_t* cb,
-                                          uint32_t* codes) {
+// the sum rounded once), the first one on ties.  Every encode path takes these steps
+// through the helpers below, so their records agree bit for bit.
+
+// fp16 bits of the token's RMS scale rho (wave-uniform).
+__device__ inline uint32_t vq_scale_bits(const double* c, int lane, int r) {
   const double c0 = lane < r ? c[lane] : 0.0, c1 = lane + 64 < r ? c[lane + 64] : 0.0;
   double sq = __dadd_rn(__dmul_rn(c0, c0), __dmul_rn(c1, c1));
   for (int o = 32; o > 0; o >>= 1) sq = __dadd_rn(sq, __shfl_xor(sq, o));
-  const uint32_t rb = f64_to_f16_rne(__builtin_sqrt(sq / (double)r));
+  return f64_to_f16_rne(__builtin_sqrt(sq / (double)r));
+}
+
+// The normalised coordinates of pair `lane` (lane < r/2).
+__device__ inline void vq_pair_inputs(const double* c, int lane, uint32_t rb, double& u0, double& u1) {
   const double rho = (double)f16_bits_to_f32(rb);
-  const int K = 1 << bits;
-  if (2 * lane < r) {
-    const double u0 = rho > 0.0 ? c[2 * lane] / rho : 0.0;
-    const double u1 = rho > 0.0 ? c[2 * lane + 1] / rho : 0.0;
-    const uint32_t* w = cb + (int64_t)lane * K;
-    double best = __builtin_inf();
-    int bi = 0;
-    for (int e0 = 0; e0 < K; e0 += 8) {
-      uint32_t we[8];
+  u0 = rho > 0.0 ? c[2 * lane] / rho : 0.0;
+  u1 = rho > 0.0 ? c[2 * lane + 1] / rho : 0.0;
+}
+
+// Float64 squared distance of (u0, u1) to codeword w, each square and the sum rounded once.
+__device__ inline double vq_dist(double u0, double u1, uint32_t w) {
+  const double d0 = u0 - (double)f16_bits_to_f32(w & 0xFFFFu);
+  const double d1 = u1 - (double)f16_bits_to_f32(w >> 16);
+  return __dadd_rn(__dmul_rn(d0, d0), __dmul_rn(d1, d1));
+}
+
+// Index of the codeword nearest (u0, u1) among the K >= 4 at w (memory), the first on
+// ties; eight codewords' loads at a time.
+__device__ inline int vq_nearest(double u0, double u1, const uint32_t* w, int K) {
+  double best = __builtin_inf();
+  int bi = 0;
+  for (int e0 = 0; e0 < K; e0 += 8) {
+    uint32_t we[8];
 #pragma unroll
-      for (int u8 = 0; u8 < 8; ++u8) we[u8] = e0 + u8 < K ? w[e0 + u8] : 0u;
+    for (int u8 = 0; u8 < 8; ++u8) we[u8] = e0 + u8 < K ? w[e0 + u8] : 0u;
 #pragma unroll
-      for (int u8 = 0; u8 < 8; ++u8) {
-        if (e0 + u8 >= K) break;  // K >= 4
-        const double d0 = u0 - (double)f16_bits_to_f32(we[u8] & 0xFFFFu);
-        const double d1 = u1 - (double)f16_bits_to_f32(we[u8] >> 16);
-        const double dist = __dadd_rn(__dmul_rn(d0, d0), __dmul_rn(d1, d1));
-        if (dist < best) {
-          best = dist;
-          bi = e0 + u8;
-        }
+    for (int u8 = 0; u8 < 8; ++u8) {
+      if (e0 + u8 >= K) break;
+      const double dist = vq_dist(u0, u1, we[u8]);
+      if (dist < best) {
+        best = dist;
+        bi = e0 + u8;
       }
     }
-    codes[lane] = (uint32_t)bi;
+  }
+  return bi;
+}
+
+// The same search over K codewords held in registers.
+template <int K>
+__device__ inline int vq_nearest_regs(double u0, double u1, const uint32_t (&w)[K]) {
+  double best = __builtin_inf();
+  int bi = 0;
+#pragma unroll
+  for (int e = 0; e < K; ++e) {
+    const double dist = vq_dist(u0, u1, w[e]);
+    if (dist < best) {
+      best = dist;
+      bi = e;
+    }
+  }
+  return bi;
+}
+
+// One token by one wave, codebook in memory: indices to codes[j]; returns the header
+// word (fp16 +0 | fp16 rho << 16).
+__device__ inline uint32_t vq_encode_wave(const double* c, int lane, int r, int bits, const uint32_t* cb,
+                                          uint32_t* codes) {
+  const uint32_t rb = vq_scale_bits(c, lane, r);
+  if (2 * lane < r) {
+    double u0, u1;
+    vq_pair_inputs(c, lane, rb, u0, u1);
+    const int K = 1 << bits;
+    codes[lane] = (uint32_t)vq_nearest(u0, u1, cb + (int64_t)lane * K, K);
   }
   return rb << 16;
 }
