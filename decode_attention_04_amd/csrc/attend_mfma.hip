@@ -11,7 +11,7 @@
 // Code -> fp16 operand without conversion: a b-bit code sitting at bit o <= 10-b
 // of a 16-bit half is the fp16 subnormal  code * 2^(o-24); masking a 32-bit word
 // with the field of the same offset in both halves yields two operands in one
-// VALU op.  The matrix cores take subnormal fp16 inputs exactly, and the 2^(o-24)
+// VALU op.  The matrix cores take subnormal fp16 inputs without flushing them, and the 2^(o-24)
 // factor is folded into the other operand (keys) or the partial (values).
 //
 // Precision: q~ and p*step are split into fp16 hi + lo parts, so products carry
