@@ -7,9 +7,10 @@ relies on, and these tests check against exact rational sums:
 * the prefill encoder's error bound E takes, per instruction, an error of at most
   k u (|C| + sum |p|) with k = 4 (u = 2^-24) for normal fp16 operands, on random
   operands over 16 binades (twice that with accumulators from far below to far
-  above the products, which the encoder does not form), and on encoder-like operands (basis hi/lo parts against Gaussian inputs
-  with outlier channels and subnormal inputs, accumulators of the size of the
-  partial sums); products far below the largest are not dropped;
+  above the products, which the encoder does not form), and on encoder-like
+  operands (basis hi/lo parts against Gaussian inputs with outlier channels and
+  subnormal inputs, accumulators of the size of the partial sums); products far
+  below the largest are not dropped;
 * the decode kernels feed b-bit codes as fp16 subnormals (code * 2^(o - 24)): their
   sums with query or probability parts are within 256 u sum |p| of exact, far inside
   the attention tolerance.
